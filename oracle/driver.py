@@ -44,7 +44,11 @@ def prepare_batch(tree: OracleTree, token_lists: Sequence[Sequence[int]]) -> Bat
         toks = [int(t) for t in toks]
         m, ps, a = tree.match(toks)
         tree.inc_lock(a)
-        ns = tree.alloc(len(toks) - m)
+        try:
+            ns = tree.alloc(len(toks) - m)
+        except OracleError:
+            tree.dec_lock(a)          # a failed request leaves no lock behind
+            raise
         t, last = tree.insert(toks, ps + ns)
         if t != m:
             raise OracleError(f"insert found {t} cached tokens after a match of {m}")
@@ -72,11 +76,17 @@ def decode_alloc(tree: OracleTree, rows: List[List[int]]) -> List[int]:
 
 
 def finish(tree: OracleTree, token_lists: Sequence[Sequence[int]], rows: Sequence[Sequence[int]],
-           last_nodes: Sequence[int]) -> List[int]:
-    """Insert finished sequences (prompt + decoded tokens) and unlock their prompt end nodes."""
+           prompt_lens: Sequence[int], last_nodes: Sequence[int]) -> List[int]:
+    """Insert finished sequences (prompt + decoded tokens) and unlock their prompt end nodes.
+
+    Positions [prompt_len, t) that the insert finds already cached keep the tree's slots;
+    the sequence's own slots for them are returned to the free list (the radix-cache
+    page: the caller frees the duplicate indices reported by insert)."""
     ends = []
-    for toks, row, a in zip(token_lists, rows, last_nodes):
-        _, end = tree.insert(list(toks), list(row))
+    for toks, row, plen, a in zip(token_lists, rows, prompt_lens, last_nodes):
+        t, end = tree.insert(list(toks), list(row))
+        if t > plen:
+            tree.free_slots(list(row)[plen:t])
         tree.dec_lock(a)
         ends.append(end)
     return ends
@@ -114,7 +124,8 @@ def run_workload_host(wl, release_last_batch: bool = True) -> RunLog:
         dec.append(decode_alloc(tree, rows))
     if steps:
         toks = [list(r.tokens) + wl.decode_tokens[:, i].tolist() for i, r in enumerate(wl.batches[-1])]
-        finish(tree, toks, rows, last.last_nodes)
+        plens = [len(r.tokens) for r in wl.batches[-1]]
+        finish(tree, toks, rows, plens, last.last_nodes)
     elif release_last_batch:
         release(tree, last.last_nodes)
     return RunLog(batches, dec, tree.take_evlog(), list(tree.free), tree.evictable,
