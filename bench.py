@@ -1,0 +1,285 @@
+"""Throughput of the prefix-shared KV hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload fewshot_bf16|decode_bf16|longctx_fp8]
+
+A step is one pass of the whole hot path over one batch of synthetic input, with the
+inputs (K/V/Q source rows) already resident in HBM:
+
+  fewshot_bf16 (default; 64 requests sharing a 1,800-token prefix that is cached before
+  the timed region, suffixes U[150, 250], GQA 32/8, d 128, bf16, 200k-slot pool):
+    rt_prepare_extend (match with split, lock, allocate, insert, relock for 64 requests)
+    -> H2D tables -> kv_scatter of the suffix K/V -> extend_attention
+    -> rt_decode_step (one slot per sequence) -> H2D -> kv_scatter -> decode_attention
+    -> rt_finish (insert prompt + decoded token, unlock) -> rt_evict of the batch's private
+       tokens (LRU leaves), so that every step meets the same cached state
+  decode_bf16: one decode step of 512 sequences over 2,048-8,192-token contexts
+  longctx_fp8: extend of 16 x 1,024 tokens over a 32,768-token prefix, then 64 decode steps
+
+Prints one JSON line.  `value` is query tokens (extend rows + decode rows) per second of
+the whole step; `roofline` is the dominant kernel's achieved rate from HIP events on the
+stream the library launches on, against MI355X's published peak; `cpu_baseline` is the
+float64 CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
+# rocprofv3 FETCH_SIZE / WRITE_SIZE of the extend kernel on the default workload, KiB per dispatch
+# (filled from profiles/; null until measured on the current kernel)
+TRAFFIC_KIB = None
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="fewshot_bf16", choices=["fewshot_bf16", "decode_bf16", "longctx_fp8"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=8, help="requests in the oracle's timed sample")
+    return ap.parse_args()
+
+
+class Timer:
+    """HIP events on torch's current stream (the stream every library call is given)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.acc = {}
+        self.pending = []
+
+    def span(self, name):
+        t = self
+        class _S:
+            def __enter__(s):
+                s.a = t.torch.cuda.Event(enable_timing=True)
+                s.b = t.torch.cuda.Event(enable_timing=True)
+                s.a.record()
+            def __exit__(s, *exc):
+                s.b.record()
+                t.pending.append((name, s.a, s.b))
+        return _S()
+
+    def collect(self):
+        self.torch.cuda.synchronize()
+        for name, a, b in self.pending:
+            ms, n = self.acc.get(name, (0.0, 0))
+            self.acc[name] = (ms + a.elapsed_time(b), n + 1)
+        self.pending = []
+
+    def reset(self):
+        self.collect()
+        self.acc = {}
+
+    def avg_ms(self, name):
+        ms, n = self.acc.get(name, (0.0, 0))
+        return ms / n if n else float("nan")
+
+
+def extend_flops(d, hq, prefix_lens, extend_lens):
+    p = np.asarray(prefix_lens, dtype=np.float64)
+    e = np.asarray(extend_lens, dtype=np.float64)
+    pairs = float((e * p + e * (e + 1) / 2).sum())
+    return 4.0 * d * hq * pairs, pairs
+
+
+def kv_row_bytes(shape):
+    eb = {"f32": 4, "bf16": 2, "fp8_e4m3": 1}[shape.pool_dtype]
+    return 2 * shape.hkv * shape.d * eb   # K and V of one token
+
+
+class FewshotBench:
+    """Default workload; see the module docstring."""
+
+    def __init__(self, torch, wl_name="fewshot_bf16"):
+        import workloads
+        from prefix_shared_kv_match_amd.runtime import Engine
+        self.torch = torch
+        self.wl = wl = workloads.make(wl_name)
+        s = wl.shape
+        self.eng = Engine(wl.pool_slots, s.hq, s.hkv, s.d, s.qo_dtype, s.pool_dtype, wl.free_order, "cuda",
+                          wl.k_scale, wl.v_scale, wl.k_inv_scale, wl.v_inv_scale, s.sm_scale)
+        self.steps_dec = int(wl.decode_tokens.shape[0])
+        self.stride = wl.max_len()
+        eng = self.eng
+        dev = torch.device("cuda")
+        # cache the shared prefix (its K/V written to the pool) before anything is timed
+        for r in wl.pre_insert:
+            hb = eng.prepare([r.tokens], self.stride)
+            self._scatter_rows(hb.new_slots, r.rows[hb.prefix_lens[0]:])
+            eng.release(hb)
+        batch = wl.batches[-1]
+        self.batch = batch
+        self.tokens = [r.tokens for r in batch]
+        self.full_tokens = [np.concatenate([r.tokens, wl.decode_tokens[:, i]]) for i, r in enumerate(batch)]
+        self.prompt_lens = [len(r.tokens) for r in batch]
+        # source rows of the batch's new tokens: every step matches exactly the cached prefix
+        pl = np.array([len(wl.pre_insert[0].tokens) if wl.pre_insert else 0] * len(batch))
+        self.new_rows = np.concatenate([r.rows[p:] for r, p in zip(batch, pl)])
+        self.k_src, self.v_src = self._src(wl.values.k(self.new_rows)), self._src(wl.values.v(self.new_rows))
+        self.q = self._src(wl.values.q(self.new_rows))
+        self.o = torch.empty_like(self.q)
+        self.dk = [self._src(wl.values.k(wl.decode_rows[s])) for s in range(self.steps_dec)]
+        self.dv = [self._src(wl.values.v(wl.decode_rows[s])) for s in range(self.steps_dec)]
+        self.dq = [self._src(wl.values.q(wl.decode_rows[s])) for s in range(self.steps_dec)]
+        self.do = torch.empty_like(self.dq[0]) if self.steps_dec else None
+        B = len(batch)
+        self.max_len = max(self.prompt_lens) + self.steps_dec
+        if self.steps_dec:
+            self.ws, self.chunk = eng.decode_workspace(B, self.max_len)
+        # device tables, refreshed from pinned host copies every step
+        self.r2t_dev = torch.empty((B, self.stride), dtype=torch.int32, device=dev)
+        self.dec_slots_dev = torch.empty(B, dtype=torch.int32, device=dev)
+        self.seq_dev = torch.empty(B, dtype=torch.int32, device=dev)
+        self.timer = Timer(torch)
+        self.n_private = None
+        self.last_tables = None
+
+    def _src(self, a):
+        t = self.torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+        if self.wl.shape.qo_dtype == "bf16":
+            t = t.to(self.torch.bfloat16)
+        return t.to("cuda")
+
+    def _scatter_rows(self, slots, rows):
+        if rows.size == 0:
+            return
+        sl = self.torch.from_numpy(np.ascontiguousarray(slots, dtype=np.int32)).to("cuda")
+        self.eng.scatter(sl, self._src(self.wl.values.k(rows)), self._src(self.wl.values.v(rows)))
+
+    def step(self):
+        import prefix_shared_kv_match_amd as pkv
+        torch, eng, T = self.torch, self.eng, self.timer
+        hb = eng.prepare(self.tokens, self.stride)                       # host: a1-a5
+        dt = eng.device_tables(hb)                                       # H2D tables + plan
+        with T.span("kv_scatter"):
+            eng.scatter(dt["new_slots"], self.k_src, self.v_src)
+        if self.wl.extend_attention:
+            with T.span("extend_attention"):
+                eng.extend(dt, self.q, self.o)
+        for s in range(self.steps_dec):
+            slots = eng.decode_alloc(hb)                                 # host: one slot per sequence
+            self.r2t_dev.copy_(torch.from_numpy(hb.req_to_token), non_blocking=False)
+            self.dec_slots_dev.copy_(torch.from_numpy(slots))
+            self.seq_dev.copy_(torch.from_numpy(hb.seq_lens))
+            with T.span("kv_scatter_decode"):
+                eng.scatter(self.dec_slots_dev, self.dk[s], self.dv[s])
+            with T.span("decode_attention"):
+                eng.decode(self.dq[s], self.r2t_dev, self.seq_dev, self.max_len, self.ws, self.chunk, self.do)
+        if self.steps_dec:
+            eng.finish(hb, self.full_tokens, self.prompt_lens)
+        else:
+            eng.release(hb)
+        n_private = int(hb.extend_lens.sum()) + self.steps_dec * hb.n
+        pkv.rt_evict(eng.tree, n_private)                                # keep only the shared prefix cached
+        self.last_tables = hb
+        return int(hb.extend_lens.sum()) + self.steps_dec * hb.n
+
+
+def cpu_baseline(wl, hb, n_req):
+    """The float64 oracle on a bounded sample: the extend rows of the first n_req requests."""
+    from oracle import attention as oa
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    reqs = wl.batches[-1][:n_req]
+    t0 = time.perf_counter()
+    rows = 0
+    for i, r in enumerate(reqs):
+        p = int(hb.prefix_lens[i])
+        oa.extend_rows(wl, r, p)
+        rows += len(r.tokens) - p
+    dt = time.perf_counter() - t0
+    return {"value": rows / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"float64 numpy oracle: extend rows of the first {len(reqs)} of {len(wl.batches[-1])} "
+                      f"requests ({rows} query tokens over their full contexts), {dt:.1f} s"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {a.gpus} is not supported by this build "
+              f"(see the sharding paragraph of the design notes)", file=sys.stderr)
+        return 2
+    import torch
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 2
+    import prefix_shared_kv_match_amd as pkv
+    pkv.lib()
+    b = FewshotBench(torch, a.workload)
+    wl = b.wl
+    for _ in range(a.warmup):
+        b.step()
+    b.timer.reset()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    tokens = 0
+    for _ in range(a.steps):
+        tokens += b.step()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    b.timer.collect()
+    hb = b.last_tables
+    s = wl.shape
+    flops, pairs = extend_flops(s.d, s.hq, hb.prefix_lens, hb.extend_lens)
+    kv_tok = kv_row_bytes(s)
+    ext_ms = b.timer.avg_ms("extend_attention")
+    dec_ms = b.timer.avg_ms("decode_attention")
+    gathered_ext = float((hb.prefix_lens.astype(np.float64) + hb.extend_lens).sum()) * kv_tok
+    kernels = {}
+    if wl.extend_attention:
+        kernels["extend_attention"] = {
+            "ms": ext_ms, "tflops": flops / ext_ms / 1e9, "frac_mfma": flops / ext_ms / 1e9 / PEAK_BF16_TFLOPS,
+            "kv_gathered_gbps": gathered_ext / ext_ms / 1e6, "flops": flops, "pairs": pairs,
+            "query_tokens": int(hb.extend_lens.sum())}
+    if b.steps_dec:
+        ctx = hb.seq_lens.astype(np.float64)
+        dec_bytes = float(ctx.sum()) * kv_tok
+        kernels["decode_attention"] = {
+            "ms": dec_ms, "kv_gathered_gbps": dec_bytes / dec_ms / 1e6,
+            "frac_hbm": dec_bytes / dec_ms / 1e6 / PEAK_HBM_GBPS, "bytes": dec_bytes,
+            "tflops": 4.0 * s.d * s.hq * float(ctx.sum()) / dec_ms / 1e9}
+    sc_ms = b.timer.avg_ms("kv_scatter")
+    n_new = int(hb.extend_lens.sum())
+    src_b = 2 * s.hkv * s.d * (4 if s.qo_dtype == "f32" else 2)
+    kernels["kv_scatter"] = {"ms": sc_ms, "gbps": n_new * (src_b + kv_tok) / sc_ms / 1e6}
+    if wl.extend_attention:
+        dom, bound = "extend_attention", "mfma"
+        achieved, peak, unit = kernels[dom]["tflops"], PEAK_BF16_TFLOPS, "TFLOP/s"
+    else:
+        dom, bound = "decode_attention", "hbm"
+        achieved, peak, unit = kernels[dom]["kv_gathered_gbps"], PEAK_HBM_GBPS, "GB/s"
+    out = {
+        "metric": "extend+decode attention tokens/s, TFLOP/s & KV GB/s vs MI355X roofline",
+        "value": tokens / el, "unit": "tokens/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": el / a.steps * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if s.qo_dtype == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": wl.name, "requests": hb.n, "query_tokens_per_step": tokens // a.steps,
+                   "hq": s.hq, "hkv": s.hkv, "head_dim": s.d, "pool_dtype": s.pool_dtype,
+                   "pool_slots": wl.pool_slots, "decode_steps_per_step": b.steps_dec},
+        "roofline": {"bound": bound, "kernel": dom, "achieved": achieved, "peak": peak, "unit": unit,
+                     "frac": achieved / peak, "traffic": TRAFFIC_KIB},
+        "kernels": kernels,
+    }
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, hb, a.cpu_sample)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

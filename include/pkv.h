@@ -1,0 +1,244 @@
+/*
+ * pkv.h - C ABI of libpkv.so: prefix-shared KV reuse for attention on MI355X (gfx950).
+ *
+ * Two halves:
+ *   rt_*   a host radix tree over token ids whose values are KV slot indices of a
+ *          token-granular KV pool, plus the pool's slot allocator.  Host memory only.
+ *   pkv_*  HIP kernels that write new tokens' K/V into pool slots and run attention
+ *          over K/V gathered through per-request slot rows.  Device memory only.
+ *
+ * Sources of the operations (the pages this library follows):
+ *   [RC]  "[SGLang] RadixAttention: Radix Tree 기반 프리픽스 캐싱의 핵심" (radix-cache
+ *         walkthrough): TreeNode fields, match_prefix with node split, _split_node,
+ *         _insert_helper, the eviction heap, inc_lock_ref, and the worked example tree.
+ *   [EX]  "論文解説: Efficiently Programming Large Language Models using SGLang"
+ *         (RadixAttention explainer): the matched length is the longest common prefix;
+ *         only the unmatched rest is prefilled; LRU eviction of unreferenced nodes.
+ *   [OV]  "SGLang: Treating LLM Interactions as Programs ..." (overview): runtime flow
+ *         "prefix match -> reuse / compute missing KV -> insert -> LRU evict", and the
+ *         feedback of generated tokens into insertion.
+ *   Attention is textbook scaled-dot-product attention (the pages do not state it):
+ *   o_i = softmax(scale * q_i K[0..i]^T) V[0..i], query head h reads kv head
+ *   h / (hq / hkv).
+ *
+ * Conventions
+ *   - Every call returns >= 0 on success (0 or a count) and a negative PKV_ERR_* code on
+ *     failure; nothing throws across the ABI.  pkv_last_error() returns a message for
+ *     the calling thread's last failure (valid until that thread's next failing call).
+ *   - rt_tree is not thread safe: one tree per thread, or external locking.
+ *   - Slot ids are int32 in [0, num_slots).  Node ids are int64; 0 is the root; ids are
+ *     never reused, so a stale id (an evicted node) is reported as PKV_ERR_NODE.
+ *   - Ownership of slots: a slot is free (in the allocator), in flight (returned by
+ *     rt_alloc, owned by the caller) or cached (held by a tree node).  rt_insert moves
+ *     the in-flight slots of the newly inserted positions to cached; eviction moves
+ *     cached slots back to free; rt_free moves in-flight slots back to free.
+ *   - Kernel entry points take device pointers owned by the caller and enqueue work on
+ *     `stream` (a hipStream_t passed as void*, NULL = the null stream); they return
+ *     after enqueueing.  Buffers must stay alive until that work completes.  They never
+ *     allocate device memory.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_OK 0
+#define PKV_ERR_INVAL (-1)       /* bad argument (null pointer, size, capacity)              */
+#define PKV_ERR_OOM (-2)         /* not enough free slots even after evicting every unlocked leaf */
+#define PKV_ERR_LOCK (-3)        /* unlock of a node whose lock reference is already 0       */
+#define PKV_ERR_SLOT (-4)        /* slot out of range, or in the wrong ownership state       */
+#define PKV_ERR_NODE (-5)        /* node id not live                                         */
+#define PKV_ERR_HIP (-6)         /* a HIP runtime call failed                                */
+#define PKV_ERR_UNSUPPORTED (-7) /* shape or dtype combination with no kernel                */
+#define PKV_ERR_INTERNAL (-8)
+
+typedef struct rt_tree rt_tree;
+typedef int64_t rt_node;
+
+const char* pkv_last_error(void);
+int pkv_version(void);
+
+/* ----------------------------------------------------------------------------------
+ * Radix tree and slot allocator (host)
+ * -------------------------------------------------------------------------------- */
+
+/* Create a tree over a pool of `num_slots` KV slots.  The allocator's free list is
+ * `free_order[0..n_free)` (head first; distinct slots in range); NULL means
+ * 0..num_slots-1 in order with n_free = num_slots.  Slots not listed are never handed
+ * out.  The root node (id 0) carries lock reference 1 and is never evicted [RC figure
+ * "Radix Tree 구조도"].  Logical clock starts at 0; node ids at 1. */
+int rt_create(int64_t num_slots, const int32_t* free_order, int64_t n_free, rt_tree** out);
+void rt_destroy(rt_tree* t);
+
+/* Longest cached prefix of key[0..n) [RC "프리픽스 매칭: match_prefix"; EX matching formula].
+ * Walks whole children keyed by their first token; if a child matches only partly
+ * (including when the key ends inside it) the child is split at the match length
+ * [RC "노드 분할"] and the walk stops.  Advances the logical clock by one and stamps
+ * every visited node (and both halves of a split) with it.  Writes the matched slots
+ * to out_slots (capacity n) and the id of the node ending the match to *out_last
+ * (0 = root when nothing matched).  Returns the matched length. */
+int64_t rt_match_prefix(rt_tree* t, const int32_t* key, int64_t n, int32_t* out_slots, rt_node* out_last);
+
+/* Insert key -> slots [RC "삽입: _insert_helper"].  Walks and splits like match (clock
+ * advanced by one, visited nodes stamped); the unmatched rest becomes a new leaf that
+ * takes slots[m..n), which must be in flight; the new leaf's tokens count as evictable.
+ * Returns the length m that was already cached; slots[0..m) are then duplicates that
+ * stay owned by the caller (free them with rt_free).  *out_last = node ending the key. */
+int64_t rt_insert(rt_tree* t, const int32_t* key, const int32_t* slots, int64_t n, rt_node* out_last);
+
+/* Lock references [RC "참조 카운트: lock_ref"]: +1 / -1 on every node from `node` up to,
+ * not including, the root.  On 0 -> 1 a node's tokens move from the evictable to the
+ * protected count (and back on 1 -> 0).  Locked nodes are never evicted.  Unlocking a
+ * node whose count is 0 fails with PKV_ERR_LOCK and changes nothing. */
+int rt_inc_lock_ref(rt_tree* t, rt_node node);
+int rt_dec_lock_ref(rt_tree* t, rt_node node);
+
+/* Evict at least num_tokens tokens [RC "Eviction 전략"; EX "LRU Evictionポリシー"]:
+ * repeatedly remove the unlocked leaf with the smallest (access time, node id), append
+ * its slots to the free list's tail in key order, log it, and consider its parent once
+ * the parent is an unlocked leaf.  Whole leaves only, so it may free more than asked.
+ * Returns the number of tokens evicted (less than asked if nothing else is evictable). */
+int64_t rt_evict(rt_tree* t, int64_t num_tokens);
+
+/* Hand out n slots from the free list's head (first in, first out).  If fewer than n
+ * are free it first evicts (n - free) tokens; if still short, returns PKV_ERR_OOM
+ * (evictions already done stay done).  Slots become in flight.  Returns n. */
+int64_t rt_alloc(rt_tree* t, int64_t n, int32_t* out);
+
+/* Return in-flight slots to the free list's tail, in the order given. */
+int rt_free(rt_tree* t, const int32_t* slots, int64_t n);
+
+/* Eviction log since the last take: node ids, their lengths, and the freed slots in
+ * eviction order.  rt_eviction_log_size reports the sizes; rt_take_eviction_log copies
+ * and clears (PKV_ERR_INVAL, nothing cleared, if a capacity is too small). */
+int rt_eviction_log_size(const rt_tree* t, int64_t* n_nodes, int64_t* n_slots);
+int rt_take_eviction_log(rt_tree* t, int64_t* node_ids, int64_t* node_lens, int64_t nodes_cap,
+                         int32_t* slots, int64_t slots_cap);
+
+int64_t rt_evictable_size(const rt_tree* t);   /* tokens in unlocked nodes  */
+int64_t rt_protected_size(const rt_tree* t);   /* tokens in locked nodes    */
+int64_t rt_free_size(const rt_tree* t);        /* slots on the free list    */
+int64_t rt_clock(const rt_tree* t);
+/* Copy the free list, head first, into out (capacity cap).  Returns its length. */
+int64_t rt_copy_free_list(const rt_tree* t, int32_t* out, int64_t cap);
+/* Serialise every live non-root node, by ascending id, as int64 records
+ * [id, parent, lock_ref, last_access, len, key[len], slots[len]].  Returns the number
+ * of int64 values; writes them only if cap is large enough. */
+int64_t rt_dump(const rt_tree* t, int64_t* out, int64_t cap);
+
+/* Batch driver: the hot path's host steps for one batch of requests, in order.
+ * For request r (tokens[tok_indptr[r] .. tok_indptr[r+1])), length L_r:
+ *   match (split, stamp) -> lock the matched node -> allocate L_r - m_r slots (evicting
+ *   on shortfall) -> insert (tokens, matched slots ++ new slots) -> lock the new end
+ *   node, unlock the matched node.
+ * Outputs (host arrays, caller-owned):
+ *   req_to_token [num_reqs, stride]: row r = all L_r slots (entries past L_r untouched)
+ *   prefix_lens[r] = m_r, extend_lens[r] = L_r - m_r, qo_indptr[0..num_reqs] = prefix
+ *   sums of extend_lens (the rows of q / o / kv_scatter source for each request),
+ *   new_slots[0..sum extend) = the fresh slots in the same row order,
+ *   out_last[r] = node ending request r (locked until rt_release).
+ * Requires stride >= max L_r and new_cap >= sum L_r.  On failure (e.g. PKV_ERR_OOM at
+ * request r) requests before r stay prepared and locked, request r and later have
+ * out_last = -1; release the prepared ones with rt_release.
+ * Returns the total number of new tokens. */
+int64_t rt_prepare_extend(rt_tree* t, int32_t num_reqs, const int32_t* tokens, const int64_t* tok_indptr,
+                          int32_t* req_to_token, int64_t stride, int32_t* prefix_lens,
+                          int32_t* extend_lens, int32_t* qo_indptr, int32_t* new_slots, int64_t new_cap,
+                          rt_node* out_last);
+
+/* Unlock out_last entries of a prepared batch (entries < 0 are skipped). */
+int rt_release(rt_tree* t, const rt_node* nodes, int32_t n);
+
+/* One decode step for `batch` sequences: allocate `batch` slots in one call (evicting on
+ * shortfall); slot b is written to req_to_token[b*stride + seq_lens[b]] and to
+ * out_slots[b], and seq_lens[b] is incremented.  Requires seq_lens[b] < stride. */
+int64_t rt_decode_step(rt_tree* t, int32_t batch, int32_t* req_to_token, int64_t stride, int32_t* seq_lens,
+                       int32_t* out_slots);
+
+/* Finish sequences [OV feedback loop from generated tokens to insertion]: for each i,
+ * insert (tokens_i, req_to_token row i [0..len_i)), free the caller's slots for
+ * positions [prompt_lens[i], m) that the insert found already cached, and unlock
+ * prompt_last[i].  out_end[i] = node ending the full sequence (may be NULL). */
+int rt_finish(rt_tree* t, int32_t n, const int32_t* tokens, const int64_t* tok_indptr,
+              const int32_t* req_to_token, int64_t stride, const int32_t* prompt_lens,
+              const rt_node* prompt_last, rt_node* out_end);
+
+/* ----------------------------------------------------------------------------------
+ * Kernels (device)
+ * -------------------------------------------------------------------------------- */
+
+typedef enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_FP8_E4M3 = 2 } pkv_dtype;
+
+/* Write new tokens' K/V into their pool slots:
+ *   k_pool[slots[i], h, :] = cvt(k_src[i, h, :]),  same for V,  i < n, h < hkv.
+ * Layouts: k_src/v_src [n, hkv, d] row-major in src_dtype; pools [num_slots, hkv, d]
+ * row-major in pool_dtype; slots device int32 [n].
+ * Supported: (F32 -> F32), (BF16 -> BF16) copies, and (BF16 -> FP8_E4M3) quantisation
+ * code = round-to-nearest-even(float32(x * inv_scale[h])) saturated to +-448 (OCP
+ * E4M3, sign kept), with k_inv_scale/v_inv_scale device float32 [hkv].
+ * Slots must be distinct and in [0, num_slots) (duplicates race).  d in {64, 128}. */
+int pkv_kv_scatter(const void* k_src, const void* v_src, int32_t src_dtype, const int32_t* slots, int64_t n,
+                   void* k_pool, void* v_pool, int32_t pool_dtype, int64_t num_slots, int32_t hkv, int32_t d,
+                   const float* k_inv_scale, const float* v_inv_scale, void* stream);
+
+/* Host-side plan for pkv_extend_attention: split each request's extend rows into query
+ * tiles of `tile` tokens and order the tiles by descending work (context length), so
+ * the longest tiles start first.  prefix_lens/extend_lens are HOST arrays [num_reqs].
+ * Writes work items (request, first extend row of the tile) as int32 pairs to
+ * out_work[2*i], out_work[2*i+1]; returns the number of items (PKV_ERR_INVAL if
+ * work_cap is too small; pkv_extend_plan_size gives the exact count). */
+int64_t pkv_extend_plan_size(const int32_t* extend_lens, int32_t num_reqs, int32_t tile);
+int64_t pkv_extend_plan(const int32_t* prefix_lens, const int32_t* extend_lens, int32_t num_reqs, int32_t tile,
+                        int32_t* out_work, int64_t work_cap);
+/* Query-tile size (in tokens) pkv_extend_attention expects for a shape. */
+int32_t pkv_extend_tile(int32_t qo_dtype, int32_t pool_dtype, int32_t hq, int32_t hkv, int32_t d);
+
+/* Extend (prefill of the unmatched suffix over a reused prefix) [EX: only the part
+ * after the matched prefix is computed].  For request r with prefix p = prefix_lens[r]
+ * and e = extend_lens[r] rows starting at q row qo_indptr[r], extend row j (token
+ * position i = p + j), query head h, kv head g = h / (hq / hkv):
+ *   o[qo_indptr[r]+j, h, :] = softmax_k(sm_scale * <q[.., h, :], K[k, g, :]>) V[k, g, :]
+ *   over k = 0..i, with K[k] = k_pool[req_to_token[r*stride + k]] (full over the
+ *   prefix, causal over the suffix).
+ * Layouts: q, o [total_q, hq, d] in qo_dtype (F32 or BF16); pools [num_slots, hkv, d];
+ * req_to_token device int32 [num_reqs, stride]; prefix_lens, extend_lens, qo_indptr
+ * device int32; work device int32 [n_work, 2] from pkv_extend_plan with the tile of
+ * pkv_extend_tile.  fp8 pools: the dequantised value is code * k_scale[g] (v_scale[g]),
+ * device float32 [hkv]; the scale is folded into the float32 logits / output.
+ * Supported: (F32 q/o, F32 pool, d 64 or 128), (BF16 q/o, BF16 or FP8_E4M3 pool,
+ * d 128), hq % hkv == 0.  Softmax and accumulation in float32. */
+int pkv_extend_attention(const void* q, void* o, int32_t qo_dtype, const void* k_pool, const void* v_pool,
+                         int32_t pool_dtype, int64_t num_slots, const float* k_scale, const float* v_scale,
+                         const int32_t* req_to_token, int64_t stride, const int32_t* prefix_lens,
+                         const int32_t* extend_lens, const int32_t* qo_indptr, int32_t num_reqs,
+                         const int32_t* work, int64_t n_work, int32_t hq, int32_t hkv, int32_t d,
+                         float sm_scale, void* stream);
+
+/* Decode: one query token per sequence, the newest one (position seq_lens[b] - 1, its
+ * own K/V included).  Split-K: the context is cut into chunks of `chunk` tokens; one
+ * partial (running max, running sum, unnormalised output) per (sequence, q head, chunk)
+ * goes to the workspace, then a reduce merges the chunks by log-sum-exp:
+ *   M = max_s m_s,  o = sum_s exp(m_s - M) acc_s / sum_s exp(m_s - M) l_s.
+ * Layouts: q, o [batch, hq, d] in qo_dtype; req_to_token device int32 [batch, stride];
+ * seq_lens device int32 [batch], each in [1, max_seq_len].  chunk: tokens per split, a
+ * multiple of 64, or 0 for automatic.  workspace: device memory of at least
+ * pkv_decode_workspace_bytes(batch, hq, d, max_seq_len, chunk) bytes.
+ * Supported shapes as for pkv_extend_attention. */
+size_t pkv_decode_workspace_bytes(int32_t batch, int32_t hq, int32_t d, int32_t max_seq_len, int32_t chunk);
+int32_t pkv_decode_chunk(int32_t batch, int32_t hkv, int32_t max_seq_len);
+int pkv_decode_attention(const void* q, void* o, int32_t qo_dtype, const void* k_pool, const void* v_pool,
+                         int32_t pool_dtype, int64_t num_slots, const float* k_scale, const float* v_scale,
+                         const int32_t* req_to_token, int64_t stride, const int32_t* seq_lens, int32_t batch,
+                         int32_t max_seq_len, int32_t hq, int32_t hkv, int32_t d, float sm_scale, int32_t chunk,
+                         void* workspace, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -1,0 +1,299 @@
+"""prefix_shared_kv_match_amd: prefix-shared KV reuse (radix tree + gathered attention) for MI355X.
+
+Python binding of libpkv.so.  Every function here has the name of the C entry point it
+calls (include/pkv.h) and only marshals arguments: host arrays as numpy, device buffers
+as torch tensors on a ROCm device.  Every step of the path runs in the library; if the
+library is missing, importing the binding functions raises.
+"""
+from __future__ import annotations
+
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+
+from ._capi import PKV_BF16, PKV_F32, PKV_FP8_E4M3, PkvError, check, lib
+
+__all__ = [
+    "PKV_F32", "PKV_BF16", "PKV_FP8_E4M3", "PkvError", "lib",
+    "rt_create", "rt_destroy", "rt_match_prefix", "rt_insert", "rt_inc_lock_ref", "rt_dec_lock_ref",
+    "rt_evict", "rt_alloc", "rt_free", "rt_take_eviction_log", "rt_evictable_size", "rt_protected_size",
+    "rt_free_size", "rt_clock", "rt_copy_free_list", "rt_dump", "rt_prepare_extend", "rt_release",
+    "rt_decode_step", "rt_finish", "pkv_kv_scatter", "pkv_extend_tile", "pkv_extend_plan",
+    "pkv_extend_attention", "pkv_decode_chunk", "pkv_decode_workspace_bytes", "pkv_decode_attention",
+]
+
+import ctypes as C
+
+
+def _i32(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+# ------------------------------------------------------------------------------------------
+# radix tree (host)
+# ------------------------------------------------------------------------------------------
+
+def rt_create(num_slots: int, free_order: Optional[Sequence[int]] = None) -> C.c_void_p:
+    h = C.c_void_p()
+    if free_order is None:
+        check(lib().rt_create(int(num_slots), None, int(num_slots), C.byref(h)))
+    else:
+        fo = _i32(free_order)
+        check(lib().rt_create(int(num_slots), _ptr(fo), fo.size, C.byref(h)))
+    return h
+
+
+def rt_destroy(t) -> None:
+    lib().rt_destroy(t)
+
+
+def rt_match_prefix(t, key) -> Tuple[int, np.ndarray, int]:
+    key = _i32(key)
+    out = np.empty(max(key.size, 1), dtype=np.int32)
+    last = C.c_int64()
+    m = check(lib().rt_match_prefix(t, _ptr(key), key.size, _ptr(out), C.byref(last)))
+    return int(m), out[:m].copy(), int(last.value)
+
+
+def rt_insert(t, key, slots) -> Tuple[int, int]:
+    key, slots = _i32(key), _i32(slots)
+    if key.size != slots.size:
+        raise ValueError("key and slots differ in length")
+    last = C.c_int64()
+    m = check(lib().rt_insert(t, _ptr(key), _ptr(slots), key.size, C.byref(last)))
+    return int(m), int(last.value)
+
+
+def rt_inc_lock_ref(t, node: int) -> None:
+    check(lib().rt_inc_lock_ref(t, int(node)))
+
+
+def rt_dec_lock_ref(t, node: int) -> None:
+    check(lib().rt_dec_lock_ref(t, int(node)))
+
+
+def rt_evict(t, num_tokens: int) -> int:
+    return int(check(lib().rt_evict(t, int(num_tokens))))
+
+
+def rt_alloc(t, n: int) -> np.ndarray:
+    out = np.empty(max(int(n), 1), dtype=np.int32)
+    check(lib().rt_alloc(t, int(n), _ptr(out)))
+    return out[:n]
+
+
+def rt_free(t, slots) -> None:
+    s = _i32(slots)
+    check(lib().rt_free(t, _ptr(s), s.size))
+
+
+def rt_take_eviction_log(t) -> List[Tuple[int, List[int]]]:
+    nn, ns = C.c_int64(), C.c_int64()
+    check(lib().rt_eviction_log_size(t, C.byref(nn), C.byref(ns)))
+    ids = np.empty(max(nn.value, 1), dtype=np.int64)
+    lens = np.empty(max(nn.value, 1), dtype=np.int64)
+    slots = np.empty(max(ns.value, 1), dtype=np.int32)
+    check(lib().rt_take_eviction_log(t, _ptr(ids), _ptr(lens), nn.value, _ptr(slots), ns.value))
+    out, k = [], 0
+    for i in range(nn.value):
+        out.append((int(ids[i]), slots[k:k + lens[i]].tolist()))
+        k += int(lens[i])
+    return out
+
+
+def rt_evictable_size(t) -> int:
+    return int(check(lib().rt_evictable_size(t)))
+
+
+def rt_protected_size(t) -> int:
+    return int(check(lib().rt_protected_size(t)))
+
+
+def rt_free_size(t) -> int:
+    return int(check(lib().rt_free_size(t)))
+
+
+def rt_clock(t) -> int:
+    return int(check(lib().rt_clock(t)))
+
+
+def rt_copy_free_list(t) -> np.ndarray:
+    n = rt_free_size(t)
+    out = np.empty(max(n, 1), dtype=np.int32)
+    check(lib().rt_copy_free_list(t, _ptr(out), n))
+    return out[:n]
+
+
+def rt_dump(t):
+    """Live non-root nodes as (id, parent, lock_ref, last_access, key tuple, slots tuple), by id."""
+    need = check(lib().rt_dump(t, None, 0))
+    buf = np.empty(max(need, 1), dtype=np.int64)
+    check(lib().rt_dump(t, _ptr(buf), need))
+    out, k = [], 0
+    while k < need:
+        nid, par, lock, last, n = (int(x) for x in buf[k:k + 5])
+        key = tuple(int(x) for x in buf[k + 5:k + 5 + n])
+        val = tuple(int(x) for x in buf[k + 5 + n:k + 5 + 2 * n])
+        out.append((nid, par, lock, last, key, val))
+        k += 5 + 2 * n
+    return out
+
+
+def rt_prepare_extend(t, tokens: np.ndarray, tok_indptr: np.ndarray, req_to_token: np.ndarray,
+                      prefix_lens: np.ndarray, extend_lens: np.ndarray, qo_indptr: np.ndarray,
+                      new_slots: np.ndarray, out_last: np.ndarray) -> int:
+    """Fills the caller's host arrays (see include/pkv.h); returns the number of new tokens."""
+    n = int(tok_indptr.size - 1)
+    for a, dt in ((tokens, np.int32), (tok_indptr, np.int64), (req_to_token, np.int32), (prefix_lens, np.int32),
+                  (extend_lens, np.int32), (qo_indptr, np.int32), (new_slots, np.int32), (out_last, np.int64)):
+        if a.dtype != dt or not a.flags.c_contiguous:
+            raise TypeError("rt_prepare_extend: host arrays must be C-contiguous with the documented dtypes")
+    if req_to_token.ndim != 2 or req_to_token.shape[0] < n or prefix_lens.size < n or extend_lens.size < n \
+            or qo_indptr.size < n + 1 or out_last.size < n:
+        raise ValueError("rt_prepare_extend: output arrays too small")
+    return int(check(lib().rt_prepare_extend(t, n, _ptr(tokens), _ptr(tok_indptr), _ptr(req_to_token),
+                                             req_to_token.shape[1], _ptr(prefix_lens), _ptr(extend_lens),
+                                             _ptr(qo_indptr), _ptr(new_slots), new_slots.size, _ptr(out_last))))
+
+
+def rt_release(t, nodes) -> None:
+    a = np.ascontiguousarray(nodes, dtype=np.int64)
+    check(lib().rt_release(t, _ptr(a), a.size))
+
+
+def rt_decode_step(t, req_to_token: np.ndarray, seq_lens: np.ndarray, out_slots: np.ndarray) -> int:
+    b = int(seq_lens.size)
+    if req_to_token.dtype != np.int32 or seq_lens.dtype != np.int32 or out_slots.dtype != np.int32 \
+            or out_slots.size < b or req_to_token.shape[0] < b:
+        raise TypeError("rt_decode_step: bad host arrays")
+    return int(check(lib().rt_decode_step(t, b, _ptr(req_to_token), req_to_token.shape[1], _ptr(seq_lens),
+                                          _ptr(out_slots))))
+
+
+def rt_finish(t, tokens: np.ndarray, tok_indptr: np.ndarray, req_to_token: np.ndarray, prompt_lens,
+              prompt_last) -> np.ndarray:
+    n = int(tok_indptr.size - 1)
+    pl = _i32(prompt_lens)
+    last = np.ascontiguousarray(prompt_last, dtype=np.int64)
+    ends = np.empty(max(n, 1), dtype=np.int64)
+    toks = _i32(tokens)
+    ip = np.ascontiguousarray(tok_indptr, dtype=np.int64)
+    check(lib().rt_finish(t, n, _ptr(toks), _ptr(ip), _ptr(req_to_token), req_to_token.shape[1], _ptr(pl),
+                          _ptr(last), _ptr(ends)))
+    return ends[:n]
+
+
+# ------------------------------------------------------------------------------------------
+# kernels (device); tensors must live on the ROCm device
+# ------------------------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return PKV_F32
+    if t.dtype == torch.bfloat16:
+        return PKV_BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return PKV_FP8_E4M3
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev(t, name, dtype=None, ndim=None):
+    torch = _torch()
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims")
+    return C.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return C.c_void_p(s.cuda_stream)
+
+
+def pkv_kv_scatter(k_src, v_src, slots, k_pool, v_pool, k_inv_scale=None, v_inv_scale=None, stream=None) -> None:
+    torch = _torch()
+    n, hkv, d = k_src.shape
+    if v_src.shape != k_src.shape or k_pool.shape != v_pool.shape or tuple(k_pool.shape[1:]) != (hkv, d) \
+            or slots.shape != (n,):
+        raise ValueError("kv_scatter: shape mismatch")
+    args = (_dev(k_src, "k_src", ndim=3), _dev(v_src, "v_src", k_src.dtype, 3), _dtype_code(k_src),
+            _dev(slots, "slots", torch.int32, 1), n, _dev(k_pool, "k_pool", ndim=3),
+            _dev(v_pool, "v_pool", k_pool.dtype, 3), _dtype_code(k_pool), k_pool.shape[0], hkv, d,
+            _dev(k_inv_scale, "k_inv_scale", torch.float32), _dev(v_inv_scale, "v_inv_scale", torch.float32),
+            _stream(stream))
+    check(lib().pkv_kv_scatter(*args))
+
+
+def pkv_extend_tile(qo_dtype: int, pool_dtype: int, hq: int, hkv: int, d: int) -> int:
+    return int(check(lib().pkv_extend_tile(qo_dtype, pool_dtype, hq, hkv, d)))
+
+
+def pkv_extend_plan(prefix_lens, extend_lens, tile: int) -> np.ndarray:
+    pl, el = _i32(prefix_lens), _i32(extend_lens)
+    n = int(check(lib().pkv_extend_plan_size(_ptr(el), el.size, int(tile))))
+    work = np.empty((max(n, 1), 2), dtype=np.int32)
+    check(lib().pkv_extend_plan(_ptr(pl), _ptr(el), el.size, int(tile), _ptr(work), n))
+    return work[:n]
+
+
+def pkv_extend_attention(q, o, k_pool, v_pool, req_to_token, prefix_lens, extend_lens, qo_indptr, work, sm_scale,
+                         k_scale=None, v_scale=None, stream=None) -> None:
+    torch = _torch()
+    tq, hq, d = q.shape
+    ns, hkv, d2 = k_pool.shape
+    if o.shape != q.shape or o.dtype != q.dtype or v_pool.shape != k_pool.shape or d2 != d:
+        raise ValueError("extend: shape mismatch")
+    nr = prefix_lens.shape[0]
+    if extend_lens.shape != (nr,) or qo_indptr.shape != (nr + 1,) or req_to_token.dim() != 2 \
+            or req_to_token.shape[0] < nr or work.dim() != 2 or work.shape[1] != 2:
+        raise ValueError("extend: table shape mismatch")
+    args = (_dev(q, "q"), _dev(o, "o"), _dtype_code(q), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool", k_pool.dtype),
+            _dtype_code(k_pool), ns, _dev(k_scale, "k_scale", torch.float32), _dev(v_scale, "v_scale", torch.float32),
+            _dev(req_to_token, "req_to_token", torch.int32), req_to_token.shape[1],
+            _dev(prefix_lens, "prefix_lens", torch.int32), _dev(extend_lens, "extend_lens", torch.int32),
+            _dev(qo_indptr, "qo_indptr", torch.int32), nr, _dev(work, "work", torch.int32), work.shape[0], hq, hkv, d,
+            float(sm_scale), _stream(stream))
+    check(lib().pkv_extend_attention(*args))
+
+
+def pkv_decode_chunk(batch: int, hkv: int, max_seq_len: int) -> int:
+    return int(lib().pkv_decode_chunk(batch, hkv, max_seq_len))
+
+
+def pkv_decode_workspace_bytes(batch: int, hq: int, d: int, max_seq_len: int, chunk: int) -> int:
+    return int(lib().pkv_decode_workspace_bytes(batch, hq, d, max_seq_len, chunk))
+
+
+def pkv_decode_attention(q, o, k_pool, v_pool, req_to_token, seq_lens, max_seq_len, sm_scale, workspace,
+                         chunk: int = 0, k_scale=None, v_scale=None, stream=None) -> None:
+    torch = _torch()
+    b, hq, d = q.shape
+    ns, hkv, d2 = k_pool.shape
+    if o.shape != q.shape or v_pool.shape != k_pool.shape or d2 != d or seq_lens.shape != (b,) \
+            or req_to_token.dim() != 2 or req_to_token.shape[0] < b:
+        raise ValueError("decode: shape mismatch")
+    args = (_dev(q, "q"), _dev(o, "o", q.dtype), _dtype_code(q), _dev(k_pool, "k_pool"),
+            _dev(v_pool, "v_pool", k_pool.dtype), _dtype_code(k_pool), ns, _dev(k_scale, "k_scale", torch.float32),
+            _dev(v_scale, "v_scale", torch.float32), _dev(req_to_token, "req_to_token", torch.int32),
+            req_to_token.shape[1], _dev(seq_lens, "seq_lens", torch.int32), b, int(max_seq_len), hq, hkv, d,
+            float(sm_scale), int(chunk), _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+            _stream(stream))
+    check(lib().pkv_decode_attention(*args))

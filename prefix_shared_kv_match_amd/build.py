@@ -1,0 +1,84 @@
+"""Builds libpkv.so in-tree: host C++ (radix tree, allocator, C ABI) plus HIP kernels for gfx950.
+
+    python -m prefix_shared_kv_match_amd.build [--debug]
+
+The host sources are compiled with g++, the .hip sources with hipcc for gfx950 only,
+and everything is linked by hipcc into prefix_shared_kv_match_amd/libpkv.so.
+"""
+from __future__ import annotations
+
+import argparse
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libpkv.so")
+
+HOST_SOURCES = ["common.cpp", "radix_tree.cpp"]
+HIP_SOURCES = ["kv_scatter.hip", "extend_attention.hip", "decode_attention.hip"]
+
+ARCH = "gfx950"
+# Packed-FP32 instructions are switched off for every HIP file.
+HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature",
+             "-Xclang", "-packed-fp32-ops", "-munsafe-fp-atomics", "-Wall", "-Wno-unused-function"]
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Wno-unused-parameter"]
+
+
+def hipcc() -> str:
+    for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("hipcc not found (ROCm is required to build libpkv)")
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError("build step failed:\n" + " ".join(cmd) + "\n" + out)
+    return out
+
+
+def build(debug: bool = False, verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    hc = hipcc()
+    extra = ["-DPKV_DEBUG=1", "-g"] if debug else []
+    jobs = []
+    objs = []
+    for s in HOST_SOURCES:
+        o = os.path.join(BUILD, s + ".o")
+        objs.append(o)
+        jobs.append(["g++", *HOST_FLAGS, *extra, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, s), "-o", o])
+    for s in HIP_SOURCES:
+        o = os.path.join(BUILD, s + ".o")
+        objs.append(o)
+        jobs.append([hc, *HIP_FLAGS, *extra, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, s), "-o", o])
+    with ThreadPoolExecutor(min(8, len(jobs))) as ex:
+        outs = list(ex.map(_run, jobs))
+    if verbose:
+        for o in outs:
+            if o.strip():
+                print(o)
+    tmp = LIB + ".tmp"
+    _run([hc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp])
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--debug", action="store_true")
+    ap.add_argument("-v", "--verbose", action="store_true")
+    a = ap.parse_args(argv)
+    print(build(a.debug, a.verbose))
+
+
+if __name__ == "__main__":
+    sys.exit(main())

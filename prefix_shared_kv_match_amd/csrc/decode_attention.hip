@@ -1,0 +1,390 @@
+// Split-K decode attention over K/V gathered through slot rows, then a log-sum-exp reduce.
+//
+// Decode is the `gen` step of the pages (one new token per sequence per step, attending
+// over its whole cached context, the newest token's own K/V included).  Per sequence b,
+// kv head g and context chunk s, one workgroup streams the chunk's K and V rows and keeps
+// a running max / running sum / unnormalised output for the G = hq/hkv query heads that
+// share kv head g, so every gathered row is read once for the whole GQA group.  The
+// reduce merges the chunks: M = max_s m_s, o = sum_s 2^(m_s-M) acc_s / sum_s 2^(m_s-M) l_s.
+//
+// Layout on gfx950: a 256-thread workgroup is 4 waves x 4 rows of 16 lanes.  A 16-lane
+// row owns one token at a time and covers the head dim (d/16 values per lane), so each
+// K or V row (256 B for bf16 d=128, 128 B for fp8) is one coalesced access per row of
+// lanes.  Dot products are reduced inside the row with DPP (no LDS).  Each 16-lane row
+// runs its own online softmax over a token sub-stream; rows and waves are merged once at
+// the end.  Work is HBM-bound (about 4 FLOP per gathered byte for bf16 GQA-4), so no
+// MFMA is used.  blockIdx.x = (b * max_splits + s) * hkv + g: consecutive workgroups
+// cycle through the kv heads, which places each kv head on one XCD when hkv = 8.
+
+#include <math.h>
+
+#include "device.h"
+
+namespace pkv {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kUnroll = 4;
+
+template <int POOL, int VEC>
+struct RowChunk;  // VEC consecutive pool elements of one (slot, head) row, as floats
+
+template <int VEC>
+struct RowChunk<PKV_F32, VEC> {
+  static constexpr int kBytes = VEC * 4;
+  float4 r[VEC / 4];
+  __device__ __forceinline__ void load(const uint8_t* p) {
+#pragma unroll
+    for (int i = 0; i < VEC / 4; ++i) r[i] = ((const float4*)p)[i];
+  }
+  __device__ __forceinline__ float get(int i) const {
+    const float4& v = r[i / 4];
+    switch (i & 3) {
+      case 0: return v.x;
+      case 1: return v.y;
+      case 2: return v.z;
+      default: return v.w;
+    }
+  }
+};
+
+template <int VEC>
+struct RowChunk<PKV_BF16, VEC> {
+  static constexpr int kBytes = VEC * 2;
+  uint32_t w[VEC / 2];
+  __device__ __forceinline__ void load(const uint8_t* p) {
+    if constexpr (VEC == 8) {
+      uint4 v = *(const uint4*)p;
+      w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+    } else {
+      uint2 v = *(const uint2*)p;
+      w[0] = v.x; w[1] = v.y;
+    }
+  }
+  __device__ __forceinline__ float get(int i) const { return (i & 1) ? bf16_hi(w[i / 2]) : bf16_lo(w[i / 2]); }
+};
+
+template <int VEC>
+struct RowChunk<PKV_FP8_E4M3, VEC> {
+  static constexpr int kBytes = VEC;
+  uint32_t w[VEC / 4];
+  __device__ __forceinline__ void load(const uint8_t* p) {
+    if constexpr (VEC == 8) {
+      uint2 v = *(const uint2*)p;
+      w[0] = v.x; w[1] = v.y;
+    } else {
+      w[0] = *(const uint32_t*)p;
+    }
+  }
+  __device__ __forceinline__ float get(int i) const {
+    return __uint_as_float(e4m3_to_bf16_bits((w[i / 4] >> (8 * (i & 3))) & 0xFFu) << 16);
+  }
+};
+
+template <typename QT>
+__device__ __forceinline__ float load_q(const QT* p, int i);
+template <>
+__device__ __forceinline__ float load_q<float>(const float* p, int i) { return p[i]; }
+template <>
+__device__ __forceinline__ float load_q<bf16>(const bf16* p, int i) { return (float)p[i]; }
+
+__device__ __forceinline__ void merge_state(float& m, float& l, float* acc, float m2, float l2, const float* acc2,
+                                            int n) {
+  const float mn = fmaxf(m, m2);
+  if (mn == -INFINITY) return;
+  const float a = exp2f(m - mn), b = exp2f(m2 - mn);
+  l = l * a + l2 * b;
+  for (int i = 0; i < n; ++i) acc[i] = acc[i] * a + acc2[i] * b;
+  m = mn;
+}
+
+template <typename QT, int POOL, int D, int G>
+__global__ __launch_bounds__(256) void decode_split(const QT* __restrict__ q, const uint8_t* __restrict__ kpool,
+                                                    const uint8_t* __restrict__ vpool, const float* __restrict__ kscale,
+                                                    const float* __restrict__ vscale,
+                                                    const int32_t* __restrict__ r2t, int64_t stride,
+                                                    const int32_t* __restrict__ seq_lens, int hkv, int chunk,
+                                                    int max_splits, float qk_scale_log2, float* __restrict__ ws_ml,
+                                                    float* __restrict__ ws_acc) {
+  constexpr int VEC = D / 16;
+  using Chunk = RowChunk<POOL, VEC>;
+  constexpr int ROWB = D * Chunk::kBytes / VEC;  // bytes of one (slot, head) row
+  __shared__ float sm_ml[kWaves][G][2];
+  __shared__ float sm_acc[kWaves][G][D];
+
+  const int g = blockIdx.x % hkv;
+  const int rest = blockIdx.x / hkv;
+  const int s = rest % max_splits;
+  const int b = rest / max_splits;
+  const int L = seq_lens[b];
+  const int t0 = s * chunk;
+  if (t0 >= L) return;  // the whole workgroup leaves together
+  const int t1 = min(t0 + chunk, L);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int grp = lane >> 4, li = lane & 15;
+  const int hq = hkv * G;
+
+  float qf[G][VEC];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const QT* qp = q + ((int64_t)b * hq + (int64_t)g * G + h) * D + li * VEC;
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) qf[h][i] = load_q<QT>(qp, i);
+  }
+  float kmul = qk_scale_log2;
+  if constexpr (POOL == PKV_FP8_E4M3) kmul *= kscale[g];
+
+  float m[G], l[G], acc[G][VEC];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m[h] = -INFINITY;
+    l[h] = 0.f;
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) acc[h][i] = 0.f;
+  }
+
+  const int32_t* row = r2t + (int64_t)b * stride;
+  const int64_t slot_bytes = (int64_t)hkv * ROWB;
+  const int64_t head_off = (int64_t)g * ROWB + li * Chunk::kBytes;
+
+  for (int base = t0 + wave * 4 + grp; base < t1; base += 16 * kUnroll) {
+    Chunk kc[kUnroll], vc[kUnroll];
+    bool valid[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int t = base + 16 * u;
+      valid[u] = t < t1;
+      const int64_t slot = row[valid[u] ? t : t0];
+      kc[u].load(kpool + slot * slot_bytes + head_off);
+      vc[u].load(vpool + slot * slot_bytes + head_off);
+    }
+    float sc[kUnroll][G];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float part = 0.f;
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) part = fmaf(qf[h][i], kc[u].get(i), part);
+        sc[u][h] = valid[u] ? row16_sum(part) * kmul : -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float mt = sc[0][h];
+#pragma unroll
+      for (int u = 1; u < kUnroll; ++u) mt = fmaxf(mt, sc[u][h]);
+      const float mn = fmaxf(m[h], mt);
+      if (mn == -INFINITY) continue;  // this row has not seen a token yet (uniform within the row)
+      const float alpha = exp2f(m[h] - mn);
+      float p[kUnroll];
+      float psum = 0.f;
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        p[u] = exp2f(sc[u][h] - mn);  // masked: exp2(-inf) = 0
+        psum += p[u];
+      }
+      l[h] = l[h] * alpha + psum;
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) {
+        float a = acc[h][i] * alpha;
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) a = fmaf(p[u], vc[u].get(i), a);
+        acc[h][i] = a;
+      }
+      m[h] = mn;
+    }
+  }
+
+  // merge the four 16-lane rows of the wave (lanes li, li+16, li+32, li+48 cover the same d)
+#pragma unroll
+  for (int off = 16; off <= 32; off *= 2) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float m2 = __shfl_xor(m[h], off);
+      const float l2 = __shfl_xor(l[h], off);
+      float a2[VEC];
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) a2[i] = __shfl_xor(acc[h][i], off);
+      merge_state(m[h], l[h], acc[h], m2, l2, a2, VEC);
+    }
+  }
+  if (grp == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) sm_acc[wave][h][li * VEC + i] = acc[h][i];
+      if (li == 0) {
+        sm_ml[wave][h][0] = m[h];
+        sm_ml[wave][h][1] = l[h];
+      }
+    }
+  }
+  __syncthreads();
+  const float vmul = POOL == PKV_FP8_E4M3 ? vscale[g] : 1.f;
+  for (int e = threadIdx.x; e < G * D; e += blockDim.x) {
+    const int h = e / D, dd = e - h * D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_ml[w][h][0]);
+    float a = 0.f, lsum = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = sm_ml[w][h][0];
+      const float f = mw == -INFINITY ? 0.f : exp2f(mw - M);
+      a += f * sm_acc[w][h][dd];
+      lsum += f * sm_ml[w][h][1];
+    }
+    const int64_t part = ((int64_t)b * hq + (int64_t)g * G + h) * max_splits + s;
+    ws_acc[part * D + dd] = a * vmul;
+    if (dd == 0) {
+      ws_ml[part * 2 + 0] = M;
+      ws_ml[part * 2 + 1] = lsum;
+    }
+  }
+}
+
+template <typename OT>
+__device__ __forceinline__ void store_o(OT* p, float v);
+template <>
+__device__ __forceinline__ void store_o<float>(float* p, float v) { *p = v; }
+template <>
+__device__ __forceinline__ void store_o<bf16>(bf16* p, float v) { *p = (bf16)v; }
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off /= 2) x = fmaxf(x, __shfl_xor(x, off));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off /= 2) x += __shfl_xor(x, off);
+  return x;
+}
+
+// One wave per (sequence, q head): merge that head's chunk partials.
+template <typename OT, int D>
+__global__ __launch_bounds__(256) void decode_reduce(const float* __restrict__ ws_ml, const float* __restrict__ ws_acc,
+                                                     const int32_t* __restrict__ seq_lens, int batch, int hq,
+                                                     int chunk, int max_splits, OT* __restrict__ o) {
+  constexpr int PER = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int idx = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  if (idx >= batch * hq) return;
+  const int b = idx / hq;
+  const int ns = (seq_lens[b] + chunk - 1) / chunk;
+  const float* ml = ws_ml + (int64_t)idx * max_splits * 2;
+  const float* acc = ws_acc + (int64_t)idx * max_splits * D;
+  float M = -INFINITY;
+  for (int s = lane; s < ns; s += 64) M = fmaxf(M, ml[2 * s]);
+  M = wave_max(M);
+  float lsum = 0.f;
+  for (int s = lane; s < ns; s += 64) lsum += exp2f(ml[2 * s] - M) * ml[2 * s + 1];
+  lsum = wave_sum(lsum);
+  float out[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) out[i] = 0.f;
+  for (int s = 0; s < ns; ++s) {
+    const float w = exp2f(ml[2 * s] - M);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) out[i] = fmaf(w, acc[(int64_t)s * D + lane * PER + i], out[i]);
+  }
+  const float inv = 1.f / lsum;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) store_o<OT>(o + (int64_t)idx * D + lane * PER + i, out[i] * inv);
+}
+
+template <typename QT, int POOL, int D>
+int launch_split(int G, dim3 grid, hipStream_t st, const void* q, const void* kp, const void* vp, const float* ks,
+                 const float* vs, const int32_t* r2t, int64_t stride, const int32_t* lens, int hkv, int chunk,
+                 int max_splits, float sc, float* ml, float* acc) {
+#define PKV_DECODE_CASE(GG)                                                                                    \
+  case GG:                                                                                                     \
+    hipLaunchKernelGGL((decode_split<QT, POOL, D, GG>), grid, dim3(256), 0, st, (const QT*)q, (const uint8_t*)kp, \
+                       (const uint8_t*)vp, ks, vs, r2t, stride, lens, hkv, chunk, max_splits, sc, ml, acc);     \
+    return PKV_OK;
+  switch (G) {
+    PKV_DECODE_CASE(1)
+    PKV_DECODE_CASE(2)
+    PKV_DECODE_CASE(4)
+    PKV_DECODE_CASE(8)
+    default:
+      return fail(PKV_ERR_UNSUPPORTED, "decode: group size %d", G);
+  }
+#undef PKV_DECODE_CASE
+}
+
+int splits_for(int max_seq_len, int chunk) { return (max_seq_len + chunk - 1) / chunk; }
+
+}  // namespace
+}  // namespace pkv
+
+using namespace pkv;
+
+extern "C" int32_t pkv_decode_chunk(int32_t batch, int32_t hkv, int32_t max_seq_len) {
+  int chunk = 1024;
+  while (chunk > 128 && (int64_t)batch * hkv * splits_for(max_seq_len, chunk) < 2048) chunk /= 2;
+  return chunk;
+}
+
+extern "C" size_t pkv_decode_workspace_bytes(int32_t batch, int32_t hq, int32_t d, int32_t max_seq_len,
+                                             int32_t chunk) {
+  if (batch <= 0 || hq <= 0 || d <= 0 || max_seq_len <= 0) return 0;
+  if (chunk <= 0) chunk = 1024;
+  const size_t parts = (size_t)batch * hq * splits_for(max_seq_len, chunk);
+  return parts * (2 + (size_t)d) * sizeof(float);
+}
+
+extern "C" int pkv_decode_attention(const void* q, void* o, int32_t qo_dtype, const void* k_pool, const void* v_pool,
+                                    int32_t pool_dtype, int64_t num_slots, const float* k_scale, const float* v_scale,
+                                    const int32_t* req_to_token, int64_t stride, const int32_t* seq_lens,
+                                    int32_t batch, int32_t max_seq_len, int32_t hq, int32_t hkv, int32_t d,
+                                    float sm_scale, int32_t chunk, void* workspace, size_t ws_bytes, void* stream) {
+  if (batch < 0 || hq <= 0 || hkv <= 0 || hq % hkv || max_seq_len <= 0 || max_seq_len > stride || num_slots <= 0)
+    return fail(PKV_ERR_INVAL, "decode: bad sizes (batch %d hq %d hkv %d max_seq_len %d stride %lld)", batch, hq,
+                hkv, max_seq_len, (long long)stride);
+  if (batch == 0) return PKV_OK;
+  if (!q || !o || !k_pool || !v_pool || !req_to_token || !seq_lens || !workspace)
+    return fail(PKV_ERR_INVAL, "decode: null pointer");
+  if (chunk == 0) chunk = pkv_decode_chunk(batch, hkv, max_seq_len);
+  if (chunk < 64 || chunk % 64) return fail(PKV_ERR_INVAL, "decode: chunk %d is not a positive multiple of 64", chunk);
+  if (ws_bytes < pkv_decode_workspace_bytes(batch, hq, d, max_seq_len, chunk))
+    return fail(PKV_ERR_INVAL, "decode: workspace of %zu bytes is too small", ws_bytes);
+  if (pool_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale)) return fail(PKV_ERR_INVAL, "decode: fp8 pool needs scales");
+  const int G = hq / hkv;
+  const int max_splits = splits_for(max_seq_len, chunk);
+  float* ml = (float*)workspace;
+  float* acc = ml + (size_t)batch * hq * max_splits * 2;
+  const dim3 grid((unsigned)((int64_t)batch * max_splits * hkv));
+  hipStream_t st = (hipStream_t)stream;
+  const float sc = sm_scale * kLog2e;
+  int rc;
+  if (qo_dtype == PKV_F32 && pool_dtype == PKV_F32 && d == 64)
+    rc = launch_split<float, PKV_F32, 64>(G, grid, st, q, k_pool, v_pool, k_scale, v_scale, req_to_token, stride,
+                                          seq_lens, hkv, chunk, max_splits, sc, ml, acc);
+  else if (qo_dtype == PKV_F32 && pool_dtype == PKV_F32 && d == 128)
+    rc = launch_split<float, PKV_F32, 128>(G, grid, st, q, k_pool, v_pool, k_scale, v_scale, req_to_token, stride,
+                                           seq_lens, hkv, chunk, max_splits, sc, ml, acc);
+  else if (qo_dtype == PKV_BF16 && pool_dtype == PKV_BF16 && d == 128)
+    rc = launch_split<bf16, PKV_BF16, 128>(G, grid, st, q, k_pool, v_pool, k_scale, v_scale, req_to_token, stride,
+                                           seq_lens, hkv, chunk, max_splits, sc, ml, acc);
+  else if (qo_dtype == PKV_BF16 && pool_dtype == PKV_FP8_E4M3 && d == 128)
+    rc = launch_split<bf16, PKV_FP8_E4M3, 128>(G, grid, st, q, k_pool, v_pool, k_scale, v_scale, req_to_token,
+                                               stride, seq_lens, hkv, chunk, max_splits, sc, ml, acc);
+  else
+    return fail(PKV_ERR_UNSUPPORTED, "decode: qo dtype %d, pool dtype %d, d %d", qo_dtype, pool_dtype, d);
+  if (rc < 0) return rc;
+  rc = hip_check(hipGetLastError(), "decode split launch");
+  if (rc < 0) return rc;
+  const dim3 rgrid((unsigned)(((int64_t)batch * hq + kWaves - 1) / kWaves));
+  if (qo_dtype == PKV_F32 && d == 64)
+    hipLaunchKernelGGL((decode_reduce<float, 64>), rgrid, dim3(256), 0, st, ml, acc, seq_lens, batch, hq, chunk,
+                       max_splits, (float*)o);
+  else if (qo_dtype == PKV_F32)
+    hipLaunchKernelGGL((decode_reduce<float, 128>), rgrid, dim3(256), 0, st, ml, acc, seq_lens, batch, hq, chunk,
+                       max_splits, (float*)o);
+  else
+    hipLaunchKernelGGL((decode_reduce<bf16, 128>), rgrid, dim3(256), 0, st, ml, acc, seq_lens, batch, hq, chunk,
+                       max_splits, (bf16*)o);
+  return hip_check(hipGetLastError(), "decode reduce launch");
+}

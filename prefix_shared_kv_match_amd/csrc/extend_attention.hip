@@ -1,0 +1,525 @@
+// Extend attention: prefill of each request's unmatched suffix over its reused prefix.
+//
+// The RadixAttention explainer's point is that the matched prefix needs no recompute and
+// only the rest of the prompt is prefilled.  For request r with p reused tokens and e new
+// ones, query row j (token position i = p + j) attends over K/V of positions 0..i, gathered
+// through the request's slot row: full over the prefix, causal over the suffix.  Query head
+// h reads kv head h / (hq/hkv).
+//
+// Work items come from a host plan: (request, first extend row of a query tile), longest
+// context first.  blockIdx.x = item * hkv + g, so consecutive workgroups cycle through the
+// kv heads and each kv head's K/V stays in one XCD's L2 when hkv = 8.
+//
+// Two kernels:
+//  - extend_mfma (bf16 q/o, bf16 or fp8 pool, d = 128): one workgroup = 4 waves = 128 query
+//    rows = (128/G tokens) x (G heads of one GQA group), so every K/V tile staged in LDS is
+//    shared by the whole group.  Per 64-token K/V tile and wave (32 query rows):
+//      S^T = K . Q^T  (A = K rows from LDS, B = Q^T held in registers), 32 MFMA 16x16x32;
+//      online softmax in the log2 domain, row max across the 4 lanes that share a query row;
+//      O^T += V^T . P^T (A = V^T from LDS, B = P^T straight from the S^T registers), 32 MFMA.
+//    The S^T row order inside each 16-row MFMA block is permuted so that each lane's four
+//    S^T values of two neighbouring blocks are 8 consecutive kv tokens, which is exactly the
+//    B-operand slice of P^T for the PV product; V is stored transposed in LDS so the A
+//    operand is one 16-byte read.  fp8 pools are decoded to bf16 (exact) while staging;
+//    the per-head scales are folded into the float32 logits and output.
+//  - extend_f32 (f32 q/o, f32 pool, d 64 or 128): one wave per (tile, q head), VALU only;
+//    it serves the small fp32 case.
+
+#include <math.h>
+
+#include <algorithm>
+#include <new>
+
+#include "device.h"
+
+namespace pkv {
+namespace {
+
+// ------------------------------------------------------------------------------------------
+// fp32 path
+// ------------------------------------------------------------------------------------------
+
+constexpr int kF32Tile = 16;   // query tokens per work item
+constexpr int kF32Kv = 64;     // kv tokens per iteration (one per lane)
+
+__device__ __forceinline__ float wave_max64(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off /= 2) x = fmaxf(x, __shfl_xor(x, off));
+  return x;
+}
+__device__ __forceinline__ float wave_sum64(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off /= 2) x += __shfl_xor(x, off);
+  return x;
+}
+
+template <int D>
+__global__ __launch_bounds__(64) void extend_f32(const float* __restrict__ q, float* __restrict__ o,
+                                                 const float* __restrict__ kpool, const float* __restrict__ vpool,
+                                                 const int32_t* __restrict__ r2t, int64_t stride,
+                                                 const int32_t* __restrict__ prefix_lens,
+                                                 const int32_t* __restrict__ extend_lens,
+                                                 const int32_t* __restrict__ qo_indptr,
+                                                 const int32_t* __restrict__ work, int hq, int hkv,
+                                                 float scale_log2) {
+  constexpr int PER = D / 64;
+  __shared__ float qs[kF32Tile][D];
+  __shared__ float ps[kF32Kv];
+  __shared__ int32_t sl[kF32Kv];
+  const int lane = threadIdx.x;
+  const int h = blockIdx.x % hq;
+  const int w = blockIdx.x / hq;
+  const int req = work[2 * w], j0 = work[2 * w + 1];
+  const int p = prefix_lens[req], e = extend_lens[req];
+  const int nq = min(kF32Tile, e - j0);
+  const int g = h / (hq / hkv);
+  const int64_t qrow0 = (int64_t)qo_indptr[req] + j0;
+  for (int x = lane; x < kF32Tile * D; x += 64) {
+    const int t = x / D, dd = x - t * D;
+    qs[t][dd] = t < nq ? q[((qrow0 + t) * hq + h) * D + dd] : 0.f;
+  }
+  float m[kF32Tile], l[kF32Tile], acc[kF32Tile][PER];
+#pragma unroll
+  for (int t = 0; t < kF32Tile; ++t) {
+    m[t] = -INFINITY;
+    l[t] = 0.f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) acc[t][i] = 0.f;
+  }
+  const int ctx = p + j0 + nq;
+  const int32_t* row = r2t + (int64_t)req * stride;
+  __syncthreads();
+  for (int kv0 = 0; kv0 < ctx; kv0 += kF32Kv) {
+    const int k = kv0 + lane;
+    const bool kin = k < ctx;
+    const int64_t slot = row[kin ? k : 0];
+    sl[lane] = (int32_t)slot;
+    const float* krow = kpool + (slot * hkv + g) * D;
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < kF32Tile; ++t) {
+      if (t < nq) {  // uniform across the wave
+        const int pos = p + j0 + t;
+        float dot = 0.f;
+        for (int dd = 0; dd < D; ++dd) dot = fmaf(qs[t][dd], krow[dd], dot);
+        const float s = (kin && k <= pos) ? dot * scale_log2 : -INFINITY;
+        const float mn = fmaxf(m[t], wave_max64(s));   // finite: kv 0 is visible to every row
+        const float alpha = exp2f(m[t] - mn);
+        const float pk = exp2f(s - mn);
+        l[t] = l[t] * alpha + wave_sum64(pk);
+        ps[lane] = pk;
+        __syncthreads();
+        const int nk = min(kF32Kv, ctx - kv0);
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+          float a = acc[t][i] * alpha;
+          for (int kk = 0; kk < nk; ++kk)
+            a = fmaf(ps[kk], vpool[((int64_t)sl[kk] * hkv + g) * D + lane + 64 * i], a);
+          acc[t][i] = a;
+        }
+        m[t] = mn;
+        __syncthreads();
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < kF32Tile; ++t) {
+    if (t < nq) {
+      const float inv = 1.f / l[t];
+#pragma unroll
+      for (int i = 0; i < PER; ++i) o[((qrow0 + t) * hq + h) * D + lane + 64 * i] = acc[t][i] * inv;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// bf16 MFMA path (d = 128)
+// ------------------------------------------------------------------------------------------
+
+constexpr int kD = 128;
+constexpr int kBN = 64;                 // kv tokens per tile
+constexpr int kRows = 128;              // query rows per workgroup (tokens x heads)
+constexpr int kKStride = kD + 8;        // bf16 elements per K row in LDS (272 B)
+constexpr int kVStride = kBN + 8;       // bf16 elements per V^T row in LDS (144 B)
+
+// kv token (tile-local) held in row rho of 16-row MFMA block mb of S^T.
+__device__ __forceinline__ int sigma(int mb, int rho) {
+  return 32 * (mb >> 1) + 8 * (rho >> 2) + 4 * (mb & 1) + (rho & 3);
+}
+
+// Staging of one 64-token K/V tile: global -> registers (prefetch) -> LDS.
+template <int POOL>
+struct TileStage;
+
+template <>
+struct TileStage<PKV_BF16> {
+  // K: 64 rows x 256 B = 1024 chunks of 16 B, 4 per thread (rows tid/16 + 16 i, chunk tid%16).
+  // V: thread -> 4 consecutive tokens (4*(tid%16) .. +3) x 8 d (8*(tid/16) .. +7).
+  uint4 k0, k1, k2, k3, v0, v1, v2, v3;
+  __device__ __forceinline__ void load(const uint8_t* kpool, const uint8_t* vpool, const int32_t* row, int kv0,
+                                       int ctx, int hkv, int g, int tid) {
+    const int64_t slot_bytes = (int64_t)hkv * kD * 2;
+    const int64_t head = (int64_t)g * kD * 2;
+    const uint8_t* kb = kpool + head + (tid & 15) * 16;
+    const uint8_t* vb = vpool + head + (tid >> 4) * 16;
+    const int kt = kv0 + (tid >> 4), vt = kv0 + 4 * (tid & 15);
+    k0 = *(const uint4*)(kb + (int64_t)row[kt < ctx ? kt : 0] * slot_bytes);
+    k1 = *(const uint4*)(kb + (int64_t)row[kt + 16 < ctx ? kt + 16 : 0] * slot_bytes);
+    k2 = *(const uint4*)(kb + (int64_t)row[kt + 32 < ctx ? kt + 32 : 0] * slot_bytes);
+    k3 = *(const uint4*)(kb + (int64_t)row[kt + 48 < ctx ? kt + 48 : 0] * slot_bytes);
+    v0 = *(const uint4*)(vb + (int64_t)row[vt < ctx ? vt : 0] * slot_bytes);
+    v1 = *(const uint4*)(vb + (int64_t)row[vt + 1 < ctx ? vt + 1 : 0] * slot_bytes);
+    v2 = *(const uint4*)(vb + (int64_t)row[vt + 2 < ctx ? vt + 2 : 0] * slot_bytes);
+    v3 = *(const uint4*)(vb + (int64_t)row[vt + 3 < ctx ? vt + 3 : 0] * slot_bytes);
+  }
+  __device__ __forceinline__ void store(bf16* Ks, bf16* Vt, int tid) const {
+    bf16* kd = Ks + (tid >> 4) * kKStride + (tid & 15) * 8;
+    *(uint4*)(kd) = k0;
+    *(uint4*)(kd + 16 * kKStride) = k1;
+    *(uint4*)(kd + 32 * kKStride) = k2;
+    *(uint4*)(kd + 48 * kKStride) = k3;
+    store_vt(Vt, tid, v0, v1, v2, v3);
+  }
+  // Writes 4 tokens x 8 d (token-major in registers) to V^T [d][token].
+  static __device__ __forceinline__ void store_vt(bf16* Vt, int tid, uint4 a, uint4 b, uint4 c, uint4 d) {
+    const int d0 = 8 * (tid >> 4), t0 = 4 * (tid & 15);
+    bf16* base = Vt + d0 * kVStride + t0;
+    const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w};
+    const uint32_t wc[4] = {c.x, c.y, c.z, c.w}, wd[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // d = d0 + 2i (low halves) and d0 + 2i + 1 (high halves)
+      const uint2 lo = make_uint2((wa[i] & 0xFFFFu) | (wb[i] << 16), (wc[i] & 0xFFFFu) | (wd[i] << 16));
+      const uint2 hi = make_uint2((wa[i] >> 16) | (wb[i] & 0xFFFF0000u), (wc[i] >> 16) | (wd[i] & 0xFFFF0000u));
+      *(uint2*)(base + (2 * i) * kVStride) = lo;
+      *(uint2*)(base + (2 * i + 1) * kVStride) = hi;
+    }
+  }
+};
+
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t codes2) {
+  return e4m3_to_bf16_bits(codes2 & 0xFFu) | (e4m3_to_bf16_bits((codes2 >> 8) & 0xFFu) << 16);
+}
+
+template <>
+struct TileStage<PKV_FP8_E4M3> {
+  // K: 64 rows x 128 B = 512 chunks of 16 B, 2 per thread (rows tid/8 + 32 i, chunk tid%8).
+  // V: thread -> 4 tokens x 8 d, 8 B of codes each.
+  uint4 k[2];
+  uint2 v[4];
+  __device__ __forceinline__ void load(const uint8_t* kpool, const uint8_t* vpool, const int32_t* row, int kv0,
+                                       int ctx, int hkv, int g, int tid) {
+    const int64_t slot_bytes = (int64_t)hkv * kD;
+    const int64_t head = (int64_t)g * kD;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int tok = kv0 + (tid >> 3) + 32 * i;
+      const int64_t slot = row[tok < ctx ? tok : 0];
+      k[i] = *(const uint4*)(kpool + slot * slot_bytes + head + (tid & 7) * 16);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int tok = kv0 + 4 * (tid & 15) + u;
+      const int64_t slot = row[tok < ctx ? tok : 0];
+      v[u] = *(const uint2*)(vpool + slot * slot_bytes + head + (tid >> 4) * 8);
+    }
+  }
+  __device__ __forceinline__ void store(bf16* Ks, bf16* Vt, int tid) const {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t c[4] = {k[i].x, k[i].y, k[i].z, k[i].w};
+      uint4 a, b;
+      a.x = e4m3x2_to_bf16x2(c[0]);
+      a.y = e4m3x2_to_bf16x2(c[0] >> 16);
+      a.z = e4m3x2_to_bf16x2(c[1]);
+      a.w = e4m3x2_to_bf16x2(c[1] >> 16);
+      b.x = e4m3x2_to_bf16x2(c[2]);
+      b.y = e4m3x2_to_bf16x2(c[2] >> 16);
+      b.z = e4m3x2_to_bf16x2(c[3]);
+      b.w = e4m3x2_to_bf16x2(c[3] >> 16);
+      bf16* dst = Ks + ((tid >> 3) + 32 * i) * kKStride + (tid & 7) * 16;
+      *(uint4*)dst = a;
+      *(uint4*)(dst + 8) = b;
+    }
+    uint4 vv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      vv[u].x = e4m3x2_to_bf16x2(v[u].x);
+      vv[u].y = e4m3x2_to_bf16x2(v[u].x >> 16);
+      vv[u].z = e4m3x2_to_bf16x2(v[u].y);
+      vv[u].w = e4m3x2_to_bf16x2(v[u].y >> 16);
+    }
+    TileStage<PKV_BF16>::store_vt(Vt, tid, vv[0], vv[1], vv[2], vv[3]);
+  }
+};
+
+template <int POOL, int G>
+__global__ __launch_bounds__(256, 2) void extend_mfma(const bf16* __restrict__ q, bf16* __restrict__ o,
+                                                      const uint8_t* __restrict__ kpool,
+                                                      const uint8_t* __restrict__ vpool,
+                                                      const float* __restrict__ kscale,
+                                                      const float* __restrict__ vscale,
+                                                      const int32_t* __restrict__ r2t, int64_t stride,
+                                                      const int32_t* __restrict__ prefix_lens,
+                                                      const int32_t* __restrict__ extend_lens,
+                                                      const int32_t* __restrict__ qo_indptr,
+                                                      const int32_t* __restrict__ work, int hkv,
+                                                      float scale_log2) {
+  constexpr int BT = kRows / G;   // query tokens per work item
+  __shared__ __attribute__((aligned(16))) bf16 Ks[kBN * kKStride];
+  __shared__ __attribute__((aligned(16))) bf16 Vt[kD * kVStride];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int ln = lane & 15, lg = lane >> 4;
+  const int g = blockIdx.x % hkv;
+  const int w = blockIdx.x / hkv;
+  const int req = work[2 * w], j0 = work[2 * w + 1];
+  const int p = prefix_lens[req], e = extend_lens[req];
+  const int nq = min(BT, e - j0);
+  const int ctx = p + j0 + nq;
+  const int hq = hkv * G;
+  const int64_t qrow0 = (int64_t)qo_indptr[req] + j0;
+  const int32_t* row = r2t + (int64_t)req * stride;
+
+  float sc = scale_log2;
+  if constexpr (POOL == PKV_FP8_E4M3) sc *= kscale[g];
+
+  // this lane's query row in each of the wave's two 16-row blocks
+  int qt[2], qh[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int r0 = 32 * wave + 16 * nb;
+    qh[nb] = g * G + r0 / BT;
+    qt[nb] = r0 % BT + ln;
+  }
+  // Q^T as B operand: lane holds d = 32 ks + 8 lg .. +7 of its query row
+  bf16x8 qf[2][4];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const bool ok = qt[nb] < nq;
+    const bf16* qp = q + ((qrow0 + (ok ? qt[nb] : 0)) * hq + qh[nb]) * kD + 8 * lg;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      uint4 v = ok ? *(const uint4*)(qp + 32 * ks) : make_uint4(0, 0, 0, 0);
+      qf[nb][ks] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+
+  floatx4 oacc[2][8];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+    for (int db = 0; db < 8; ++db) oacc[nb][db] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float m[2] = {-INFINITY, -INFINITY};
+  float l[2] = {0.f, 0.f};
+  const int qpos0 = p + j0;   // position of the tile's first query token
+
+  TileStage<POOL> stage;
+  const int n_tiles = (ctx + kBN - 1) / kBN;
+  stage.load(kpool, vpool, row, 0, ctx, hkv, g, tid);
+  for (int kt = 0; kt < n_tiles; ++kt) {
+    const int kv0 = kt * kBN;
+    __syncthreads();
+    stage.store(Ks, Vt, tid);
+    __syncthreads();
+    if (kt + 1 < n_tiles) stage.load(kpool, vpool, row, kv0 + kBN, ctx, hkv, g, tid);
+
+    // S^T = K . Q^T
+    floatx4 s[4][2];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) s[mb][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const bf16x8 a = *(const bf16x8*)(Ks + sigma(mb, ln) * kKStride + 32 * ks + 8 * lg);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) s[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[nb][ks], s[mb][nb], 0, 0, 0);
+      }
+    }
+
+    // scale, mask (only tiles reaching past the first query position), online softmax
+    const bool need_mask = kv0 + kBN > qpos0 + 1;
+    bf16x8 pf[2][2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int pos = qpos0 + qt[nb];
+      float mt = -INFINITY;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float x = s[mb][nb][i] * sc;
+          if (need_mask) {
+            const int k = kv0 + sigma(mb, 4 * lg + i);
+            x = (k <= pos && k < ctx) ? x : -INFINITY;
+          }
+          s[mb][nb][i] = x;
+          mt = fmaxf(mt, x);
+        }
+      mt = fmaxf(mt, __shfl_xor(mt, 16));
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      const float mn = fmaxf(m[nb], mt);
+      const float alpha = exp2f(m[nb] - mn);
+      m[nb] = mn;
+      float ls = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        bf16x8 pv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p0 = exp2f(s[2 * kk][nb][i] - mn);
+          const float p1 = exp2f(s[2 * kk + 1][nb][i] - mn);
+          ls += p0 + p1;
+          pv[i] = (bf16)p0;
+          pv[4 + i] = (bf16)p1;
+        }
+        pf[nb][kk] = pv;
+      }
+      l[nb] = l[nb] * alpha + ls;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) oacc[nb][db] *= alpha;
+    }
+
+    // O^T += V^T . P^T
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const bf16x8 a = *(const bf16x8*)(Vt + (16 * db + ln) * kVStride + 32 * kk + 8 * lg);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+          oacc[nb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[nb][kk], oacc[nb][db], 0, 0, 0);
+      }
+    }
+  }
+
+  float omul = 1.f;
+  if constexpr (POOL == PKV_FP8_E4M3) omul = vscale[g];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    float lt = l[nb];
+    lt += __shfl_xor(lt, 16);
+    lt += __shfl_xor(lt, 32);
+    if (qt[nb] >= nq) continue;
+    const float inv = omul / lt;
+    bf16* op = o + ((qrow0 + qt[nb]) * hq + qh[nb]) * kD + 4 * lg;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const uint32_t w0 = f32_to_bf16_bits(oacc[nb][db][0] * inv) | (f32_to_bf16_bits(oacc[nb][db][1] * inv) << 16);
+      const uint32_t w1 = f32_to_bf16_bits(oacc[nb][db][2] * inv) | (f32_to_bf16_bits(oacc[nb][db][3] * inv) << 16);
+      *(uint2*)(op + 16 * db) = make_uint2(w0, w1);
+    }
+  }
+}
+
+int mfma_tile(int G) { return kRows / G; }
+
+}  // namespace
+}  // namespace pkv
+
+using namespace pkv;
+
+extern "C" int32_t pkv_extend_tile(int32_t qo_dtype, int32_t pool_dtype, int32_t hq, int32_t hkv, int32_t d) {
+  if (hq <= 0 || hkv <= 0 || hq % hkv) return PKV_ERR_INVAL;
+  const int G = hq / hkv;
+  if (qo_dtype == PKV_F32 && pool_dtype == PKV_F32 && (d == 64 || d == 128)) return kF32Tile;
+  if (qo_dtype == PKV_BF16 && (pool_dtype == PKV_BF16 || pool_dtype == PKV_FP8_E4M3) && d == 128 &&
+      (G == 1 || G == 2 || G == 4 || G == 8))
+    return mfma_tile(G);
+  return PKV_ERR_UNSUPPORTED;
+}
+
+extern "C" int64_t pkv_extend_plan_size(const int32_t* extend_lens, int32_t num_reqs, int32_t tile) {
+  if (num_reqs < 0 || tile <= 0 || (num_reqs > 0 && !extend_lens)) return fail(PKV_ERR_INVAL, "plan: bad arguments");
+  int64_t n = 0;
+  for (int32_t r = 0; r < num_reqs; ++r) {
+    if (extend_lens[r] < 0) return fail(PKV_ERR_INVAL, "plan: negative extend length");
+    n += (extend_lens[r] + tile - 1) / tile;
+  }
+  return n;
+}
+
+extern "C" int64_t pkv_extend_plan(const int32_t* prefix_lens, const int32_t* extend_lens, int32_t num_reqs,
+                                   int32_t tile, int32_t* out_work, int64_t work_cap) {
+  const int64_t n = pkv_extend_plan_size(extend_lens, num_reqs, tile);
+  if (n < 0) return n;
+  if (n > 0 && (!prefix_lens || !out_work)) return fail(PKV_ERR_INVAL, "plan: null pointer");
+  if (work_cap < n) return fail(PKV_ERR_INVAL, "plan: needs %lld items", (long long)n);
+  // (context length of the tile's last query, request, tile start): longest first, then by
+  // request and tile so the order is deterministic
+  struct Item {
+    int64_t ctx;
+    int32_t req, j0;
+  };
+  Item* items = new (std::nothrow) Item[(size_t)n + 1];
+  if (!items) return fail(PKV_ERR_INTERNAL, "plan: host allocation failed");
+  int64_t k = 0;
+  for (int32_t r = 0; r < num_reqs; ++r)
+    for (int32_t j0 = 0; j0 < extend_lens[r]; j0 += tile) {
+      const int32_t nq = extend_lens[r] - j0 < tile ? extend_lens[r] - j0 : tile;
+      items[k++] = Item{(int64_t)prefix_lens[r] + j0 + nq, r, j0};
+    }
+  std::stable_sort(items, items + n, [](const Item& a, const Item& b) { return a.ctx > b.ctx; });
+  for (int64_t i = 0; i < n; ++i) {
+    out_work[2 * i] = items[i].req;
+    out_work[2 * i + 1] = items[i].j0;
+  }
+  delete[] items;
+  return n;
+}
+
+extern "C" int pkv_extend_attention(const void* q, void* o, int32_t qo_dtype, const void* k_pool, const void* v_pool,
+                                    int32_t pool_dtype, int64_t num_slots, const float* k_scale,
+                                    const float* v_scale, const int32_t* req_to_token, int64_t stride,
+                                    const int32_t* prefix_lens, const int32_t* extend_lens,
+                                    const int32_t* qo_indptr, int32_t num_reqs, const int32_t* work,
+                                    int64_t n_work, int32_t hq, int32_t hkv, int32_t d, float sm_scale,
+                                    void* stream) {
+  if (num_reqs < 0 || n_work < 0 || hq <= 0 || hkv <= 0 || hq % hkv || stride <= 0 || num_slots <= 0)
+    return fail(PKV_ERR_INVAL, "extend: bad sizes");
+  if (n_work == 0) return PKV_OK;
+  if (!q || !o || !k_pool || !v_pool || !req_to_token || !prefix_lens || !extend_lens || !qo_indptr || !work)
+    return fail(PKV_ERR_INVAL, "extend: null pointer");
+  if (pkv_extend_tile(qo_dtype, pool_dtype, hq, hkv, d) < 0)
+    return fail(PKV_ERR_UNSUPPORTED, "extend: qo dtype %d, pool dtype %d, hq %d, hkv %d, d %d", qo_dtype,
+                pool_dtype, hq, hkv, d);
+  if (pool_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale)) return fail(PKV_ERR_INVAL, "extend: fp8 pool needs scales");
+  if ((int64_t)n_work * (qo_dtype == PKV_F32 ? hq : hkv) > 0x7FFFFFFFLL) return fail(PKV_ERR_INVAL, "extend: grid too large");
+  hipStream_t st = (hipStream_t)stream;
+  const float sc = sm_scale * kLog2e;
+  const int G = hq / hkv;
+  if (qo_dtype == PKV_F32) {
+    const dim3 grid((unsigned)(n_work * hq));
+    if (d == 64)
+      hipLaunchKernelGGL((extend_f32<64>), grid, dim3(64), 0, st, (const float*)q, (float*)o, (const float*)k_pool,
+                         (const float*)v_pool, req_to_token, stride, prefix_lens, extend_lens, qo_indptr, work, hq,
+                         hkv, sc);
+    else
+      hipLaunchKernelGGL((extend_f32<128>), grid, dim3(64), 0, st, (const float*)q, (float*)o, (const float*)k_pool,
+                         (const float*)v_pool, req_to_token, stride, prefix_lens, extend_lens, qo_indptr, work, hq,
+                         hkv, sc);
+    return hip_check(hipGetLastError(), "extend_f32 launch");
+  }
+  const dim3 grid((unsigned)(n_work * hkv));
+#define PKV_EXTEND_CASE(PP, GG)                                                                                  \
+  if (pool_dtype == PP && G == GG) {                                                                             \
+    hipLaunchKernelGGL((extend_mfma<PP, GG>), grid, dim3(256), 0, st, (const bf16*)q, (bf16*)o,                  \
+                       (const uint8_t*)k_pool, (const uint8_t*)v_pool, k_scale, v_scale, req_to_token, stride,   \
+                       prefix_lens, extend_lens, qo_indptr, work, hkv, sc);                                      \
+    return hip_check(hipGetLastError(), "extend_mfma launch");                                                   \
+  }
+  PKV_EXTEND_CASE(PKV_BF16, 1)
+  PKV_EXTEND_CASE(PKV_BF16, 2)
+  PKV_EXTEND_CASE(PKV_BF16, 4)
+  PKV_EXTEND_CASE(PKV_BF16, 8)
+  PKV_EXTEND_CASE(PKV_FP8_E4M3, 1)
+  PKV_EXTEND_CASE(PKV_FP8_E4M3, 2)
+  PKV_EXTEND_CASE(PKV_FP8_E4M3, 4)
+  PKV_EXTEND_CASE(PKV_FP8_E4M3, 8)
+#undef PKV_EXTEND_CASE
+  return fail(PKV_ERR_UNSUPPORTED, "extend: no kernel for group %d", G);
+}

@@ -103,9 +103,23 @@ class ValueTable:
             raise IndexError("value row out of range")
         out = np.empty((rows.size, self._width(tag)), dtype=np.float32)
         blocks = rows // BLOCK_ROWS
-        for b in np.unique(blocks):
-            sel = np.nonzero(blocks == b)[0]
-            out[sel] = self._block(tag, int(b))[rows[sel] - b * BLOCK_ROWS]
+        ub = np.unique(blocks)
+        if ub.size > 32:
+            # many blocks: draw them in parallel without caching
+            order = np.argsort(blocks, kind="stable")
+            bounds = np.searchsorted(blocks[order], ub, side="left").tolist() + [rows.size]
+
+            def fill(i: int) -> None:
+                sel = order[bounds[i]:bounds[i + 1]]
+                b = int(ub[i])
+                out[sel] = self._gen_block(tag, b)[rows[sel] - b * BLOCK_ROWS]
+
+            with ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as ex:
+                list(ex.map(fill, range(ub.size)))
+        else:
+            for b in ub:
+                sel = np.nonzero(blocks == b)[0]
+                out[sel] = self._block(tag, int(b))[rows[sel] - b * BLOCK_ROWS]
         h = self.shape.hq if tag == TAG_Q else self.shape.hkv
         return out.reshape(rows.size, h, self.shape.d)
 
