@@ -48,7 +48,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="fewshot_bf16", choices=["fewshot_bf16", "decode_bf16", "longctx_fp8"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=8, help="requests in the oracle's timed sample")
+    ap.add_argument("--cpu-sample", type=int, default=64, help="requests in the oracle's timed sample")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -188,8 +190,9 @@ class FewshotBench:
         return int(hb.extend_lens.sum()) + self.steps_dec * hb.n
 
 
-def cpu_baseline(wl, hb, n_req):
-    """The float64 oracle on a bounded sample: the extend rows of the first n_req requests."""
+def cpu_baseline(wl, hb, n_req, min_seconds=10.0):
+    """The float64 oracle on a bounded sample: the extend rows of the first n_req requests,
+    repeated until at least min_seconds of CPU work."""
     from oracle import attention as oa
     try:
         cores = len(os.sched_getaffinity(0))
@@ -197,15 +200,20 @@ def cpu_baseline(wl, hb, n_req):
         cores = os.cpu_count() or 1
     reqs = wl.batches[-1][:n_req]
     t0 = time.perf_counter()
-    rows = 0
-    for i, r in enumerate(reqs):
-        p = int(hb.prefix_lens[i])
-        oa.extend_rows(wl, r, p)
-        rows += len(r.tokens) - p
-    dt = time.perf_counter() - t0
+    rows, passes = 0, 0
+    while True:
+        for i, r in enumerate(reqs):
+            p = int(hb.prefix_lens[i])
+            oa.extend_rows(wl, r, p)
+            rows += len(r.tokens) - p
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
     return {"value": rows / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"float64 numpy oracle: extend rows of the first {len(reqs)} of {len(wl.batches[-1])} "
-                      f"requests ({rows} query tokens over their full contexts), {dt:.1f} s"}
+            "sample": f"float64 numpy oracle (BLAS threads = {cores}): extend rows of the first {len(reqs)} of "
+                      f"{len(wl.batches[-1])} requests over their full contexts, {passes} pass(es), "
+                      f"{rows} query tokens in {dt:.1f} s"}
 
 
 def main():
@@ -222,6 +230,13 @@ def main():
     pkv.lib()
     b = FewshotBench(torch, a.workload)
     wl = b.wl
+    if a.copy_calib_mib:
+        n = a.copy_calib_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(a.warmup):
         b.step()
     b.timer.reset()

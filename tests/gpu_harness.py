@@ -62,7 +62,7 @@ class Run:
     """Executes a workload: pre-insert, batches (scatter + extend), decode steps."""
 
     def __init__(self, wl, dev="cuda", oracle_host=True, sample_rows: Optional[int] = None, seed=0,
-                 check_pool=False):
+                 check_pool=False, req_stride: int = 1):
         import torch
         self.torch = torch
         self.wl = wl
@@ -72,6 +72,7 @@ class Run:
         self.sample_rows = sample_rows
         self.rng = np.random.default_rng(seed)
         self.check_pool = check_pool
+        self.req_stride = req_stride      # check every req_stride-th request of a batch
         self.stats: List[Dict] = []
         self.oracle_log = od.run_workload_host(wl) if oracle_host else None
 
@@ -138,7 +139,7 @@ class Run:
         got_rows, ref_rows = [], []
         for i, r in enumerate(batch):
             p, e = int(hb.prefix_lens[i]), int(hb.extend_lens[i])
-            if e == 0:
+            if e == 0 or i % self.req_stride:
                 continue
             q0 = int(hb.qo_indptr[i])
             if self.sample_rows is None or e <= self.sample_rows:
