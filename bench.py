@@ -102,51 +102,68 @@ def kv_row_bytes(shape):
     return 2 * shape.hkv * shape.d * eb   # K and V of one token
 
 
-class FewshotBench:
-    """Default workload; see the module docstring."""
+class PathBench:
+    """One workload's hot path; see the module docstring for what a step is."""
 
-    def __init__(self, torch, wl_name="fewshot_bf16"):
+    CHUNK_ROWS = 65536   # setup scatter in chunks, so host memory stays bounded
+
+    def __init__(self, torch, wl_name="fewshot_bf16", total_steps=64):
         import workloads
         from prefix_shared_kv_match_amd.runtime import Engine
         self.torch = torch
-        self.wl = wl = workloads.make(wl_name)
+        kw = {"steps": max(32, total_steps)} if wl_name == "decode_bf16" else {}
+        self.wl = wl = workloads.make(wl_name, **kw)
+        self.name = wl_name
+        self.decode_only = not wl.extend_attention
         s = wl.shape
         self.eng = Engine(wl.pool_slots, s.hq, s.hkv, s.d, s.qo_dtype, s.pool_dtype, wl.free_order, "cuda",
                           wl.k_scale, wl.v_scale, wl.k_inv_scale, wl.v_inv_scale, s.sm_scale)
+        eng = self.eng
         self.steps_dec = int(wl.decode_tokens.shape[0])
         self.stride = wl.max_len()
-        eng = self.eng
-        dev = torch.device("cuda")
-        # cache the shared prefix (its K/V written to the pool) before anything is timed
+        batch = wl.batches[-1]
+        B = len(batch)
+        self.batch = batch
+        self.timer = Timer(torch)
+        # cache the shared prefixes (their K/V written to the pool) before anything is timed
         for r in wl.pre_insert:
             hb = eng.prepare([r.tokens], self.stride)
             self._scatter_rows(hb.new_slots, r.rows[hb.prefix_lens[0]:])
             eng.release(hb)
-        batch = wl.batches[-1]
-        self.batch = batch
         self.tokens = [r.tokens for r in batch]
-        self.full_tokens = [np.concatenate([r.tokens, wl.decode_tokens[:, i]]) for i, r in enumerate(batch)]
         self.prompt_lens = [len(r.tokens) for r in batch]
-        # source rows of the batch's new tokens: every step matches exactly the cached prefix
-        pl = np.array([len(wl.pre_insert[0].tokens) if wl.pre_insert else 0] * len(batch))
-        self.new_rows = np.concatenate([r.rows[p:] for r, p in zip(batch, pl)])
-        self.k_src, self.v_src = self._src(wl.values.k(self.new_rows)), self._src(wl.values.v(self.new_rows))
-        self.q = self._src(wl.values.q(self.new_rows))
-        self.o = torch.empty_like(self.q)
-        self.dk = [self._src(wl.values.k(wl.decode_rows[s])) for s in range(self.steps_dec)]
-        self.dv = [self._src(wl.values.v(wl.decode_rows[s])) for s in range(self.steps_dec)]
-        self.dq = [self._src(wl.values.q(wl.decode_rows[s])) for s in range(self.steps_dec)]
-        self.do = torch.empty_like(self.dq[0]) if self.steps_dec else None
-        B = len(batch)
-        self.max_len = max(self.prompt_lens) + self.steps_dec
-        if self.steps_dec:
+        dev = torch.device("cuda")
+        if self.decode_only:
+            # the decode batch's contexts are prepared and written once; each step is one decode step
+            hb = eng.prepare(self.tokens, self.stride)
+            new_rows = np.concatenate([r.rows[p:] for r, p in zip(batch, hb.prefix_lens)])
+            self._scatter_rows(hb.new_slots, new_rows)
+            self.hb = hb
+            self.r2t_dev = torch.from_numpy(hb.req_to_token.copy()).to(dev)
+            self.max_len = self.stride
+            self.step_i = 0
+        else:
+            pl = np.array([len(wl.pre_insert[0].tokens) if wl.pre_insert else 0] * B)
+            self.new_rows = np.concatenate([r.rows[p:] for r, p in zip(batch, pl)])
+            self.k_src, self.v_src = self._src(wl.values.k(self.new_rows)), self._src(wl.values.v(self.new_rows))
+            self.q = self._src(wl.values.q(self.new_rows))
+            self.o = torch.empty_like(self.q)
+            self.full_tokens = [np.concatenate([r.tokens, wl.decode_tokens[:, i]]) for i, r in enumerate(batch)]
+            self.max_len = max(self.prompt_lens) + self.steps_dec
+        n_dec = self.steps_dec
+        self.dk = [self._src(wl.values.k(wl.decode_rows[i])) for i in range(n_dec)]
+        self.dv = [self._src(wl.values.v(wl.decode_rows[i])) for i in range(n_dec)]
+        self.dq = [self._src(wl.values.q(wl.decode_rows[i])) for i in range(n_dec)]
+        self.do = torch.empty_like(self.dq[0]) if n_dec else None
+        if n_dec:
             self.ws, self.chunk = eng.decode_workspace(B, self.max_len)
-        # device tables, refreshed from pinned host copies every step
-        self.r2t_dev = torch.empty((B, self.stride), dtype=torch.int32, device=dev)
+        # two pinned staging buffers for the per-step slots / lengths, each guarded by an event, so
+        # the host can prepare step i+1 while the GPU still copies step i's values
+        self.stage = [(torch.empty(B, dtype=torch.int32).pin_memory(), torch.empty(B, dtype=torch.int32).pin_memory(),
+                       torch.cuda.Event()) for _ in range(2)]
+        self.stage_i = 0
         self.dec_slots_dev = torch.empty(B, dtype=torch.int32, device=dev)
         self.seq_dev = torch.empty(B, dtype=torch.int32, device=dev)
-        self.timer = Timer(torch)
-        self.n_private = None
         self.last_tables = None
 
     def _src(self, a):
@@ -156,30 +173,50 @@ class FewshotBench:
         return t.to("cuda")
 
     def _scatter_rows(self, slots, rows):
-        if rows.size == 0:
-            return
-        sl = self.torch.from_numpy(np.ascontiguousarray(slots, dtype=np.int32)).to("cuda")
-        self.eng.scatter(sl, self._src(self.wl.values.k(rows)), self._src(self.wl.values.v(rows)))
+        for lo in range(0, rows.size, self.CHUNK_ROWS):
+            r = rows[lo:lo + self.CHUNK_ROWS]
+            sl = self.torch.from_numpy(np.ascontiguousarray(slots[lo:lo + self.CHUNK_ROWS], dtype=np.int32)).to("cuda")
+            self.eng.scatter(sl, self._src(self.wl.values.k(r)), self._src(self.wl.values.v(r)))
+        self.torch.cuda.synchronize()
+
+    def _decode_step(self, hb, r2t_dev, i):
+        """rt_decode_step -> H2D (slots, lengths) -> append to the device table -> kv_scatter -> decode."""
+        import prefix_shared_kv_match_amd as pkv
+        torch, eng, T = self.torch, self.eng, self.timer
+        slots = eng.decode_alloc(hb)
+        sh, lh, ev = self.stage[self.stage_i]
+        self.stage_i ^= 1
+        ev.synchronize()                      # the copies that last read this staging buffer are done
+        sh.numpy()[:] = slots
+        lh.numpy()[:] = hb.seq_lens
+        self.dec_slots_dev.copy_(sh, non_blocking=True)
+        self.seq_dev.copy_(lh, non_blocking=True)
+        ev.record()
+        pkv.pkv_append_slots(r2t_dev, self.seq_dev, self.dec_slots_dev)
+        with T.span("kv_scatter_decode"):
+            eng.scatter(self.dec_slots_dev, self.dk[i], self.dv[i])
+        with T.span("decode_attention"):
+            eng.decode(self.dq[i], r2t_dev, self.seq_dev, self.max_len, self.ws, self.chunk, self.do)
 
     def step(self):
         import prefix_shared_kv_match_amd as pkv
-        torch, eng, T = self.torch, self.eng, self.timer
-        hb = eng.prepare(self.tokens, self.stride)                       # host: a1-a5
+        eng, T = self.eng, self.timer
+        if self.decode_only:
+            i = self.step_i % self.steps_dec
+            self.step_i += 1
+            if int(self.hb.seq_lens.max()) >= self.stride:
+                raise RuntimeError("decode bench ran past the table stride; use fewer steps")
+            self._decode_step(self.hb, self.r2t_dev, i)
+            self.last_tables = self.hb
+            return self.hb.n
+        hb = eng.prepare(self.tokens, self.stride)                       # host: match/lock/alloc/insert
         dt = eng.device_tables(hb)                                       # H2D tables + plan
         with T.span("kv_scatter"):
             eng.scatter(dt["new_slots"], self.k_src, self.v_src)
-        if self.wl.extend_attention:
-            with T.span("extend_attention"):
-                eng.extend(dt, self.q, self.o)
-        for s in range(self.steps_dec):
-            slots = eng.decode_alloc(hb)                                 # host: one slot per sequence
-            self.r2t_dev.copy_(torch.from_numpy(hb.req_to_token), non_blocking=False)
-            self.dec_slots_dev.copy_(torch.from_numpy(slots))
-            self.seq_dev.copy_(torch.from_numpy(hb.seq_lens))
-            with T.span("kv_scatter_decode"):
-                eng.scatter(self.dec_slots_dev, self.dk[s], self.dv[s])
-            with T.span("decode_attention"):
-                eng.decode(self.dq[s], self.r2t_dev, self.seq_dev, self.max_len, self.ws, self.chunk, self.do)
+        with T.span("extend_attention"):
+            eng.extend(dt, self.q, self.o)
+        for i in range(self.steps_dec):
+            self._decode_step(hb, dt["req_to_token"], i)
         if self.steps_dec:
             eng.finish(hb, self.full_tokens, self.prompt_lens)
         else:
@@ -190,9 +227,10 @@ class FewshotBench:
         return int(hb.extend_lens.sum()) + self.steps_dec * hb.n
 
 
-def cpu_baseline(wl, hb, n_req, min_seconds=10.0):
-    """The float64 oracle on a bounded sample: the extend rows of the first n_req requests,
-    repeated until at least min_seconds of CPU work."""
+def cpu_baseline(wl, hb, n_req, decode_only=False, steps_done=0, min_seconds=10.0):
+    """The float64 oracle on a bounded sample, repeated until at least min_seconds of CPU work:
+    the extend rows of the first n_req requests, or (decode workload) the newest decode row of
+    the first n_req sequences over their whole current context."""
     from oracle import attention as oa
     try:
         cores = len(os.sched_getaffinity(0))
@@ -203,17 +241,22 @@ def cpu_baseline(wl, hb, n_req, min_seconds=10.0):
     rows, passes = 0, 0
     while True:
         for i, r in enumerate(reqs):
-            p = int(hb.prefix_lens[i])
-            oa.extend_rows(wl, r, p)
-            rows += len(r.tokens) - p
+            if decode_only:
+                oa.decode_row(wl, np.concatenate([r.rows, wl.decode_rows[:steps_done, i]]))
+                rows += 1
+            else:
+                p = int(hb.prefix_lens[i])
+                oa.extend_rows(wl, r, p)
+                rows += len(r.tokens) - p
         passes += 1
         dt = time.perf_counter() - t0
         if dt >= min_seconds:
             break
     return {"value": rows / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"float64 numpy oracle (BLAS threads = {cores}): extend rows of the first {len(reqs)} of "
-                      f"{len(wl.batches[-1])} requests over their full contexts, {passes} pass(es), "
-                      f"{rows} query tokens in {dt:.1f} s"}
+            "sample": f"float64 numpy oracle (BLAS threads = {cores}): "
+                      f"{'newest decode row' if decode_only else 'extend rows'} of the first {len(reqs)} of "
+                      f"{len(wl.batches[-1])} {'sequences' if decode_only else 'requests'} over their full contexts, "
+                      f"{passes} pass(es), {rows} query tokens in {dt:.1f} s"}
 
 
 def main():
@@ -228,7 +271,7 @@ def main():
         return 2
     import prefix_shared_kv_match_amd as pkv
     pkv.lib()
-    b = FewshotBench(torch, a.workload)
+    b = PathBench(torch, a.workload, a.warmup + a.steps)
     wl = b.wl
     if a.copy_calib_mib:
         n = a.copy_calib_mib * (1 << 20) // 4
@@ -268,8 +311,9 @@ def main():
             "ms": dec_ms, "kv_gathered_gbps": dec_bytes / dec_ms / 1e6,
             "frac_hbm": dec_bytes / dec_ms / 1e6 / PEAK_HBM_GBPS, "bytes": dec_bytes,
             "tflops": 4.0 * s.d * s.hq * float(ctx.sum()) / dec_ms / 1e9}
-    sc_ms = b.timer.avg_ms("kv_scatter")
-    n_new = int(hb.extend_lens.sum())
+    sc_name = "kv_scatter_decode" if b.decode_only else "kv_scatter"
+    sc_ms = b.timer.avg_ms(sc_name)
+    n_new = hb.n if b.decode_only else int(hb.extend_lens.sum())
     src_b = 2 * s.hkv * s.d * (4 if s.qo_dtype == "f32" else 2)
     kernels["kv_scatter"] = {"ms": sc_ms, "gbps": n_new * (src_b + kv_tok) / sc_ms / 1e6}
     if wl.extend_attention:
@@ -285,13 +329,14 @@ def main():
         "dtype": "bf16" if s.qo_dtype == "bf16" else "f32", "data": "synthetic",
         "config": {"workload": wl.name, "requests": hb.n, "query_tokens_per_step": tokens // a.steps,
                    "hq": s.hq, "hkv": s.hkv, "head_dim": s.d, "pool_dtype": s.pool_dtype,
-                   "pool_slots": wl.pool_slots, "decode_steps_per_step": b.steps_dec},
+                   "pool_slots": wl.pool_slots, "decode_steps_per_step": 1 if b.decode_only else b.steps_dec},
         "roofline": {"bound": bound, "kernel": dom, "achieved": achieved, "peak": peak, "unit": unit,
                      "frac": achieved / peak, "traffic": TRAFFIC_KIB},
         "kernels": kernels,
+        "library": os.path.relpath(pkv._capi.LIB_PATH, ROOT),
     }
     if not a.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, hb, a.cpu_sample)
+        out["cpu_baseline"] = cpu_baseline(wl, hb, a.cpu_sample, b.decode_only, b.step_i if b.decode_only else 0)
     print(json.dumps(out), flush=True)
     return 0
 

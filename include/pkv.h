@@ -186,6 +186,13 @@ int pkv_kv_scatter(const void* k_src, const void* v_src, int32_t src_dtype, cons
                    void* k_pool, void* v_pool, int32_t pool_dtype, int64_t num_slots, int32_t hkv, int32_t d,
                    const float* k_inv_scale, const float* v_inv_scale, void* stream);
 
+/* Device side of one decode step's table emit (rt_decode_step fills the host table):
+ * req_to_token[b*stride + seq_lens[b] - 1] = slots[b] for b < batch, where seq_lens are the
+ * lengths AFTER the step (the new token included).  Entries whose position falls outside
+ * [0, stride) are skipped.  All pointers are device pointers. */
+int pkv_append_slots(int32_t* req_to_token, int64_t stride, const int32_t* seq_lens, const int32_t* slots,
+                     int32_t batch, void* stream);
+
 /* Host-side plan for pkv_extend_attention: split each request's extend rows into query
  * tiles of `tile` tokens and order the tiles by descending work (context length), so
  * the longest tiles start first.  prefix_lens/extend_lens are HOST arrays [num_reqs].

@@ -18,7 +18,7 @@ __all__ = [
     "rt_create", "rt_destroy", "rt_match_prefix", "rt_insert", "rt_inc_lock_ref", "rt_dec_lock_ref",
     "rt_evict", "rt_alloc", "rt_free", "rt_take_eviction_log", "rt_evictable_size", "rt_protected_size",
     "rt_free_size", "rt_clock", "rt_copy_free_list", "rt_dump", "rt_prepare_extend", "rt_release",
-    "rt_decode_step", "rt_finish", "pkv_kv_scatter", "pkv_extend_tile", "pkv_extend_plan",
+    "rt_decode_step", "rt_finish", "pkv_kv_scatter", "pkv_append_slots", "pkv_extend_tile", "pkv_extend_plan",
     "pkv_extend_attention", "pkv_decode_chunk", "pkv_decode_workspace_bytes", "pkv_decode_attention",
 ]
 
@@ -240,6 +240,16 @@ def pkv_kv_scatter(k_src, v_src, slots, k_pool, v_pool, k_inv_scale=None, v_inv_
             _dev(k_inv_scale, "k_inv_scale", torch.float32), _dev(v_inv_scale, "v_inv_scale", torch.float32),
             _stream(stream))
     check(lib().pkv_kv_scatter(*args))
+
+
+def pkv_append_slots(req_to_token, seq_lens, slots, stream=None) -> None:
+    torch = _torch()
+    b = slots.shape[0]
+    if seq_lens.shape != (b,) or req_to_token.dim() != 2 or req_to_token.shape[0] < b:
+        raise ValueError("append_slots: shape mismatch")
+    check(lib().pkv_append_slots(_dev(req_to_token, "req_to_token", torch.int32), req_to_token.shape[1],
+                                 _dev(seq_lens, "seq_lens", torch.int32), _dev(slots, "slots", torch.int32), b,
+                                 _stream(stream)))
 
 
 def pkv_extend_tile(qo_dtype: int, pool_dtype: int, hq: int, hkv: int, d: int) -> int:

@@ -5,7 +5,8 @@ import ctypes as C
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpkv.so")
+# PKV_LIBRARY overrides the in-tree build (for comparing builds); there is no other fallback
+LIB_PATH = os.environ.get("PKV_LIBRARY") or os.path.join(_HERE, "libpkv.so")
 
 PKV_F32, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2
 ERRORS = {-1: "PKV_ERR_INVAL", -2: "PKV_ERR_OOM", -3: "PKV_ERR_LOCK", -4: "PKV_ERR_SLOT", -5: "PKV_ERR_NODE",
@@ -48,6 +49,7 @@ SIGNATURES = {
     "rt_decode_step": (_i64, [_p, _i32, _p, _i64, _p, _p]),
     "rt_finish": (C.c_int, [_p, _i32, _p, _p, _p, _i64, _p, _p, _p]),
     "pkv_kv_scatter": (C.c_int, [_p, _p, _i32, _p, _i64, _p, _p, _i32, _i64, _i32, _i32, _p, _p, _p]),
+    "pkv_append_slots": (C.c_int, [_p, _i64, _p, _p, _i32, _p]),
     "pkv_extend_plan_size": (_i64, [_p, _i32, _i32]),
     "pkv_extend_plan": (_i64, [_p, _p, _i32, _i32, _p, _i64]),
     "pkv_extend_tile": (_i32, [_i32, _i32, _i32, _i32, _i32]),

@@ -147,7 +147,14 @@ __device__ __forceinline__ int sigma(int mb, int rho) {
   return 32 * (mb >> 1) + 8 * (rho >> 2) + 4 * (mb & 1) + (rho & 3);
 }
 
-// Staging of one 64-token K/V tile: global -> registers (prefetch) -> LDS.
+// LDS row of kv token t in the K tile.  With a 272 B row stride a row starts at bank 4*row
+// (mod 64), and one MFMA block reads tokens {0-3, 8-11, 16-19, 24-27} (+4, +32): flipping
+// bit 2 of the row for the upper half of each 32-token group makes those 16 rows start on
+// 16 different banks, so the 16-byte A-operand reads are conflict free.
+__device__ __forceinline__ int krow(int t) { return t ^ (((t >> 4) & 1) << 2); }
+
+// Staging of one 64-token K/V tile: global -> registers (prefetch) -> LDS.  Native vector
+// types keep the prefetch registers in VGPRs.
 template <int POOL>
 struct TileStage;
 
@@ -155,7 +162,7 @@ template <>
 struct TileStage<PKV_BF16> {
   // K: 64 rows x 256 B = 1024 chunks of 16 B, 4 per thread (rows tid/16 + 16 i, chunk tid%16).
   // V: thread -> 4 consecutive tokens (4*(tid%16) .. +3) x 8 d (8*(tid/16) .. +7).
-  uint4 k0, k1, k2, k3, v0, v1, v2, v3;
+  u32x4 k0, k1, k2, k3, v0, v1, v2, v3;
   __device__ __forceinline__ void load(const uint8_t* kpool, const uint8_t* vpool, const int32_t* row, int kv0,
                                        int ctx, int hkv, int g, int tid) {
     const int64_t slot_bytes = (int64_t)hkv * kD * 2;
@@ -163,36 +170,35 @@ struct TileStage<PKV_BF16> {
     const uint8_t* kb = kpool + head + (tid & 15) * 16;
     const uint8_t* vb = vpool + head + (tid >> 4) * 16;
     const int kt = kv0 + (tid >> 4), vt = kv0 + 4 * (tid & 15);
-    k0 = *(const uint4*)(kb + (int64_t)row[kt < ctx ? kt : 0] * slot_bytes);
-    k1 = *(const uint4*)(kb + (int64_t)row[kt + 16 < ctx ? kt + 16 : 0] * slot_bytes);
-    k2 = *(const uint4*)(kb + (int64_t)row[kt + 32 < ctx ? kt + 32 : 0] * slot_bytes);
-    k3 = *(const uint4*)(kb + (int64_t)row[kt + 48 < ctx ? kt + 48 : 0] * slot_bytes);
-    v0 = *(const uint4*)(vb + (int64_t)row[vt < ctx ? vt : 0] * slot_bytes);
-    v1 = *(const uint4*)(vb + (int64_t)row[vt + 1 < ctx ? vt + 1 : 0] * slot_bytes);
-    v2 = *(const uint4*)(vb + (int64_t)row[vt + 2 < ctx ? vt + 2 : 0] * slot_bytes);
-    v3 = *(const uint4*)(vb + (int64_t)row[vt + 3 < ctx ? vt + 3 : 0] * slot_bytes);
+    k0 = *(const u32x4*)(kb + (int64_t)row[kt < ctx ? kt : 0] * slot_bytes);
+    k1 = *(const u32x4*)(kb + (int64_t)row[kt + 16 < ctx ? kt + 16 : 0] * slot_bytes);
+    k2 = *(const u32x4*)(kb + (int64_t)row[kt + 32 < ctx ? kt + 32 : 0] * slot_bytes);
+    k3 = *(const u32x4*)(kb + (int64_t)row[kt + 48 < ctx ? kt + 48 : 0] * slot_bytes);
+    v0 = *(const u32x4*)(vb + (int64_t)row[vt < ctx ? vt : 0] * slot_bytes);
+    v1 = *(const u32x4*)(vb + (int64_t)row[vt + 1 < ctx ? vt + 1 : 0] * slot_bytes);
+    v2 = *(const u32x4*)(vb + (int64_t)row[vt + 2 < ctx ? vt + 2 : 0] * slot_bytes);
+    v3 = *(const u32x4*)(vb + (int64_t)row[vt + 3 < ctx ? vt + 3 : 0] * slot_bytes);
   }
   __device__ __forceinline__ void store(bf16* Ks, bf16* Vt, int tid) const {
-    bf16* kd = Ks + (tid >> 4) * kKStride + (tid & 15) * 8;
-    *(uint4*)(kd) = k0;
-    *(uint4*)(kd + 16 * kKStride) = k1;
-    *(uint4*)(kd + 32 * kKStride) = k2;
-    *(uint4*)(kd + 48 * kKStride) = k3;
+    const int r = tid >> 4;   // tokens r, r+16, r+32, r+48
+    bf16* kd = Ks + (tid & 15) * 8;
+    *(u32x4*)(kd + krow(r) * kKStride) = k0;
+    *(u32x4*)(kd + krow(r + 16) * kKStride) = k1;
+    *(u32x4*)(kd + krow(r + 32) * kKStride) = k2;
+    *(u32x4*)(kd + krow(r + 48) * kKStride) = k3;
     store_vt(Vt, tid, v0, v1, v2, v3);
   }
   // Writes 4 tokens x 8 d (token-major in registers) to V^T [d][token].
-  static __device__ __forceinline__ void store_vt(bf16* Vt, int tid, uint4 a, uint4 b, uint4 c, uint4 d) {
+  static __device__ __forceinline__ void store_vt(bf16* Vt, int tid, u32x4 a, u32x4 b, u32x4 c, u32x4 d) {
     const int d0 = 8 * (tid >> 4), t0 = 4 * (tid & 15);
     bf16* base = Vt + d0 * kVStride + t0;
-    const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w};
-    const uint32_t wc[4] = {c.x, c.y, c.z, c.w}, wd[4] = {d.x, d.y, d.z, d.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       // d = d0 + 2i (low halves) and d0 + 2i + 1 (high halves)
-      const uint2 lo = make_uint2((wa[i] & 0xFFFFu) | (wb[i] << 16), (wc[i] & 0xFFFFu) | (wd[i] << 16));
-      const uint2 hi = make_uint2((wa[i] >> 16) | (wb[i] & 0xFFFF0000u), (wc[i] >> 16) | (wd[i] & 0xFFFF0000u));
-      *(uint2*)(base + (2 * i) * kVStride) = lo;
-      *(uint2*)(base + (2 * i + 1) * kVStride) = hi;
+      const u32x2 lo = {(a[i] & 0xFFFFu) | (b[i] << 16), (c[i] & 0xFFFFu) | (d[i] << 16)};
+      const u32x2 hi = {(a[i] >> 16) | (b[i] & 0xFFFF0000u), (c[i] >> 16) | (d[i] & 0xFFFF0000u)};
+      *(u32x2*)(base + (2 * i) * kVStride) = lo;
+      *(u32x2*)(base + (2 * i + 1) * kVStride) = hi;
     }
   }
 };
@@ -205,53 +211,43 @@ template <>
 struct TileStage<PKV_FP8_E4M3> {
   // K: 64 rows x 128 B = 512 chunks of 16 B, 2 per thread (rows tid/8 + 32 i, chunk tid%8).
   // V: thread -> 4 tokens x 8 d, 8 B of codes each.
-  uint4 k[2];
-  uint2 v[4];
+  u32x4 k0, k1;
+  u32x2 v0, v1, v2, v3;
   __device__ __forceinline__ void load(const uint8_t* kpool, const uint8_t* vpool, const int32_t* row, int kv0,
                                        int ctx, int hkv, int g, int tid) {
     const int64_t slot_bytes = (int64_t)hkv * kD;
     const int64_t head = (int64_t)g * kD;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int tok = kv0 + (tid >> 3) + 32 * i;
-      const int64_t slot = row[tok < ctx ? tok : 0];
-      k[i] = *(const uint4*)(kpool + slot * slot_bytes + head + (tid & 7) * 16);
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int tok = kv0 + 4 * (tid & 15) + u;
-      const int64_t slot = row[tok < ctx ? tok : 0];
-      v[u] = *(const uint2*)(vpool + slot * slot_bytes + head + (tid >> 4) * 8);
-    }
+    const uint8_t* kb = kpool + head + (tid & 7) * 16;
+    const uint8_t* vb = vpool + head + (tid >> 4) * 8;
+    const int kt = kv0 + (tid >> 3), vt = kv0 + 4 * (tid & 15);
+    k0 = *(const u32x4*)(kb + (int64_t)row[kt < ctx ? kt : 0] * slot_bytes);
+    k1 = *(const u32x4*)(kb + (int64_t)row[kt + 32 < ctx ? kt + 32 : 0] * slot_bytes);
+    v0 = *(const u32x2*)(vb + (int64_t)row[vt < ctx ? vt : 0] * slot_bytes);
+    v1 = *(const u32x2*)(vb + (int64_t)row[vt + 1 < ctx ? vt + 1 : 0] * slot_bytes);
+    v2 = *(const u32x2*)(vb + (int64_t)row[vt + 2 < ctx ? vt + 2 : 0] * slot_bytes);
+    v3 = *(const u32x2*)(vb + (int64_t)row[vt + 3 < ctx ? vt + 3 : 0] * slot_bytes);
+  }
+  static __device__ __forceinline__ u32x4 dec4(u32x2 c) {
+    return u32x4{e4m3x2_to_bf16x2(c[0]), e4m3x2_to_bf16x2(c[0] >> 16), e4m3x2_to_bf16x2(c[1]),
+                 e4m3x2_to_bf16x2(c[1] >> 16)};
+  }
+  static __device__ __forceinline__ void store_k(bf16* dst, u32x4 c) {
+    *(u32x4*)dst = dec4(u32x2{c[0], c[1]});
+    *(u32x4*)(dst + 8) = dec4(u32x2{c[2], c[3]});
   }
   __device__ __forceinline__ void store(bf16* Ks, bf16* Vt, int tid) const {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const uint32_t c[4] = {k[i].x, k[i].y, k[i].z, k[i].w};
-      uint4 a, b;
-      a.x = e4m3x2_to_bf16x2(c[0]);
-      a.y = e4m3x2_to_bf16x2(c[0] >> 16);
-      a.z = e4m3x2_to_bf16x2(c[1]);
-      a.w = e4m3x2_to_bf16x2(c[1] >> 16);
-      b.x = e4m3x2_to_bf16x2(c[2]);
-      b.y = e4m3x2_to_bf16x2(c[2] >> 16);
-      b.z = e4m3x2_to_bf16x2(c[3]);
-      b.w = e4m3x2_to_bf16x2(c[3] >> 16);
-      bf16* dst = Ks + ((tid >> 3) + 32 * i) * kKStride + (tid & 7) * 16;
-      *(uint4*)dst = a;
-      *(uint4*)(dst + 8) = b;
-    }
-    uint4 vv[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      vv[u].x = e4m3x2_to_bf16x2(v[u].x);
-      vv[u].y = e4m3x2_to_bf16x2(v[u].x >> 16);
-      vv[u].z = e4m3x2_to_bf16x2(v[u].y);
-      vv[u].w = e4m3x2_to_bf16x2(v[u].y >> 16);
-    }
-    TileStage<PKV_BF16>::store_vt(Vt, tid, vv[0], vv[1], vv[2], vv[3]);
+    const int r = tid >> 3;   // tokens r, r+32
+    bf16* kd = Ks + (tid & 7) * 16;
+    store_k(kd + krow(r) * kKStride, k0);
+    store_k(kd + krow(r + 32) * kKStride, k1);
+    TileStage<PKV_BF16>::store_vt(Vt, tid, dec4(v0), dec4(v1), dec4(v2), dec4(v3));
   }
 };
+
+// Lazy rescaling: a row's reference max only moves when a tile's max exceeds it by more than
+// this many log2 units, so P = 2^(s - m) stays <= 2^8 (fine for bf16 and fp32 sums) and the
+// 64-register output rescale runs on the first tile and almost never after.
+constexpr float kRescaleSlack = 8.f;
 
 template <int POOL, int G>
 __global__ __launch_bounds__(256, 2) void extend_mfma(const bf16* __restrict__ q, bf16* __restrict__ o,
@@ -266,6 +262,7 @@ __global__ __launch_bounds__(256, 2) void extend_mfma(const bf16* __restrict__ q
                                                       const int32_t* __restrict__ work, int hkv,
                                                       float scale_log2) {
   constexpr int BT = kRows / G;   // query tokens per work item
+  // K (row-major) and V^T tiles; the next tile is prefetched into registers during compute
   __shared__ __attribute__((aligned(16))) bf16 Ks[kBN * kKStride];
   __shared__ __attribute__((aligned(16))) bf16 Vt[kD * kVStride];
 
@@ -301,25 +298,37 @@ __global__ __launch_bounds__(256, 2) void extend_mfma(const bf16* __restrict__ q
     const bf16* qp = q + ((qrow0 + (ok ? qt[nb] : 0)) * hq + qh[nb]) * kD + 8 * lg;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      uint4 v = ok ? *(const uint4*)(qp + 32 * ks) : make_uint4(0, 0, 0, 0);
+      const u32x4 v = ok ? *(const u32x4*)(qp + 32 * ks) : u32x4{0u, 0u, 0u, 0u};
       qf[nb][ks] = __builtin_bit_cast(bf16x8, v);
     }
   }
 
   floatx4 oacc[2][8];
+  // lsum[nb] = (ones row) . P^T: element 0 of lanes 0..15 holds the softmax row sum of the
+  // bf16 P that the PV product uses (the other rows of this 16-row block are zero)
+  floatx4 lsum[2];
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb)
+  for (int nb = 0; nb < 2; ++nb) {
+    lsum[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int db = 0; db < 8; ++db) oacc[nb][db] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
   float m[2] = {-INFINITY, -INFINITY};
-  float l[2] = {0.f, 0.f};
+  const bf16 one = (bf16)(ln == 0 ? 1.f : 0.f);
+  const bf16x8 ones_row = {one, one, one, one, one, one, one, one};
   const int qpos0 = p + j0;   // position of the tile's first query token
+  // last visible kv position of this lane's rows (padded rows see the whole context)
+  int vis[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) vis[nb] = min(qpos0 + qt[nb], ctx - 1);
 
   TileStage<POOL> stage;
   const int n_tiles = (ctx + kBN - 1) / kBN;
   stage.load(kpool, vpool, row, 0, ctx, hkv, g, tid);
   for (int kt = 0; kt < n_tiles; ++kt) {
     const int kv0 = kt * kBN;
+    const bf16* K = Ks;
+    const bf16* V = Vt;
     __syncthreads();
     stage.store(Ks, Vt, tid);
     __syncthreads();
@@ -335,75 +344,82 @@ __global__ __launch_bounds__(256, 2) void extend_mfma(const bf16* __restrict__ q
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
-        const bf16x8 a = *(const bf16x8*)(Ks + sigma(mb, ln) * kKStride + 32 * ks + 8 * lg);
+        const bf16x8 a = *(const bf16x8*)(K + krow(sigma(mb, ln)) * kKStride + 32 * ks + 8 * lg);
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) s[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[nb][ks], s[mb][nb], 0, 0, 0);
       }
     }
 
-    // scale, mask (only tiles reaching past the first query position), online softmax
-    const bool need_mask = kv0 + kBN > qpos0 + 1;
+    // causal / context mask, only on tiles reaching past the first query position
+    if (kv0 + kBN > qpos0 + 1) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const int lim = vis[nb] - kv0 - 8 * lg;   // visible iff token offset - 8 lg <= lim
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int off = 32 * (mb >> 1) + 4 * (mb & 1) + i;
+            s[mb][nb][i] = off <= lim ? s[mb][nb][i] : -INFINITY;
+          }
+      }
+    }
+
+    // online softmax (log2 domain) with lazy rescaling
     bf16x8 pf[2][2];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      const int pos = qpos0 + qt[nb];
-      float mt = -INFINITY;
+      float mt = fmaxf(fmaxf(s[0][nb][0], s[0][nb][1]), fmaxf(s[0][nb][2], s[0][nb][3]));
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float x = s[mb][nb][i] * sc;
-          if (need_mask) {
-            const int k = kv0 + sigma(mb, 4 * lg + i);
-            x = (k <= pos && k < ctx) ? x : -INFINITY;
-          }
-          s[mb][nb][i] = x;
-          mt = fmaxf(mt, x);
-        }
+      for (int mb = 1; mb < 4; ++mb)
+        mt = fmaxf(mt, fmaxf(fmaxf(s[mb][nb][0], s[mb][nb][1]), fmaxf(s[mb][nb][2], s[mb][nb][3])));
       mt = fmaxf(mt, __shfl_xor(mt, 16));
       mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float mn = fmaxf(m[nb], mt);
-      const float alpha = exp2f(m[nb] - mn);
-      m[nb] = mn;
-      float ls = 0.f;
+      mt *= sc;
+      const bool up = mt > m[nb] + kRescaleSlack;
+      const float mn = up ? mt : m[nb];
+      if (__any(up)) {   // wave-uniform
+        const float alpha = __builtin_amdgcn_exp2f(m[nb] - mn);   // 1 for rows that keep their max
+        lsum[nb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) oacc[nb][db] *= alpha;
+        m[nb] = mn;
+      }
+      const float nm = -m[nb];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         bf16x8 pv;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float p0 = exp2f(s[2 * kk][nb][i] - mn);
-          const float p1 = exp2f(s[2 * kk + 1][nb][i] - mn);
-          ls += p0 + p1;
-          pv[i] = (bf16)p0;
-          pv[4 + i] = (bf16)p1;
+          pv[i] = (bf16)__builtin_amdgcn_exp2f(fmaf(s[2 * kk][nb][i], sc, nm));
+          pv[4 + i] = (bf16)__builtin_amdgcn_exp2f(fmaf(s[2 * kk + 1][nb][i], sc, nm));
         }
         pf[nb][kk] = pv;
       }
-      l[nb] = l[nb] * alpha + ls;
-#pragma unroll
-      for (int db = 0; db < 8; ++db) oacc[nb][db] *= alpha;
     }
 
-    // O^T += V^T . P^T
+    // O^T += V^T . P^T, and the row sums
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+        lsum[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_row, pf[nb][kk], lsum[nb], 0, 0, 0);
+#pragma unroll
       for (int db = 0; db < 8; ++db) {
-        const bf16x8 a = *(const bf16x8*)(Vt + (16 * db + ln) * kVStride + 32 * kk + 8 * lg);
+        const bf16x8 a = *(const bf16x8*)(V + (16 * db + ln) * kVStride + 32 * kk + 8 * lg);
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
           oacc[nb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[nb][kk], oacc[nb][db], 0, 0, 0);
       }
     }
+
   }
 
   float omul = 1.f;
   if constexpr (POOL == PKV_FP8_E4M3) omul = vscale[g];
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
-    float lt = l[nb];
-    lt += __shfl_xor(lt, 16);
-    lt += __shfl_xor(lt, 32);
+    const float lt = __shfl(lsum[nb][0], ln);   // row sum sits in lane ln (row 0 of the block)
     if (qt[nb] >= nq) continue;
     const float inv = omul / lt;
     bf16* op = o + ((qrow0 + qt[nb]) * hq + qh[nb]) * kD + 4 * lg;
@@ -411,7 +427,7 @@ __global__ __launch_bounds__(256, 2) void extend_mfma(const bf16* __restrict__ q
     for (int db = 0; db < 8; ++db) {
       const uint32_t w0 = f32_to_bf16_bits(oacc[nb][db][0] * inv) | (f32_to_bf16_bits(oacc[nb][db][1] * inv) << 16);
       const uint32_t w1 = f32_to_bf16_bits(oacc[nb][db][2] * inv) | (f32_to_bf16_bits(oacc[nb][db][3] * inv) << 16);
-      *(uint2*)(op + 16 * db) = make_uint2(w0, w1);
+      *(u32x2*)(op + 16 * db) = u32x2{w0, w1};
     }
   }
 }
@@ -488,6 +504,7 @@ extern "C" int pkv_extend_attention(const void* q, void* o, int32_t qo_dtype, co
     return fail(PKV_ERR_UNSUPPORTED, "extend: qo dtype %d, pool dtype %d, hq %d, hkv %d, d %d", qo_dtype,
                 pool_dtype, hq, hkv, d);
   if (pool_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale)) return fail(PKV_ERR_INVAL, "extend: fp8 pool needs scales");
+  if (!(sm_scale > 0.f)) return fail(PKV_ERR_INVAL, "extend: sm_scale must be positive");
   if ((int64_t)n_work * (qo_dtype == PKV_F32 ? hq : hkv) > 0x7FFFFFFFLL) return fail(PKV_ERR_INVAL, "extend: grid too large");
   hipStream_t st = (hipStream_t)stream;
   const float sc = sm_scale * kLog2e;

@@ -55,10 +55,30 @@ __global__ __launch_bounds__(256) void scatter_fp8(const uint4* __restrict__ ksr
   vpool[dst] = make_uint2(pack4_e4m3(v.x, v.y, vs), pack4_e4m3(v.z, v.w, vs));
 }
 
+// Device copy of the table emit of one decode step: req_to_token[b, seq_lens[b] - 1] = slots[b].
+__global__ __launch_bounds__(256) void append_slots(int32_t* __restrict__ r2t, int64_t stride,
+                                                    const int32_t* __restrict__ seq_lens,
+                                                    const int32_t* __restrict__ slots, int32_t batch) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= batch) return;
+  const int pos = seq_lens[b] - 1;
+  if (pos >= 0 && pos < stride) r2t[(int64_t)b * stride + pos] = slots[b];
+}
+
 }  // namespace
 }  // namespace pkv
 
 using namespace pkv;
+
+extern "C" int pkv_append_slots(int32_t* req_to_token, int64_t stride, const int32_t* seq_lens, const int32_t* slots,
+                                int32_t batch, void* stream) {
+  if (batch < 0 || stride <= 0) return fail(PKV_ERR_INVAL, "append_slots: bad sizes");
+  if (batch == 0) return PKV_OK;
+  if (!req_to_token || !seq_lens || !slots) return fail(PKV_ERR_INVAL, "append_slots: null pointer");
+  hipLaunchKernelGGL(append_slots, dim3((batch + 255) / 256), dim3(256), 0, (hipStream_t)stream, req_to_token, stride,
+                     seq_lens, slots, batch);
+  return hip_check(hipGetLastError(), "append_slots launch");
+}
 
 extern "C" int pkv_kv_scatter(const void* k_src, const void* v_src, int32_t src_dtype, const int32_t* slots, int64_t n,
                               void* k_pool, void* v_pool, int32_t pool_dtype, int64_t num_slots, int32_t hkv,
