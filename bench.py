@@ -55,20 +55,27 @@ def parse():
 
 
 class Timer:
-    """HIP events on torch's current stream (the stream every library call is given)."""
+    """HIP events on torch's current stream (the stream every library call is given).
 
-    def __init__(self, torch):
+    Events are created once, up front, and recycled: creating timing events inside the
+    timed loop costs far more host time than the kernels it measures."""
+
+    def __init__(self, torch, pool=4096):
         self.torch = torch
+        self.free = [torch.cuda.Event(enable_timing=True) for _ in range(pool)]
         self.acc = {}
         self.pending = []
 
     def span(self, name):
         t = self
+
         class _S:
             def __enter__(s):
-                s.a = t.torch.cuda.Event(enable_timing=True)
-                s.b = t.torch.cuda.Event(enable_timing=True)
+                if len(t.free) < 2:
+                    t.collect()
+                s.a, s.b = t.free.pop(), t.free.pop()
                 s.a.record()
+
             def __exit__(s, *exc):
                 s.b.record()
                 t.pending.append((name, s.a, s.b))
@@ -79,6 +86,7 @@ class Timer:
         for name, a, b in self.pending:
             ms, n = self.acc.get(name, (0.0, 0))
             self.acc[name] = (ms + a.elapsed_time(b), n + 1)
+            self.free += [a, b]
         self.pending = []
 
     def reset(self):
@@ -210,7 +218,7 @@ class PathBench:
             self.last_tables = self.hb
             return self.hb.n
         hb = eng.prepare(self.tokens, self.stride)                       # host: match/lock/alloc/insert
-        dt = eng.device_tables(hb)                                       # H2D tables + plan
+        dt = eng.device_tables(hb, staged=True)                          # H2D tables + plan (async)
         with T.span("kv_scatter"):
             eng.scatter(dt["new_slots"], self.k_src, self.v_src)
         with T.span("extend_attention"):

@@ -103,11 +103,43 @@ class Engine:
     def to_dev(self, a: np.ndarray):
         return self.torch.from_numpy(np.ascontiguousarray(a)).to(self.device, non_blocking=False)
 
-    def device_tables(self, hb: HostBatch):
-        work = pkv_extend_plan(hb.prefix_lens, hb.extend_lens, self.tile)
-        return dict(req_to_token=self.to_dev(hb.req_to_token), prefix_lens=self.to_dev(hb.prefix_lens),
-                    extend_lens=self.to_dev(hb.extend_lens), qo_indptr=self.to_dev(hb.qo_indptr),
-                    new_slots=self.to_dev(hb.new_slots), work=self.to_dev(work.reshape(-1, 2)))
+    def device_tables(self, hb: HostBatch, staged: bool = False):
+        """Copy one batch's tables (and its extend plan) to the device.
+
+        staged=True copies through two alternating pinned host buffers with asynchronous
+        copies on the current stream, so the host can prepare the next batch while the GPU
+        still works on this one; the returned device tensors are reused by the next staged
+        call (stream order keeps that safe)."""
+        work = pkv_extend_plan(hb.prefix_lens, hb.extend_lens, self.tile).reshape(-1, 2)
+        arrays = dict(req_to_token=hb.req_to_token, prefix_lens=hb.prefix_lens, extend_lens=hb.extend_lens,
+                      qo_indptr=hb.qo_indptr, new_slots=hb.new_slots, work=work)
+        if not staged:
+            return {k: self.to_dev(v) for k, v in arrays.items()}
+        torch = self.torch
+        if not hasattr(self, "_stage"):
+            self._stage = [dict(host={}, event=torch.cuda.Event()) for _ in range(2)]
+            self._stage_i = 0
+            self._dev_tables = {}
+        st = self._stage[self._stage_i]
+        self._stage_i ^= 1
+        st["event"].synchronize()          # the copies that last read these pinned buffers are done
+        out = {}
+        for k, a in arrays.items():
+            a = np.ascontiguousarray(a)
+            h = st["host"].get(k)
+            if h is None or h.numel() < a.size:
+                h = torch.empty(max(a.size, 1) * 2, dtype=torch.int32).pin_memory()
+                st["host"][k] = h
+            d = self._dev_tables.get(k)
+            if d is None or d.numel() < a.size:
+                d = torch.empty(max(a.size, 1) * 2, dtype=torch.int32, device=self.device)
+                self._dev_tables[k] = d
+            h.numpy()[:a.size] = a.reshape(-1)
+            dv = d[:a.size]
+            dv.copy_(h[:a.size], non_blocking=True)
+            out[k] = dv.view(a.shape)
+        st["event"].record()
+        return out
 
     # -- steps ---------------------------------------------------------------------------
     def prepare(self, token_lists, stride: int) -> HostBatch:
