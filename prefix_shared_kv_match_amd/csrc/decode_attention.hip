@@ -67,18 +67,22 @@ struct RowChunk<PKV_BF16, VEC> {
 template <int VEC>
 struct RowChunk<PKV_FP8_E4M3, VEC> {
   static constexpr int kBytes = VEC;
-  uint32_t w[VEC / 4];
+  float f[VEC];   // decoded once per load (hardware E4M3 conversion, two codes per instruction)
   __device__ __forceinline__ void load(const uint8_t* p) {
+    uint32_t w[VEC / 4];
     if constexpr (VEC == 8) {
-      uint2 v = *(const uint2*)p;
+      const uint2 v = *(const uint2*)p;
       w[0] = v.x; w[1] = v.y;
     } else {
       w[0] = *(const uint32_t*)p;
     }
+#pragma unroll
+    for (int j = 0; j < VEC / 4; ++j) {
+      const float2 a = e4m3x2_to_f32<false>(w[j]), b = e4m3x2_to_f32<true>(w[j]);
+      f[4 * j] = a.x; f[4 * j + 1] = a.y; f[4 * j + 2] = b.x; f[4 * j + 3] = b.y;
+    }
   }
-  __device__ __forceinline__ float get(int i) const {
-    return __uint_as_float(e4m3_to_bf16_bits((w[i / 4] >> (8 * (i & 3))) & 0xFFu) << 16);
-  }
+  __device__ __forceinline__ float get(int i) const { return f[i]; }
 };
 
 template <typename QT>
@@ -244,6 +248,144 @@ __global__ __launch_bounds__(256) void decode_split(const QT* __restrict__ q, co
   }
 }
 
+// All kv heads of a sequence in one workgroup: 16 rows of 16 lanes = HKV heads x (16/HKV)
+// token streams.  Every token's K (and V) slot row of HKV*d values is then read as one
+// contiguous run by the HKV rows of a stream, instead of HKV separate 256-byte pieces
+// fetched by different workgroups at different times.  Streams of one head are merged in
+// LDS at the end.  blockIdx.x = b * max_splits + s.
+template <typename QT, int POOL, int D, int G, int HKV>
+__global__ __launch_bounds__(256) void decode_split_slot(const QT* __restrict__ q, const uint8_t* __restrict__ kpool,
+                                                         const uint8_t* __restrict__ vpool,
+                                                         const float* __restrict__ kscale,
+                                                         const float* __restrict__ vscale,
+                                                         const int32_t* __restrict__ r2t, int64_t stride,
+                                                         const int32_t* __restrict__ seq_lens, int chunk,
+                                                         int max_splits, float qk_scale_log2,
+                                                         float* __restrict__ ws_ml, float* __restrict__ ws_acc) {
+  constexpr int VEC = D / 16;
+  constexpr int STREAMS = 16 / HKV;
+  using Chunk = RowChunk<POOL, VEC>;
+  constexpr int ROWB = D * Chunk::kBytes / VEC;
+  __shared__ float sm_ml[(STREAMS - 1) * HKV][G][2];
+  __shared__ float sm_acc[(STREAMS - 1) * HKV][G][D];
+
+  const int s = blockIdx.x % max_splits;
+  const int b = blockIdx.x / max_splits;
+  const int L = seq_lens[b];
+  const int t0 = s * chunk;
+  if (t0 >= L) return;  // the whole workgroup leaves together
+  const int t1 = min(t0 + chunk, L);
+  const int r = threadIdx.x >> 4, li = threadIdx.x & 15;
+  const int g = r % HKV, stream = r / HKV;
+  const int hq = HKV * G;
+
+  float qf[G][VEC];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const QT* qp = q + ((int64_t)b * hq + (int64_t)g * G + h) * D + li * VEC;
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) qf[h][i] = load_q<QT>(qp, i);
+  }
+  float kmul = qk_scale_log2;
+  if constexpr (POOL == PKV_FP8_E4M3) kmul *= kscale[g];
+
+  float m[G], l[G], acc[G][VEC];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m[h] = -INFINITY;
+    l[h] = 0.f;
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) acc[h][i] = 0.f;
+  }
+  const int32_t* row = r2t + (int64_t)b * stride;
+  constexpr int64_t slot_bytes = (int64_t)HKV * ROWB;
+  const int64_t head_off = (int64_t)g * ROWB + li * Chunk::kBytes;
+
+  for (int base = t0 + stream; base < t1; base += STREAMS * kUnroll) {
+    Chunk kc[kUnroll], vc[kUnroll];
+    bool valid[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int t = base + STREAMS * u;
+      valid[u] = t < t1;
+      const int64_t slot = row[valid[u] ? t : t0];
+      kc[u].load(kpool + slot * slot_bytes + head_off);
+      vc[u].load(vpool + slot * slot_bytes + head_off);
+    }
+    float sc[kUnroll][G];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float part = 0.f;
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) part = fmaf(qf[h][i], kc[u].get(i), part);
+        sc[u][h] = valid[u] ? row16_sum(part) * kmul : -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float mt = sc[0][h];
+#pragma unroll
+      for (int u = 1; u < kUnroll; ++u) mt = fmaxf(mt, sc[u][h]);
+      const float mn = fmaxf(m[h], mt);
+      if (mn == -INFINITY) continue;  // this row has not seen a token yet (uniform within the row)
+      const float alpha = __builtin_amdgcn_exp2f(m[h] - mn);
+      float p[kUnroll];
+      float psum = 0.f;
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        p[u] = __builtin_amdgcn_exp2f(sc[u][h] - mn);  // masked: 2^-inf = 0
+        psum += p[u];
+      }
+      l[h] = l[h] * alpha + psum;
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) {
+        float a = acc[h][i] * alpha;
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) a = fmaf(p[u], vc[u].get(i), a);
+        acc[h][i] = a;
+      }
+      m[h] = mn;
+    }
+  }
+
+  // merge the streams of each head into stream 0
+  if (stream > 0) {
+    const int slot_r = (stream - 1) * HKV + g;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) sm_acc[slot_r][h][li * VEC + i] = acc[h][i];
+      if (li == 0) {
+        sm_ml[slot_r][h][0] = m[h];
+        sm_ml[slot_r][h][1] = l[h];
+      }
+    }
+  }
+  __syncthreads();
+  if (stream == 0) {
+    const float vmul = POOL == PKV_FP8_E4M3 ? vscale[g] : 1.f;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      for (int st = 1; st < STREAMS; ++st) {
+        const int slot_r = (st - 1) * HKV + g;
+        float a2[VEC];
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) a2[i] = sm_acc[slot_r][h][li * VEC + i];
+        merge_state(m[h], l[h], acc[h], sm_ml[slot_r][h][0], sm_ml[slot_r][h][1], a2, VEC);
+      }
+      const int64_t part = ((int64_t)b * hq + (int64_t)g * G + h) * max_splits + s;
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) ws_acc[part * D + li * VEC + i] = acc[h][i] * vmul;
+      if (li == 0) {
+        ws_ml[part * 2 + 0] = m[h];
+        ws_ml[part * 2 + 1] = l[h];
+      }
+    }
+  }
+}
+
 template <typename OT>
 __device__ __forceinline__ void store_o(OT* p, float v);
 template <>
@@ -294,6 +436,27 @@ __global__ __launch_bounds__(256) void decode_reduce(const float* __restrict__ w
   for (int i = 0; i < PER; ++i) store_o<OT>(o + (int64_t)idx * D + lane * PER + i, out[i] * inv);
 }
 
+template <typename QT, int POOL, int D, int HKV>
+int launch_slot(int G, dim3 grid, hipStream_t st, const void* q, const void* kp, const void* vp, const float* ks,
+                const float* vs, const int32_t* r2t, int64_t stride, const int32_t* lens, int chunk, int max_splits,
+                float sc, float* ml, float* acc) {
+#define PKV_SLOT_CASE(GG)                                                                                        \
+  case GG:                                                                                                       \
+    hipLaunchKernelGGL((decode_split_slot<QT, POOL, D, GG, HKV>), grid, dim3(256), 0, st, (const QT*)q,          \
+                       (const uint8_t*)kp, (const uint8_t*)vp, ks, vs, r2t, stride, lens, chunk, max_splits, sc, \
+                       ml, acc);                                                                                 \
+    return PKV_OK;
+  switch (G) {
+    PKV_SLOT_CASE(1)
+    PKV_SLOT_CASE(2)
+    PKV_SLOT_CASE(4)
+    PKV_SLOT_CASE(8)
+    default:
+      return fail(PKV_ERR_UNSUPPORTED, "decode: group size %d", G);
+  }
+#undef PKV_SLOT_CASE
+}
+
 template <typename QT, int POOL, int D>
 int launch_split(int G, dim3 grid, hipStream_t st, const void* q, const void* kp, const void* vp, const float* ks,
                  const float* vs, const int32_t* r2t, int64_t stride, const int32_t* lens, int hkv, int chunk,
@@ -303,6 +466,13 @@ int launch_split(int G, dim3 grid, hipStream_t st, const void* q, const void* kp
     hipLaunchKernelGGL((decode_split<QT, POOL, D, GG>), grid, dim3(256), 0, st, (const QT*)q, (const uint8_t*)kp, \
                        (const uint8_t*)vp, ks, vs, r2t, stride, lens, hkv, chunk, max_splits, sc, ml, acc);     \
     return PKV_OK;
+  const dim3 slot_grid(grid.x / hkv);
+  if (hkv == 8) return launch_slot<QT, POOL, D, 8>(G, slot_grid, st, q, kp, vp, ks, vs, r2t, stride, lens, chunk,
+                                                  max_splits, sc, ml, acc);
+  if (hkv == 4) return launch_slot<QT, POOL, D, 4>(G, slot_grid, st, q, kp, vp, ks, vs, r2t, stride, lens, chunk,
+                                                  max_splits, sc, ml, acc);
+  if (hkv == 2) return launch_slot<QT, POOL, D, 2>(G, slot_grid, st, q, kp, vp, ks, vs, r2t, stride, lens, chunk,
+                                                  max_splits, sc, ml, acc);
   switch (G) {
     PKV_DECODE_CASE(1)
     PKV_DECODE_CASE(2)

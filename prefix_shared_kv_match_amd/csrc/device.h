@@ -72,6 +72,15 @@ __device__ __forceinline__ float dpp_mov(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
 }
 
+// Two E4M3 codes (bytes 0 and 1 of `w`, or bytes 2 and 3 when hi) -> two floats, exactly.
+// gfx950's conversion instruction decodes the OCP E4M3 format (checked against the
+// format's definition for all 256 codes).
+template <bool HI>
+__device__ __forceinline__ float2 e4m3x2_to_f32(uint32_t w) {
+  const auto v = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
+  return make_float2(v[0], v[1]);
+}
+
 // Sum over the 16 lanes of a DPP row; every lane of the row receives the same bits
 // (each step adds a lane's value to its partner's, and addition commutes).
 __device__ __forceinline__ float row16_sum(float x) {

@@ -203,8 +203,10 @@ struct TileStage<PKV_BF16> {
   }
 };
 
+// two E4M3 codes (low 16 bits) -> two bf16 (exact: every E4M3 value is a bf16 value)
 __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t codes2) {
-  return e4m3_to_bf16_bits(codes2 & 0xFFu) | (e4m3_to_bf16_bits((codes2 >> 8) & 0xFFu) << 16);
+  const float2 f = e4m3x2_to_f32<false>(codes2);
+  return (__float_as_uint(f.x) >> 16) | (__float_as_uint(f.y) & 0xFFFF0000u);
 }
 
 template <>
