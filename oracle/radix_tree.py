@@ -29,6 +29,19 @@ Readings where the page leaves a step open (each is listed in the design notes):
   to the tail in the order given;
 - allocation evicts (requested - free) tokens when the free list is short, then
   fails with OOM if it is still short.
+
+Eviction policies (the page names lru, lfu, slru, fifo, mru, filo and priority as
+strategy objects without their keys; these are the readings taken, each an ascending
+heap key ending in the node id so the order is total):
+- lru (default): (last access, id)            - mru: (-last access, id)
+- fifo: (created, id)                          - filo: (-created, id)
+- lfu: (hit count, last access, id)            - priority: (priority, last access, id)
+- slru: (protected, last access, id), protected = hit count >= 2 (probationary first)
+Node fields behind them: hit count = number of match calls that reused at least one of the
+node's tokens (a split's upper half takes the old count + 1, the lower half keeps the old
+count); created = clock of the insert that first cached the node's first token (a split's
+upper half inherits it); priority = max of the priorities of the inserts through the node
+(a split's upper half inherits it, as the page's split code copies priority).
 """
 from __future__ import annotations
 
@@ -57,11 +70,14 @@ class NodeError(OracleError):
     pass
 
 
+POLICIES = ("lru", "lfu", "slru", "fifo", "mru", "filo", "priority")
+
+
 class Node:
-    __slots__ = ("id", "parent", "children", "key", "value", "lock_ref", "last")
+    __slots__ = ("id", "parent", "children", "key", "value", "lock_ref", "last", "hits", "created", "priority")
 
     def __init__(self, nid: int, parent: Optional["Node"], key: List[int], value: List[int],
-                 lock_ref: int, last: int):
+                 lock_ref: int, last: int, hits: int = 0, created: int = 0, priority: int = 0):
         self.id = nid
         self.parent = parent
         self.children: Dict[int, "Node"] = {}
@@ -69,6 +85,27 @@ class Node:
         self.value = value
         self.lock_ref = lock_ref
         self.last = last
+        self.hits = hits
+        self.created = created
+        self.priority = priority
+
+
+def evict_key(policy: str, n: Node):
+    if policy == "lru":
+        return (n.last, n.id)
+    if policy == "mru":
+        return (-n.last, n.id)
+    if policy == "fifo":
+        return (n.created, n.id)
+    if policy == "filo":
+        return (-n.created, n.id)
+    if policy == "lfu":
+        return (n.hits, n.last, n.id)
+    if policy == "slru":
+        return (1 if n.hits >= 2 else 0, n.last, n.id)
+    if policy == "priority":
+        return (n.priority, n.last, n.id)
+    raise ValueError(policy)
 
 
 def lcp(a: Sequence[int], b: Sequence[int]) -> int:
@@ -81,7 +118,10 @@ def lcp(a: Sequence[int], b: Sequence[int]) -> int:
 
 
 class OracleTree:
-    def __init__(self, pool_slots: int, free_order: Optional[Sequence[int]] = None):
+    def __init__(self, pool_slots: int, free_order: Optional[Sequence[int]] = None, policy: str = "lru"):
+        if policy not in POLICIES:
+            raise OracleError(f"unknown eviction policy {policy}")
+        self.policy = policy
         self.pool_slots = int(pool_slots)
         order = list(range(pool_slots)) if free_order is None else [int(s) for s in free_order]
         if len(set(order)) != len(order) or any(s < 0 or s >= pool_slots for s in order):
@@ -107,7 +147,8 @@ class OracleTree:
     def _split(self, child: Node, k: int) -> Node:
         """Cut ``child`` after its first k tokens; return the new upper node."""
         parent = child.parent
-        upper = Node(self.next_id, parent, child.key[:k], child.value[:k], child.lock_ref, self.clock)
+        upper = Node(self.next_id, parent, child.key[:k], child.value[:k], child.lock_ref, self.clock,
+                     child.hits, child.created, child.priority)
         self.next_id += 1
         self.nodes[upper.id] = upper
         child.key = child.key[k:]
@@ -130,15 +171,32 @@ class OracleTree:
             k = lcp(child.key, key)
             if k < len(child.key):
                 upper = self._split(child, k)
+                upper.hits += 1
                 slots.extend(upper.value)
                 node = upper
                 break
+            child.hits += 1
             slots.extend(child.value)
             node = child
             key = key[k:]
         return len(slots), slots, node.id
 
-    def insert(self, key: Sequence[int], value: Sequence[int]) -> Tuple[int, int]:
+    def peek(self, key: Sequence[int]) -> int:
+        """Length of the cached prefix of ``key``; changes nothing (no split, no stamp)."""
+        key = [int(t) for t in key]
+        node = self.root
+        m = 0
+        while key and key[0] in node.children:
+            child = node.children[key[0]]
+            k = lcp(child.key, key)
+            m += k
+            if k < len(child.key):
+                break
+            node = child
+            key = key[k:]
+        return m
+
+    def insert(self, key: Sequence[int], value: Sequence[int], priority: int = 0) -> Tuple[int, int]:
         """Insert key -> value; return (already-cached length, id of the node ending the key)."""
         if len(key) != len(value):
             raise OracleError("key and value lengths differ")
@@ -156,10 +214,12 @@ class OracleTree:
             value = value[k:]
             if k < len(child.key):
                 node = self._split(child, k)
+                node.priority = max(node.priority, priority)
                 break
+            child.priority = max(child.priority, priority)
             node = child
         if key:
-            leaf = Node(self.next_id, node, key, value, 0, self.clock)
+            leaf = Node(self.next_id, node, key, value, 0, self.clock, 0, self.clock, priority)
             self.next_id += 1
             self.nodes[leaf.id] = leaf
             node.children[key[0]] = leaf
@@ -188,7 +248,7 @@ class OracleTree:
             node = node.parent
 
     def evict(self, num_tokens: int) -> int:
-        heap = [(n.last, n.id) for n in self.nodes.values()
+        heap = [(evict_key(self.policy, n), n.id) for n in self.nodes.values()
                 if n is not self.root and not n.children and n.lock_ref == 0]
         heapq.heapify(heap)
         evicted = 0
@@ -205,7 +265,7 @@ class OracleTree:
             del parent.children[x.key[0]]
             del self.nodes[x.id]
             if parent is not self.root and not parent.children and parent.lock_ref == 0:
-                heapq.heappush(heap, (parent.last, parent.id))
+                heapq.heappush(heap, (evict_key(self.policy, parent), parent.id))
         return evicted
 
     def alloc(self, n: int) -> List[int]:
@@ -248,6 +308,10 @@ class OracleTree:
                 continue
             out.append((n.id, n.parent.id, n.lock_ref, n.last, tuple(n.key), tuple(n.value)))
         return out
+
+    def dump_stats(self) -> List[Tuple[int, int, int, int]]:
+        """Live non-root nodes as (id, hit count, created, priority), by id."""
+        return [(n.id, n.hits, n.created, n.priority) for nid, n in sorted(self.nodes.items()) if n is not self.root]
 
     def path_tokens(self, nid: int) -> List[int]:
         node = self._node(nid)

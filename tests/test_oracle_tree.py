@@ -144,6 +144,7 @@ def run_against_brute_force(seqs, capacity, release_pattern, seed):
     held = []
     for i, toks in enumerate(seqs):
         exp_m, exp_slots = brute_match(model, toks)
+        assert t.peek(toks) == exp_m
         try:
             bt = driver.prepare_batch(t, [toks])
         except OOMError:
@@ -275,3 +276,119 @@ def test_insert_stamps_visited_nodes():
     lasts = {tuple(t.path_tokens(nid)): last for nid, _, _, last, _, _ in t.dump()}
     assert lasts[(1, 2)] == lasts[(1, 2, 3, 4)] == lasts[(1, 2, 3, 4, 9)] == c + 1
     assert lasts[(1, 2, 5)] == c
+
+
+# ---------------------------------------------------------------------------------------------
+# eviction-policy family and the read-only peek (the radix-cache page's strategy list; the
+# keys are readings documented in the oracle's module docstring)
+# ---------------------------------------------------------------------------------------------
+
+from oracle.radix_tree import POLICIES, evict_key  # noqa: E402
+
+
+def brute_evict_policy(t, n):
+    """Expected eviction from a snapshot under t.policy: repeatedly drop the unlocked childless
+    node with the smallest policy key (keys recomputed from the dumped fields)."""
+    stats = {nid: (h, c, p) for nid, h, c, p in t.dump_stats()}
+    nodes = {}
+    for nid, par, lock, last, _, v in t.dump():
+        h, c, p = stats[nid]
+        nodes[nid] = dict(par=par, lock=lock, val=list(v), key=None, last=last, hits=h, created=c, priority=p)
+
+    class N:
+        pass
+    out, got = [], 0
+    while got < n:
+        parents = {x["par"] for x in nodes.values()}
+        cands = []
+        for nid, x in nodes.items():
+            if x["lock"] or nid in parents:
+                continue
+            o = N()
+            o.id, o.last, o.hits, o.created, o.priority = nid, x["last"], x["hits"], x["created"], x["priority"]
+            cands.append((evict_key(t.policy, o), nid))
+        if not cands:
+            break
+        _, nid = min(cands)
+        out.append((nid, nodes[nid]["val"]))
+        got += len(nodes[nid]["val"])
+        del nodes[nid]
+    return out
+
+
+@pytest.mark.parametrize("policy", POLICIES)
+@settings(max_examples=60, deadline=None)
+@given(seqs=seq_strategy, n=st.integers(1, 30), seed=st.integers(0, 1000), keep=st.integers(0, 3),
+       matches=st.lists(st.lists(st.integers(0, 2), min_size=1, max_size=8), max_size=6))
+def test_policy_eviction_matches_brute_force(policy, seqs, n, seed, keep, matches):
+    rng = random.Random(seed)
+    t = OracleTree(200, list(rng.sample(range(200), 200)), policy=policy)
+    held = []
+    for i, toks in enumerate(seqs):
+        bt = driver.prepare_batch(t, [toks])
+        t.insert(toks, bt.rows[0], priority=i % 3)
+        held.append(bt.last_nodes[0])
+    for toks in matches:
+        t.match(toks)
+    for nid in held[keep:]:
+        driver.release(t, [nid])
+    expect = brute_evict_policy(t, n)
+    t.evict(n)
+    assert [(nid, list(s)) for nid, s in t.take_evlog()] == expect
+    check_invariants(t)
+
+
+def _three_leaves(policy):
+    # leaves A=[1,1] (created first), B=[2,2], C=[3,3] under the root, all unlocked
+    t = OracleTree(16, policy=policy)
+    for toks, prio in (([1, 1], 2), ([2, 2], 0), ([3, 3], 1)):
+        bt = driver.prepare_batch(t, [toks])
+        t.insert(toks, bt.rows[0], priority=prio)
+        driver.release(t, bt.last_nodes)
+    return t
+
+
+def evicted_key_first(t):
+    t.evict(1)
+    log = t.take_evlog()
+    return log[0][1]
+
+
+def test_policy_orders_on_a_hand_example():
+    # slots: A -> [0,1], B -> [2,3], C -> [4,5]; then A is matched twice, C once
+    def prep(policy):
+        t = _three_leaves(policy)
+        t.match([1, 1])
+        t.match([1, 1])
+        t.match([3, 3])
+        return t
+    assert evicted_key_first(prep("lru")) == [2, 3]        # B: least recently used
+    assert evicted_key_first(prep("mru")) == [4, 5]        # C: most recently used
+    assert evicted_key_first(prep("fifo")) == [0, 1]       # A: created first
+    assert evicted_key_first(prep("filo")) == [4, 5]       # C: created last
+    assert evicted_key_first(prep("lfu")) == [2, 3]        # B: never hit
+    assert evicted_key_first(prep("priority")) == [2, 3]   # B: priority 0
+    t = prep("slru")                                       # A protected (2 hits); B, C probationary
+    assert evicted_key_first(t) == [2, 3]
+    assert evicted_key_first(t) == [4, 5]
+    assert evicted_key_first(t) == [0, 1]
+
+
+def test_hit_count_and_created_across_a_split():
+    t = OracleTree(16)
+    bt = driver.prepare_batch(t, [[1, 2, 3, 4]])     # leaf created by this insert
+    driver.release(t, bt.last_nodes)
+    c0 = [c for _, _, c, _ in t.dump_stats()][0]
+    t.match([1, 2, 3, 4])                              # full hit: hits 1
+    t.match([1, 2, 9])                                 # partial: split at 2
+    stats = {tuple(t.path_tokens(nid)): (h, c) for nid, h, c, _ in t.dump_stats()}
+    assert stats[(1, 2)] == (2, c0) and stats[(1, 2, 3, 4)] == (1, c0)
+
+
+def test_peek_changes_nothing():
+    t = OracleTree(32)
+    for toks in ([1, 2, 3, 4], [1, 2, 5], [7]):
+        driver.release(t, driver.prepare_batch(t, [toks]).last_nodes)
+    before = (t.dump(), t.dump_stats(), t.clock)
+    assert t.peek([1, 2, 3, 9]) == 3 and t.peek([1, 2]) == 2 and t.peek([8]) == 0 and t.peek([7, 7]) == 1
+    assert (t.dump(), t.dump_stats(), t.clock) == before
