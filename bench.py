@@ -36,9 +36,39 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
-# rocprofv3 FETCH_SIZE / WRITE_SIZE of the extend kernel on the default workload, KiB per dispatch
-# (filled from profiles/; null until measured on the current kernel)
-TRAFFIC_KIB = None
+CSRC = os.path.join(ROOT, "prefix_shared_kv_match_amd", "csrc")
+# HBM bytes per launch of each workload's dominant kernel from two rocprofv3 --pmc passes
+# (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch; profiles/<workload>_kernels.md), scaled by
+# what the same counters read for a plain 1 GiB device copy (FETCH x2.0, WRITE x1.0).  Each
+# entry holds the hash of the kernel sources it was taken on; a changed kernel reports null.
+TRAFFIC = {
+    "fewshot_bf16": dict(kernel="extend_attention", src_hash="14e86bafad890a3a",
+                         fetch_kib=177659.8125, write_kib=102969.703125),
+    "decode_bf16": dict(kernel="decode_attention", src_hash="60535949e129ec94",
+                        fetch_kib=5050624.125, write_kib=47878.21875),
+    "longctx_fp8": dict(kernel="extend_attention", src_hash="14e86bafad890a3a",
+                        fetch_kib=1400990.5625, write_kib=262144.0625),
+}
+FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
+KERNEL_SOURCES = {"extend_attention": ["extend_attention.hip", "device.h"],
+                  "decode_attention": ["decode_attention.hip", "device.h"]}
+
+
+def kernel_src_hash(kernel: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for n in KERNEL_SOURCES[kernel]:
+        h.update(n.encode())
+        with open(os.path.join(CSRC, n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_bytes(workload: str, kernel: str):
+    t = TRAFFIC.get(workload)
+    if t is None or t["kernel"] != kernel or kernel_src_hash(kernel) != t["src_hash"]:
+        return None
+    return (t["fetch_kib"] * FETCH_SCALE + t["write_kib"] * WRITE_SCALE) * 1024.0
 
 
 def parse():
@@ -339,7 +369,7 @@ def main():
                    "hq": s.hq, "hkv": s.hkv, "head_dim": s.d, "pool_dtype": s.pool_dtype,
                    "pool_slots": wl.pool_slots, "decode_steps_per_step": 1 if b.decode_only else b.steps_dec},
         "roofline": {"bound": bound, "kernel": dom, "achieved": achieved, "peak": peak, "unit": unit,
-                     "frac": achieved / peak, "traffic": TRAFFIC_KIB},
+                     "frac": achieved / peak, "traffic": traffic_bytes(wl.name, dom)},
         "kernels": kernels,
         "library": os.path.relpath(pkv._capi.LIB_PATH, ROOT),
     }

@@ -62,6 +62,8 @@ typedef int64_t rt_node;
 
 const char* pkv_last_error(void);
 int pkv_version(void);
+/* Hash of the sources this library was built from (the binding refuses a stale build). */
+const char* pkv_source_hash(void);
 
 /* ----------------------------------------------------------------------------------
  * Radix tree and slot allocator (host)

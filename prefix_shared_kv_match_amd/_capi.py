@@ -27,6 +27,7 @@ _pi32, _pi64 = C.POINTER(C.c_int32), C.POINTER(C.c_int64)
 SIGNATURES = {
     "pkv_last_error": (C.c_char_p, []),
     "pkv_version": (C.c_int, []),
+    "pkv_source_hash": (C.c_char_p, []),
     "rt_create": (C.c_int, [_i64, _p, _i64, C.POINTER(_p)]),
     "rt_destroy": (None, [_p]),
     "rt_match_prefix": (_i64, [_p, _p, _i64, _p, _pi64]),
@@ -75,6 +76,12 @@ def lib() -> C.CDLL:
             f = getattr(h, name)
             f.restype = res
             f.argtypes = args
+        if LIB_PATH == os.path.join(_HERE, "libpkv.so"):
+            from .build import source_hash
+            built = h.pkv_source_hash().decode()
+            if built != source_hash():
+                raise ImportError(f"{LIB_PATH} was built from other sources (build {built}, sources "
+                                  f"{source_hash()}): rebuild with `python -m prefix_shared_kv_match_amd.build`")
         _lib = h
     return _lib
 

@@ -46,10 +46,24 @@ def _run(cmd):
     return out
 
 
+def source_hash() -> str:
+    """sha256 over every source the library is built from (kernels, host code, the C ABI header)."""
+    import hashlib
+    h = hashlib.sha256()
+    for d, names in ((CSRC, sorted(os.listdir(CSRC))), (INCLUDE, ["pkv.h"])):
+        for n in names:
+            if n.endswith((".cpp", ".h", ".hip")):
+                h.update(n.encode())
+                with open(os.path.join(d, n), "rb") as f:
+                    h.update(f.read())
+    return h.hexdigest()[:16]
+
+
 def build(debug: bool = False, verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     hc = hipcc()
     extra = ["-DPKV_DEBUG=1", "-g"] if debug else []
+    extra = extra + [f'-DPKV_SOURCE_HASH="{source_hash()}"']
     jobs = []
     objs = []
     for s in HOST_SOURCES:

@@ -18,3 +18,8 @@ int fail(int code, const char* fmt, ...) {
 
 extern "C" const char* pkv_last_error(void) { return pkv::g_last_error.c_str(); }
 extern "C" int pkv_version(void) { return 1; }
+
+#ifndef PKV_SOURCE_HASH
+#define PKV_SOURCE_HASH "unknown"
+#endif
+extern "C" const char* pkv_source_hash(void) { return PKV_SOURCE_HASH; }
