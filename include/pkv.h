@@ -77,6 +77,29 @@ const char* pkv_source_hash(void);
 int rt_create(int64_t num_slots, const int32_t* free_order, int64_t n_free, rt_tree** out);
 void rt_destroy(rt_tree* t);
 
+/* Eviction policies [RC "Eviction 전략" (strategy selection) and the closing remarks on
+ * several policies; RC "TreeNode 구조" for the hit count and priority fields].  Each is an
+ * ascending heap key over unlocked leaves, ending in the node id:
+ *   LRU (last access)              MRU (-last access)
+ *   FIFO (creation clock)          FILO (-creation clock)
+ *   LFU (hit count, last access)   PRIORITY (priority, last access)
+ *   SLRU (hit count >= 2 ? 1 : 0, last access): a leaf hit at least twice sits in the
+ *        protected segment and goes only after every probationary leaf.
+ * Hit count = number of match calls that reused at least one token of the node (a split's
+ * upper half starts from the old count and takes this match's hit; the lower half keeps
+ * the old count).  Creation clock = clock of the insert that created the node (a split's
+ * upper half inherits it).  Priority = max of the priorities of the inserts that walked
+ * through or created the node (a split's upper half inherits it). */
+typedef enum {
+  RT_POLICY_LRU = 0, RT_POLICY_LFU = 1, RT_POLICY_SLRU = 2, RT_POLICY_FIFO = 3,
+  RT_POLICY_MRU = 4, RT_POLICY_FILO = 5, RT_POLICY_PRIORITY = 6
+} rt_policy;
+
+/* rt_create with an eviction policy (rt_create is RT_POLICY_LRU).  An unknown policy
+ * fails with PKV_ERR_INVAL. */
+int rt_create_policy(int64_t num_slots, const int32_t* free_order, int64_t n_free, int32_t policy,
+                     rt_tree** out);
+
 /* Longest cached prefix of key[0..n) [RC "프리픽스 매칭: match_prefix"; EX matching formula].
  * Walks whole children keyed by their first token; if a child matches only partly
  * (including when the key ends inside it) the child is split at the match length
@@ -92,6 +115,23 @@ int64_t rt_match_prefix(rt_tree* t, const int32_t* key, int64_t n, int32_t* out_
  * Returns the length m that was already cached; slots[0..m) are then duplicates that
  * stay owned by the caller (free them with rt_free).  *out_last = node ending the key. */
 int64_t rt_insert(rt_tree* t, const int32_t* key, const int32_t* slots, int64_t n, rt_node* out_last);
+/* rt_insert carrying a priority [RC "삽입: _insert_helper" priority argument]: every node the
+ * walk passes (and a split's upper half) takes max(its priority, priority); a new leaf
+ * takes priority.  rt_insert is priority 0.  Only RT_POLICY_PRIORITY reads it. */
+int64_t rt_insert_priority(rt_tree* t, const int32_t* key, const int32_t* slots, int64_t n, int32_t priority,
+                           rt_node* out_last);
+
+/* Read-only prefix length: what rt_match_prefix would return for key[0..n), without a
+ * split, a clock tick, a stamp or a hit.  Used to order waiting requests by cache hit
+ * [OV and EX: cache-aware scheduling].  Returns the length or a negative error. */
+int64_t rt_peek_prefix(const rt_tree* t, const int32_t* key, int64_t n);
+
+/* Cache-aware order of waiting requests [OV and EX: longest-shared-prefix-first scheduling]:
+ * order[0..num_reqs) = request indices sorted by descending rt_peek_prefix length, ties kept
+ * in index (arrival) order; match_lens[r] (may be NULL) = request r's peek length.  The tree
+ * is not changed.  Requests are tokens[tok_indptr[r] .. tok_indptr[r+1]). */
+int rt_schedule_longest_prefix(const rt_tree* t, int32_t num_reqs, const int32_t* tokens,
+                               const int64_t* tok_indptr, int32_t* order, int64_t* match_lens);
 
 /* Lock references [RC "참조 카운트: lock_ref"]: +1 / -1 on every node from `node` up to,
  * not including, the root.  On 0 -> 1 a node's tokens move from the evictable to the
@@ -101,7 +141,7 @@ int rt_inc_lock_ref(rt_tree* t, rt_node node);
 int rt_dec_lock_ref(rt_tree* t, rt_node node);
 
 /* Evict at least num_tokens tokens [RC "Eviction 전략"; EX "LRU Evictionポリシー"]:
- * repeatedly remove the unlocked leaf with the smallest (access time, node id), append
+ * repeatedly remove the unlocked leaf with the smallest policy key (LRU: access time, node id), append
  * its slots to the free list's tail in key order, log it, and consider its parent once
  * the parent is an unlocked leaf.  Whole leaves only, so it may free more than asked.
  * Returns the number of tokens evicted (less than asked if nothing else is evictable). */
@@ -132,6 +172,10 @@ int64_t rt_copy_free_list(const rt_tree* t, int32_t* out, int64_t cap);
  * [id, parent, lock_ref, last_access, len, key[len], slots[len]].  Returns the number
  * of int64 values; writes them only if cap is large enough. */
 int64_t rt_dump(const rt_tree* t, int64_t* out, int64_t cap);
+/* Per-node policy state of every live non-root node, by ascending id, as int64 records
+ * [id, hit_count, creation_clock, priority].  Returns 4 x live nodes; writes only if cap
+ * is large enough. */
+int64_t rt_dump_stats(const rt_tree* t, int64_t* out, int64_t cap);
 
 /* Batch driver: the hot path's host steps for one batch of requests, in order.
  * For request r (tokens[tok_indptr[r] .. tok_indptr[r+1])), length L_r:
@@ -152,6 +196,11 @@ int64_t rt_prepare_extend(rt_tree* t, int32_t num_reqs, const int32_t* tokens, c
                           int32_t* req_to_token, int64_t stride, int32_t* prefix_lens,
                           int32_t* extend_lens, int32_t* qo_indptr, int32_t* new_slots, int64_t new_cap,
                           rt_node* out_last);
+/* rt_prepare_extend whose insert of request r carries priorities[r] (NULL = all 0). */
+int64_t rt_prepare_extend_prio(rt_tree* t, int32_t num_reqs, const int32_t* tokens, const int64_t* tok_indptr,
+                               const int32_t* priorities, int32_t* req_to_token, int64_t stride,
+                               int32_t* prefix_lens, int32_t* extend_lens, int32_t* qo_indptr,
+                               int32_t* new_slots, int64_t new_cap, rt_node* out_last);
 
 /* Unlock out_last entries of a prepared batch (entries < 0 are skipped). */
 int rt_release(rt_tree* t, const rt_node* nodes, int32_t n);

@@ -22,7 +22,7 @@ tokens back to insertion, applied at request granularity).
 from __future__ import annotations
 
 import dataclasses
-from typing import List, Sequence
+from typing import List, Optional, Sequence
 
 import numpy as np
 
@@ -38,9 +38,12 @@ class BatchTables:
     new_slots: List[int]         # fresh slots, concatenated in request order (= extend rows)
 
 
-def prepare_batch(tree: OracleTree, token_lists: Sequence[Sequence[int]]) -> BatchTables:
+def prepare_batch(tree: OracleTree, token_lists: Sequence[Sequence[int]],
+                  priorities: Optional[Sequence[int]] = None) -> BatchTables:
+    """Steps 1-6 for each request in order; request i's insert carries priorities[i]
+    (default 0), the priority argument of the radix-cache page's insert helper."""
     out = BatchTables([], [], [], [], [])
-    for toks in token_lists:
+    for i, toks in enumerate(token_lists):
         toks = [int(t) for t in toks]
         m, ps, a = tree.match(toks)
         tree.inc_lock(a)
@@ -49,7 +52,7 @@ def prepare_batch(tree: OracleTree, token_lists: Sequence[Sequence[int]]) -> Bat
         except OracleError:
             tree.dec_lock(a)          # a failed request leaves no lock behind
             raise
-        t, last = tree.insert(toks, ps + ns)
+        t, last = tree.insert(toks, ps + ns, 0 if priorities is None else int(priorities[i]))
         if t != m:
             raise OracleError(f"insert found {t} cached tokens after a match of {m}")
         tree.inc_lock(last)
@@ -104,9 +107,9 @@ class RunLog:
     dump: list
 
 
-def run_workload_host(wl, release_last_batch: bool = True) -> RunLog:
+def run_workload_host(wl, release_last_batch: bool = True, policy: str = "lru") -> RunLog:
     """Drive a ``workloads.Workload`` through the oracle tree (host side only)."""
-    tree = OracleTree(wl.pool_slots, wl.free_order)
+    tree = OracleTree(wl.pool_slots, wl.free_order, policy)
     batches = []
     for r in wl.pre_insert:
         bt = prepare_batch(tree, [r.tokens])

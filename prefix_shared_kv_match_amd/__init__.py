@@ -15,7 +15,9 @@ from ._capi import PKV_BF16, PKV_F32, PKV_FP8_E4M3, PkvError, check, lib
 
 __all__ = [
     "PKV_F32", "PKV_BF16", "PKV_FP8_E4M3", "PkvError", "lib",
-    "rt_create", "rt_destroy", "rt_match_prefix", "rt_insert", "rt_inc_lock_ref", "rt_dec_lock_ref",
+    "RT_POLICIES", "rt_create", "rt_create_policy", "rt_destroy", "rt_match_prefix", "rt_insert",
+    "rt_insert_priority", "rt_peek_prefix", "rt_schedule_longest_prefix", "rt_dump_stats", "rt_prepare_extend_prio",
+    "rt_inc_lock_ref", "rt_dec_lock_ref",
     "rt_evict", "rt_alloc", "rt_free", "rt_take_eviction_log", "rt_evictable_size", "rt_protected_size",
     "rt_free_size", "rt_clock", "rt_copy_free_list", "rt_dump", "rt_prepare_extend", "rt_release",
     "rt_decode_step", "rt_finish", "pkv_kv_scatter", "pkv_append_slots", "pkv_extend_tile", "pkv_extend_plan",
@@ -47,6 +49,21 @@ def rt_create(num_slots: int, free_order: Optional[Sequence[int]] = None) -> C.c
     return h
 
 
+# rt_policy codes of include/pkv.h, by name
+RT_POLICIES = {"lru": 0, "lfu": 1, "slru": 2, "fifo": 3, "mru": 4, "filo": 5, "priority": 6}
+
+
+def rt_create_policy(num_slots: int, free_order: Optional[Sequence[int]] = None, policy="lru") -> C.c_void_p:
+    code = RT_POLICIES[policy] if isinstance(policy, str) else int(policy)
+    h = C.c_void_p()
+    if free_order is None:
+        check(lib().rt_create_policy(int(num_slots), None, int(num_slots), code, C.byref(h)))
+    else:
+        fo = _i32(free_order)
+        check(lib().rt_create_policy(int(num_slots), _ptr(fo), fo.size, code, C.byref(h)))
+    return h
+
+
 def rt_destroy(t) -> None:
     lib().rt_destroy(t)
 
@@ -66,6 +83,39 @@ def rt_insert(t, key, slots) -> Tuple[int, int]:
     last = C.c_int64()
     m = check(lib().rt_insert(t, _ptr(key), _ptr(slots), key.size, C.byref(last)))
     return int(m), int(last.value)
+
+
+def rt_insert_priority(t, key, slots, priority: int) -> Tuple[int, int]:
+    key, slots = _i32(key), _i32(slots)
+    if key.size != slots.size:
+        raise ValueError("key and slots differ in length")
+    last = C.c_int64()
+    m = check(lib().rt_insert_priority(t, _ptr(key), _ptr(slots), key.size, int(priority), C.byref(last)))
+    return int(m), int(last.value)
+
+
+def rt_peek_prefix(t, key) -> int:
+    key = _i32(key)
+    return int(check(lib().rt_peek_prefix(t, _ptr(key), key.size)))
+
+
+def rt_schedule_longest_prefix(t, tokens: np.ndarray, tok_indptr: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """(order, match_lens): waiting requests by descending cached-prefix length, ties in index order."""
+    tokens = _i32(tokens)
+    tok_indptr = np.ascontiguousarray(tok_indptr, dtype=np.int64)
+    n = int(tok_indptr.size - 1)
+    order = np.empty(max(n, 1), dtype=np.int32)
+    lens = np.empty(max(n, 1), dtype=np.int64)
+    check(lib().rt_schedule_longest_prefix(t, n, _ptr(tokens), _ptr(tok_indptr), _ptr(order), _ptr(lens)))
+    return order[:n], lens[:n]
+
+
+def rt_dump_stats(t):
+    """Live non-root nodes as (id, hit count, creation clock, priority), by id."""
+    need = check(lib().rt_dump_stats(t, None, 0))
+    buf = np.empty(max(need, 1), dtype=np.int64)
+    check(lib().rt_dump_stats(t, _ptr(buf), need))
+    return [tuple(int(x) for x in buf[k:k + 4]) for k in range(0, need, 4)]
 
 
 def rt_inc_lock_ref(t, node: int) -> None:
@@ -158,6 +208,27 @@ def rt_prepare_extend(t, tokens: np.ndarray, tok_indptr: np.ndarray, req_to_toke
     return int(check(lib().rt_prepare_extend(t, n, _ptr(tokens), _ptr(tok_indptr), _ptr(req_to_token),
                                              req_to_token.shape[1], _ptr(prefix_lens), _ptr(extend_lens),
                                              _ptr(qo_indptr), _ptr(new_slots), new_slots.size, _ptr(out_last))))
+
+
+def rt_prepare_extend_prio(t, tokens: np.ndarray, tok_indptr: np.ndarray, priorities, req_to_token: np.ndarray,
+                           prefix_lens: np.ndarray, extend_lens: np.ndarray, qo_indptr: np.ndarray,
+                           new_slots: np.ndarray, out_last: np.ndarray) -> int:
+    """rt_prepare_extend whose inserts carry one priority per request (None = all 0)."""
+    n = int(tok_indptr.size - 1)
+    for a, dt in ((tokens, np.int32), (tok_indptr, np.int64), (req_to_token, np.int32), (prefix_lens, np.int32),
+                  (extend_lens, np.int32), (qo_indptr, np.int32), (new_slots, np.int32), (out_last, np.int64)):
+        if a.dtype != dt or not a.flags.c_contiguous:
+            raise TypeError("rt_prepare_extend_prio: host arrays must be C-contiguous with the documented dtypes")
+    if req_to_token.ndim != 2 or req_to_token.shape[0] < n or prefix_lens.size < n or extend_lens.size < n \
+            or qo_indptr.size < n + 1 or out_last.size < n:
+        raise ValueError("rt_prepare_extend_prio: output arrays too small")
+    pr = None if priorities is None else _i32(priorities)
+    if pr is not None and pr.size < n:
+        raise ValueError("rt_prepare_extend_prio: one priority per request")
+    return int(check(lib().rt_prepare_extend_prio(t, n, _ptr(tokens), _ptr(tok_indptr), _ptr(pr), _ptr(req_to_token),
+                                                  req_to_token.shape[1], _ptr(prefix_lens), _ptr(extend_lens),
+                                                  _ptr(qo_indptr), _ptr(new_slots), new_slots.size,
+                                                  _ptr(out_last))))
 
 
 def rt_release(t, nodes) -> None:

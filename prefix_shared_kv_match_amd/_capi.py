@@ -29,9 +29,14 @@ SIGNATURES = {
     "pkv_version": (C.c_int, []),
     "pkv_source_hash": (C.c_char_p, []),
     "rt_create": (C.c_int, [_i64, _p, _i64, C.POINTER(_p)]),
+    "rt_create_policy": (C.c_int, [_i64, _p, _i64, _i32, C.POINTER(_p)]),
     "rt_destroy": (None, [_p]),
     "rt_match_prefix": (_i64, [_p, _p, _i64, _p, _pi64]),
     "rt_insert": (_i64, [_p, _p, _p, _i64, _pi64]),
+    "rt_insert_priority": (_i64, [_p, _p, _p, _i64, _i32, _pi64]),
+    "rt_peek_prefix": (_i64, [_p, _p, _i64]),
+    "rt_schedule_longest_prefix": (C.c_int, [_p, _i32, _p, _p, _p, _p]),
+    "rt_dump_stats": (_i64, [_p, _p, _i64]),
     "rt_inc_lock_ref": (C.c_int, [_p, _i64]),
     "rt_dec_lock_ref": (C.c_int, [_p, _i64]),
     "rt_evict": (_i64, [_p, _i64]),
@@ -46,6 +51,7 @@ SIGNATURES = {
     "rt_copy_free_list": (_i64, [_p, _p, _i64]),
     "rt_dump": (_i64, [_p, _p, _i64]),
     "rt_prepare_extend": (_i64, [_p, _i32, _p, _p, _p, _i64, _p, _p, _p, _p, _i64, _p]),
+    "rt_prepare_extend_prio": (_i64, [_p, _i32, _p, _p, _p, _p, _i64, _p, _p, _p, _p, _i64, _p]),
     "rt_release": (C.c_int, [_p, _p, _i32]),
     "rt_decode_step": (_i64, [_p, _i32, _p, _i64, _p, _p]),
     "rt_finish": (C.c_int, [_p, _i32, _p, _p, _p, _i64, _p, _p, _p]),

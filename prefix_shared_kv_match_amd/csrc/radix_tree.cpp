@@ -18,6 +18,12 @@
 //  - eviction removes whole leaves and stops once >= the requested tokens are freed;
 //  - the free list is FIFO: allocate from the head, free/evict to the tail;
 //  - allocation evicts (n - free) tokens on shortfall, then reports OOM.
+//  - the page's policy family (lru, lfu, slru, fifo, mru, filo, priority) are ascending
+//    heap keys ending in the node id: lru (last access), mru (-last access), fifo / filo
+//    (+-creation clock), lfu (hit count, last access), priority (priority, last access), slru
+//    (protected = hit count >= 2, last access).  Hit count = match calls that reused a token of
+//    the node (a split's upper half takes the old count + 1); creation clock and priority are
+//    inherited by a split's upper half; priority is the max over inserts through the node.
 //
 // Storage: nodes live in a vector indexed by id (ids are never reused); a compact list
 // of live ids keeps the eviction scan proportional to the live tree.  Slot ownership
@@ -42,8 +48,34 @@ struct Node {
   std::unordered_map<int32_t, int64_t> children;
   int64_t lock_ref = 0;
   int64_t last = 0;
+  int64_t hits = 0;
+  int64_t created = 0;
+  int64_t priority = 0;
   int64_t live_pos = -1;  // index in Tree::live, -1 when dead
 };
+
+enum Policy : int32_t { kLRU = 0, kLFU = 1, kSLRU = 2, kFIFO = 3, kMRU = 4, kFILO = 5, kPriority = 6 };
+
+struct EvictKey {
+  int64_t a, b, id;
+  bool operator>(const EvictKey& o) const {
+    if (a != o.a) return a > o.a;
+    if (b != o.b) return b > o.b;
+    return id > o.id;
+  }
+};
+
+inline EvictKey evict_key(int32_t policy, const Node& n, int64_t id) {
+  switch (policy) {
+    case kMRU: return EvictKey{-n.last, 0, id};
+    case kFIFO: return EvictKey{n.created, 0, id};
+    case kFILO: return EvictKey{-n.created, 0, id};
+    case kLFU: return EvictKey{n.hits, n.last, id};
+    case kSLRU: return EvictKey{n.hits >= 2 ? 1 : 0, n.last, id};
+    case kPriority: return EvictKey{n.priority, n.last, id};
+    default: return EvictKey{n.last, 0, id};
+  }
+}
 
 inline int64_t lcp(const int32_t* a, int64_t na, const int32_t* b, int64_t nb) {
   const int64_t n = std::min(na, nb);
@@ -55,6 +87,7 @@ inline int64_t lcp(const int32_t* a, int64_t na, const int32_t* b, int64_t nb) {
 }  // namespace
 
 struct rt_tree {
+  int32_t policy = kLRU;
   int64_t num_slots = 0;
   std::vector<uint8_t> state;      // per slot
   std::vector<int32_t> ring;       // FIFO free list storage
@@ -111,6 +144,9 @@ struct rt_tree {
     U.parent = C.parent;
     U.lock_ref = C.lock_ref;
     U.last = clock;
+    U.hits = C.hits;
+    U.created = C.created;
+    U.priority = C.priority;
     U.key.assign(C.key.begin(), C.key.begin() + k);
     U.value.assign(C.value.begin(), C.value.begin() + k);
     C.key.erase(C.key.begin(), C.key.begin() + k);
@@ -149,11 +185,13 @@ struct rt_tree {
       int64_t k = lcp(nodes[c].key.data(), klen, key + pos, n - pos);
       if (k < klen) {
         int64_t up = split(c, k);
+        ++nodes[up].hits;
         std::memcpy(out + pos, nodes[up].value.data(), sizeof(int32_t) * k);
         pos += k;
         cur = up;
         break;
       }
+      ++nodes[c].hits;
       std::memcpy(out + pos, nodes[c].value.data(), sizeof(int32_t) * k);
       pos += k;
       cur = c;
@@ -178,7 +216,7 @@ struct rt_tree {
     return rc;
   }
 
-  int64_t insert(const int32_t* key, const int32_t* slots, int64_t n, int64_t* out_last) {
+  int64_t insert(const int32_t* key, const int32_t* slots, int64_t n, int64_t* out_last, int64_t priority = 0) {
     int64_t m = peek(key, n);
     int rc = check_in_flight(slots + m, n - m);
     if (rc < 0) return rc;
@@ -194,8 +232,10 @@ struct rt_tree {
       pos += k;
       if (k < klen) {
         cur = split(c, k);
+        nodes[cur].priority = std::max(nodes[cur].priority, priority);
         break;
       }
+      nodes[c].priority = std::max(nodes[c].priority, priority);
       cur = c;
     }
     if (pos != m) return pkv::fail(PKV_ERR_INTERNAL, "insert walk disagrees with peek (%lld vs %lld)",
@@ -207,6 +247,8 @@ struct rt_tree {
       L.key.assign(key + pos, key + n);
       L.value.assign(slots + pos, slots + n);
       L.last = clock;
+      L.created = clock;
+      L.priority = priority;
       nodes[cur].children[key[pos]] = leaf;
       evictable += n - pos;
       for (int64_t i = pos; i < n; ++i) state[slots[i]] = kCached;
@@ -247,15 +289,14 @@ struct rt_tree {
   }
 
   int64_t evict(int64_t num_tokens) {
-    typedef std::pair<int64_t, int64_t> Key;  // (last access, id)
-    std::priority_queue<Key, std::vector<Key>, std::greater<Key>> heap;
+    std::priority_queue<EvictKey, std::vector<EvictKey>, std::greater<EvictKey>> heap;
     for (int64_t id : live) {
       const Node& x = nodes[id];
-      if (x.children.empty() && x.lock_ref == 0) heap.push(Key(x.last, id));
+      if (x.children.empty() && x.lock_ref == 0) heap.push(evict_key(policy, x, id));
     }
     int64_t evicted = 0;
     while (evicted < num_tokens && !heap.empty()) {
-      int64_t id = heap.top().second;
+      int64_t id = heap.top().id;
       heap.pop();
       Node& x = nodes[id];
       for (int32_t s : x.value) push_free(s);
@@ -268,7 +309,7 @@ struct rt_tree {
       nodes[p].children.erase(x.key[0]);
       kill(id);
       const Node& P = nodes[p];
-      if (p != 0 && P.children.empty() && P.lock_ref == 0) heap.push(Key(P.last, p));
+      if (p != 0 && P.children.empty() && P.lock_ref == 0) heap.push(evict_key(policy, P, p));
     }
     return evicted;
   }
@@ -308,7 +349,12 @@ auto guard(F&& f) -> decltype(f()) {
 extern "C" {
 
 int rt_create(int64_t num_slots, const int32_t* free_order, int64_t n_free, rt_tree** out) {
+  return rt_create_policy(num_slots, free_order, n_free, kLRU, out);
+}
+
+int rt_create_policy(int64_t num_slots, const int32_t* free_order, int64_t n_free, int32_t policy, rt_tree** out) {
   return guard([&]() -> int {
+    if (policy < kLRU || policy > kPriority) return pkv::fail(PKV_ERR_INVAL, "unknown eviction policy %d", policy);
     if (!out) return pkv::fail(PKV_ERR_INVAL, "out is null");
     *out = nullptr;
     if (num_slots <= 0 || num_slots > INT32_MAX) return pkv::fail(PKV_ERR_INVAL, "num_slots out of range");
@@ -328,6 +374,7 @@ int rt_create(int64_t num_slots, const int32_t* free_order, int64_t n_free, rt_t
     }
     t->nodes.emplace_back();  // root
     t->nodes[0].lock_ref = 1;
+    t->policy = policy;
     *out = t;
     return PKV_OK;
   });
@@ -344,11 +391,57 @@ int64_t rt_match_prefix(rt_tree* t, const int32_t* key, int64_t n, int32_t* out_
 }
 
 int64_t rt_insert(rt_tree* t, const int32_t* key, const int32_t* slots, int64_t n, rt_node* out_last) {
+  return rt_insert_priority(t, key, slots, n, 0, out_last);
+}
+
+int64_t rt_insert_priority(rt_tree* t, const int32_t* key, const int32_t* slots, int64_t n, int32_t priority,
+                           rt_node* out_last) {
   return guard([&]() -> int64_t {
     if (!t || !out_last || n < 0 || (n > 0 && (!key || !slots)))
       return pkv::fail(PKV_ERR_INVAL, "bad arguments to rt_insert");
-    return t->insert(key, slots, n, out_last);
+    return t->insert(key, slots, n, out_last, priority);
   });
+}
+
+int64_t rt_peek_prefix(const rt_tree* t, const int32_t* key, int64_t n) {
+  if (!t || n < 0 || (n > 0 && !key)) return pkv::fail(PKV_ERR_INVAL, "bad arguments to rt_peek_prefix");
+  return t->peek(key, n);
+}
+
+int rt_schedule_longest_prefix(const rt_tree* t, int32_t num_reqs, const int32_t* tokens, const int64_t* tok_indptr,
+                               int32_t* order, int64_t* match_lens) {
+  return guard([&]() -> int {
+    if (!t || num_reqs < 0 || (num_reqs > 0 && (!tokens || !tok_indptr || !order)))
+      return pkv::fail(PKV_ERR_INVAL, "bad arguments to rt_schedule_longest_prefix");
+    std::vector<int64_t> m((size_t)num_reqs);
+    for (int32_t r = 0; r < num_reqs; ++r) {
+      const int64_t L = tok_indptr[r + 1] - tok_indptr[r];
+      if (L < 0) return pkv::fail(PKV_ERR_INVAL, "request %d has a negative length", r);
+      m[r] = t->peek(tokens + tok_indptr[r], L);
+      order[r] = r;
+    }
+    std::stable_sort(order, order + num_reqs, [&](int32_t a, int32_t b) { return m[a] > m[b]; });
+    if (match_lens)
+      for (int32_t r = 0; r < num_reqs; ++r) match_lens[r] = m[r];
+    return PKV_OK;
+  });
+}
+
+int64_t rt_dump_stats(const rt_tree* t, int64_t* out, int64_t cap) {
+  if (!t) return pkv::fail(PKV_ERR_INVAL, "tree is null");
+  std::vector<int64_t> ids(t->live.begin(), t->live.end());
+  std::sort(ids.begin(), ids.end());
+  const int64_t need = 4 * (int64_t)ids.size();
+  if (!out || cap < need) return need;
+  int64_t k = 0;
+  for (int64_t id : ids) {
+    const Node& x = t->nodes[id];
+    out[k++] = id;
+    out[k++] = x.hits;
+    out[k++] = x.created;
+    out[k++] = x.priority;
+  }
+  return need;
 }
 
 int rt_inc_lock_ref(rt_tree* t, rt_node node) {
@@ -440,6 +533,14 @@ int64_t rt_dump(const rt_tree* t, int64_t* out, int64_t cap) {
 int64_t rt_prepare_extend(rt_tree* t, int32_t num_reqs, const int32_t* tokens, const int64_t* tok_indptr,
                           int32_t* req_to_token, int64_t stride, int32_t* prefix_lens, int32_t* extend_lens,
                           int32_t* qo_indptr, int32_t* new_slots, int64_t new_cap, rt_node* out_last) {
+  return rt_prepare_extend_prio(t, num_reqs, tokens, tok_indptr, nullptr, req_to_token, stride, prefix_lens,
+                                extend_lens, qo_indptr, new_slots, new_cap, out_last);
+}
+
+int64_t rt_prepare_extend_prio(rt_tree* t, int32_t num_reqs, const int32_t* tokens, const int64_t* tok_indptr,
+                               const int32_t* priorities, int32_t* req_to_token, int64_t stride,
+                               int32_t* prefix_lens, int32_t* extend_lens, int32_t* qo_indptr, int32_t* new_slots,
+                               int64_t new_cap, rt_node* out_last) {
   return guard([&]() -> int64_t {
     if (!t || num_reqs < 0 || !tok_indptr || !req_to_token || !prefix_lens || !extend_lens || !qo_indptr ||
         !out_last || stride <= 0)
@@ -472,7 +573,7 @@ int64_t rt_prepare_extend(rt_tree* t, int32_t num_reqs, const int32_t* tokens, c
         return rc;
       }
       int64_t last = 0;
-      const int64_t tm = t->insert(key, row, L, &last);
+      const int64_t tm = t->insert(key, row, L, &last, priorities ? priorities[r] : 0);
       if (tm < 0) {
         t->dec_lock(a);
         return tm;

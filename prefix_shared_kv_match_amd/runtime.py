@@ -21,7 +21,8 @@ import numpy as np
 
 from . import (PKV_BF16, PKV_F32, PKV_FP8_E4M3, pkv_decode_attention, pkv_decode_chunk,
                pkv_decode_workspace_bytes, pkv_extend_attention, pkv_extend_plan, pkv_extend_tile, pkv_kv_scatter,
-               rt_create, rt_decode_step, rt_destroy, rt_finish, rt_prepare_extend, rt_release)
+               rt_create, rt_create_policy, rt_dec_lock_ref, rt_decode_step, rt_destroy, rt_finish, rt_peek_prefix,
+               rt_prepare_extend, rt_prepare_extend_prio, rt_release, rt_schedule_longest_prefix)
 
 _DT = {"f32": PKV_F32, "bf16": PKV_BF16, "fp8_e4m3": PKV_FP8_E4M3}
 
@@ -71,7 +72,7 @@ class Engine:
 
     def __init__(self, num_slots: int, hq: int, hkv: int, d: int, qo_dtype: str, pool_dtype: str,
                  free_order: Optional[np.ndarray] = None, device: str = "cuda", k_scale=None, v_scale=None,
-                 k_inv_scale=None, v_inv_scale=None, sm_scale: Optional[float] = None):
+                 k_inv_scale=None, v_inv_scale=None, sm_scale: Optional[float] = None, policy: str = "lru"):
         import torch
         self.torch = torch
         self.num_slots, self.hq, self.hkv, self.d = int(num_slots), hq, hkv, d
@@ -79,7 +80,7 @@ class Engine:
         self.qo_torch = torch.float32 if qo_dtype == "f32" else torch.bfloat16
         pool_torch = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8_e4m3": torch.uint8}[pool_dtype]
         self.device = torch.device(device)
-        self.tree = rt_create(num_slots, free_order)
+        self.tree = rt_create_policy(num_slots, free_order, policy)
         self.k_pool = torch.zeros((num_slots, hkv, d), dtype=pool_torch, device=self.device)
         self.v_pool = torch.zeros((num_slots, hkv, d), dtype=pool_torch, device=self.device)
         f = lambda a: None if a is None else torch.as_tensor(np.asarray(a, dtype=np.float32), device=self.device)
@@ -181,12 +182,12 @@ class Engine:
         return rt_finish(self.tree, toks, indptr, hb.req_to_token, prompt_lens, hb.last_nodes)
 
 
-def run_workload_host(wl, release_last_batch: bool = True):
+def run_workload_host(wl, release_last_batch: bool = True, policy: str = "lru"):
     """Drive a workload's host steps through the library's tree (no device work).
 
     Returns (batches, decode slots per step, eviction log, free list, evictable, protected, dump)."""
     from . import (rt_copy_free_list, rt_dump, rt_evictable_size, rt_protected_size, rt_take_eviction_log)
-    tree = rt_create(wl.pool_slots, wl.free_order)
+    tree = rt_create_policy(wl.pool_slots, wl.free_order, policy)
     try:
         stride = wl.max_len()
         for r in wl.pre_insert:
@@ -216,3 +217,105 @@ def run_workload_host(wl, release_last_batch: bool = True):
                 rt_protected_size(tree), rt_dump(tree))
     finally:
         rt_destroy(tree)
+
+
+def prepare_prio(tree, token_lists: Sequence[np.ndarray], stride: int, priorities=None) -> HostBatch:
+    """prepare() whose inserts carry one priority per request."""
+    toks, indptr = flatten(token_lists)
+    n = len(token_lists)
+    r2t = np.full((max(n, 1), stride), -1, dtype=np.int32)
+    pl = np.zeros(max(n, 1), dtype=np.int32)
+    el = np.zeros(max(n, 1), dtype=np.int32)
+    qo = np.zeros(n + 1, dtype=np.int32)
+    new = np.empty(max(int(indptr[-1]), 1), dtype=np.int32)
+    last = np.full(max(n, 1), -1, dtype=np.int64)
+    n_new = rt_prepare_extend_prio(tree, toks, indptr, priorities, r2t, pl, el, qo, new, last)
+    seq = (indptr[1:] - indptr[:-1]).astype(np.int32)
+    return HostBatch(n, r2t[:n], pl[:n], el[:n], qo, new[:n_new], last[:n], seq)
+
+
+def serve(tree, token_lists: Sequence[np.ndarray], after: Sequence[int], order: str, batch: int, window: int,
+          stride: int, priorities=None, on_batch=None):
+    """Cache-aware serve loop over a fixed arrival order (one batch per round).
+
+    The scheduler sees the `window` oldest requests not yet scheduled; a request whose
+    `after` request has not been scheduled in an earlier round waits.  `order` "fcfs" takes
+    the eligible requests in arrival order, "lpm" by descending cached prefix
+    (rt_schedule_longest_prefix, ties in arrival order).  Each round's batch is prepared,
+    handed to on_batch(pick, host_batch) for its device work, and released.
+    Returns [(pick, host_batch)] in round order."""
+    if order not in ("fcfs", "lpm"):
+        raise ValueError(f"unknown scheduling order {order!r}")
+    if batch < 1 or window < 1:
+        raise ValueError("batch and window must be positive")
+    n = len(token_lists)
+    scheduled = np.zeros(n, dtype=bool)
+    nxt, queue, out = 0, [], []
+    while nxt < n or queue:
+        while nxt < n and len(queue) < window:
+            queue.append(nxt)
+            nxt += 1
+        elig = [i for i in queue if after[i] < 0 or scheduled[after[i]]]
+        if not elig:
+            raise RuntimeError("no eligible request (a dependency points forward)")
+        if order == "lpm":
+            toks, indptr = flatten([token_lists[i] for i in elig])
+            ordr, _ = rt_schedule_longest_prefix(tree, toks, indptr)
+            pick = [elig[j] for j in ordr[:batch]]
+        else:
+            pick = elig[:batch]
+        hb = prepare_prio(tree, [token_lists[i] for i in pick], stride,
+                          None if priorities is None else [priorities[i] for i in pick])
+        if on_batch is not None:
+            on_batch(pick, hb)
+        rt_release(tree, hb.last_nodes)
+        scheduled[pick] = True
+        queue = [i for i in queue if not scheduled[i]]
+        out.append((pick, hb))
+    return out
+
+
+def chunked_prefill(tree, token_lists: Sequence[np.ndarray], budget: int, stride: int, on_launch=None):
+    """Prefill one batch in launches of at most `budget` new tokens.
+
+    Requests are taken in order; the head request contributes min(remaining uncached
+    tokens, budget left), and a request cut by the budget continues in the next launch.  A
+    chunk ending at position e is prepared as the truncated token list [:e] so its match
+    reuses the earlier chunks; the end node of a request's previous chunk stays locked until
+    its next chunk is prepared.  on_launch(reqs, ends, host_batch) runs each launch's device
+    work before the finished requests are released.  Returns [(reqs, ends, host_batch)]."""
+    if budget < 1:
+        raise ValueError("chunk budget must be positive")
+    n = len(token_lists)
+    done = [0] * n
+    held = [-1] * n
+    out = []
+    head = 0
+    while head < n:
+        left = budget
+        reqs, ends = [], []
+        r = head
+        while r < n and left > 0:
+            L = len(token_lists[r])
+            start = done[r] if held[r] >= 0 else rt_peek_prefix(tree, token_lists[r])
+            take = min(L - start, left)
+            reqs.append(r)
+            ends.append(start + take)
+            left -= take
+            r += 1
+        hb = prepare(tree, [np.asarray(token_lists[i])[:e] for i, e in zip(reqs, ends)], stride)
+        for i, e, last in zip(reqs, ends, hb.last_nodes.tolist()):
+            if held[i] >= 0:
+                rt_dec_lock_ref(tree, held[i])
+            held[i] = last
+            done[i] = e
+        if on_launch is not None:
+            on_launch(reqs, ends, hb)
+        finished = [i for i in reqs if done[i] >= len(token_lists[i])]
+        rt_release(tree, [held[i] for i in finished])
+        for i in finished:
+            held[i] = -1
+        out.append((reqs, ends, hb))
+        while head < n and done[head] >= len(token_lists[head]) and held[head] < 0:
+            head += 1
+    return out

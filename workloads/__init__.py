@@ -64,6 +64,8 @@ class Request:
     tokens: np.ndarray   # int32 [L]
     rows: np.ndarray     # int64 [L]: canonical value row of each position
     tag: str = ""        # human readable origin, e.g. "conv17/turn3"
+    after: int = -1      # arrival index of a request that must be served first (previous turn), -1 none
+    priority: int = 0    # importance class a caller assigns (read only by the priority eviction policy)
 
 
 class ValueTable:
@@ -308,9 +310,14 @@ def multiturn_bf16(seed: int = 3, n_conv: int = 256, turns: int = 4, turn_range=
     order = np.repeat(np.arange(n_conv), turns)
     rng.shuffle(order)
     nxt = [0] * n_conv
+    prev = [-1] * n_conv
     arrivals = []
     for c in order.tolist():
-        arrivals.append(conv_reqs[c][nxt[c]])
+        r = conv_reqs[c][nxt[c]]
+        r.after = prev[c]
+        r.priority = 1 if c % 4 == 0 else 0
+        prev[c] = len(arrivals)
+        arrivals.append(r)
         nxt[c] += 1
     batches = [arrivals[i:i + batch] for i in range(0, len(arrivals), batch)]
     free = _free_order(rng, pool_slots, capacity)
