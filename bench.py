@@ -76,7 +76,13 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="fewshot_bf16", choices=["fewshot_bf16", "decode_bf16", "longctx_fp8"])
+    ap.add_argument("--workload", default="fewshot_bf16",
+                    choices=["fewshot_bf16", "decode_bf16", "longctx_fp8", "multiturn_bf16", "tot_bf16"])
+    ap.add_argument("--schedule", default="lpm", choices=["fcfs", "lpm"],
+                    help="multiturn_bf16: batch order of the serve loop")
+    ap.add_argument("--policy", default="lru", help="eviction policy of the radix tree (multiturn_bf16, tot_bf16)")
+    ap.add_argument("--window", type=int, default=128, help="multiturn_bf16: waiting requests the scheduler sees")
+    ap.add_argument("--batch", type=int, default=32, help="multiturn_bf16: requests per round")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=64, help="requests in the oracle's timed sample")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -265,6 +271,224 @@ class PathBench:
         return int(hb.extend_lens.sum()) + self.steps_dec * hb.n
 
 
+class JobBench:
+    """A whole multi-round job per step, with every round's inputs resident in HBM.
+
+    multiturn_bf16: the serve loop over all 1,024 arrivals (rt_schedule_longest_prefix or
+    arrival order, rt_prepare_extend_prio, staged tables, kv_scatter, extend_attention,
+    rt_release per round).  tot_bf16: the four tree levels in order, then 16 decode steps
+    of the 256 leaves and rt_finish.  A step ends by evicting what it inserted (the ToT
+    root stays cached), so every step meets the same tree."""
+
+    def __init__(self, torch, a):
+        import workloads
+        from prefix_shared_kv_match_amd import runtime
+        from prefix_shared_kv_match_amd.runtime import Engine
+        self.torch, self.rt = torch, runtime
+        self.wl = wl = workloads.make(a.workload)
+        self.name, self.a = a.workload, a
+        s = wl.shape
+        self.eng = eng = Engine(wl.pool_slots, s.hq, s.hkv, s.d, s.qo_dtype, s.pool_dtype, wl.free_order, "cuda",
+                                sm_scale=s.sm_scale, policy=a.policy)
+        self.stride = wl.max_len()
+        self.timer = Timer(torch)
+        self.decode_only = False
+        # every canonical K/V/Q row on the device (bf16), so a round's inputs are one gather away
+        self.K = self._table(workloads.TAG_K)
+        self.V = self._table(workloads.TAG_V)
+        self.Q = self._table(workloads.TAG_Q)
+        self.root_len = 0
+        for r in wl.pre_insert:
+            hb = eng.prepare([r.tokens], self.stride)
+            self._scatter_rows(hb.new_slots, r.rows[hb.prefix_lens[0]:])
+            eng.release(hb)
+            self.root_len += len(r.tokens)
+        self.arr = [x for b in wl.batches for x in b]
+        # dry run of the host steps on a twin tree: which rows each round extends
+        twin = runtime.rt_create_policy(wl.pool_slots, wl.free_order, a.policy)
+        try:
+            for r in wl.pre_insert:
+                runtime.rt_release(twin, runtime.prepare(twin, [r.tokens], self.stride).last_nodes)
+            self.plan = self._host_rounds(twin, None)
+        finally:
+            runtime.rt_destroy(twin)
+        self.inputs = []
+        for pick, pl in self.plan:
+            rows = np.concatenate([self.arr[i].rows[p:] for i, p in zip(pick, pl)]) if pick else np.zeros(0)
+            idx = torch.from_numpy(rows.astype(np.int64)).cuda()
+            self.inputs.append((self.K.index_select(0, idx), self.V.index_select(0, idx), self.Q.index_select(0, idx)))
+        self.o = torch.empty((max(x[2].shape[0] for x in self.inputs), s.hq, s.d), dtype=torch.bfloat16, device="cuda")
+        self.steps_dec = int(wl.decode_tokens.shape[0])
+        if self.steps_dec:
+            last = wl.batches[-1]
+            B = len(last)
+            dr = torch.from_numpy(wl.decode_rows.astype(np.int64)).cuda()
+            self.dk = [self.K.index_select(0, dr[i]) for i in range(self.steps_dec)]
+            self.dv = [self.V.index_select(0, dr[i]) for i in range(self.steps_dec)]
+            self.dq = [self.Q.index_select(0, dr[i]) for i in range(self.steps_dec)]
+            self.do = torch.empty_like(self.dq[0])
+            self.max_len = max(len(r.tokens) for r in last) + self.steps_dec
+            self.ws, self.chunk = eng.decode_workspace(B, self.max_len)
+            self.full_tokens = [np.concatenate([r.tokens, wl.decode_tokens[:, i]]) for i, r in enumerate(last)]
+            self.prompt_lens = [len(r.tokens) for r in last]
+            self.dec_slots_dev = torch.empty(B, dtype=torch.int32, device="cuda")
+            self.seq_dev = torch.empty(B, dtype=torch.int32, device="cuda")
+        torch.cuda.synchronize()
+        self.flops = 0.0
+        self.ext_tokens = 0
+        for pick, pl in self.plan:
+            el = [len(self.arr[i].tokens) - p for i, p in zip(pick, pl)]
+            self.flops += extend_flops(s.d, s.hq, pl, el)[0]
+            self.ext_tokens += int(sum(el))
+        self.prompt_tokens = sum(len(r.tokens) for r in self.arr)
+        self.cached_tokens = sum(int(sum(pl)) for _, pl in self.plan)
+
+    def _table(self, tag):
+        full = self.wl.values.full(tag)
+        t = self.torch.from_numpy(full).to("cuda").to(self.torch.bfloat16)
+        del full
+        return t
+
+    def _scatter_rows(self, slots, rows):
+        torch = self.torch
+        idx = torch.from_numpy(np.asarray(rows, dtype=np.int64)).cuda()
+        sl = torch.from_numpy(np.ascontiguousarray(slots, dtype=np.int32)).cuda()
+        self.eng.scatter(sl, self.K.index_select(0, idx), self.V.index_select(0, idx))
+        torch.cuda.synchronize()
+
+    def _host_rounds(self, tree, on_round):
+        """Runs the job's host steps on `tree`; on_round(k, host_batch) does round k's device work.
+        Returns [(request indices, prefix lengths)] per round."""
+        rt, wl, a = self.rt, self.wl, self.a
+        out = []
+        if self.name == "multiturn_bf16":
+            def cb(pick, hb):
+                if on_round is not None:
+                    on_round(len(out), hb)
+                out.append((list(pick), hb.prefix_lens.tolist()))
+            rt.serve(tree, [r.tokens for r in self.arr], [r.after for r in self.arr], a.schedule, a.batch, a.window,
+                     self.stride, priorities=[r.priority for r in self.arr], on_batch=cb)
+            return out
+        base = 0
+        for bi, batch in enumerate(wl.batches):
+            hb = rt.prepare(tree, [r.tokens for r in batch], self.stride)
+            if on_round is not None:
+                on_round(len(out), hb)
+            out.append((list(range(base, base + len(batch))), hb.prefix_lens.tolist()))
+            base += len(batch)
+            if bi < len(wl.batches) - 1 or not wl.decode_tokens.shape[0]:
+                rt.rt_release(tree, hb.last_nodes)
+            else:
+                self._last_hb = hb
+        return out
+
+    def _round(self, k, hb):
+        eng, T = self.eng, self.timer
+        pick, pl = self.plan[k]
+        if hb.prefix_lens.tolist() != pl:
+            raise RuntimeError(f"round {k} matched differently from the planning run")
+        dt = eng.device_tables(hb, staged=True)
+        ks, vs, qs = self.inputs[k]
+        if hb.n_new:
+            with T.span("kv_scatter"):
+                eng.scatter(dt["new_slots"], ks, vs)
+            with T.span("extend_attention"):
+                eng.extend(dt, qs, self.o[:hb.n_new])
+        self._last_dt = dt
+
+    def step(self):
+        import prefix_shared_kv_match_amd as pkv
+        eng, T = self.eng, self.timer
+        self._host_rounds(eng.tree, self._round)
+        n = self.ext_tokens
+        if self.steps_dec:
+            hb = self._last_hb
+            r2t = self._last_dt["req_to_token"]
+            for i in range(self.steps_dec):
+                slots = eng.decode_alloc(hb)
+                self.dec_slots_dev.copy_(torch_from(self.torch, slots))
+                self.seq_dev.copy_(torch_from(self.torch, hb.seq_lens))
+                pkv.pkv_append_slots(r2t, self.seq_dev, self.dec_slots_dev)
+                with T.span("kv_scatter_decode"):
+                    eng.scatter(self.dec_slots_dev, self.dk[i], self.dv[i])
+                with T.span("decode_attention"):
+                    eng.decode(self.dq[i], r2t, self.seq_dev, self.max_len, self.ws, self.chunk, self.do)
+            eng.finish(hb, self.full_tokens, self.prompt_lens)
+            n += self.steps_dec * hb.n
+        pkv.rt_evict(eng.tree, pkv.rt_evictable_size(eng.tree) - self.root_len)
+        return n
+
+    def host_hit_rates(self):
+        """Cached-prefix share of the prompt tokens for every eviction policy x batch order (host only)."""
+        rt = self.rt
+        out = {}
+        for order in ("fcfs", "lpm"):
+            for pol in ("lru", "lfu", "slru", "fifo", "mru", "filo", "priority"):
+                t = rt.rt_create_policy(self.wl.pool_slots, self.wl.free_order, pol)
+                try:
+                    res = rt.serve(t, [r.tokens for r in self.arr], [r.after for r in self.arr], order, self.a.batch,
+                                   self.a.window, self.stride, priorities=[r.priority for r in self.arr])
+                finally:
+                    rt.rt_destroy(t)
+                cached = sum(int(hb.prefix_lens.sum()) for _, hb in res)
+                prio_c = sum(int(hb.prefix_lens[j]) for p, hb in res for j, i in enumerate(p) if self.arr[i].priority)
+                prio_t = sum(len(r.tokens) for r in self.arr if r.priority)
+                out[f"{order}/{pol}"] = {"all": round(cached / self.prompt_tokens, 4),
+                                         "priority_class": round(prio_c / max(prio_t, 1), 4)}
+        return out
+
+
+def torch_from(torch, a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+
+
+def main_job(a, torch):
+    import prefix_shared_kv_match_amd as pkv
+    b = JobBench(torch, a)
+    wl, s = b.wl, b.wl.shape
+    for _ in range(a.warmup):
+        b.step()
+    b.timer.reset()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    tokens = 0
+    for _ in range(a.steps):
+        tokens += b.step()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    b.timer.collect()
+    ext_ms, n_ext = b.timer.acc.get("extend_attention", (0.0, 0))
+    ext_ms_job = ext_ms / a.steps
+    kernels = {"extend_attention": {"ms_per_job": ext_ms_job, "launches_per_job": n_ext // a.steps,
+                                    "tflops": b.flops / ext_ms_job / 1e9,
+                                    "frac_mfma": b.flops / ext_ms_job / 1e9 / PEAK_BF16_TFLOPS}}
+    if b.steps_dec:
+        dm, dn = b.timer.acc.get("decode_attention", (0.0, 0))
+        kernels["decode_attention"] = {"ms": dm / max(dn, 1)}
+    out = {
+        "metric": "served prompt tokens/s over a whole multi-round job (radix reuse + extend + decode)",
+        "value": b.prompt_tokens * a.steps / el, "unit": "prompt tokens/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": el / a.steps * 1e3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "requests": len(b.arr), "rounds": len(b.plan), "policy": a.policy,
+                   "schedule": a.schedule if wl.name == "multiturn_bf16" else "levels in order",
+                   "window": a.window if wl.name == "multiturn_bf16" else None,
+                   "hq": s.hq, "hkv": s.hkv, "head_dim": s.d, "pool_slots": wl.pool_slots,
+                   "capacity": int(len(wl.free_order))},
+        "prompt_tokens_per_job": b.prompt_tokens, "cached_tokens_per_job": b.cached_tokens,
+        "hit_rate": b.cached_tokens / b.prompt_tokens, "query_tokens_per_s": tokens / el,
+        "roofline": {"bound": "mfma", "kernel": "extend_attention", "achieved": b.flops / ext_ms_job / 1e9,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": b.flops / ext_ms_job / 1e9 / PEAK_BF16_TFLOPS, "traffic": None},
+        "kernels": kernels,
+        "library": os.path.relpath(pkv._capi.LIB_PATH, ROOT),
+    }
+    if wl.name == "multiturn_bf16":
+        out["host_hit_rates"] = b.host_hit_rates()
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def cpu_baseline(wl, hb, n_req, decode_only=False, steps_done=0, min_seconds=10.0):
     """The float64 oracle on a bounded sample, repeated until at least min_seconds of CPU work:
     the extend rows of the first n_req requests, or (decode workload) the newest decode row of
@@ -300,8 +524,8 @@ def cpu_baseline(wl, hb, n_req, decode_only=False, steps_done=0, min_seconds=10.
 def main():
     a = parse()
     if a.gpus != 1:
-        print(f"bench.py runs on one GPU only; --gpus {a.gpus} is not supported by this build "
-              f"(see the sharding paragraph of the design notes)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported (the library runs one GPU per "
+              f"process and has no multi-GPU path)", file=sys.stderr)
         return 2
     import torch
     if not torch.cuda.is_available():
@@ -309,6 +533,8 @@ def main():
         return 2
     import prefix_shared_kv_match_amd as pkv
     pkv.lib()
+    if a.workload in ("multiturn_bf16", "tot_bf16"):
+        return main_job(a, torch)
     b = PathBench(torch, a.workload, a.warmup + a.steps)
     wl = b.wl
     if a.copy_calib_mib:

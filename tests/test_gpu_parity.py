@@ -121,6 +121,15 @@ def test_longctx_small_every_row():
     report("longctx small", stats)
 
 
+def test_tot_small_every_row():
+    log("tot small")
+    # multi-head attention (group size 1) on a branching tree: many template splits, short extends
+    wl = workloads.tot_bf16(root_len=200, branching=3, depth=3, thought_range=(10, 40), decode_steps=3,
+                            pool_slots=20000)
+    stats = Run(wl, check_pool=True).run()
+    report("tot small", stats)
+
+
 # ---------------------------------------------------------------------------------------------
 # edge cases
 # ---------------------------------------------------------------------------------------------
@@ -212,3 +221,9 @@ def test_multiturn_full_sampled():
     log("multiturn full")
     stats = Run(workloads.multiturn_bf16(), sample_rows=3, req_stride=4).run()
     report("multiturn full", stats)
+
+
+def test_tot_full_sampled():
+    log("tot full")
+    stats = Run(workloads.tot_bf16(decode_steps=4), sample_rows=4, req_stride=2).run(decode_sample=32)
+    report("tot full", stats)

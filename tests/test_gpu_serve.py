@@ -1,0 +1,105 @@
+"""GPU parity of the serve-loop paths: cache-aware scheduling (fcfs / lpm over the multi-turn
+workload, with eviction) and chunked prefill (launches capped at a token budget).  Host tables
+must equal the oracle scheduler's bit-exactly; every extend row is compared with the oracle's
+attention over the request's full context (bf16: max|d| <= 2e-2, relative RMS <= 5e-3)."""
+import numpy as np
+import pytest
+
+import workloads
+from oracle import attention as oa
+from oracle import driver as od
+from oracle import scheduler as osch
+from oracle.radix_tree import OracleTree
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+from tests.gpu_harness import compare, log, make_engine, src_tensor  # noqa: E402
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import prefix_shared_kv_match_amd as pkv
+    pkv.lib()
+
+
+def _extend_and_check(eng, wl, reqs, ends, hb, what):
+    """Scatter the launch's new K/V, run extend, compare every row with the oracle."""
+    new_rows = np.concatenate([reqs[k].rows[int(hb.prefix_lens[k]):e] for k, e in enumerate(ends)]) \
+        if hb.n_new else np.zeros(0, dtype=np.int64)
+    assert new_rows.size == hb.n_new
+    if not hb.n_new:
+        return None
+    sl = torch.from_numpy(np.ascontiguousarray(hb.new_slots, dtype=np.int32)).cuda()
+    eng.scatter(sl, src_tensor(torch, wl.values.k(new_rows), wl.shape, "cuda"),
+                src_tensor(torch, wl.values.v(new_rows), wl.shape, "cuda"))
+    dt = eng.device_tables(hb)
+    o = eng.extend(dt, src_tensor(torch, wl.values.q(new_rows), wl.shape, "cuda"))
+    torch.cuda.synchronize()
+    got = o.float().cpu().numpy()
+    ref = []
+    for k, e in enumerate(ends):
+        p = int(hb.prefix_lens[k])
+        if e > p:
+            ref.append(oa.extend_rows(wl, reqs[k], p, sample=np.arange(p, e)))
+    return compare(got, np.concatenate(ref), wl.shape.qo_dtype, what)
+
+
+@pytest.mark.parametrize("order", ["fcfs", "lpm"])
+def test_serve_multiturn_small(order):
+    from prefix_shared_kv_match_amd import runtime
+    log(f"serve multiturn small {order}")
+    wl = workloads.multiturn_bf16(n_conv=24, turns=4, turn_range=(16, 96), batch=8, pool_slots=20000,
+                                  capacity=8000)
+    arr = [r for b in wl.batches for r in b]
+    after = [r.after for r in arr]
+    olog = osch.serve(OracleTree(wl.pool_slots, wl.free_order), [r.tokens.tolist() for r in arr], after, order,
+                      batch=6, window=24)
+    eng = make_engine(wl)
+    stats = []
+
+    def on_batch(pick, hb):
+        k = len(stats)
+        assert pick == olog.picks[k]
+        assert hb.prefix_lens.tolist() == olog.tables[k].prefix_lens
+        assert hb.new_slots.tolist() == olog.tables[k].new_slots
+        reqs = [arr[i] for i in pick]
+        stats.append(_extend_and_check(eng, wl, reqs, [len(r.tokens) for r in reqs], hb, f"round {k}"))
+
+    runtime.serve(eng.tree, [r.tokens for r in arr], after, order, 6, 24, wl.max_len(), on_batch=on_batch)
+    assert len(stats) == len(olog.picks)
+    log(f"  {len(stats)} rounds, hit rate {olog.hit_rate:.3f}, worst {max(s['rel_rms'] for s in stats if s)}")
+
+
+@pytest.mark.parametrize("budget", [64, 200, 1000])
+def test_chunked_prefill_fewshot_small(budget):
+    from prefix_shared_kv_match_amd import runtime
+    log(f"chunked prefill budget {budget}")
+    wl = workloads.fewshot_bf16(n_req=8, prefix_len=300, suffix_range=(20, 200), decode_steps=0)
+    reqs = wl.batches[0]
+    o = OracleTree(wl.pool_slots, wl.free_order)
+    for r in wl.pre_insert:
+        od.release(o, od.prepare_batch(o, [r.tokens]).last_nodes)
+    launches = osch.chunked_prefill(o, [r.tokens.tolist() for r in reqs], budget)
+    eng = make_engine(wl)
+    for r in wl.pre_insert:
+        hb = eng.prepare([r.tokens], wl.max_len())
+        sl = torch.from_numpy(hb.new_slots.astype(np.int32)).cuda()
+        eng.scatter(sl, src_tensor(torch, wl.values.k(r.rows), wl.shape, "cuda"),
+                    src_tensor(torch, wl.values.v(r.rows), wl.shape, "cuda"))
+        eng.release(hb)
+    stats = []
+
+    def on_launch(idx, ends, hb):
+        k = len(stats)
+        assert (idx, ends) == (launches[k].reqs, launches[k].ends)
+        assert hb.prefix_lens.tolist() == launches[k].tables.prefix_lens
+        assert hb.new_slots.tolist() == launches[k].tables.new_slots
+        assert int(hb.extend_lens.sum()) <= budget
+        stats.append(_extend_and_check(eng, wl, [reqs[i] for i in idx], ends, hb, f"launch {k}"))
+
+    runtime.chunked_prefill(eng.tree, [r.tokens for r in reqs], budget, wl.max_len(), on_launch=on_launch)
+    assert len(stats) == len(launches) >= (1 if budget >= 1000 else 2)
+    log(f"  {len(stats)} launches, worst {max(s['rel_rms'] for s in stats if s)}")

@@ -1,0 +1,81 @@
+"""The library-side serve loop (rt_schedule_longest_prefix + rt_prepare_extend_prio) and
+chunked prefill (rt_peek_prefix + rt_prepare_extend) on the CPU: bit-exact with the oracle's
+scheduler (batch picks, slot tables, final tree, free list)."""
+import numpy as np
+import pytest
+
+import prefix_shared_kv_match_amd as pkv
+from prefix_shared_kv_match_amd import runtime
+from oracle import driver, scheduler
+from oracle.radix_tree import OracleTree
+
+
+def same_tree(t, o):
+    assert pkv.rt_dump(t) == o.dump()
+    assert pkv.rt_dump_stats(t) == o.dump_stats()
+    assert pkv.rt_copy_free_list(t).tolist() == list(o.free)
+    assert pkv.rt_take_eviction_log(t) == [(i, list(s)) for i, s in o.take_evlog()]
+
+
+@pytest.mark.parametrize("order,policy", [("fcfs", "lru"), ("lpm", "lru"), ("lpm", "lfu"), ("fcfs", "priority"),
+                                          ("lpm", "slru")])
+def test_serve_matches_oracle(order, policy):
+    import workloads
+    wl = workloads.multiturn_bf16(n_conv=64, capacity=120_000)
+    arr = [r for b in wl.batches for r in b]
+    after = [r.after for r in arr]
+    prio = [r.priority for r in arr]
+    o = OracleTree(wl.pool_slots, wl.free_order, policy)
+    log = scheduler.serve(o, [r.tokens.tolist() for r in arr], after, order, batch=16, window=64, priorities=prio)
+    t = pkv.rt_create_policy(wl.pool_slots, wl.free_order, policy)
+    try:
+        seen = []
+        out = runtime.serve(t, [r.tokens for r in arr], after, order, 16, 64, wl.max_len(), priorities=prio,
+                            on_batch=lambda pick, hb: seen.append(len(pick)))
+        assert [p for p, _ in out] == log.picks
+        assert seen == [len(p) for p in log.picks]
+        for (pick, hb), bt in zip(out, log.tables):
+            assert hb.prefix_lens.tolist() == bt.prefix_lens
+            assert hb.new_slots.tolist() == bt.new_slots
+            for i, row in enumerate(bt.rows):
+                assert hb.req_to_token[i, :len(row)].tolist() == row
+        same_tree(t, o)
+    finally:
+        pkv.rt_destroy(t)
+
+
+def test_serve_rejects_bad_arguments():
+    t = pkv.rt_create(16)
+    try:
+        with pytest.raises(ValueError):
+            runtime.serve(t, [np.array([1])], [-1], "random", 1, 1, 4)
+        with pytest.raises(ValueError):
+            runtime.serve(t, [np.array([1])], [-1], "fcfs", 0, 1, 4)
+        with pytest.raises(RuntimeError):
+            runtime.serve(t, [np.array([1]), np.array([2])], [1, -1], "fcfs", 1, 1, 4)
+    finally:
+        pkv.rt_destroy(t)
+
+
+@pytest.mark.parametrize("budget", [1, 5, 33, 200, 10**6])
+def test_chunked_prefill_matches_oracle(budget):
+    import workloads
+    wl = workloads.fewshot_bf16(n_req=6, prefix_len=90, suffix_range=(20, 60))
+    reqs = [r.tokens for r in wl.batches[0]] + [wl.batches[0][0].tokens[:50]]   # one fully cached request
+    o = OracleTree(wl.pool_slots, wl.free_order)
+    t = pkv.rt_create(wl.pool_slots, wl.free_order)
+    try:
+        for r in wl.pre_insert:
+            driver.release(o, driver.prepare_batch(o, [r.tokens]).last_nodes)
+            pkv.rt_release(t, runtime.prepare(t, [r.tokens], 256).last_nodes)
+        ls = scheduler.chunked_prefill(o, [x.tolist() for x in reqs], budget)
+        got = runtime.chunked_prefill(t, reqs, budget, 256)
+        assert [(r_, e_) for r_, e_, _ in got] == [(l.reqs, l.ends) for l in ls]
+        for (_, _, hb), l in zip(got, ls):
+            assert hb.prefix_lens.tolist() == l.tables.prefix_lens
+            assert hb.extend_lens.tolist() == l.tables.extend_lens
+            assert hb.new_slots.tolist() == l.tables.new_slots
+        same_tree(t, o)
+        assert pkv.rt_protected_size(t) == 0
+    finally:
+        pkv.rt_destroy(t)

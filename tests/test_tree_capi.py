@@ -253,3 +253,15 @@ def test_workload_longctx_host():
     import workloads
     ob = compare_workload(workloads.longctx_fp8(steps=8))
     assert ob.batches[0].prefix_lens == [32768] * 16
+
+
+def test_workload_tot_host():
+    import workloads
+    ob = compare_workload(workloads.tot_bf16())
+    # level 1 reuses the root; later levels reuse the root and the parent's path
+    assert ob.batches[0].prefix_lens[0] == 1024
+    assert all(p >= 1024 for b in ob.batches for p in b.prefix_lens)
+    # the template run is shared by siblings: all but the first sibling reuse it
+    fam = ob.batches[3]
+    for f in range(0, 256, 4):
+        assert all(fam.prefix_lens[f + c] == fam.prefix_lens[f] + 8 for c in range(1, 4))

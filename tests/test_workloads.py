@@ -39,7 +39,7 @@ def equal_token_paths_have_equal_rows(reqs):
             node = node[t][1]
 
 
-@pytest.mark.parametrize("name", ["tiny_f32", "fewshot_bf16", "multiturn_bf16"])
+@pytest.mark.parametrize("name", ["tiny_f32", "fewshot_bf16", "multiturn_bf16", "tot_bf16"])
 def test_equal_token_paths_carry_equal_rows(name):
     kw = {"n_conv": 40} if name == "multiturn_bf16" else {}
     wl = workloads.make(name, **kw)
@@ -59,3 +59,24 @@ def test_fp8_scales():
     wl = workloads.longctx_fp8(prefix_len=600, suffix_len=40, n_req=3, steps=2, pool_slots=2048)
     assert wl.k_scale.shape == (8,) and np.all(wl.k_scale > 0)
     assert np.all(wl.k_inv_scale == (np.float32(1) / wl.k_scale).astype(np.float32))
+
+
+def test_tot_structure():
+    wl = workloads.tot_bf16()
+    assert [len(b) for b in wl.batches] == [4, 16, 64, 256]
+    assert wl.shape.hq == wl.shape.hkv == 32 and wl.shape.d == 128
+    root = wl.pre_insert[0].tokens
+    assert len(root) == 1024
+    for lvl, batch in enumerate(wl.batches, 1):
+        for r in batch:
+            assert np.array_equal(r.tokens[:1024], root)
+            assert r.tag.count(".") == lvl
+    # siblings share the parent's path plus the 8-token template, then differ at the next token
+    parent, a, b = wl.batches[0][0], wl.batches[1][0], wl.batches[1][1]
+    m = min(len(a.tokens), len(b.tokens))
+    assert int(np.argmax(a.tokens[:m] != b.tokens[:m])) == len(parent.tokens) + 8
+    # each level's request extends its parent's request
+    for parent_i, parent in enumerate(wl.batches[2]):
+        for c in range(4):
+            child = wl.batches[3][4 * parent_i + c]
+            assert np.array_equal(child.tokens[:len(parent.tokens)], parent.tokens)

@@ -374,6 +374,44 @@ def longctx_fp8(seed: int = 5, n_req: int = 16, prefix_len: int = 32768, suffix_
     return wl
 
 
+def tot_bf16(seed: int = 6, root_len: int = 1024, branching: int = 4, depth: int = 4, template_len: int = 8,
+             thought_range=(96, 224), decode_steps: int = 16, pool_slots: int = 262_144) -> Workload:
+    """Tree-of-Thought: a 1,024-token root prompt expanded breadth-first, 4 children per node, 4 levels
+    (4 + 16 + 64 + 256 requests); MHA 32/32, d 128 (the LLaMA-7B attention shape), bf16.
+
+    Every node's thought is a step template of 8 tokens shared by all children of one parent,
+    then its own U[96, 224] tokens, so siblings share a short run and split it on insert.  The
+    request of a node is the root plus the thoughts on its path; each level is one batch, whose
+    requests reuse the root and their parent's path (inserted by the level before) and extend
+    the template (first sibling only) and the new thought.  The last level decodes 16 tokens."""
+    rng = np.random.default_rng(seed)
+    b = _Builder(rng, LLAMA3_VOCAB)
+    shape = Shape(32, 32, 128, "bf16", "bf16", 1.0 / math.sqrt(128))
+    root = b.segment(0, root_len)
+    pre = [Request(root[1].copy(), root[2].copy(), "root")]
+    lo, hi = thought_range
+    frontier = [([root], "n")]
+    batches = []
+    for level in range(1, depth + 1):
+        nxt, reqs = [], []
+        for path, name in frontier:
+            tpl = b.segment(path[-1][0], template_len)
+            for c in range(branching):
+                th = b.segment(tpl[0], int(rng.integers(lo, hi + 1)))
+                p = path + [tpl, th]
+                r = _concat(p)
+                r.tag = f"{name}.{c}"
+                reqs.append(r)
+                nxt.append((p, f"{name}.{c}"))
+        batches.append(reqs)
+        frontier = nxt
+    free = _free_order(rng, pool_slots, pool_slots)
+    dt, dr = _decode(b, len(batches[-1]), decode_steps)
+    return Workload("tot_bf16", seed, shape, pool_slots, free, pre, batches, True, dt, dr,
+                    ValueTable(seed, b.next_row, shape),
+                    note=f"{sum(len(x) for x in batches)} requests over {depth} levels")
+
+
 FP8_E4M3_MAX = 448.0
 
 
@@ -398,6 +436,7 @@ CONFIGS = {
     "multiturn_bf16": multiturn_bf16,
     "decode_bf16": decode_bf16,
     "longctx_fp8": longctx_fp8,
+    "tot_bf16": tot_bf16,
 }
 
 
