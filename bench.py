@@ -42,12 +42,12 @@ CSRC = os.path.join(ROOT, "prefix_shared_kv_match_amd", "csrc")
 # what the same counters read for a plain 1 GiB device copy (FETCH x2.0, WRITE x1.0).  Each
 # entry holds the hash of the kernel sources it was taken on; a changed kernel reports null.
 TRAFFIC = {
-    "fewshot_bf16": dict(kernel="extend_attention", src_hash="14e86bafad890a3a",
-                         fetch_kib=177659.8125, write_kib=102969.703125),
+    "fewshot_bf16": dict(kernel="extend_attention", src_hash="119d90842719c39a",
+                         fetch_kib=213644.125, write_kib=102968.0),
     "decode_bf16": dict(kernel="decode_attention", src_hash="60535949e129ec94",
-                        fetch_kib=5050624.125, write_kib=47878.21875),
-    "longctx_fp8": dict(kernel="extend_attention", src_hash="14e86bafad890a3a",
-                        fetch_kib=1400990.5625, write_kib=262144.0625),
+                        fetch_kib=5038933.25, write_kib=47879.53125),
+    "longctx_fp8": dict(kernel="extend_attention", src_hash="119d90842719c39a",
+                        fetch_kib=1713570.5625, write_kib=262144.328125),
 }
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 KERNEL_SOURCES = {"extend_attention": ["extend_attention.hip", "device.h"],

@@ -15,13 +15,17 @@
 //    rows = (128/G tokens) x (G heads of one GQA group), so every K/V tile staged in LDS is
 //    shared by the whole group.  Per 64-token K/V tile and wave (32 query rows):
 //      S^T = K . Q^T  (A = K rows from LDS, B = Q^T held in registers), 32 MFMA 16x16x32;
-//      online softmax in the log2 domain, row max across the 4 lanes that share a query row;
-//      O^T += V^T . P^T (A = V^T from LDS, B = P^T straight from the S^T registers), 32 MFMA.
+//      online softmax in the log2 domain with a lazily moved reference max;
+//      O^T += V^T . P^T (A = V^T from LDS, B = P^T straight from the S^T registers), 32 MFMA,
+//      and the row sums with 4 more MFMA against a row of ones.
 //    The S^T row order inside each 16-row MFMA block is permuted so that each lane's four
 //    S^T values of two neighbouring blocks are 8 consecutive kv tokens, which is exactly the
 //    B-operand slice of P^T for the PV product; V is stored transposed in LDS so the A
-//    operand is one 16-byte read.  fp8 pools are decoded to bf16 (exact) while staging;
-//    the per-head scales are folded into the float32 logits and output.
+//    operand is one 16-byte read.  Tiles are double-buffered in LDS (one barrier per tile)
+//    and gathered with buffer loads (no address arithmetic on the vector ALU, which is the
+//    unit that bounds this loop next to the matrix cores).  fp8 pools are decoded to bf16
+//    (exact) while staging; the per-head scales are folded into the float32 logits and
+//    output.
 //  - extend_f32 (f32 q/o, f32 pool, d 64 or 128): one wave per (tile, q head), VALU only;
 //    it serves the small fp32 case.
 
@@ -153,8 +157,26 @@ __device__ __forceinline__ int sigma(int mb, int rho) {
 // 16 different banks, so the 16-byte A-operand reads are conflict free.
 __device__ __forceinline__ int krow(int t) { return t ^ (((t >> 4) & 1) << 2); }
 
+// Buffer loads.  The K/V pools are read as structured buffers (record = one slot of
+// hkv*d values, record index = slot), and the slot table as a raw buffer, so a gathered
+// row costs no address arithmetic: the slot loaded from the table is the record index,
+// the per-thread column offset is fixed, and out-of-range records read as zero.
+__device__ u32x4 buf_load_rec_x4(__amdgpu_buffer_rsrc_t rsrc, int rec, int voffset, int soffset,
+                                 int aux) __asm("llvm.amdgcn.struct.ptr.buffer.load.v4i32");
+__device__ u32x2 buf_load_rec_x2(__amdgpu_buffer_rsrc_t rsrc, int rec, int voffset, int soffset,
+                                 int aux) __asm("llvm.amdgcn.struct.ptr.buffer.load.v2i32");
+__device__ int buf_load_i32(__amdgpu_buffer_rsrc_t rsrc, int voffset, int soffset,
+                            int aux) __asm("llvm.amdgcn.raw.ptr.buffer.load.i32");
+constexpr int kBufWord3 = 0x00020000;   // 32-bit data format, no swizzle
+
+struct Gather {
+  __amdgpu_buffer_rsrc_t kp, vp, tab;   // K pool, V pool (record = slot), slot table
+  int row_bytes;                         // byte offset of this request's table row
+};
+
 // Staging of one 64-token K/V tile: global -> registers (prefetch) -> LDS.  Native vector
-// types keep the prefetch registers in VGPRs.
+// types keep the prefetch registers in VGPRs.  Tokens at or past the context read whatever
+// slot the table holds there (or zero past the table's end); they are masked later.
 template <int POOL>
 struct TileStage;
 
@@ -163,21 +185,23 @@ struct TileStage<PKV_BF16> {
   // K: 64 rows x 256 B = 1024 chunks of 16 B, 4 per thread (rows tid/16 + 16 i, chunk tid%16).
   // V: thread -> 4 consecutive tokens (4*(tid%16) .. +3) x 8 d (8*(tid/16) .. +7).
   u32x4 k0, k1, k2, k3, v0, v1, v2, v3;
-  __device__ __forceinline__ void load(const uint8_t* kpool, const uint8_t* vpool, const int32_t* row, int kv0,
-                                       int ctx, int hkv, int g, int tid) {
-    const int64_t slot_bytes = (int64_t)hkv * kD * 2;
-    const int64_t head = (int64_t)g * kD * 2;
-    const uint8_t* kb = kpool + head + (tid & 15) * 16;
-    const uint8_t* vb = vpool + head + (tid >> 4) * 16;
-    const int kt = kv0 + (tid >> 4), vt = kv0 + 4 * (tid & 15);
-    k0 = *(const u32x4*)(kb + (int64_t)row[kt < ctx ? kt : 0] * slot_bytes);
-    k1 = *(const u32x4*)(kb + (int64_t)row[kt + 16 < ctx ? kt + 16 : 0] * slot_bytes);
-    k2 = *(const u32x4*)(kb + (int64_t)row[kt + 32 < ctx ? kt + 32 : 0] * slot_bytes);
-    k3 = *(const u32x4*)(kb + (int64_t)row[kt + 48 < ctx ? kt + 48 : 0] * slot_bytes);
-    v0 = *(const u32x4*)(vb + (int64_t)row[vt < ctx ? vt : 0] * slot_bytes);
-    v1 = *(const u32x4*)(vb + (int64_t)row[vt + 1 < ctx ? vt + 1 : 0] * slot_bytes);
-    v2 = *(const u32x4*)(vb + (int64_t)row[vt + 2 < ctx ? vt + 2 : 0] * slot_bytes);
-    v3 = *(const u32x4*)(vb + (int64_t)row[vt + 3 < ctx ? vt + 3 : 0] * slot_bytes);
+  __device__ __forceinline__ void load(const Gather& gt, int kv0, int g, int tid) {
+    // the whole byte offset goes in the vector offset, which the buffer's range check covers
+    const int tb = gt.row_bytes + 4 * kv0;
+    const int kto = tb + 4 * (tid >> 4), vto = tb + 16 * (tid & 15);
+    const int ks0 = buf_load_i32(gt.tab, kto, 0, 0), ks1 = buf_load_i32(gt.tab, kto + 64, 0, 0);
+    const int ks2 = buf_load_i32(gt.tab, kto + 128, 0, 0), ks3 = buf_load_i32(gt.tab, kto + 192, 0, 0);
+    const int vs0 = buf_load_i32(gt.tab, vto, 0, 0), vs1 = buf_load_i32(gt.tab, vto + 4, 0, 0);
+    const int vs2 = buf_load_i32(gt.tab, vto + 8, 0, 0), vs3 = buf_load_i32(gt.tab, vto + 12, 0, 0);
+    const int kc = g * kD * 2 + (tid & 15) * 16, vc = g * kD * 2 + (tid >> 4) * 16;
+    k0 = buf_load_rec_x4(gt.kp, ks0, kc, 0, 0);
+    k1 = buf_load_rec_x4(gt.kp, ks1, kc, 0, 0);
+    k2 = buf_load_rec_x4(gt.kp, ks2, kc, 0, 0);
+    k3 = buf_load_rec_x4(gt.kp, ks3, kc, 0, 0);
+    v0 = buf_load_rec_x4(gt.vp, vs0, vc, 0, 0);
+    v1 = buf_load_rec_x4(gt.vp, vs1, vc, 0, 0);
+    v2 = buf_load_rec_x4(gt.vp, vs2, vc, 0, 0);
+    v3 = buf_load_rec_x4(gt.vp, vs3, vc, 0, 0);
   }
   __device__ __forceinline__ void store(bf16* Ks, bf16* Vt, int tid) const {
     const int r = tid >> 4;   // tokens r, r+16, r+32, r+48
@@ -188,15 +212,16 @@ struct TileStage<PKV_BF16> {
     *(u32x4*)(kd + krow(r + 48) * kKStride) = k3;
     store_vt(Vt, tid, v0, v1, v2, v3);
   }
-  // Writes 4 tokens x 8 d (token-major in registers) to V^T [d][token].
+  // Writes 4 tokens x 8 d (token-major in registers) to V^T [d][token]; one byte permute
+  // builds each pair of 16-bit values.
   static __device__ __forceinline__ void store_vt(bf16* Vt, int tid, u32x4 a, u32x4 b, u32x4 c, u32x4 d) {
     const int d0 = 8 * (tid >> 4), t0 = 4 * (tid & 15);
     bf16* base = Vt + d0 * kVStride + t0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       // d = d0 + 2i (low halves) and d0 + 2i + 1 (high halves)
-      const u32x2 lo = {(a[i] & 0xFFFFu) | (b[i] << 16), (c[i] & 0xFFFFu) | (d[i] << 16)};
-      const u32x2 hi = {(a[i] >> 16) | (b[i] & 0xFFFF0000u), (c[i] >> 16) | (d[i] & 0xFFFF0000u)};
+      const u32x2 lo = {__builtin_amdgcn_perm(b[i], a[i], 0x05040100u), __builtin_amdgcn_perm(d[i], c[i], 0x05040100u)};
+      const u32x2 hi = {__builtin_amdgcn_perm(b[i], a[i], 0x07060302u), __builtin_amdgcn_perm(d[i], c[i], 0x07060302u)};
       *(u32x2*)(base + (2 * i) * kVStride) = lo;
       *(u32x2*)(base + (2 * i + 1) * kVStride) = hi;
     }
@@ -206,7 +231,7 @@ struct TileStage<PKV_BF16> {
 // two E4M3 codes (low 16 bits) -> two bf16 (exact: every E4M3 value is a bf16 value)
 __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t codes2) {
   const float2 f = e4m3x2_to_f32<false>(codes2);
-  return (__float_as_uint(f.x) >> 16) | (__float_as_uint(f.y) & 0xFFFF0000u);
+  return __builtin_amdgcn_perm(__float_as_uint(f.y), __float_as_uint(f.x), 0x07060302u);
 }
 
 template <>
@@ -215,19 +240,19 @@ struct TileStage<PKV_FP8_E4M3> {
   // V: thread -> 4 tokens x 8 d, 8 B of codes each.
   u32x4 k0, k1;
   u32x2 v0, v1, v2, v3;
-  __device__ __forceinline__ void load(const uint8_t* kpool, const uint8_t* vpool, const int32_t* row, int kv0,
-                                       int ctx, int hkv, int g, int tid) {
-    const int64_t slot_bytes = (int64_t)hkv * kD;
-    const int64_t head = (int64_t)g * kD;
-    const uint8_t* kb = kpool + head + (tid & 7) * 16;
-    const uint8_t* vb = vpool + head + (tid >> 4) * 8;
-    const int kt = kv0 + (tid >> 3), vt = kv0 + 4 * (tid & 15);
-    k0 = *(const u32x4*)(kb + (int64_t)row[kt < ctx ? kt : 0] * slot_bytes);
-    k1 = *(const u32x4*)(kb + (int64_t)row[kt + 32 < ctx ? kt + 32 : 0] * slot_bytes);
-    v0 = *(const u32x2*)(vb + (int64_t)row[vt < ctx ? vt : 0] * slot_bytes);
-    v1 = *(const u32x2*)(vb + (int64_t)row[vt + 1 < ctx ? vt + 1 : 0] * slot_bytes);
-    v2 = *(const u32x2*)(vb + (int64_t)row[vt + 2 < ctx ? vt + 2 : 0] * slot_bytes);
-    v3 = *(const u32x2*)(vb + (int64_t)row[vt + 3 < ctx ? vt + 3 : 0] * slot_bytes);
+  __device__ __forceinline__ void load(const Gather& gt, int kv0, int g, int tid) {
+    const int tb = gt.row_bytes + 4 * kv0;
+    const int kto = tb + 4 * (tid >> 3), vto = tb + 16 * (tid & 15);
+    const int ks0 = buf_load_i32(gt.tab, kto, 0, 0), ks1 = buf_load_i32(gt.tab, kto + 128, 0, 0);
+    const int vs0 = buf_load_i32(gt.tab, vto, 0, 0), vs1 = buf_load_i32(gt.tab, vto + 4, 0, 0);
+    const int vs2 = buf_load_i32(gt.tab, vto + 8, 0, 0), vs3 = buf_load_i32(gt.tab, vto + 12, 0, 0);
+    const int kc = g * kD + (tid & 7) * 16, vc = g * kD + (tid >> 4) * 8;
+    k0 = buf_load_rec_x4(gt.kp, ks0, kc, 0, 0);
+    k1 = buf_load_rec_x4(gt.kp, ks1, kc, 0, 0);
+    v0 = buf_load_rec_x2(gt.vp, vs0, vc, 0, 0);
+    v1 = buf_load_rec_x2(gt.vp, vs1, vc, 0, 0);
+    v2 = buf_load_rec_x2(gt.vp, vs2, vc, 0, 0);
+    v3 = buf_load_rec_x2(gt.vp, vs3, vc, 0, 0);
   }
   static __device__ __forceinline__ u32x4 dec4(u32x2 c) {
     return u32x4{e4m3x2_to_bf16x2(c[0]), e4m3x2_to_bf16x2(c[0] >> 16), e4m3x2_to_bf16x2(c[1]),
@@ -262,11 +287,13 @@ __global__ __launch_bounds__(256, 2) void extend_mfma(const bf16* __restrict__ q
                                                       const int32_t* __restrict__ extend_lens,
                                                       const int32_t* __restrict__ qo_indptr,
                                                       const int32_t* __restrict__ work, int hkv,
-                                                      float scale_log2) {
+                                                      float scale_log2, int num_slots, int table_bytes) {
   constexpr int BT = kRows / G;   // query tokens per work item
   // K (row-major) and V^T tiles; the next tile is prefetched into registers during compute
-  __shared__ __attribute__((aligned(16))) bf16 Ks[kBN * kKStride];
-  __shared__ __attribute__((aligned(16))) bf16 Vt[kD * kVStride];
+  // two K (row-major) / V^T tile buffers: tile t is computed from buffer t & 1 while tile
+  // t + 1 is written to the other one, so one barrier per tile suffices
+  __shared__ __attribute__((aligned(16))) bf16 Ks[2][kBN * kKStride];
+  __shared__ __attribute__((aligned(16))) bf16 Vt[2][kD * kVStride];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -279,7 +306,12 @@ __global__ __launch_bounds__(256, 2) void extend_mfma(const bf16* __restrict__ q
   const int ctx = p + j0 + nq;
   const int hq = hkv * G;
   const int64_t qrow0 = (int64_t)qo_indptr[req] + j0;
-  const int32_t* row = r2t + (int64_t)req * stride;
+  constexpr int kSlotBytes = POOL == PKV_FP8_E4M3 ? kD : 2 * kD;
+  Gather gt;
+  gt.kp = __builtin_amdgcn_make_buffer_rsrc((void*)kpool, (short)(hkv * kSlotBytes), num_slots, kBufWord3);
+  gt.vp = __builtin_amdgcn_make_buffer_rsrc((void*)vpool, (short)(hkv * kSlotBytes), num_slots, kBufWord3);
+  gt.tab = __builtin_amdgcn_make_buffer_rsrc((void*)r2t, (short)0, table_bytes, kBufWord3);
+  gt.row_bytes = (int)((int64_t)req * stride * 4);
 
   float sc = scale_log2;
   if constexpr (POOL == PKV_FP8_E4M3) sc *= kscale[g];
@@ -326,15 +358,20 @@ __global__ __launch_bounds__(256, 2) void extend_mfma(const bf16* __restrict__ q
 
   TileStage<POOL> stage;
   const int n_tiles = (ctx + kBN - 1) / kBN;
-  stage.load(kpool, vpool, row, 0, ctx, hkv, g, tid);
+  stage.load(gt, 0, g, tid);
+  stage.store(Ks[0], Vt[0], tid);
+  stage.load(gt, min(1, n_tiles - 1) * kBN, g, tid);
+  __syncthreads();
   for (int kt = 0; kt < n_tiles; ++kt) {
     const int kv0 = kt * kBN;
-    const bf16* K = Ks;
-    const bf16* V = Vt;
-    __syncthreads();
-    stage.store(Ks, Vt, tid);
-    __syncthreads();
-    if (kt + 1 < n_tiles) stage.load(kpool, vpool, row, kv0 + kBN, ctx, hkv, g, tid);
+    const bf16* K = Ks[kt & 1];
+    const bf16* V = Vt[kt & 1];
+    // tile kt + 1 (in registers since the last iteration) goes to the other buffer, whose
+    // readers (tile kt - 1) all passed the previous barrier; then prefetch tile kt + 2.
+    // Branch-free, so it interleaves with the S^T products below: past the last tile the
+    // last tile is fetched again (from L2) and stored to a buffer nobody reads any more.
+    stage.store(Ks[(kt + 1) & 1], Vt[(kt + 1) & 1], tid);
+    stage.load(gt, min(kt + 2, n_tiles - 1) * kBN, g, tid);
 
     // S^T = K . Q^T
     floatx4 s[4][2];
@@ -367,26 +404,34 @@ __global__ __launch_bounds__(256, 2) void extend_mfma(const bf16* __restrict__ q
       }
     }
 
-    // online softmax (log2 domain) with lazy rescaling
-    bf16x8 pf[2][2];
+    // online softmax (log2 domain) with lazy rescaling.  Each lane's max over its 16 logits
+    // of a row; the row max across the 4 lanes that share the query row is only formed when
+    // some lane may move the reference max (one wave-uniform test for both row blocks).
+    float mt[2];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      float mt = fmaxf(fmaxf(s[0][nb][0], s[0][nb][1]), fmaxf(s[0][nb][2], s[0][nb][3]));
+      float x = fmaxf(fmaxf(s[0][nb][0], s[0][nb][1]), fmaxf(s[0][nb][2], s[0][nb][3]));
 #pragma unroll
       for (int mb = 1; mb < 4; ++mb)
-        mt = fmaxf(mt, fmaxf(fmaxf(s[mb][nb][0], s[mb][nb][1]), fmaxf(s[mb][nb][2], s[mb][nb][3])));
-      mt = fmaxf(mt, __shfl_xor(mt, 16));
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      mt *= sc;
-      const bool up = mt > m[nb] + kRescaleSlack;
-      const float mn = up ? mt : m[nb];
-      if (__any(up)) {   // wave-uniform
+        x = fmaxf(x, fmaxf(fmaxf(s[mb][nb][0], s[mb][nb][1]), fmaxf(s[mb][nb][2], s[mb][nb][3])));
+      mt[nb] = x * sc;
+    }
+    if (__any(mt[0] > m[0] + kRescaleSlack || mt[1] > m[1] + kRescaleSlack)) {   // rare after the first tile
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        float x = fmaxf(mt[nb], __shfl_xor(mt[nb], 16));
+        x = fmaxf(x, __shfl_xor(x, 32));
+        const float mn = x > m[nb] + kRescaleSlack ? x : m[nb];
         const float alpha = __builtin_amdgcn_exp2f(m[nb] - mn);   // 1 for rows that keep their max
         lsum[nb] *= alpha;
 #pragma unroll
         for (int db = 0; db < 8; ++db) oacc[nb][db] *= alpha;
         m[nb] = mn;
       }
+    }
+    bf16x8 pf[2][2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
       const float nm = -m[nb];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
@@ -415,6 +460,7 @@ __global__ __launch_bounds__(256, 2) void extend_mfma(const bf16* __restrict__ q
       }
     }
 
+    __syncthreads();
   }
 
   float omul = 1.f;
@@ -523,12 +569,17 @@ extern "C" int pkv_extend_attention(const void* q, void* o, int32_t qo_dtype, co
                          hkv, sc);
     return hip_check(hipGetLastError(), "extend_f32 launch");
   }
+  const int64_t slot_bytes = (int64_t)hkv * (pool_dtype == PKV_FP8_E4M3 ? 128 : 256);
+  const int64_t table_bytes = (int64_t)num_reqs * stride * 4;
+  if (slot_bytes > 16383) return fail(PKV_ERR_UNSUPPORTED, "extend: a slot of %lld bytes is too wide", (long long)slot_bytes);
+  if (table_bytes > 0x7FFFFFFFLL || num_slots > 0x7FFFFFFFLL)
+    return fail(PKV_ERR_UNSUPPORTED, "extend: slot table or pool too large for 32-bit buffer offsets");
   const dim3 grid((unsigned)(n_work * hkv));
 #define PKV_EXTEND_CASE(PP, GG)                                                                                  \
   if (pool_dtype == PP && G == GG) {                                                                             \
     hipLaunchKernelGGL((extend_mfma<PP, GG>), grid, dim3(256), 0, st, (const bf16*)q, (bf16*)o,                  \
                        (const uint8_t*)k_pool, (const uint8_t*)v_pool, k_scale, v_scale, req_to_token, stride,   \
-                       prefix_lens, extend_lens, qo_indptr, work, hkv, sc);                                      \
+                       prefix_lens, extend_lens, qo_indptr, work, hkv, sc, (int)num_slots, (int)table_bytes);     \
     return hip_check(hipGetLastError(), "extend_mfma launch");                                                   \
   }
   PKV_EXTEND_CASE(PKV_BF16, 1)
