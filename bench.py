@@ -43,11 +43,11 @@ CSRC = os.path.join(ROOT, "prefix_shared_kv_match_amd", "csrc")
 # entry holds the hash of the kernel sources it was taken on; a changed kernel reports null.
 TRAFFIC = {
     "fewshot_bf16": dict(kernel="extend_attention", src_hash="119d90842719c39a",
-                         fetch_kib=213644.125, write_kib=102968.0),
-    "decode_bf16": dict(kernel="decode_attention", src_hash="60535949e129ec94",
-                        fetch_kib=5038933.25, write_kib=47879.53125),
+                         fetch_kib=213503.625, write_kib=102968.0),
+    "decode_bf16": dict(kernel="decode_attention", src_hash="debb9625db3c04e1",
+                        fetch_kib=5099971.03125, write_kib=47887.828125),
     "longctx_fp8": dict(kernel="extend_attention", src_hash="119d90842719c39a",
-                        fetch_kib=1713570.5625, write_kib=262144.328125),
+                        fetch_kib=1712441.71875, write_kib=262144.703125),
 }
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 KERNEL_SOURCES = {"extend_attention": ["extend_attention.hip", "device.h"],
@@ -83,6 +83,9 @@ def parse():
     ap.add_argument("--policy", default="lru", help="eviction policy of the radix tree (multiturn_bf16, tot_bf16)")
     ap.add_argument("--window", type=int, default=128, help="multiturn_bf16: waiting requests the scheduler sees")
     ap.add_argument("--batch", type=int, default=32, help="multiturn_bf16: requests per round")
+    ap.add_argument("--chunk-budget", type=int, default=0,
+                    help="fewshot_bf16: chunked prefill with at most this many new tokens per extend launch "
+                         "(times the whole chunked job; 0 = the default one-batch step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=64, help="requests in the oracle's timed sample")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -209,6 +212,7 @@ class PathBench:
         self.dec_slots_dev = torch.empty(B, dtype=torch.int32, device=dev)
         self.seq_dev = torch.empty(B, dtype=torch.int32, device=dev)
         self.last_tables = None
+        self.host_prepare_s = 0.0
 
     def _src(self, a):
         t = self.torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
@@ -253,7 +257,9 @@ class PathBench:
             self._decode_step(self.hb, self.r2t_dev, i)
             self.last_tables = self.hb
             return self.hb.n
+        th = time.perf_counter()
         hb = eng.prepare(self.tokens, self.stride)                       # host: match/lock/alloc/insert
+        self.host_prepare_s += time.perf_counter() - th
         dt = eng.device_tables(hb, staged=True)                          # H2D tables + plan (async)
         with T.span("kv_scatter"):
             eng.scatter(dt["new_slots"], self.k_src, self.v_src)
@@ -285,7 +291,8 @@ class JobBench:
         from prefix_shared_kv_match_amd import runtime
         from prefix_shared_kv_match_amd.runtime import Engine
         self.torch, self.rt = torch, runtime
-        self.wl = wl = workloads.make(a.workload)
+        kw = {"decode_steps": 0} if a.workload == "fewshot_bf16" else {}
+        self.wl = wl = workloads.make(a.workload, **kw)
         self.name, self.a = a.workload, a
         s = wl.shape
         self.eng = eng = Engine(wl.pool_slots, s.hq, s.hkv, s.d, s.qo_dtype, s.pool_dtype, wl.free_order, "cuda",
@@ -313,8 +320,8 @@ class JobBench:
         finally:
             runtime.rt_destroy(twin)
         self.inputs = []
-        for pick, pl in self.plan:
-            rows = np.concatenate([self.arr[i].rows[p:] for i, p in zip(pick, pl)]) if pick else np.zeros(0)
+        for pick, pl, ends in self.plan:
+            rows = np.concatenate([self.arr[i].rows[p:e] for i, p, e in zip(pick, pl, ends)]) if pick else np.zeros(0)
             idx = torch.from_numpy(rows.astype(np.int64)).cuda()
             self.inputs.append((self.K.index_select(0, idx), self.V.index_select(0, idx), self.Q.index_select(0, idx)))
         self.o = torch.empty((max(x[2].shape[0] for x in self.inputs), s.hq, s.d), dtype=torch.bfloat16, device="cuda")
@@ -336,12 +343,18 @@ class JobBench:
         torch.cuda.synchronize()
         self.flops = 0.0
         self.ext_tokens = 0
-        for pick, pl in self.plan:
-            el = [len(self.arr[i].tokens) - p for i, p in zip(pick, pl)]
+        for pick, pl, ends in self.plan:
+            el = [e - p for p, e in zip(pl, ends)]
             self.flops += extend_flops(s.d, s.hq, pl, el)[0]
             self.ext_tokens += int(sum(el))
         self.prompt_tokens = sum(len(r.tokens) for r in self.arr)
-        self.cached_tokens = sum(int(sum(pl)) for _, pl in self.plan)
+        # tokens served from the cache: each request's first prefix length (later chunks of a
+        # request reuse its own earlier chunks, which were computed in this job)
+        first = {}
+        for pick, pl, _ in self.plan:
+            for i, p in zip(pick, pl):
+                first.setdefault(i, p)
+        self.cached_tokens = sum(first.values())
 
     def _table(self, tag):
         full = self.wl.values.full(tag)
@@ -358,14 +371,21 @@ class JobBench:
 
     def _host_rounds(self, tree, on_round):
         """Runs the job's host steps on `tree`; on_round(k, host_batch) does round k's device work.
-        Returns [(request indices, prefix lengths)] per round."""
+        Returns [(request indices, prefix lengths, end positions)] per round."""
         rt, wl, a = self.rt, self.wl, self.a
         out = []
+        if self.name == "fewshot_bf16":   # chunked prefill of the 64-request batch
+            def cb(reqs, ends, hb):
+                if on_round is not None:
+                    on_round(len(out), hb)
+                out.append((list(reqs), hb.prefix_lens.tolist(), list(ends)))
+            rt.chunked_prefill(tree, [r.tokens for r in self.arr], a.chunk_budget, self.stride, on_launch=cb)
+            return out
         if self.name == "multiturn_bf16":
             def cb(pick, hb):
                 if on_round is not None:
                     on_round(len(out), hb)
-                out.append((list(pick), hb.prefix_lens.tolist()))
+                out.append((list(pick), hb.prefix_lens.tolist(), [len(self.arr[i].tokens) for i in pick]))
             rt.serve(tree, [r.tokens for r in self.arr], [r.after for r in self.arr], a.schedule, a.batch, a.window,
                      self.stride, priorities=[r.priority for r in self.arr], on_batch=cb)
             return out
@@ -374,7 +394,7 @@ class JobBench:
             hb = rt.prepare(tree, [r.tokens for r in batch], self.stride)
             if on_round is not None:
                 on_round(len(out), hb)
-            out.append((list(range(base, base + len(batch))), hb.prefix_lens.tolist()))
+            out.append((list(range(base, base + len(batch))), hb.prefix_lens.tolist(), [len(r.tokens) for r in batch]))
             base += len(batch)
             if bi < len(wl.batches) - 1 or not wl.decode_tokens.shape[0]:
                 rt.rt_release(tree, hb.last_nodes)
@@ -384,7 +404,7 @@ class JobBench:
 
     def _round(self, k, hb):
         eng, T = self.eng, self.timer
-        pick, pl = self.plan[k]
+        pick, pl, _ = self.plan[k]
         if hb.prefix_lens.tolist() != pl:
             raise RuntimeError(f"round {k} matched differently from the planning run")
         dt = eng.device_tables(hb, staged=True)
@@ -442,6 +462,25 @@ def torch_from(torch, a):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
 
 
+def practical_hbm_gbps(torch, mib=1024, reps=5):
+    """A plain device-to-device copy of `mib` MiB (read + write), best of `reps`: the HBM rate a
+    streaming kernel reaches on this GPU, next to the published 8 TB/s."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    best = float("inf")
+    for _ in range(reps + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1))
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2.0 * n * 4 / best / 1e6
+
+
 def main_job(a, torch):
     import prefix_shared_kv_match_amd as pkv
     b = JobBench(torch, a)
@@ -471,7 +510,9 @@ def main_job(a, torch):
         "warmup": a.warmup, "ms_per_step": el / a.steps * 1e3, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wl.name, "requests": len(b.arr), "rounds": len(b.plan), "policy": a.policy,
-                   "schedule": a.schedule if wl.name == "multiturn_bf16" else "levels in order",
+                   "schedule": a.schedule if wl.name == "multiturn_bf16" else (
+                       f"chunked prefill, {a.chunk_budget} new tokens per launch" if wl.name == "fewshot_bf16"
+                       else "levels in order"),
                    "window": a.window if wl.name == "multiturn_bf16" else None,
                    "hq": s.hq, "hkv": s.hkv, "head_dim": s.d, "pool_slots": wl.pool_slots,
                    "capacity": int(len(wl.free_order))},
@@ -533,7 +574,7 @@ def main():
         return 2
     import prefix_shared_kv_match_amd as pkv
     pkv.lib()
-    if a.workload in ("multiturn_bf16", "tot_bf16"):
+    if a.workload in ("multiturn_bf16", "tot_bf16") or (a.workload == "fewshot_bf16" and a.chunk_budget > 0):
         return main_job(a, torch)
     b = PathBench(torch, a.workload, a.warmup + a.steps)
     wl = b.wl
@@ -547,6 +588,7 @@ def main():
     for _ in range(a.warmup):
         b.step()
     b.timer.reset()
+    b.host_prepare_s = 0.0
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     tokens = 0
@@ -555,6 +597,7 @@ def main():
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     b.timer.collect()
+    hbm_practical = practical_hbm_gbps(torch)
     hb = b.last_tables
     s = wl.shape
     flops, pairs = extend_flops(s.d, s.hq, hb.prefix_lens, hb.extend_lens)
@@ -567,13 +610,18 @@ def main():
         kernels["extend_attention"] = {
             "ms": ext_ms, "tflops": flops / ext_ms / 1e9, "frac_mfma": flops / ext_ms / 1e9 / PEAK_BF16_TFLOPS,
             "kv_gathered_gbps": gathered_ext / ext_ms / 1e6, "flops": flops, "pairs": pairs,
-            "query_tokens": int(hb.extend_lens.sum())}
+            "query_tokens": int(hb.extend_lens.sum()),
+            "q_o_bytes": 2.0 * float(hb.extend_lens.sum()) * s.hq * s.d * (4 if s.qo_dtype == "f32" else 2),
+            "unique_kv_bytes": float(np.unique(np.concatenate(
+                [hb.req_to_token[i, :hb.seq_lens[i]] for i in range(hb.n)])).size) * kv_tok,
+            "host_prepare_ms": b.host_prepare_s / a.steps * 1e3}
     if b.steps_dec:
         ctx = hb.seq_lens.astype(np.float64)
         dec_bytes = float(ctx.sum()) * kv_tok
         kernels["decode_attention"] = {
             "ms": dec_ms, "kv_gathered_gbps": dec_bytes / dec_ms / 1e6,
             "frac_hbm": dec_bytes / dec_ms / 1e6 / PEAK_HBM_GBPS, "bytes": dec_bytes,
+            "frac_hbm_practical": dec_bytes / dec_ms / 1e6 / hbm_practical,
             "tflops": 4.0 * s.d * s.hq * float(ctx.sum()) / dec_ms / 1e9}
     sc_name = "kv_scatter_decode" if b.decode_only else "kv_scatter"
     sc_ms = b.timer.avg_ms(sc_name)
@@ -597,6 +645,7 @@ def main():
         "roofline": {"bound": bound, "kernel": dom, "achieved": achieved, "peak": peak, "unit": unit,
                      "frac": achieved / peak, "traffic": traffic_bytes(wl.name, dom)},
         "kernels": kernels,
+        "hbm_practical_gbps": hbm_practical,
         "library": os.path.relpath(pkv._capi.LIB_PATH, ROOT),
     }
     if not a.no_cpu_baseline:

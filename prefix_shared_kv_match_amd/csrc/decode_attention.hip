@@ -251,10 +251,12 @@ __global__ __launch_bounds__(256) void decode_split(const QT* __restrict__ q, co
 // All kv heads of a sequence in one workgroup: 16 rows of 16 lanes = HKV heads x (16/HKV)
 // token streams.  Every token's K (and V) slot row of HKV*d values is then read as one
 // contiguous run by the HKV rows of a stream, instead of HKV separate 256-byte pieces
-// fetched by different workgroups at different times.  Streams of one head are merged in
-// LDS at the end.  blockIdx.x = b * max_splits + s.
+// fetched by different workgroups at different times.  Each stream keeps the next group of
+// kUnroll tokens in flight (two register buffers) while it consumes the current one; with a
+// bf16 pool the q.k products are packed bf16 dot products.  Streams of one head are merged
+// in LDS at the end.  blockIdx.x = b * max_splits + s.
 template <typename QT, int POOL, int D, int G, int HKV>
-__global__ __launch_bounds__(256) void decode_split_slot(const QT* __restrict__ q, const uint8_t* __restrict__ kpool,
+__global__ __launch_bounds__(256, (G >= 8 ? 2 : 3)) void decode_split_slot(const QT* __restrict__ q, const uint8_t* __restrict__ kpool,
                                                          const uint8_t* __restrict__ vpool,
                                                          const float* __restrict__ kscale,
                                                          const float* __restrict__ vscale,
@@ -279,12 +281,21 @@ __global__ __launch_bounds__(256) void decode_split_slot(const QT* __restrict__ 
   const int g = r % HKV, stream = r / HKV;
   const int hq = HKV * G;
 
+  // bf16 q and pool: the q.k products run as packed bf16 dot products (two per instruction,
+  // float32 accumulation); otherwise q is widened to float once
+  constexpr bool kDot2 = POOL == PKV_BF16 && sizeof(QT) == 2 && VEC == 8;
   float qf[G][VEC];
+  bf16x2 q2[G][VEC / 2];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     const QT* qp = q + ((int64_t)b * hq + (int64_t)g * G + h) * D + li * VEC;
+    if constexpr (kDot2) {
 #pragma unroll
-    for (int i = 0; i < VEC; ++i) qf[h][i] = load_q<QT>(qp, i);
+      for (int i = 0; i < VEC / 2; ++i) q2[h][i] = bf16x2{(bf16)load_q<QT>(qp, 2 * i), (bf16)load_q<QT>(qp, 2 * i + 1)};
+    } else {
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) qf[h][i] = load_q<QT>(qp, i);
+    }
   }
   float kmul = qk_scale_log2;
   if constexpr (POOL == PKV_FP8_E4M3) kmul *= kscale[g];
@@ -300,27 +311,35 @@ __global__ __launch_bounds__(256) void decode_split_slot(const QT* __restrict__ 
   const int32_t* row = r2t + (int64_t)b * stride;
   constexpr int64_t slot_bytes = (int64_t)HKV * ROWB;
   const int64_t head_off = (int64_t)g * ROWB + li * Chunk::kBytes;
+  constexpr int kStep = STREAMS * kUnroll;
 
-  for (int base = t0 + stream; base < t1; base += STREAMS * kUnroll) {
-    Chunk kc[kUnroll], vc[kUnroll];
-    bool valid[kUnroll];
+  // tokens base + STREAMS*u; those at or past t1 re-read token t0 and are masked
+  auto load = [&](int base, Chunk* kc, Chunk* vc) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int t = base + STREAMS * u;
-      valid[u] = t < t1;
-      const int64_t slot = row[valid[u] ? t : t0];
+      const int64_t slot = row[t < t1 ? t : t0];
       kc[u].load(kpool + slot * slot_bytes + head_off);
       vc[u].load(vpool + slot * slot_bytes + head_off);
     }
+  };
+  auto consume = [&](int base, const Chunk* kc, const Chunk* vc) {
     float sc[kUnroll][G];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
+      const bool valid = base + STREAMS * u < t1;
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         float part = 0.f;
+        if constexpr (kDot2) {
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) part = fmaf(qf[h][i], kc[u].get(i), part);
-        sc[u][h] = valid[u] ? row16_sum(part) * kmul : -INFINITY;
+          for (int i = 0; i < VEC / 2; ++i)
+            part = __builtin_amdgcn_fdot2_f32_bf16(q2[h][i], __builtin_bit_cast(bf16x2, kc[u].w[i]), part, false);
+        } else {
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) part = fmaf(qf[h][i], kc[u].get(i), part);
+        }
+        sc[u][h] = valid ? row16_sum(part) * kmul : -INFINITY;
       }
     }
 #pragma unroll
@@ -331,23 +350,37 @@ __global__ __launch_bounds__(256) void decode_split_slot(const QT* __restrict__ 
       const float mn = fmaxf(m[h], mt);
       if (mn == -INFINITY) continue;  // this row has not seen a token yet (uniform within the row)
       const float alpha = __builtin_amdgcn_exp2f(m[h] - mn);
-      float p[kUnroll];
+      float pr[kUnroll];
       float psum = 0.f;
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
-        p[u] = __builtin_amdgcn_exp2f(sc[u][h] - mn);  // masked: 2^-inf = 0
-        psum += p[u];
+        pr[u] = __builtin_amdgcn_exp2f(sc[u][h] - mn);  // masked: 2^-inf = 0
+        psum += pr[u];
       }
       l[h] = l[h] * alpha + psum;
 #pragma unroll
       for (int i = 0; i < VEC; ++i) {
         float a = acc[h][i] * alpha;
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) a = fmaf(p[u], vc[u].get(i), a);
+        for (int u = 0; u < kUnroll; ++u) a = fmaf(pr[u], vc[u].get(i), a);
         acc[h][i] = a;
       }
       m[h] = mn;
     }
+  };
+
+  // two register buffers: the next group of tokens is in flight while this one is consumed
+  Chunk ka[kUnroll], va[kUnroll], kb[kUnroll], vb[kUnroll];
+  int base = t0 + stream;
+  if (base < t1) load(base, ka, va);
+  while (base < t1) {
+    load(base + kStep, kb, vb);
+    consume(base, ka, va);
+    base += kStep;
+    if (base >= t1) break;
+    load(base + kStep, ka, va);
+    consume(base, kb, vb);
+    base += kStep;
   }
 
   // merge the streams of each head into stream 0
@@ -492,8 +525,10 @@ int splits_for(int max_seq_len, int chunk) { return (max_seq_len + chunk - 1) / 
 using namespace pkv;
 
 extern "C" int32_t pkv_decode_chunk(int32_t batch, int32_t hkv, int32_t max_seq_len) {
+  // workgroups per (sequence, chunk): one for all kv heads when hkv is 2, 4 or 8, else one per head
+  const int64_t per_chunk = (hkv == 2 || hkv == 4 || hkv == 8) ? 1 : hkv;
   int chunk = 1024;
-  while (chunk > 128 && (int64_t)batch * hkv * splits_for(max_seq_len, chunk) < 2048) chunk /= 2;
+  while (chunk > 128 && (int64_t)batch * per_chunk * splits_for(max_seq_len, chunk) < 2048) chunk /= 2;
   return chunk;
 }
 
