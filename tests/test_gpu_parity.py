@@ -114,6 +114,15 @@ def test_decode_small_every_row():
     report("decode small", stats)
 
 
+def test_decode_two_long_sequences_many_splits():
+    log("decode two long sequences")
+    # two sequences only: the automatic chunk drops to 128 tokens, about 110 splits each
+    wl = workloads.decode_bf16(n_seq=2, n_prefix=1, prefix_len=1024, ctx_range=(12000, 15000), steps=2,
+                               pool_slots=40000)
+    stats = Run(wl).run()
+    report("decode two long sequences", stats)
+
+
 def test_longctx_small_every_row():
     log("longctx small")
     wl = workloads.longctx_fp8(prefix_len=2048, suffix_len=200, n_req=4, steps=3, pool_slots=8192)

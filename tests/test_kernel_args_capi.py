@@ -106,6 +106,14 @@ def test_workspace_and_chunk_helpers():
     for b in (1, 64, 512):
         c = lib.pkv_decode_chunk(b, 8, 8192)
         assert 128 <= c <= 1024 and c % 64 == 0
+    # the all-heads kernel (hkv 2, 4, 8) launches one workgroup per (sequence, chunk): halve the
+    # chunk until 2048 of them are launched (64 x 2,000-token few-shot sequences: 128-token
+    # chunks; 16 x 33,856: 256; 512 x 8,224: 1,024); per-head kernels count kv heads too
+    assert lib.pkv_decode_chunk(64, 8, 2000) == 128
+    assert lib.pkv_decode_chunk(16, 8, 33856) == 256
+    assert lib.pkv_decode_chunk(512, 8, 8224) == 1024
+    assert lib.pkv_decode_chunk(256, 32, 1897) == 1024
+    assert lib.pkv_decode_chunk(4, 32, 1000) == 128
     assert lib.pkv_extend_tile(PKV_BF16, PKV_BF16, 32, 8, 128) == 32
     assert lib.pkv_extend_tile(PKV_BF16, PKV_BF16, 32, 32, 128) == 128
     assert lib.pkv_extend_tile(PKV_F32, PKV_F32, 8, 8, 64) > 0
