@@ -103,3 +103,28 @@ def test_chunked_prefill_fewshot_small(budget):
     runtime.chunked_prefill(eng.tree, [r.tokens for r in reqs], budget, wl.max_len(), on_launch=on_launch)
     assert len(stats) == len(launches) >= (1 if budget >= 1000 else 2)
     log(f"  {len(stats)} launches, worst {max(s['rel_rms'] for s in stats if s)}")
+
+
+def test_staged_tables_match_plain_upload():
+    """The packed, double-buffered table upload the bench and the job loops use gives the same
+    extend output as a plain upload, over three consecutive batches (both staging buffers and
+    the reuse of the device pack)."""
+    log("staged tables")
+    wl = workloads.multiturn_bf16(n_conv=12, turns=3, turn_range=(16, 80), batch=6, pool_slots=20000,
+                                  capacity=12000)
+    eng = make_engine(wl)
+    for bi, batch in enumerate(wl.batches[:3]):
+        hb = eng.prepare([r.tokens for r in batch], wl.max_len())
+        rows = np.concatenate([r.rows[p:] for r, p in zip(batch, hb.prefix_lens)])
+        sl = torch.from_numpy(np.ascontiguousarray(hb.new_slots, dtype=np.int32)).cuda()
+        eng.scatter(sl, src_tensor(torch, wl.values.k(rows), wl.shape, "cuda"),
+                    src_tensor(torch, wl.values.v(rows), wl.shape, "cuda"))
+        q = src_tensor(torch, wl.values.q(rows), wl.shape, "cuda")
+        plain = eng.extend(eng.device_tables(hb), q)
+        staged_tables = eng.device_tables(hb, staged=True)
+        for k, v in eng.device_tables(hb).items():
+            assert torch.equal(staged_tables[k].cpu(), v.cpu()), (bi, k)
+        staged = eng.extend(staged_tables, q)
+        torch.cuda.synchronize()
+        assert torch.equal(plain, staged), bi
+        eng.release(hb)
