@@ -351,6 +351,8 @@ __global__ __launch_bounds__(256, 2) void extend_mfma(const bf16* __restrict__ q
   const bf16 one = (bf16)(ln == 0 ? 1.f : 0.f);
   const bf16x8 ones_row = {one, one, one, one, one, one, one, one};
   const int qpos0 = p + j0;   // position of the tile's first query token
+  // only for G = 1 (a wave's rows are 32 consecutive tokens): is any of them a real query?
+  const bool active = G != 1 || 32 * wave < nq;
   // last visible kv position of this lane's rows (padded rows see the whole context)
   int vis[2];
 #pragma unroll
@@ -373,90 +375,97 @@ __global__ __launch_bounds__(256, 2) void extend_mfma(const bf16* __restrict__ q
     stage.store(Ks[(kt + 1) & 1], Vt[(kt + 1) & 1], tid);
     stage.load(gt, min(kt + 2, n_tiles - 1) * kBN, g, tid);
 
-    // S^T = K . Q^T
-    floatx4 s[4][2];
+    if (active) {   // wave-uniform; with one head per item a wave of only padding tokens just stages
+      // S^T = K . Q^T
+      floatx4 s[4][2];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+      for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) s[mb][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int nb = 0; nb < 2; ++nb) s[mb][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+      for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        const bf16x8 a = *(const bf16x8*)(K + krow(sigma(mb, ln)) * kKStride + 32 * ks + 8 * lg);
+        for (int mb = 0; mb < 4; ++mb) {
+          const bf16x8 a = *(const bf16x8*)(K + krow(sigma(mb, ln)) * kKStride + 32 * ks + 8 * lg);
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) s[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[nb][ks], s[mb][nb], 0, 0, 0);
+          for (int nb = 0; nb < 2; ++nb) s[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[nb][ks], s[mb][nb], 0, 0, 0);
+        }
       }
-    }
 
-    // causal / context mask, only on tiles reaching past the first query position
-    if (kv0 + kBN > qpos0 + 1) {
+      // causal / context mask, only on tiles reaching past the first query position
+      if (kv0 + kBN > qpos0 + 1) {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          const int lim = vis[nb] - kv0 - 8 * lg;   // visible iff token offset - 8 lg <= lim
+#pragma unroll
+          for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int off = 32 * (mb >> 1) + 4 * (mb & 1) + i;
+              s[mb][nb][i] = off <= lim ? s[mb][nb][i] : -INFINITY;
+            }
+        }
+      }
+
+      // online softmax (log2 domain) with lazy rescaling.  Each lane's max over its 16 logits
+      // of a row; the row max across the 4 lanes that share the query row is only formed when
+      // some lane may move the reference max (one wave-uniform test for both row blocks).
+      float mt[2];
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
-        const int lim = vis[nb] - kv0 - 8 * lg;   // visible iff token offset - 8 lg <= lim
+        // a linear chain, so each step is one three-input max
+        float x = fmaxf(fmaxf(s[0][nb][0], s[0][nb][1]), s[0][nb][2]);
+        x = fmaxf(fmaxf(x, s[0][nb][3]), s[1][nb][0]);
+        x = fmaxf(fmaxf(x, s[1][nb][1]), s[1][nb][2]);
+        x = fmaxf(fmaxf(x, s[1][nb][3]), s[2][nb][0]);
+        x = fmaxf(fmaxf(x, s[2][nb][1]), s[2][nb][2]);
+        x = fmaxf(fmaxf(x, s[2][nb][3]), s[3][nb][0]);
+        x = fmaxf(fmaxf(x, s[3][nb][1]), s[3][nb][2]);
+        x = fmaxf(x, s[3][nb][3]);
+        mt[nb] = x * sc;
+      }
+      if (__any(mt[0] > m[0] + kRescaleSlack || mt[1] > m[1] + kRescaleSlack)) {   // rare after the first tile
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
+        for (int nb = 0; nb < 2; ++nb) {
+          float x = fmaxf(mt[nb], __shfl_xor(mt[nb], 16));
+          x = fmaxf(x, __shfl_xor(x, 32));
+          const float mn = x > m[nb] + kRescaleSlack ? x : m[nb];
+          const float alpha = __builtin_amdgcn_exp2f(m[nb] - mn);   // 1 for rows that keep their max
+          lsum[nb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < 8; ++db) oacc[nb][db] *= alpha;
+          m[nb] = mn;
+        }
+      }
+      bf16x8 pf[2][2];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const float nm = -m[nb];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          bf16x8 pv;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int off = 32 * (mb >> 1) + 4 * (mb & 1) + i;
-            s[mb][nb][i] = off <= lim ? s[mb][nb][i] : -INFINITY;
+            pv[i] = (bf16)__builtin_amdgcn_exp2f(fmaf(s[2 * kk][nb][i], sc, nm));
+            pv[4 + i] = (bf16)__builtin_amdgcn_exp2f(fmaf(s[2 * kk + 1][nb][i], sc, nm));
           }
+          pf[nb][kk] = pv;
+        }
       }
-    }
 
-    // online softmax (log2 domain) with lazy rescaling.  Each lane's max over its 16 logits
-    // of a row; the row max across the 4 lanes that share the query row is only formed when
-    // some lane may move the reference max (one wave-uniform test for both row blocks).
-    float mt[2];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      float x = fmaxf(fmaxf(s[0][nb][0], s[0][nb][1]), fmaxf(s[0][nb][2], s[0][nb][3]));
-#pragma unroll
-      for (int mb = 1; mb < 4; ++mb)
-        x = fmaxf(x, fmaxf(fmaxf(s[mb][nb][0], s[mb][nb][1]), fmaxf(s[mb][nb][2], s[mb][nb][3])));
-      mt[nb] = x * sc;
-    }
-    if (__any(mt[0] > m[0] + kRescaleSlack || mt[1] > m[1] + kRescaleSlack)) {   // rare after the first tile
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        float x = fmaxf(mt[nb], __shfl_xor(mt[nb], 16));
-        x = fmaxf(x, __shfl_xor(x, 32));
-        const float mn = x > m[nb] + kRescaleSlack ? x : m[nb];
-        const float alpha = __builtin_amdgcn_exp2f(m[nb] - mn);   // 1 for rows that keep their max
-        lsum[nb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < 8; ++db) oacc[nb][db] *= alpha;
-        m[nb] = mn;
-      }
-    }
-    bf16x8 pf[2][2];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const float nm = -m[nb];
+      // O^T += V^T . P^T, and the row sums
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        bf16x8 pv;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pv[i] = (bf16)__builtin_amdgcn_exp2f(fmaf(s[2 * kk][nb][i], sc, nm));
-          pv[4 + i] = (bf16)__builtin_amdgcn_exp2f(fmaf(s[2 * kk + 1][nb][i], sc, nm));
-        }
-        pf[nb][kk] = pv;
-      }
-    }
-
-    // O^T += V^T . P^T, and the row sums
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-        lsum[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_row, pf[nb][kk], lsum[nb], 0, 0, 0);
-#pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        const bf16x8 a = *(const bf16x8*)(V + (16 * db + ln) * kVStride + 32 * kk + 8 * lg);
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
-          oacc[nb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[nb][kk], oacc[nb][db], 0, 0, 0);
+          lsum[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_row, pf[nb][kk], lsum[nb], 0, 0, 0);
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+          const bf16x8 a = *(const bf16x8*)(V + (16 * db + ln) * kVStride + 32 * kk + 8 * lg);
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb)
+            oacc[nb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[nb][kk], oacc[nb][db], 0, 0, 0);
+        }
       }
     }
 
