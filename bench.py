@@ -42,12 +42,12 @@ CSRC = os.path.join(ROOT, "prefix_shared_kv_match_amd", "csrc")
 # what the same counters read for a plain 1 GiB device copy (FETCH x2.0, WRITE x1.0).  Each
 # entry holds the hash of the kernel sources it was taken on; a changed kernel reports null.
 TRAFFIC = {
-    "fewshot_bf16": dict(kernel="extend_attention", src_hash="119d90842719c39a",
-                         fetch_kib=213503.625, write_kib=102968.0),
+    "fewshot_bf16": dict(kernel="extend_attention", src_hash="2a37b0b77ba0fbb8",
+                         fetch_kib=212688.03125, write_kib=102968.0),
     "decode_bf16": dict(kernel="decode_attention", src_hash="debb9625db3c04e1",
-                        fetch_kib=5099971.03125, write_kib=47887.828125),
-    "longctx_fp8": dict(kernel="extend_attention", src_hash="119d90842719c39a",
-                        fetch_kib=1712441.71875, write_kib=262144.703125),
+                        fetch_kib=5113414.0625, write_kib=47890.953125),
+    "longctx_fp8": dict(kernel="extend_attention", src_hash="2a37b0b77ba0fbb8",
+                        fetch_kib=1715781.0625, write_kib=262144.375),
 }
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 KERNEL_SOURCES = {"extend_attention": ["extend_attention.hip", "device.h"],
