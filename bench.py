@@ -44,7 +44,7 @@ CSRC = os.path.join(ROOT, "prefix_shared_kv_match_amd", "csrc")
 TRAFFIC = {
     "fewshot_bf16": dict(kernel="extend_attention", src_hash="2a37b0b77ba0fbb8",
                          fetch_kib=212688.03125, write_kib=102968.0),
-    "decode_bf16": dict(kernel="decode_attention", src_hash="debb9625db3c04e1",
+    "decode_bf16": dict(kernel="decode_attention", src_hash="94f2f02a17783c31",
                         fetch_kib=5113414.0625, write_kib=47890.953125),
     "longctx_fp8": dict(kernel="extend_attention", src_hash="2a37b0b77ba0fbb8",
                         fetch_kib=1715781.0625, write_kib=262144.375),

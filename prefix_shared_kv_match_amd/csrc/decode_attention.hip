@@ -1,20 +1,24 @@
 // Split-K decode attention over K/V gathered through slot rows, then a log-sum-exp reduce.
 //
 // Decode is the `gen` step of the pages (one new token per sequence per step, attending
-// over its whole cached context, the newest token's own K/V included).  Per sequence b,
-// kv head g and context chunk s, one workgroup streams the chunk's K and V rows and keeps
-// a running max / running sum / unnormalised output for the G = hq/hkv query heads that
-// share kv head g, so every gathered row is read once for the whole GQA group.  The
-// reduce merges the chunks: M = max_s m_s, o = sum_s 2^(m_s-M) acc_s / sum_s 2^(m_s-M) l_s.
+// over its whole cached context, the newest token's own K/V included).  The context of
+// sequence b is cut into chunks; for each chunk s a workgroup streams the chunk's K and V
+// rows and keeps a running max / running sum / unnormalised output for the G = hq/hkv
+// query heads that share a kv head, so every gathered row is read once for the whole GQA
+// group.  The reduce merges the chunks: M = max_s m_s, o = sum_s 2^(m_s-M) acc_s /
+// sum_s 2^(m_s-M) l_s.
 //
-// Layout on gfx950: a 256-thread workgroup is 4 waves x 4 rows of 16 lanes.  A 16-lane
-// row owns one token at a time and covers the head dim (d/16 values per lane), so each
-// K or V row (256 B for bf16 d=128, 128 B for fp8) is one coalesced access per row of
-// lanes.  Dot products are reduced inside the row with DPP (no LDS).  Each 16-lane row
-// runs its own online softmax over a token sub-stream; rows and waves are merged once at
-// the end.  Work is HBM-bound (about 4 FLOP per gathered byte for bf16 GQA-4), so no
-// MFMA is used.  blockIdx.x = (b * max_splits + s) * hkv + g: consecutive workgroups
-// cycle through the kv heads, which places each kv head on one XCD when hkv = 8.
+// Layout on gfx950: a 256-thread workgroup is 16 rows of 16 lanes.  A 16-lane row owns one
+// token at a time and covers the head dim (d/16 values per lane), so each K or V row
+// (256 B for bf16 d=128, 128 B for fp8) is one coalesced access per row of lanes.  Dot
+// products are reduced inside the row with DPP (no LDS).  Each row runs its own online
+// softmax over a token sub-stream; rows of one head are merged once at the end.  Work is
+// HBM-bound (about 4 FLOP per gathered byte for bf16 GQA-4), so no MFMA is used.
+//  - decode_split_slot (hkv 2, 4 or 8): one workgroup per (sequence, chunk) covering every
+//    kv head, so a token's whole slot row is read at once; blockIdx.x = b * max_splits + s.
+//  - decode_split (other hkv, e.g. multi-head attention): one workgroup per (sequence,
+//    chunk, kv head); blockIdx.x = (b * max_splits + s) * hkv + g, so consecutive
+//    workgroups cycle through the kv heads.
 
 #include <math.h>
 
