@@ -43,11 +43,11 @@ CSRC = os.path.join(ROOT, "prefix_shared_kv_match_amd", "csrc")
 # entry holds the hash of the kernel sources it was taken on; a changed kernel reports null.
 TRAFFIC = {
     "fewshot_bf16": dict(kernel="extend_attention", src_hash="2a37b0b77ba0fbb8",
-                         fetch_kib=212688.03125, write_kib=102968.0),
-    "decode_bf16": dict(kernel="decode_attention", src_hash="94f2f02a17783c31",
-                        fetch_kib=5113414.0625, write_kib=47890.953125),
+                         fetch_kib=212857.96875, write_kib=102968.0),
+    "decode_bf16": dict(kernel="decode_attention", src_hash="1c25a75dd0c3e5a3",
+                        fetch_kib=5097152.96875, write_kib=47959.75),
     "longctx_fp8": dict(kernel="extend_attention", src_hash="2a37b0b77ba0fbb8",
-                        fetch_kib=1715781.0625, write_kib=262144.375),
+                        fetch_kib=1719060.40625, write_kib=262144.46875),
 }
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 KERNEL_SOURCES = {"extend_attention": ["extend_attention.hip", "device.h"],

@@ -290,7 +290,8 @@ int pkv_extend_attention(const void* q, void* o, int32_t qo_dtype, const void* k
 size_t pkv_decode_workspace_bytes(int32_t batch, int32_t hq, int32_t d, int32_t max_seq_len, int32_t chunk);
 /* The automatic chunk: 1024 tokens, halved (not below 128) while the split phase would launch
  * fewer than 2048 workgroups (one per (sequence, chunk) when hkv is 2, 4 or 8, one per
- * (sequence, chunk, kv head) otherwise). */
+ * (sequence, chunk, group of 8 kv heads) for other multiples of 8, one per (sequence, chunk,
+ * kv head) otherwise). */
 int32_t pkv_decode_chunk(int32_t batch, int32_t hkv, int32_t max_seq_len);
 int pkv_decode_attention(const void* q, void* o, int32_t qo_dtype, const void* k_pool, const void* v_pool,
                          int32_t pool_dtype, int64_t num_slots, const float* k_scale, const float* v_scale,

@@ -14,11 +14,12 @@
 // products are reduced inside the row with DPP (no LDS).  Each row runs its own online
 // softmax over a token sub-stream; rows of one head are merged once at the end.  Work is
 // HBM-bound (about 4 FLOP per gathered byte for bf16 GQA-4), so no MFMA is used.
-//  - decode_split_slot (hkv 2, 4 or 8): one workgroup per (sequence, chunk) covering every
-//    kv head, so a token's whole slot row is read at once; blockIdx.x = b * max_splits + s.
-//  - decode_split (other hkv, e.g. multi-head attention): one workgroup per (sequence,
-//    chunk, kv head); blockIdx.x = (b * max_splits + s) * hkv + g, so consecutive
-//    workgroups cycle through the kv heads.
+//  - decode_split_slot (hkv 2, 4 or 8, or any multiple of 8 in groups of 8 heads, e.g.
+//    multi-head attention): one workgroup per (sequence, chunk, head group), so a token's
+//    slot row (or its 8-head part) is read at once; blockIdx.x = (b * max_splits + s) *
+//    groups + group.
+//  - decode_split (other hkv): one workgroup per (sequence, chunk, kv head); blockIdx.x =
+//    (b * max_splits + s) * hkv + g, so consecutive workgroups cycle through the kv heads.
 
 #include <math.h>
 
@@ -267,7 +268,8 @@ __global__ __launch_bounds__(256, (G >= 8 ? 2 : 3)) void decode_split_slot(const
                                                          const int32_t* __restrict__ r2t, int64_t stride,
                                                          const int32_t* __restrict__ seq_lens, int chunk,
                                                          int max_splits, float qk_scale_log2,
-                                                         float* __restrict__ ws_ml, float* __restrict__ ws_acc) {
+                                                         float* __restrict__ ws_ml, float* __restrict__ ws_acc,
+                                                         int hkv_total) {
   constexpr int VEC = D / 16;
   constexpr int STREAMS = 16 / HKV;
   using Chunk = RowChunk<POOL, VEC>;
@@ -275,15 +277,19 @@ __global__ __launch_bounds__(256, (G >= 8 ? 2 : 3)) void decode_split_slot(const
   __shared__ float sm_ml[(STREAMS - 1) * HKV][G][2];
   __shared__ float sm_acc[(STREAMS - 1) * HKV][G][D];
 
-  const int s = blockIdx.x % max_splits;
-  const int b = blockIdx.x / max_splits;
+  // kv heads in groups of HKV: blockIdx.x = (b * max_splits + s) * groups + group
+  const int groups = hkv_total / HKV;
+  const int group = blockIdx.x % groups;
+  const int s = (blockIdx.x / groups) % max_splits;
+  const int b = blockIdx.x / groups / max_splits;
   const int L = seq_lens[b];
   const int t0 = s * chunk;
   if (t0 >= L) return;  // the whole workgroup leaves together
   const int t1 = min(t0 + chunk, L);
   const int r = threadIdx.x >> 4, li = threadIdx.x & 15;
-  const int g = r % HKV, stream = r / HKV;
-  const int hq = HKV * G;
+  const int gl = r % HKV, stream = r / HKV;   // this row's head within the group, token stream
+  const int g = group * HKV + gl;
+  const int hq = hkv_total * G;
 
   // bf16 q and pool: the q.k products run as packed bf16 dot products (two per instruction,
   // float32 accumulation); otherwise q is widened to float once
@@ -313,7 +319,7 @@ __global__ __launch_bounds__(256, (G >= 8 ? 2 : 3)) void decode_split_slot(const
     for (int i = 0; i < VEC; ++i) acc[h][i] = 0.f;
   }
   const int32_t* row = r2t + (int64_t)b * stride;
-  constexpr int64_t slot_bytes = (int64_t)HKV * ROWB;
+  const int64_t slot_bytes = (int64_t)hkv_total * ROWB;
   const int64_t head_off = (int64_t)g * ROWB + li * Chunk::kBytes;
   constexpr int kStep = STREAMS * kUnroll;
 
@@ -389,7 +395,7 @@ __global__ __launch_bounds__(256, (G >= 8 ? 2 : 3)) void decode_split_slot(const
 
   // merge the streams of each head into stream 0
   if (stream > 0) {
-    const int slot_r = (stream - 1) * HKV + g;
+    const int slot_r = (stream - 1) * HKV + gl;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
 #pragma unroll
@@ -406,7 +412,7 @@ __global__ __launch_bounds__(256, (G >= 8 ? 2 : 3)) void decode_split_slot(const
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       for (int st = 1; st < STREAMS; ++st) {
-        const int slot_r = (st - 1) * HKV + g;
+        const int slot_r = (st - 1) * HKV + gl;
         float a2[VEC];
 #pragma unroll
         for (int i = 0; i < VEC; ++i) a2[i] = sm_acc[slot_r][h][li * VEC + i];
@@ -476,12 +482,12 @@ __global__ __launch_bounds__(256) void decode_reduce(const float* __restrict__ w
 template <typename QT, int POOL, int D, int HKV>
 int launch_slot(int G, dim3 grid, hipStream_t st, const void* q, const void* kp, const void* vp, const float* ks,
                 const float* vs, const int32_t* r2t, int64_t stride, const int32_t* lens, int chunk, int max_splits,
-                float sc, float* ml, float* acc) {
+                float sc, float* ml, float* acc, int hkv_total) {
 #define PKV_SLOT_CASE(GG)                                                                                        \
   case GG:                                                                                                       \
     hipLaunchKernelGGL((decode_split_slot<QT, POOL, D, GG, HKV>), grid, dim3(256), 0, st, (const QT*)q,          \
                        (const uint8_t*)kp, (const uint8_t*)vp, ks, vs, r2t, stride, lens, chunk, max_splits, sc, \
-                       ml, acc);                                                                                 \
+                       ml, acc, hkv_total);                                                                      \
     return PKV_OK;
   switch (G) {
     PKV_SLOT_CASE(1)
@@ -503,13 +509,18 @@ int launch_split(int G, dim3 grid, hipStream_t st, const void* q, const void* kp
     hipLaunchKernelGGL((decode_split<QT, POOL, D, GG>), grid, dim3(256), 0, st, (const QT*)q, (const uint8_t*)kp, \
                        (const uint8_t*)vp, ks, vs, r2t, stride, lens, hkv, chunk, max_splits, sc, ml, acc);     \
     return PKV_OK;
+  // all heads of a slot row per workgroup for 2, 4 or 8 kv heads; groups of 8 heads for
+  // any multiple of 8 (multi-head attention)
   const dim3 slot_grid(grid.x / hkv);
   if (hkv == 8) return launch_slot<QT, POOL, D, 8>(G, slot_grid, st, q, kp, vp, ks, vs, r2t, stride, lens, chunk,
-                                                  max_splits, sc, ml, acc);
+                                                  max_splits, sc, ml, acc, hkv);
   if (hkv == 4) return launch_slot<QT, POOL, D, 4>(G, slot_grid, st, q, kp, vp, ks, vs, r2t, stride, lens, chunk,
-                                                  max_splits, sc, ml, acc);
+                                                  max_splits, sc, ml, acc, hkv);
   if (hkv == 2) return launch_slot<QT, POOL, D, 2>(G, slot_grid, st, q, kp, vp, ks, vs, r2t, stride, lens, chunk,
-                                                  max_splits, sc, ml, acc);
+                                                  max_splits, sc, ml, acc, hkv);
+  if (hkv % 8 == 0)
+    return launch_slot<QT, POOL, D, 8>(G, dim3(grid.x / 8), st, q, kp, vp, ks, vs, r2t, stride, lens, chunk,
+                                       max_splits, sc, ml, acc, hkv);
   switch (G) {
     PKV_DECODE_CASE(1)
     PKV_DECODE_CASE(2)
@@ -530,7 +541,7 @@ using namespace pkv;
 
 extern "C" int32_t pkv_decode_chunk(int32_t batch, int32_t hkv, int32_t max_seq_len) {
   // workgroups per (sequence, chunk): one for all kv heads when hkv is 2, 4 or 8, else one per head
-  const int64_t per_chunk = (hkv == 2 || hkv == 4 || hkv == 8) ? 1 : hkv;
+  const int64_t per_chunk = (hkv == 2 || hkv == 4 || hkv == 8) ? 1 : (hkv % 8 == 0 ? hkv / 8 : hkv);
   int chunk = 1024;
   while (chunk > 128 && (int64_t)batch * per_chunk * splits_for(max_seq_len, chunk) < 2048) chunk /= 2;
   return chunk;
