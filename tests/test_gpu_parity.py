@@ -163,6 +163,36 @@ def _edge_workload(qo):
                               np.zeros((0, 5), np.int32), np.zeros((0, 5), np.int64), vt)
 
 
+def _shape_workload(hq, hkv, pool):
+    """A shared 300-token prefix, five suffixes of 1-200 tokens and 3 decode steps for one head
+    layout: every group size and kv-head count the kernels dispatch on."""
+    shape = workloads.Shape(hq, hkv, 128, "bf16", pool, 1 / math.sqrt(128))
+    rng = np.random.default_rng(hq * 100 + hkv)
+    b = workloads._Builder(rng, 5000)
+    pre = b.segment(0, 300)
+    reqs = [workloads._concat([pre, b.segment(pre[0], n)]) for n in (1, 37, 64, 129, 200)]
+    vt = workloads.ValueTable(hq * 100 + hkv, b.next_row + 3 * len(reqs), shape)
+    free = rng.permutation(8192).astype(np.int32)
+    dt = rng.integers(0, 5000, size=(3, len(reqs)), dtype=np.int64).astype(np.int32)
+    dr = (b.next_row + np.arange(3 * len(reqs), dtype=np.int64)).reshape(3, len(reqs))
+    wl = workloads.Workload(f"shape{hq}x{hkv}", 0, shape, 8192, free,
+                            [workloads.Request(pre[1].copy(), pre[2].copy(), "prefix")], [reqs], True, dt, dr, vt)
+    if pool == "fp8_e4m3":
+        wl.k_scale, wl.v_scale = workloads.fp8_scales(vt)
+        wl.k_inv_scale = (np.float32(1.0) / wl.k_scale).astype(np.float32)
+        wl.v_inv_scale = (np.float32(1.0) / wl.v_scale).astype(np.float32)
+    return wl
+
+
+@pytest.mark.parametrize("hq,hkv,pool", [(32, 16, "bf16"), (16, 16, "bf16"), (16, 8, "bf16"), (32, 32, "fp8_e4m3"),
+                                         (16, 2, "bf16"), (32, 4, "fp8_e4m3"), (8, 1, "bf16")])
+def test_head_layouts_every_row(hq, hkv, pool):
+    log(f"head layout {hq}/{hkv} {pool}")
+    stats = Run(_shape_workload(hq, hkv, pool), check_pool=True).run()
+    report(f"head layout {hq}/{hkv} {pool}", stats)
+    assert {s["kind"] for s in stats} == {"extend", "decode"}
+
+
 @pytest.mark.parametrize("qo", ["bf16", "f32"])
 def test_edge_cases(qo):
     log(f"edge {qo}")
