@@ -10,22 +10,24 @@
 // context first.  blockIdx.x = item * hkv + g, so consecutive workgroups cycle through the
 // kv heads and each kv head's K/V stays in one XCD's L2 when hkv = 8.
 //
-// Two kernels:
-//  - extend_mfma (bf16 q/o, bf16 or fp8 pool, d = 128): one workgroup = 4 waves = 128 query
-//    rows = (128/G tokens) x (G heads of one GQA group), so every K/V tile staged in LDS is
-//    shared by the whole group.  Per 64-token K/V tile and wave (32 query rows):
+// Three kernels:
+//  - extend_dma (bf16 q/o, bf16 pool, d = 128) and extend_mfma (bf16 q/o, fp8 E4M3 pool,
+//    d = 128) share the per-tile arithmetic (WaveAttn below): one workgroup = 4 waves = 128
+//    query rows = (128/G tokens) x (G heads of one GQA group), so every K/V tile staged in LDS
+//    is shared by the whole group.  Per 64-token K/V tile and wave (32 query rows):
 //      S^T = K . Q^T  (A = K rows from LDS, B = Q^T held in registers), 32 MFMA 16x16x32;
 //      online softmax in the log2 domain with a lazily moved reference max;
 //      O^T += V^T . P^T (A = V^T from LDS, B = P^T straight from the S^T registers), 32 MFMA,
 //      and the row sums with 4 more MFMA against a row of ones.
 //    The S^T row order inside each 16-row MFMA block is permuted so that each lane's four
 //    S^T values of two neighbouring blocks are 8 consecutive kv tokens, which is exactly the
-//    B-operand slice of P^T for the PV product; V is stored transposed in LDS so the A
-//    operand is one 16-byte read.  Tiles are double-buffered in LDS (one barrier per tile)
-//    and gathered with buffer loads (no address arithmetic on the vector ALU, which is the
-//    unit that bounds this loop next to the matrix cores).  fp8 pools are decoded to bf16
-//    (exact) while staging; the per-head scales are folded into the float32 logits and
-//    output.
+//    B-operand slice of P^T for the PV product.  Tiles are double-buffered in LDS (one barrier
+//    per tile).  extend_dma stages them with buffer-to-LDS loads (no registers, no vector ALU
+//    work) in a token-row layout and reads V^T with the transposing LDS read of gfx950;
+//    extend_mfma gathers fp8 codes into registers, decodes them to bf16 (exact) and stores
+//    K row-major and V transposed; the per-head scales are folded into the float32 logits and
+//    output.  The slot table is read with buffer loads one tile ahead of the K/V records it
+//    addresses, so a gathered row costs no address arithmetic and no dependent-load stall.
 //  - extend_f32 (f32 q/o, f32 pool, d 64 or 128): one wave per (tile, q head), VALU only;
 //    it serves the small fp32 case.
 
@@ -137,25 +139,17 @@ __global__ __launch_bounds__(64) void extend_f32(const float* __restrict__ q, fl
 }
 
 // ------------------------------------------------------------------------------------------
-// bf16 MFMA path (d = 128)
+// bf16 MFMA paths (d = 128)
 // ------------------------------------------------------------------------------------------
 
 constexpr int kD = 128;
 constexpr int kBN = 64;                 // kv tokens per tile
 constexpr int kRows = 128;              // query rows per workgroup (tokens x heads)
-constexpr int kKStride = kD + 8;        // bf16 elements per K row in LDS (272 B)
-constexpr int kVStride = kBN + 8;       // bf16 elements per V^T row in LDS (144 B)
 
 // kv token (tile-local) held in row rho of 16-row MFMA block mb of S^T.
 __device__ __forceinline__ int sigma(int mb, int rho) {
   return 32 * (mb >> 1) + 8 * (rho >> 2) + 4 * (mb & 1) + (rho & 3);
 }
-
-// LDS row of kv token t in the K tile.  With a 272 B row stride a row starts at bank 4*row
-// (mod 64), and one MFMA block reads tokens {0-3, 8-11, 16-19, 24-27} (+4, +32): flipping
-// bit 2 of the row for the upper half of each 32-token group makes those 16 rows start on
-// 16 different banks, so the 16-byte A-operand reads are conflict free.
-__device__ __forceinline__ int krow(int t) { return t ^ (((t >> 4) & 1) << 2); }
 
 // Buffer loads.  The K/V pools are read as structured buffers (record = one slot of
 // hkv*d values, record index = slot), and the slot table as a raw buffer, so a gathered
@@ -165,55 +159,374 @@ __device__ u32x4 buf_load_rec_x4(__amdgpu_buffer_rsrc_t rsrc, int rec, int voffs
                                  int aux) __asm("llvm.amdgcn.struct.ptr.buffer.load.v4i32");
 __device__ u32x2 buf_load_rec_x2(__amdgpu_buffer_rsrc_t rsrc, int rec, int voffset, int soffset,
                                  int aux) __asm("llvm.amdgcn.struct.ptr.buffer.load.v2i32");
-__device__ int buf_load_i32(__amdgpu_buffer_rsrc_t rsrc, int voffset, int soffset,
-                            int aux) __asm("llvm.amdgcn.raw.ptr.buffer.load.i32");
+__device__ u32x4 buf_load_raw_x4(__amdgpu_buffer_rsrc_t rsrc, int voffset, int soffset,
+                                 int aux) __asm("llvm.amdgcn.raw.ptr.buffer.load.v4i32");
+__device__ u32x2 buf_load_raw_x2(__amdgpu_buffer_rsrc_t rsrc, int voffset, int soffset,
+                                 int aux) __asm("llvm.amdgcn.raw.ptr.buffer.load.v2i32");
 constexpr int kBufWord3 = 0x00020000;   // 32-bit data format, no swizzle
 
-struct Gather {
-  __amdgpu_buffer_rsrc_t kp, vp, tab;   // K pool, V pool (record = slot), slot table
-  int row_bytes;                         // byte offset of this request's table row
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t pool_rsrc(const void* p, int slot_bytes, int num_slots) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)slot_bytes, num_slots, kBufWord3);
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t table_rsrc(const void* p, int table_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, table_bytes, kBufWord3);
+}
+
+// Lazy rescaling: a row's reference max only moves when a tile's max exceeds it by more than
+// this many log2 units, so P = 2^(s - m) stays <= 2^8 (fine for bf16 and fp32 sums) and the
+// 64-register output rescale runs on the first tile and almost never after.
+constexpr float kRescaleSlack = 8.f;
+
+// One wave's 32 query rows (two 16-row MFMA blocks nb) and their online-softmax state.
+template <int G>
+struct WaveAttn {
+  static constexpr int BT = kRows / G;   // query tokens per work item
+  int ln, lg;
+  int qt[2], qh[2];      // this lane's query token (in the item) and head, per row block
+  int vis[2];            // last visible kv position of this lane's rows
+  bf16x8 qf[2][4];       // Q^T as B operand: d = 32 ks + 8 lg .. +7 of the lane's query row
+  floatx4 oacc[2][8];    // O^T, d block db
+  floatx4 lsum[2];       // (ones row) . P^T: element 0 of lanes 0..15 holds the row sum
+  float m[2];            // reference max (log2 units)
+  float sc;              // softmax scale in log2 units (times the K scale for fp8 pools)
+  int qpos0;             // position of the item's first query token
+  bf16x8 ones_row;
+
+  __device__ __forceinline__ void init(const bf16* q, int64_t qrow0, int hq, int g, int wave, int lane, int nq,
+                                       int p, int j0, int ctx, float scale) {
+    ln = lane & 15;
+    lg = lane >> 4;
+    sc = scale;
+    qpos0 = p + j0;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int r0 = 32 * wave + 16 * nb;
+      qh[nb] = g * G + r0 / BT;
+      qt[nb] = r0 % BT + ln;
+      vis[nb] = min(qpos0 + qt[nb], ctx - 1);   // padded rows see the whole context
+      const bool ok = qt[nb] < nq;
+      const bf16* qp = q + ((qrow0 + (ok ? qt[nb] : 0)) * hq + qh[nb]) * kD + 8 * lg;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const u32x4 v = ok ? *(const u32x4*)(qp + 32 * ks) : u32x4{0u, 0u, 0u, 0u};
+        qf[nb][ks] = __builtin_bit_cast(bf16x8, v);
+      }
+      lsum[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int db = 0; db < 8; ++db) oacc[nb][db] = floatx4{0.f, 0.f, 0.f, 0.f};
+      m[nb] = -INFINITY;
+    }
+    const bf16 one = (bf16)(ln == 0 ? 1.f : 0.f);
+    ones_row = bf16x8{one, one, one, one, one, one, one, one};
+  }
+
+  // One 64-token tile at kv position kv0.  kop(mb, ks) returns the K operand (tokens of S^T
+  // block mb, d = 32 ks + 8 lg .. +7), vop(kk, db) the V^T operand (d = 16 db + ln, tokens
+  // 32 kk + 8 lg .. +7), both read from LDS.
+  template <class KOp, class VOp>
+  __device__ __forceinline__ void tile(int kv0, KOp kop, VOp vop) {
+    // S^T = K . Q^T
+    floatx4 s[4][2];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) s[mb][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const bf16x8 a = kop(mb, ks);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) s[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[nb][ks], s[mb][nb], 0, 0, 0);
+      }
+    }
+
+    // causal / context mask, only on tiles reaching past the first query position
+    if (kv0 + kBN > qpos0 + 1) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const int lim = vis[nb] - kv0 - 8 * lg;   // visible iff token offset - 8 lg <= lim
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int off = 32 * (mb >> 1) + 4 * (mb & 1) + i;
+            s[mb][nb][i] = off <= lim ? s[mb][nb][i] : -INFINITY;
+          }
+      }
+    }
+
+    // online softmax (log2 domain) with lazy rescaling.  Each lane's max over its 16 logits
+    // of a row; the row max across the 4 lanes that share the query row is only formed when
+    // some lane may move the reference max (one wave-uniform test for both row blocks).
+    float mt[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      // a linear chain, so each step is one three-input max
+      float x = fmaxf(fmaxf(s[0][nb][0], s[0][nb][1]), s[0][nb][2]);
+      x = fmaxf(fmaxf(x, s[0][nb][3]), s[1][nb][0]);
+      x = fmaxf(fmaxf(x, s[1][nb][1]), s[1][nb][2]);
+      x = fmaxf(fmaxf(x, s[1][nb][3]), s[2][nb][0]);
+      x = fmaxf(fmaxf(x, s[2][nb][1]), s[2][nb][2]);
+      x = fmaxf(fmaxf(x, s[2][nb][3]), s[3][nb][0]);
+      x = fmaxf(fmaxf(x, s[3][nb][1]), s[3][nb][2]);
+      x = fmaxf(x, s[3][nb][3]);
+      mt[nb] = x * sc;
+    }
+    if (__any(mt[0] > m[0] + kRescaleSlack || mt[1] > m[1] + kRescaleSlack)) {   // rare after the first tile
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        float x = fmaxf(mt[nb], __shfl_xor(mt[nb], 16));
+        x = fmaxf(x, __shfl_xor(x, 32));
+        const float mn = x > m[nb] + kRescaleSlack ? x : m[nb];
+        const float alpha = __builtin_amdgcn_exp2f(m[nb] - mn);   // 1 for rows that keep their max
+        lsum[nb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) oacc[nb][db] *= alpha;
+        m[nb] = mn;
+      }
+    }
+    bf16x8 pf[2][2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const float nm = -m[nb];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        bf16x8 pv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pv[i] = (bf16)__builtin_amdgcn_exp2f(fmaf(s[2 * kk][nb][i], sc, nm));
+          pv[4 + i] = (bf16)__builtin_amdgcn_exp2f(fmaf(s[2 * kk + 1][nb][i], sc, nm));
+        }
+        pf[nb][kk] = pv;
+      }
+    }
+
+    // O^T += V^T . P^T, and the row sums
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+        lsum[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_row, pf[nb][kk], lsum[nb], 0, 0, 0);
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const bf16x8 a = vop(kk, db);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+          oacc[nb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[nb][kk], oacc[nb][db], 0, 0, 0);
+      }
+    }
+  }
+
+  // O = O^T / row sum (times the V scale for fp8 pools), bf16, for the item's real rows
+  __device__ __forceinline__ void store(bf16* o, int64_t qrow0, int hq, int nq, float omul) const {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const float lt = __shfl(lsum[nb][0], ln);   // row sum sits in lane ln (row 0 of the block)
+      if (qt[nb] >= nq) continue;
+      const float inv = omul / lt;
+      bf16* op = o + ((qrow0 + qt[nb]) * hq + qh[nb]) * kD + 4 * lg;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const uint32_t w0 = f32_to_bf16_bits(oacc[nb][db][0] * inv) | (f32_to_bf16_bits(oacc[nb][db][1] * inv) << 16);
+        const uint32_t w1 = f32_to_bf16_bits(oacc[nb][db][2] * inv) | (f32_to_bf16_bits(oacc[nb][db][3] * inv) << 16);
+        *(u32x2*)(op + 16 * db) = u32x2{w0, w1};
+      }
+    }
+  }
 };
 
-// Staging of one 64-token K/V tile: global -> registers (prefetch) -> LDS.  Native vector
-// types keep the prefetch registers in VGPRs.  Tokens at or past the context read whatever
-// slot the table holds there (or zero past the table's end); they are masked later.
-template <int POOL>
-struct TileStage;
+// ------------------------------------------------------------------------------------------
+// bf16 pools: tiles staged by buffer-to-LDS loads
+// ------------------------------------------------------------------------------------------
+//
+// LDS layout of a 64-token K (or V) tile: 16 blocks of 4 token rows (256 B each), block
+// stride 1040 B, so block j starts 4 banks after block j - 1.  Token t (bits t0..t5) sits in
+// block 2 t0 + 4 t1 + t4 + 8 t3, row t2 + 2 t5.  A buffer-to-LDS load writes 16 bytes per lane
+// at consecutive addresses, so one load fills one block, 16 lanes per token row, which keeps
+// the global reads of a row contiguous.  The 16 tokens of one S^T operand read differ in bits
+// t0, t1, t3, t4 and so lie in 16 different blocks (16 different bank groups), and the 4
+// tokens x 2 chunks of a 16-lane transposing V^T read cover 8 different bank groups.  All
+// operand reads are at immediate offsets from a few per-lane bases.
+constexpr int kBlk = 1040;
+constexpr int kTileBytes = 16 * kBlk;
+__device__ __forceinline__ int kv_off(int t) {
+  const int blk = 2 * (t & 1) + 4 * ((t >> 1) & 1) + ((t >> 4) & 1) + 8 * ((t >> 3) & 1);
+  const int row = ((t >> 2) & 1) + 2 * ((t >> 5) & 1);
+  return blk * kBlk + row * 256;
+}
+// token in row r of block j (the inverse of the placement above)
+__device__ __forceinline__ int kv_tok(int j, int r) {
+  return ((j >> 1) & 1) + 2 * ((j >> 2) & 1) + 4 * (r & 1) + 8 * ((j >> 3) & 1) + 16 * (j & 1) + 32 * (r >> 1);
+}
 
-template <>
-struct TileStage<PKV_BF16> {
-  // K: 64 rows x 256 B = 1024 chunks of 16 B, 4 per thread (rows tid/16 + 16 i, chunk tid%16).
-  // V: thread -> 4 consecutive tokens (4*(tid%16) .. +3) x 8 d (8*(tid/16) .. +7).
-  u32x4 k0, k1, k2, k3, v0, v1, v2, v3;
-  __device__ __forceinline__ void load(const Gather& gt, int kv0, int g, int tid) {
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Eight bf16 of one column of a row-major tile: two transposing reads.  In each 16-lane
+// group, ds_read_b64_tr_b16 hands lane i element i of the 4 rows addressed by lanes
+// 4j + i/4 (j = 0..3), i.e. lane k supplies the address of row k/4, columns 4(k%4) .. +3.
+__device__ __forceinline__ bf16x8 lds_read_tr2(const char* p0, const char* p1) {
+  const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p0);
+  const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p1);
+  const v4i16 ab[2] = {a, b};
+  return __builtin_bit_cast(bf16x8, ab);
+}
+
+template <int G>
+__global__ __launch_bounds__(256, 2) void extend_dma(const bf16* __restrict__ q, bf16* __restrict__ o,
+                                                     const uint8_t* __restrict__ kpool,
+                                                     const uint8_t* __restrict__ vpool,
+                                                     const int32_t* __restrict__ r2t, int64_t stride,
+                                                     const int32_t* __restrict__ prefix_lens,
+                                                     const int32_t* __restrict__ extend_lens,
+                                                     const int32_t* __restrict__ qo_indptr,
+                                                     const int32_t* __restrict__ work, int hkv,
+                                                     float scale_log2, int num_slots, int table_bytes) {
+  // two buffers of K and V tiles, as separate arrays so that the loads into one buffer and the
+  // reads of the other are known not to overlap (no wait for the loads before those reads)
+  __shared__ __attribute__((aligned(16))) char k0s[kTileBytes], v0s[kTileBytes], k1s[kTileBytes], v1s[kTileBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ln = lane & 15, lg = lane >> 4;
+  const int g = blockIdx.x % hkv;
+  const int w = blockIdx.x / hkv;
+  const int req = work[2 * w], j0 = work[2 * w + 1];
+  const int p = prefix_lens[req], e = extend_lens[req];
+  const int nq = min(WaveAttn<G>::BT, e - j0);
+  const int ctx = p + j0 + nq;
+  const int hq = hkv * G;
+  const int64_t qrow0 = (int64_t)qo_indptr[req] + j0;
+  const __amdgpu_buffer_rsrc_t kp = pool_rsrc(kpool, hkv * 2 * kD, num_slots);
+  const __amdgpu_buffer_rsrc_t vp = pool_rsrc(vpool, hkv * 2 * kD, num_slots);
+  const __amdgpu_buffer_rsrc_t tab = table_rsrc(r2t, table_bytes);
+  const int row_bytes = (int)((int64_t)req * stride * 4);
+
+  // staging: wave w fills blocks 4w + i (i = 0..3) of the K and V tiles; lane l writes row
+  // l / 16 (token kv_tok(4w + i, l / 16)), byte column 16 (l % 16) of kv head g.  Those tokens
+  // are t, t + 16, t + 1, t + 17 for i = 0..3: two 8-byte table reads.
+  const int tok0 = kv_tok(4 * wave, lg);
+  const int col = g * kD * 2 + 16 * ln;
+  auto slots = [&](int kv0, u32x2* sl) {
     // the whole byte offset goes in the vector offset, which the buffer's range check covers
-    const int tb = gt.row_bytes + 4 * kv0;
-    const int kto = tb + 4 * (tid >> 4), vto = tb + 16 * (tid & 15);
-    const int ks0 = buf_load_i32(gt.tab, kto, 0, 0), ks1 = buf_load_i32(gt.tab, kto + 64, 0, 0);
-    const int ks2 = buf_load_i32(gt.tab, kto + 128, 0, 0), ks3 = buf_load_i32(gt.tab, kto + 192, 0, 0);
-    const int vs0 = buf_load_i32(gt.tab, vto, 0, 0), vs1 = buf_load_i32(gt.tab, vto + 4, 0, 0);
-    const int vs2 = buf_load_i32(gt.tab, vto + 8, 0, 0), vs3 = buf_load_i32(gt.tab, vto + 12, 0, 0);
-    const int kc = g * kD * 2 + (tid & 15) * 16, vc = g * kD * 2 + (tid >> 4) * 16;
-    k0 = buf_load_rec_x4(gt.kp, ks0, kc, 0, 0);
-    k1 = buf_load_rec_x4(gt.kp, ks1, kc, 0, 0);
-    k2 = buf_load_rec_x4(gt.kp, ks2, kc, 0, 0);
-    k3 = buf_load_rec_x4(gt.kp, ks3, kc, 0, 0);
-    v0 = buf_load_rec_x4(gt.vp, vs0, vc, 0, 0);
-    v1 = buf_load_rec_x4(gt.vp, vs1, vc, 0, 0);
-    v2 = buf_load_rec_x4(gt.vp, vs2, vc, 0, 0);
-    v3 = buf_load_rec_x4(gt.vp, vs3, vc, 0, 0);
+    sl[0] = buf_load_raw_x2(tab, row_bytes + 4 * (kv0 + tok0), 0, 0);
+    sl[1] = buf_load_raw_x2(tab, row_bytes + 4 * (kv0 + tok0 + 16), 0, 0);
+  };
+  auto stage = [&](char* kd, char* vd, const u32x2* sl) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = 4 * wave + i;
+      const int slot = (int)sl[i & 1][i >> 1];
+      __builtin_amdgcn_struct_ptr_buffer_load_lds(kp, (lds_void*)(kd + kBlk * j), 16, slot, col, 0, 0, 0);
+      __builtin_amdgcn_struct_ptr_buffer_load_lds(vp, (lds_void*)(vd + kBlk * j), 16, slot, col, 0, 0, 0);
+    }
+  };
+
+  WaveAttn<G> wa;
+  wa.init(q, qrow0, hq, g, wave, lane, nq, p, j0, ctx, scale_log2);
+  // only for G = 1 (a wave's rows are 32 consecutive tokens): is any of them a real query?
+  const bool active = G != 1 || 32 * wave < nq;
+  // operand read bases (bytes within a tile): K row sigma(mb, ln) at chunk lg (+ 4 ks);
+  // V rows 32 kk + 8 lg + 4 h + ln / 4 at d = 4 (ln % 4) (+ 16 db)
+  int kb[4], vb[2][2];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) kb[mb] = kv_off(sigma(mb, ln)) + 16 * lg;
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) vb[kk][h] = kv_off(32 * kk + 8 * lg + 4 * h + (ln >> 2)) + 8 * (ln & 3);
+
+  const int n_tiles = (ctx + kBN - 1) / kBN;
+  const int last = n_tiles - 1;
+  u32x2 sl[2];
+  slots(0, sl);
+  stage(k0s, v0s, sl);
+  slots(min(1, last) * kBN, sl);
+  // this wave's buffer-to-LDS loads are complete (vmcnt(0): the table loads issued after them
+  // are waited for too); then the barrier publishes the tile to the other waves
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+  // iteration kt computes tile kt from (K, V) and loads tile kt + 1 into (Kn, Vn), whose
+  // readers (tile kt - 1) all passed the previous barrier
+  auto step = [&](int kt, const char* K, const char* V, char* Kn, char* Vn) {
+    // past the last tile the last one is loaded again into a buffer nobody reads
+    stage(Kn, Vn, sl);
+    slots(min(kt + 2, last) * kBN, sl);
+    if (active)   // wave-uniform; with one head per item a wave of only padding tokens just stages
+      wa.tile(
+          kt * kBN, [&](int mb, int ks) { return *(const bf16x8*)(K + kb[mb] + 64 * ks); },
+          [&](int kk, int db) { return lds_read_tr2(V + vb[kk][0] + 32 * db, V + vb[kk][1] + 32 * db); });
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // this wave's loads of tile kt + 1 are in LDS
+    __syncthreads();
+  };
+  int kt = 0;
+  for (; kt + 1 < n_tiles; kt += 2) {
+    step(kt, k0s, v0s, k1s, v1s);
+    step(kt + 1, k1s, v1s, k0s, v0s);
   }
-  __device__ __forceinline__ void store(bf16* Ks, bf16* Vt, int tid) const {
-    const int r = tid >> 4;   // tokens r, r+16, r+32, r+48
-    bf16* kd = Ks + (tid & 15) * 8;
-    *(u32x4*)(kd + krow(r) * kKStride) = k0;
-    *(u32x4*)(kd + krow(r + 16) * kKStride) = k1;
-    *(u32x4*)(kd + krow(r + 32) * kKStride) = k2;
-    *(u32x4*)(kd + krow(r + 48) * kKStride) = k3;
-    store_vt(Vt, tid, v0, v1, v2, v3);
+  if (kt < n_tiles) step(kt, k0s, v0s, k1s, v1s);
+
+  wa.store(o, qrow0, hq, nq, 1.f);
+}
+
+// ------------------------------------------------------------------------------------------
+// fp8 E4M3 pools: tiles gathered into registers, decoded to bf16, stored to LDS
+// ------------------------------------------------------------------------------------------
+
+constexpr int kKStride = kD + 8;        // bf16 elements per K row in LDS (272 B)
+constexpr int kVStride = kBN + 8;       // bf16 elements per V^T row in LDS (144 B)
+
+// LDS row of kv token t in the K tile.  With a 272 B row stride a row starts at bank 4*row
+// (mod 64), and one MFMA block reads tokens {0-3, 8-11, 16-19, 24-27} (+4, +32): flipping
+// bit 2 of the row for the upper half of each 32-token group makes those 16 rows start on
+// 16 different banks.
+__device__ __forceinline__ int krow(int t) { return t ^ (((t >> 4) & 1) << 2); }
+
+// two E4M3 codes (low 16 bits) -> two bf16 (exact: every E4M3 value is a bf16 value)
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t codes2) {
+  const float2 f = e4m3x2_to_f32<false>(codes2);
+  return __builtin_amdgcn_perm(__float_as_uint(f.y), __float_as_uint(f.x), 0x07060302u);
+}
+__device__ __forceinline__ u32x4 dec4(u32x2 c) {
+  return u32x4{e4m3x2_to_bf16x2(c[0]), e4m3x2_to_bf16x2(c[0] >> 16), e4m3x2_to_bf16x2(c[1]),
+               e4m3x2_to_bf16x2(c[1] >> 16)};
+}
+
+// Staging of one 64-token tile of codes: global -> registers (prefetch) -> LDS.
+//   K: 64 rows x 128 B = 512 chunks of 16 B, 2 per thread (rows 2*(tid/8), +1, chunk tid%8).
+//   V: thread -> 4 consecutive tokens (4*(tid%16) .. +3) x 8 d (8*(tid/16) .. +7).
+// The table entries of a thread's 2 K tokens and 4 V tokens are one 8- and one 16-byte read.
+// Tokens at or past the context read whatever slot the table holds there (or zero past the
+// table's end); they are masked later.
+struct Fp8Stage {
+  struct Slots {
+    u32x2 k;
+    u32x4 v;
+  };
+  u32x4 k0, k1;
+  u32x2 v0, v1, v2, v3;
+  static __device__ __forceinline__ Slots slots(__amdgpu_buffer_rsrc_t tab, int row_bytes, int kv0, int tid) {
+    const int tb = row_bytes + 4 * kv0;
+    return Slots{buf_load_raw_x2(tab, tb + 8 * (tid >> 3), 0, 0), buf_load_raw_x4(tab, tb + 16 * (tid & 15), 0, 0)};
   }
-  // Writes 4 tokens x 8 d (token-major in registers) to V^T [d][token]; one byte permute
-  // builds each pair of 16-bit values.
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t kp, __amdgpu_buffer_rsrc_t vp, const Slots& sl, int g,
+                                       int tid) {
+    const int kc = g * kD + (tid & 7) * 16, vc = g * kD + (tid >> 4) * 8;
+    k0 = buf_load_rec_x4(kp, (int)sl.k[0], kc, 0, 0);
+    k1 = buf_load_rec_x4(kp, (int)sl.k[1], kc, 0, 0);
+    v0 = buf_load_rec_x2(vp, (int)sl.v[0], vc, 0, 0);
+    v1 = buf_load_rec_x2(vp, (int)sl.v[1], vc, 0, 0);
+    v2 = buf_load_rec_x2(vp, (int)sl.v[2], vc, 0, 0);
+    v3 = buf_load_rec_x2(vp, (int)sl.v[3], vc, 0, 0);
+  }
+  static __device__ __forceinline__ void store_k(bf16* dst, u32x4 c) {
+    *(u32x4*)dst = dec4(u32x2{c[0], c[1]});
+    *(u32x4*)(dst + 8) = dec4(u32x2{c[2], c[3]});
+  }
+  // 4 tokens x 8 d (token-major in registers) to V^T [d][token]; one byte permute builds each
+  // pair of 16-bit values
   static __device__ __forceinline__ void store_vt(bf16* Vt, int tid, u32x4 a, u32x4 b, u32x4 c, u32x4 d) {
     const int d0 = 8 * (tid >> 4), t0 = 4 * (tid & 15);
     bf16* base = Vt + d0 * kVStride + t0;
@@ -226,57 +539,16 @@ struct TileStage<PKV_BF16> {
       *(u32x2*)(base + (2 * i + 1) * kVStride) = hi;
     }
   }
-};
-
-// two E4M3 codes (low 16 bits) -> two bf16 (exact: every E4M3 value is a bf16 value)
-__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t codes2) {
-  const float2 f = e4m3x2_to_f32<false>(codes2);
-  return __builtin_amdgcn_perm(__float_as_uint(f.y), __float_as_uint(f.x), 0x07060302u);
-}
-
-template <>
-struct TileStage<PKV_FP8_E4M3> {
-  // K: 64 rows x 128 B = 512 chunks of 16 B, 2 per thread (rows tid/8 + 32 i, chunk tid%8).
-  // V: thread -> 4 tokens x 8 d, 8 B of codes each.
-  u32x4 k0, k1;
-  u32x2 v0, v1, v2, v3;
-  __device__ __forceinline__ void load(const Gather& gt, int kv0, int g, int tid) {
-    const int tb = gt.row_bytes + 4 * kv0;
-    const int kto = tb + 4 * (tid >> 3), vto = tb + 16 * (tid & 15);
-    const int ks0 = buf_load_i32(gt.tab, kto, 0, 0), ks1 = buf_load_i32(gt.tab, kto + 128, 0, 0);
-    const int vs0 = buf_load_i32(gt.tab, vto, 0, 0), vs1 = buf_load_i32(gt.tab, vto + 4, 0, 0);
-    const int vs2 = buf_load_i32(gt.tab, vto + 8, 0, 0), vs3 = buf_load_i32(gt.tab, vto + 12, 0, 0);
-    const int kc = g * kD + (tid & 7) * 16, vc = g * kD + (tid >> 4) * 8;
-    k0 = buf_load_rec_x4(gt.kp, ks0, kc, 0, 0);
-    k1 = buf_load_rec_x4(gt.kp, ks1, kc, 0, 0);
-    v0 = buf_load_rec_x2(gt.vp, vs0, vc, 0, 0);
-    v1 = buf_load_rec_x2(gt.vp, vs1, vc, 0, 0);
-    v2 = buf_load_rec_x2(gt.vp, vs2, vc, 0, 0);
-    v3 = buf_load_rec_x2(gt.vp, vs3, vc, 0, 0);
-  }
-  static __device__ __forceinline__ u32x4 dec4(u32x2 c) {
-    return u32x4{e4m3x2_to_bf16x2(c[0]), e4m3x2_to_bf16x2(c[0] >> 16), e4m3x2_to_bf16x2(c[1]),
-                 e4m3x2_to_bf16x2(c[1] >> 16)};
-  }
-  static __device__ __forceinline__ void store_k(bf16* dst, u32x4 c) {
-    *(u32x4*)dst = dec4(u32x2{c[0], c[1]});
-    *(u32x4*)(dst + 8) = dec4(u32x2{c[2], c[3]});
-  }
   __device__ __forceinline__ void store(bf16* Ks, bf16* Vt, int tid) const {
-    const int r = tid >> 3;   // tokens r, r+32
+    const int r = 2 * (tid >> 3);   // tokens r, r+1
     bf16* kd = Ks + (tid & 7) * 16;
     store_k(kd + krow(r) * kKStride, k0);
-    store_k(kd + krow(r + 32) * kKStride, k1);
-    TileStage<PKV_BF16>::store_vt(Vt, tid, dec4(v0), dec4(v1), dec4(v2), dec4(v3));
+    store_k(kd + krow(r + 1) * kKStride, k1);
+    store_vt(Vt, tid, dec4(v0), dec4(v1), dec4(v2), dec4(v3));
   }
 };
 
-// Lazy rescaling: a row's reference max only moves when a tile's max exceeds it by more than
-// this many log2 units, so P = 2^(s - m) stays <= 2^8 (fine for bf16 and fp32 sums) and the
-// 64-register output rescale runs on the first tile and almost never after.
-constexpr float kRescaleSlack = 8.f;
-
-template <int POOL, int G>
+template <int G>
 __global__ __launch_bounds__(256, 2) void extend_mfma(const bf16* __restrict__ q, bf16* __restrict__ o,
                                                       const uint8_t* __restrict__ kpool,
                                                       const uint8_t* __restrict__ vpool,
@@ -288,8 +560,6 @@ __global__ __launch_bounds__(256, 2) void extend_mfma(const bf16* __restrict__ q
                                                       const int32_t* __restrict__ qo_indptr,
                                                       const int32_t* __restrict__ work, int hkv,
                                                       float scale_log2, int num_slots, int table_bytes) {
-  constexpr int BT = kRows / G;   // query tokens per work item
-  // K (row-major) and V^T tiles; the next tile is prefetched into registers during compute
   // two K (row-major) / V^T tile buffers: tile t is computed from buffer t & 1 while tile
   // t + 1 is written to the other one, so one barrier per tile suffices
   __shared__ __attribute__((aligned(16))) bf16 Ks[2][kBN * kKStride];
@@ -302,191 +572,45 @@ __global__ __launch_bounds__(256, 2) void extend_mfma(const bf16* __restrict__ q
   const int w = blockIdx.x / hkv;
   const int req = work[2 * w], j0 = work[2 * w + 1];
   const int p = prefix_lens[req], e = extend_lens[req];
-  const int nq = min(BT, e - j0);
+  const int nq = min(WaveAttn<G>::BT, e - j0);
   const int ctx = p + j0 + nq;
   const int hq = hkv * G;
   const int64_t qrow0 = (int64_t)qo_indptr[req] + j0;
-  constexpr int kSlotBytes = POOL == PKV_FP8_E4M3 ? kD : 2 * kD;
-  Gather gt;
-  gt.kp = __builtin_amdgcn_make_buffer_rsrc((void*)kpool, (short)(hkv * kSlotBytes), num_slots, kBufWord3);
-  gt.vp = __builtin_amdgcn_make_buffer_rsrc((void*)vpool, (short)(hkv * kSlotBytes), num_slots, kBufWord3);
-  gt.tab = __builtin_amdgcn_make_buffer_rsrc((void*)r2t, (short)0, table_bytes, kBufWord3);
-  gt.row_bytes = (int)((int64_t)req * stride * 4);
+  const __amdgpu_buffer_rsrc_t kp = pool_rsrc(kpool, hkv * kD, num_slots);
+  const __amdgpu_buffer_rsrc_t vp = pool_rsrc(vpool, hkv * kD, num_slots);
+  const __amdgpu_buffer_rsrc_t tab = table_rsrc(r2t, table_bytes);
+  const int row_bytes = (int)((int64_t)req * stride * 4);
 
-  float sc = scale_log2;
-  if constexpr (POOL == PKV_FP8_E4M3) sc *= kscale[g];
-
-  // this lane's query row in each of the wave's two 16-row blocks
-  int qt[2], qh[2];
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int r0 = 32 * wave + 16 * nb;
-    qh[nb] = g * G + r0 / BT;
-    qt[nb] = r0 % BT + ln;
-  }
-  // Q^T as B operand: lane holds d = 32 ks + 8 lg .. +7 of its query row
-  bf16x8 qf[2][4];
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const bool ok = qt[nb] < nq;
-    const bf16* qp = q + ((qrow0 + (ok ? qt[nb] : 0)) * hq + qh[nb]) * kD + 8 * lg;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const u32x4 v = ok ? *(const u32x4*)(qp + 32 * ks) : u32x4{0u, 0u, 0u, 0u};
-      qf[nb][ks] = __builtin_bit_cast(bf16x8, v);
-    }
-  }
-
-  floatx4 oacc[2][8];
-  // lsum[nb] = (ones row) . P^T: element 0 of lanes 0..15 holds the softmax row sum of the
-  // bf16 P that the PV product uses (the other rows of this 16-row block are zero)
-  floatx4 lsum[2];
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    lsum[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int db = 0; db < 8; ++db) oacc[nb][db] = floatx4{0.f, 0.f, 0.f, 0.f};
-  }
-  float m[2] = {-INFINITY, -INFINITY};
-  const bf16 one = (bf16)(ln == 0 ? 1.f : 0.f);
-  const bf16x8 ones_row = {one, one, one, one, one, one, one, one};
-  const int qpos0 = p + j0;   // position of the tile's first query token
-  // only for G = 1 (a wave's rows are 32 consecutive tokens): is any of them a real query?
+  WaveAttn<G> wa;
+  wa.init(q, qrow0, hq, g, wave, lane, nq, p, j0, ctx, scale_log2 * kscale[g]);
   const bool active = G != 1 || 32 * wave < nq;
-  // last visible kv position of this lane's rows (padded rows see the whole context)
-  int vis[2];
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) vis[nb] = min(qpos0 + qt[nb], ctx - 1);
 
-  TileStage<POOL> stage;
+  Fp8Stage stage;
   const int n_tiles = (ctx + kBN - 1) / kBN;
-  stage.load(gt, 0, g, tid);
+  stage.load(kp, vp, Fp8Stage::slots(tab, row_bytes, 0, tid), g, tid);
   stage.store(Ks[0], Vt[0], tid);
-  stage.load(gt, min(1, n_tiles - 1) * kBN, g, tid);
+  stage.load(kp, vp, Fp8Stage::slots(tab, row_bytes, min(1, n_tiles - 1) * kBN, tid), g, tid);
+  // slot-table entries run one tile ahead of the K/V records they address
+  auto nslots = Fp8Stage::slots(tab, row_bytes, min(2, n_tiles - 1) * kBN, tid);
   __syncthreads();
   for (int kt = 0; kt < n_tiles; ++kt) {
-    const int kv0 = kt * kBN;
     const bf16* K = Ks[kt & 1];
     const bf16* V = Vt[kt & 1];
     // tile kt + 1 (in registers since the last iteration) goes to the other buffer, whose
     // readers (tile kt - 1) all passed the previous barrier; then prefetch tile kt + 2.
-    // Branch-free, so it interleaves with the S^T products below: past the last tile the
-    // last tile is fetched again (from L2) and stored to a buffer nobody reads any more.
+    // Branch-free, so it interleaves with the S^T products: past the last tile the last tile
+    // is fetched again (from L2) and stored to a buffer nobody reads any more.
     stage.store(Ks[(kt + 1) & 1], Vt[(kt + 1) & 1], tid);
-    stage.load(gt, min(kt + 2, n_tiles - 1) * kBN, g, tid);
-
-    if (active) {   // wave-uniform; with one head per item a wave of only padding tokens just stages
-      // S^T = K . Q^T
-      floatx4 s[4][2];
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) s[mb][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-          const bf16x8 a = *(const bf16x8*)(K + krow(sigma(mb, ln)) * kKStride + 32 * ks + 8 * lg);
-#pragma unroll
-          for (int nb = 0; nb < 2; ++nb) s[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[nb][ks], s[mb][nb], 0, 0, 0);
-        }
-      }
-
-      // causal / context mask, only on tiles reaching past the first query position
-      if (kv0 + kBN > qpos0 + 1) {
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          const int lim = vis[nb] - kv0 - 8 * lg;   // visible iff token offset - 8 lg <= lim
-#pragma unroll
-          for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int off = 32 * (mb >> 1) + 4 * (mb & 1) + i;
-              s[mb][nb][i] = off <= lim ? s[mb][nb][i] : -INFINITY;
-            }
-        }
-      }
-
-      // online softmax (log2 domain) with lazy rescaling.  Each lane's max over its 16 logits
-      // of a row; the row max across the 4 lanes that share the query row is only formed when
-      // some lane may move the reference max (one wave-uniform test for both row blocks).
-      float mt[2];
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        // a linear chain, so each step is one three-input max
-        float x = fmaxf(fmaxf(s[0][nb][0], s[0][nb][1]), s[0][nb][2]);
-        x = fmaxf(fmaxf(x, s[0][nb][3]), s[1][nb][0]);
-        x = fmaxf(fmaxf(x, s[1][nb][1]), s[1][nb][2]);
-        x = fmaxf(fmaxf(x, s[1][nb][3]), s[2][nb][0]);
-        x = fmaxf(fmaxf(x, s[2][nb][1]), s[2][nb][2]);
-        x = fmaxf(fmaxf(x, s[2][nb][3]), s[3][nb][0]);
-        x = fmaxf(fmaxf(x, s[3][nb][1]), s[3][nb][2]);
-        x = fmaxf(x, s[3][nb][3]);
-        mt[nb] = x * sc;
-      }
-      if (__any(mt[0] > m[0] + kRescaleSlack || mt[1] > m[1] + kRescaleSlack)) {   // rare after the first tile
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          float x = fmaxf(mt[nb], __shfl_xor(mt[nb], 16));
-          x = fmaxf(x, __shfl_xor(x, 32));
-          const float mn = x > m[nb] + kRescaleSlack ? x : m[nb];
-          const float alpha = __builtin_amdgcn_exp2f(m[nb] - mn);   // 1 for rows that keep their max
-          lsum[nb] *= alpha;
-#pragma unroll
-          for (int db = 0; db < 8; ++db) oacc[nb][db] *= alpha;
-          m[nb] = mn;
-        }
-      }
-      bf16x8 pf[2][2];
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const float nm = -m[nb];
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          bf16x8 pv;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            pv[i] = (bf16)__builtin_amdgcn_exp2f(fmaf(s[2 * kk][nb][i], sc, nm));
-            pv[4 + i] = (bf16)__builtin_amdgcn_exp2f(fmaf(s[2 * kk + 1][nb][i], sc, nm));
-          }
-          pf[nb][kk] = pv;
-        }
-      }
-
-      // O^T += V^T . P^T, and the row sums
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-          lsum[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_row, pf[nb][kk], lsum[nb], 0, 0, 0);
-#pragma unroll
-        for (int db = 0; db < 8; ++db) {
-          const bf16x8 a = *(const bf16x8*)(V + (16 * db + ln) * kVStride + 32 * kk + 8 * lg);
-#pragma unroll
-          for (int nb = 0; nb < 2; ++nb)
-            oacc[nb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[nb][kk], oacc[nb][db], 0, 0, 0);
-        }
-      }
-    }
-
+    stage.load(kp, vp, nslots, g, tid);
+    nslots = Fp8Stage::slots(tab, row_bytes, min(kt + 3, n_tiles - 1) * kBN, tid);
+    if (active)
+      wa.tile(
+          kt * kBN,
+          [&](int mb, int ks) { return *(const bf16x8*)(K + krow(sigma(mb, ln)) * kKStride + 32 * ks + 8 * lg); },
+          [&](int kk, int db) { return *(const bf16x8*)(V + (16 * db + ln) * kVStride + 32 * kk + 8 * lg); });
     __syncthreads();
   }
-
-  float omul = 1.f;
-  if constexpr (POOL == PKV_FP8_E4M3) omul = vscale[g];
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const float lt = __shfl(lsum[nb][0], ln);   // row sum sits in lane ln (row 0 of the block)
-    if (qt[nb] >= nq) continue;
-    const float inv = omul / lt;
-    bf16* op = o + ((qrow0 + qt[nb]) * hq + qh[nb]) * kD + 4 * lg;
-#pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      const uint32_t w0 = f32_to_bf16_bits(oacc[nb][db][0] * inv) | (f32_to_bf16_bits(oacc[nb][db][1] * inv) << 16);
-      const uint32_t w1 = f32_to_bf16_bits(oacc[nb][db][2] * inv) | (f32_to_bf16_bits(oacc[nb][db][3] * inv) << 16);
-      *(u32x2*)(op + 16 * db) = u32x2{w0, w1};
-    }
-  }
+  wa.store(o, qrow0, hq, nq, vscale[g]);
 }
 
 int mfma_tile(int G) { return kRows / G; }
@@ -586,15 +710,23 @@ extern "C" int pkv_extend_attention(const void* q, void* o, int32_t qo_dtype, co
   const dim3 grid((unsigned)(n_work * hkv));
 #define PKV_EXTEND_CASE(PP, GG)                                                                                  \
   if (pool_dtype == PP && G == GG) {                                                                             \
-    hipLaunchKernelGGL((extend_mfma<PP, GG>), grid, dim3(256), 0, st, (const bf16*)q, (bf16*)o,                  \
+    hipLaunchKernelGGL((extend_mfma<GG>), grid, dim3(256), 0, st, (const bf16*)q, (bf16*)o,                      \
                        (const uint8_t*)k_pool, (const uint8_t*)v_pool, k_scale, v_scale, req_to_token, stride,   \
                        prefix_lens, extend_lens, qo_indptr, work, hkv, sc, (int)num_slots, (int)table_bytes);     \
     return hip_check(hipGetLastError(), "extend_mfma launch");                                                   \
   }
-  PKV_EXTEND_CASE(PKV_BF16, 1)
-  PKV_EXTEND_CASE(PKV_BF16, 2)
-  PKV_EXTEND_CASE(PKV_BF16, 4)
-  PKV_EXTEND_CASE(PKV_BF16, 8)
+#define PKV_EXTEND_DMA(GG)                                                                                       \
+  if (pool_dtype == PKV_BF16 && G == GG) {                                                                       \
+    hipLaunchKernelGGL((extend_dma<GG>), grid, dim3(256), 0, st, (const bf16*)q, (bf16*)o, (const uint8_t*)k_pool, \
+                       (const uint8_t*)v_pool, req_to_token, stride, prefix_lens, extend_lens, qo_indptr, work, hkv, sc, \
+                       (int)num_slots, (int)table_bytes);                                                        \
+    return hip_check(hipGetLastError(), "extend_dma launch");                                                    \
+  }
+  PKV_EXTEND_DMA(1)
+  PKV_EXTEND_DMA(2)
+  PKV_EXTEND_DMA(4)
+  PKV_EXTEND_DMA(8)
+#undef PKV_EXTEND_DMA
   PKV_EXTEND_CASE(PKV_FP8_E4M3, 1)
   PKV_EXTEND_CASE(PKV_FP8_E4M3, 2)
   PKV_EXTEND_CASE(PKV_FP8_E4M3, 4)
