@@ -302,7 +302,10 @@ struct WaveAttn {
       }
     }
 
-    // O^T += V^T . P^T, and the row sums
+    // O^T += V^T . P^T, and the row sums.  The wave issues them at raised priority: on a SIMD
+    // shared with a wave in its softmax, the products go first and the other wave's vector
+    // work fills the cycles between them.
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
@@ -316,6 +319,7 @@ struct WaveAttn {
           oacc[nb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[nb][kk], oacc[nb][db], 0, 0, 0);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   }
 
   // O = O^T / row sum (times the V scale for fp8 pools), bf16, for the item's real rows
