@@ -261,7 +261,7 @@ class PathBench:
             self.last_tables = self.hb
             return self.hb.n
         th = time.perf_counter()
-        hb = eng.prepare(self.flat, self.stride)                         # host: match/lock/alloc/insert
+        hb = eng.prepare_staged(self.flat, self.stride)                  # host: match/lock/alloc/insert
         self.host_prepare_s += time.perf_counter() - th
         dt = eng.device_tables(hb, staged=True)                          # H2D tables + plan (async)
         with T.span("kv_scatter"):

@@ -162,6 +162,11 @@ int rt_eviction_log_size(const rt_tree* t, int64_t* n_nodes, int64_t* n_slots);
 int rt_take_eviction_log(rt_tree* t, int64_t* node_ids, int64_t* node_lens, int64_t nodes_cap,
                          int32_t* slots, int64_t slots_cap);
 
+/* Turn the eviction log on (enabled != 0, the default for a new tree) or off.  A loop that
+ * never takes the log should turn it off, or the log grows with every eviction.  Turning it
+ * off also drops what it holds. */
+int rt_set_eviction_log(rt_tree* t, int32_t enabled);
+
 int64_t rt_evictable_size(const rt_tree* t);   /* tokens in unlocked nodes  */
 int64_t rt_protected_size(const rt_tree* t);   /* tokens in locked nodes    */
 int64_t rt_free_size(const rt_tree* t);        /* slots on the free list    */

@@ -18,7 +18,8 @@ __all__ = [
     "RT_POLICIES", "rt_create", "rt_create_policy", "rt_destroy", "rt_match_prefix", "rt_insert",
     "rt_insert_priority", "rt_peek_prefix", "rt_schedule_longest_prefix", "rt_dump_stats", "rt_prepare_extend_prio",
     "rt_inc_lock_ref", "rt_dec_lock_ref",
-    "rt_evict", "rt_alloc", "rt_free", "rt_take_eviction_log", "rt_evictable_size", "rt_protected_size",
+    "rt_evict", "rt_alloc", "rt_free", "rt_take_eviction_log", "rt_set_eviction_log", "rt_evictable_size",
+    "rt_protected_size",
     "rt_free_size", "rt_clock", "rt_copy_free_list", "rt_dump", "rt_prepare_extend", "rt_release",
     "rt_decode_step", "rt_finish", "pkv_kv_scatter", "pkv_append_slots", "pkv_extend_tile", "pkv_extend_plan",
     "pkv_extend_attention", "pkv_decode_chunk", "pkv_decode_workspace_bytes", "pkv_decode_attention",
@@ -32,7 +33,9 @@ def _i32(a) -> np.ndarray:
 
 
 def _ptr(a: Optional[np.ndarray]):
-    return None if a is None else a.ctypes.data_as(C.c_void_p)
+    # the buffer address as an int (ctypes passes it for a void* argument); the caller keeps
+    # the array alive for the duration of the call
+    return None if a is None else a.ctypes.data
 
 
 # ------------------------------------------------------------------------------------------
@@ -139,6 +142,10 @@ def rt_alloc(t, n: int) -> np.ndarray:
 def rt_free(t, slots) -> None:
     s = _i32(slots)
     check(lib().rt_free(t, _ptr(s), s.size))
+
+
+def rt_set_eviction_log(t, enabled: bool) -> None:
+    check(lib().rt_set_eviction_log(t, 1 if enabled else 0))
 
 
 def rt_take_eviction_log(t) -> List[Tuple[int, List[int]]]:

@@ -43,6 +43,7 @@ SIGNATURES = {
     "rt_alloc": (_i64, [_p, _i64, _p]),
     "rt_free": (C.c_int, [_p, _p, _i64]),
     "rt_eviction_log_size": (C.c_int, [_p, _pi64, _pi64]),
+    "rt_set_eviction_log": (C.c_int, [_p, C.c_int32]),
     "rt_take_eviction_log": (C.c_int, [_p, _p, _p, _i64, _p, _i64]),
     "rt_evictable_size": (_i64, [_p]),
     "rt_protected_size": (_i64, [_p]),

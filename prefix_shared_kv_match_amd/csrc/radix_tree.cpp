@@ -77,9 +77,13 @@ inline EvictKey evict_key(int32_t policy, const Node& n, int64_t id) {
   }
 }
 
+// Length of the common prefix of a[0..na) and b[0..nb): whole 64-token blocks are compared
+// with memcmp (vectorised in the C library), the first differing block token by token.
 inline int64_t lcp(const int32_t* a, int64_t na, const int32_t* b, int64_t nb) {
   const int64_t n = std::min(na, nb);
+  constexpr int64_t kBlock = 64;
   int64_t i = 0;
+  while (i + kBlock <= n && std::memcmp(a + i, b + i, kBlock * sizeof(int32_t)) == 0) i += kBlock;
   while (i < n && a[i] == b[i]) ++i;
   return i;
 }
@@ -98,19 +102,24 @@ struct rt_tree {
   int64_t evictable = 0, protected_ = 0;
   std::vector<int64_t> log_ids, log_lens;
   std::vector<int32_t> log_slots;
+  bool log_on = true;
 
   bool is_live(int64_t id) const {
     return id == 0 || (id > 0 && id < (int64_t)nodes.size() && nodes[id].live_pos >= 0);
   }
 
+  // the free list is a ring of ring.size() entries (head < ring.size(), count <= ring.size());
+  // index arithmetic wraps with one compare instead of a division
   void push_free(int32_t s) {
-    ring[(head + count) % (int64_t)ring.size()] = s;
+    int64_t i = head + count;
+    if (i >= (int64_t)ring.size()) i -= (int64_t)ring.size();
+    ring[i] = s;
     ++count;
     state[s] = kFree;
   }
   int32_t pop_free() {
     int32_t s = ring[head];
-    head = (head + 1) % (int64_t)ring.size();
+    if (++head == (int64_t)ring.size()) head = 0;
     --count;
     state[s] = kInFlight;
     return s;
@@ -373,9 +382,11 @@ struct rt_tree {
       heap.pop();
       Node& x = nodes[id];
       for (int32_t s : x.value) push_free(s);
-      log_ids.push_back(id);
-      log_lens.push_back((int64_t)x.value.size());
-      log_slots.insert(log_slots.end(), x.value.begin(), x.value.end());
+      if (log_on) {
+        log_ids.push_back(id);
+        log_lens.push_back((int64_t)x.value.size());
+        log_slots.insert(log_slots.end(), x.value.begin(), x.value.end());
+      }
       evicted += (int64_t)x.value.size();
       evictable -= (int64_t)x.key.size();
       int64_t p = x.parent;
@@ -550,6 +561,17 @@ int rt_eviction_log_size(const rt_tree* t, int64_t* n_nodes, int64_t* n_slots) {
   if (!t || !n_nodes || !n_slots) return pkv::fail(PKV_ERR_INVAL, "bad arguments to rt_eviction_log_size");
   *n_nodes = (int64_t)t->log_ids.size();
   *n_slots = (int64_t)t->log_slots.size();
+  return PKV_OK;
+}
+
+int rt_set_eviction_log(rt_tree* t, int32_t enabled) {
+  if (!t) return pkv::fail(PKV_ERR_INVAL, "bad arguments to rt_set_eviction_log");
+  t->log_on = enabled != 0;
+  if (!t->log_on) {
+    std::vector<int64_t>().swap(t->log_ids);
+    std::vector<int64_t>().swap(t->log_lens);
+    std::vector<int32_t>().swap(t->log_slots);
+  }
   return PKV_OK;
 }
 

@@ -19,7 +19,7 @@ from typing import List, Optional, Sequence
 
 import numpy as np
 
-from . import (PKV_BF16, PKV_F32, PKV_FP8_E4M3, pkv_decode_attention, pkv_decode_chunk,
+from . import (PKV_BF16, PKV_F32, PKV_FP8_E4M3, pkv_decode_attention, pkv_decode_chunk, rt_set_eviction_log,
                pkv_decode_workspace_bytes, pkv_extend_attention, pkv_extend_plan, pkv_extend_tile, pkv_kv_scatter,
                rt_create, rt_create_policy, rt_dec_lock_ref, rt_decode_step, rt_destroy, rt_finish, rt_peek_prefix,
                rt_prepare_extend, rt_prepare_extend_prio, rt_release, rt_schedule_longest_prefix)
@@ -53,12 +53,17 @@ def flatten(token_lists: Sequence[np.ndarray]):
     return np.ascontiguousarray(toks, dtype=np.int32), indptr
 
 
-def prepare(tree, token_lists, stride: int) -> HostBatch:
+def prepare(tree, token_lists, stride: int, r2t: Optional[np.ndarray] = None) -> HostBatch:
     """rt_prepare_extend over a list of token arrays, or over an already flattened
-    (tokens, indptr) pair (as `flatten` returns), which saves the concatenation."""
+    (tokens, indptr) pair (as `flatten` returns), which saves the concatenation.
+
+    r2t, if given, is the int32 [>= max(n, 1), stride] array the slot rows are written to
+    (e.g. a view into a pinned staging buffer); entries past a request's length are then left
+    as they were (no kernel reads them), otherwise they are -1."""
     toks, indptr = token_lists if isinstance(token_lists, tuple) else flatten(token_lists)
     n = int(indptr.size - 1)
-    r2t = np.full((max(n, 1), stride), -1, dtype=np.int32)
+    if r2t is None:
+        r2t = np.full((max(n, 1), stride), -1, dtype=np.int32)
     pl = np.zeros(max(n, 1), dtype=np.int32)
     el = np.zeros(max(n, 1), dtype=np.int32)
     qo = np.zeros(n + 1, dtype=np.int32)
@@ -83,6 +88,7 @@ class Engine:
         pool_torch = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8_e4m3": torch.uint8}[pool_dtype]
         self.device = torch.device(device)
         self.tree = rt_create_policy(num_slots, free_order, policy)
+        rt_set_eviction_log(self.tree, False)   # nothing here reads it; a serving loop must not grow it
         self.k_pool = torch.zeros((num_slots, hkv, d), dtype=pool_torch, device=self.device)
         self.v_pool = torch.zeros((num_slots, hkv, d), dtype=pool_torch, device=self.device)
         f = lambda a: None if a is None else torch.as_tensor(np.asarray(a, dtype=np.float32), device=self.device)
@@ -106,43 +112,72 @@ class Engine:
     def to_dev(self, a: np.ndarray):
         return self.torch.from_numpy(np.ascontiguousarray(a)).to(self.device, non_blocking=False)
 
+    def _next_stage(self, need: int):
+        """The pinned staging buffer the next staged upload uses, once the copy that last read
+        it is done, holding at least `need` int32."""
+        torch = self.torch
+        if not hasattr(self, "_stage"):
+            self._stage = [dict(host=None, np=None, event=torch.cuda.Event()) for _ in range(2)]
+            self._stage_i = 0
+            self._dev_pack = None
+        st = self._stage[self._stage_i]
+        st["event"].synchronize()          # the copy that last read this pinned buffer is done
+        if st["host"] is None or st["host"].numel() < need:
+            old = st["np"]
+            st["host"] = torch.empty(max(need * 2, 64), dtype=torch.int32).pin_memory()
+            st["np"] = st["host"].numpy()
+            if old is not None:
+                st["np"][:old.size] = old
+        return st
+
+    def prepare_staged(self, token_lists, stride: int) -> HostBatch:
+        """prepare() whose slot rows are written straight into the pinned buffer the next
+        device_tables(staged=True) call uploads (no host copy of the table).  The rows stay
+        valid until the second staged upload after that one; entries past a request's length
+        are unspecified."""
+        toks, indptr = token_lists if isinstance(token_lists, tuple) else flatten(token_lists)
+        n = max(int(indptr.size - 1), 1)
+        st = self._next_stage(n * stride + 4 * n + 2 * int(indptr[-1]) + 1024)
+        hb = prepare(self.tree, (toks, indptr), stride, r2t=st["np"][:n * stride].reshape(n, stride))
+        hb.staged_in = st
+        return hb
+
     def device_tables(self, hb: HostBatch, staged: bool = False):
         """Copy one batch's tables (and its extend plan) to the device.
 
         staged=True copies through two alternating pinned host buffers with asynchronous
         copies on the current stream, so the host can prepare the next batch while the GPU
         still works on this one; the returned device tensors are reused by the next staged
-        call (stream order keeps that safe)."""
+        call (stream order keeps that safe).  A batch from prepare_staged already has its slot
+        rows in place."""
         work = pkv_extend_plan(hb.prefix_lens, hb.extend_lens, self.tile).reshape(-1, 2)
         arrays = dict(req_to_token=hb.req_to_token, prefix_lens=hb.prefix_lens, extend_lens=hb.extend_lens,
                       qo_indptr=hb.qo_indptr, new_slots=hb.new_slots, work=work)
         if not staged:
             return {k: self.to_dev(v) for k, v in arrays.items()}
-        # all tables packed into one pinned buffer (each array 256-byte aligned) and moved with
-        # one asynchronous copy; two such buffers alternate so the host can fill the next batch's
-        # while the GPU still copies this one.  The device views stay valid until the next
-        # staged call (stream order keeps the reuse safe).
+        # all tables packed into one pinned buffer (the slot rows first, each array 256-byte
+        # aligned) and moved with one asynchronous copy; two such buffers alternate so the host
+        # can fill the next batch's while the GPU still copies this one.  The device views stay
+        # valid until the next staged call (stream order keeps the reuse safe).
         torch = self.torch
-        if not hasattr(self, "_stage"):
-            self._stage = [dict(host=None, event=torch.cuda.Event()) for _ in range(2)]
-            self._stage_i = 0
-            self._dev_pack = None
         offs, total = {}, 0
         for k, a in arrays.items():
             offs[k] = total
             total += (a.size + 63) // 64 * 64
         total = max(total, 64)
-        st = self._stage[self._stage_i]
+        inplace = getattr(hb, "staged_in", None) is not None and hb.staged_in is self._stage[self._stage_i] \
+            if hasattr(self, "_stage") else False
+        st = self._next_stage(total)
         self._stage_i ^= 1
-        st["event"].synchronize()          # the copy that last read this pinned buffer is done
-        if st["host"] is None or st["host"].numel() < total:
-            st["host"] = torch.empty(total * 2, dtype=torch.int32).pin_memory()
-            st["np"] = st["host"].numpy()
         if self._dev_pack is None or self._dev_pack.numel() < total:
             self._dev_pack = torch.empty(total * 2, dtype=torch.int32, device=self.device)
         hn = st["np"]
         for k, a in arrays.items():
+            if inplace and k == "req_to_token":
+                continue                   # written there by rt_prepare_extend
             hn[offs[k]:offs[k] + a.size] = a.reshape(-1)
+        if inplace:
+            hb.staged_in = None
         self._dev_pack[:total].copy_(st["host"][:total], non_blocking=True)
         st["event"].record()
         return {k: self._dev_pack[offs[k]:offs[k] + a.size].view(a.shape) for k, a in arrays.items()}

@@ -202,6 +202,41 @@ def test_prepare_rejects_small_stride():
         pkv.rt_destroy(t)
 
 
+def test_eviction_log_switch():
+    """The log records evictions while on (the default), drops its contents when turned off,
+    records nothing while off, and the tree itself evicts the same either way."""
+    t = pkv.rt_create(16)
+    try:
+        for key in ([1, 2, 3], [4, 5], [6]):
+            pkv.rt_release(t, runtime.prepare(t, [np.array(key)], 8).last_nodes)
+        assert pkv.rt_evict(t, 3) == 3                  # [1, 2, 3] (oldest) goes first
+        pkv.rt_set_eviction_log(t, False)
+        assert pkv.rt_take_eviction_log(t) == []        # turning it off dropped the entry
+        assert pkv.rt_evict(t, 2) == 2
+        assert pkv.rt_take_eviction_log(t) == []
+        pkv.rt_set_eviction_log(t, True)
+        assert pkv.rt_evict(t, 1) == 1
+        log = pkv.rt_take_eviction_log(t)
+        assert len(log) == 1 and len(log[0][1]) == 1
+        assert pkv.rt_free_size(t) == 16 and pkv.rt_dump(t) == []
+    finally:
+        pkv.rt_destroy(t)
+
+
+def test_runtime_prepare_into_given_rows():
+    """prepare() writes the slot rows into a caller's array (the staged upload path) and
+    leaves entries past each request's length untouched."""
+    t = pkv.rt_create(64)
+    try:
+        rows = np.full((2, 8), 77, dtype=np.int32)
+        hb = runtime.prepare(t, [np.array([1, 2, 3]), np.array([1, 2, 9, 9])], 8, r2t=rows)
+        assert hb.req_to_token.base is rows or hb.req_to_token is rows or np.shares_memory(hb.req_to_token, rows)
+        assert rows[0, :3].tolist() == [0, 1, 2] and rows[1, :4].tolist() == [0, 1, 3, 4]
+        assert rows[0, 3:].tolist() == [77] * 5 and rows[1, 4:].tolist() == [77] * 4
+    finally:
+        pkv.rt_destroy(t)
+
+
 def compare_workload(wl):
     ob = driver.run_workload_host(wl)
     lb, ldec, levlog, lfree, lev, lprot, ldump = runtime.run_workload_host(wl)
