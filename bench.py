@@ -42,12 +42,12 @@ CSRC = os.path.join(ROOT, "prefix_shared_kv_match_amd", "csrc")
 # what the same counters read for a plain 1 GiB device copy (FETCH x2.0, WRITE x1.0).  Each
 # entry holds the hash of the kernel sources it was taken on; a changed kernel reports null.
 TRAFFIC = {
-    "fewshot_bf16": dict(kernel="extend_attention", src_hash="ea8dda4ddfe97d66",
-                         fetch_kib=215474.5, write_kib=102968.125),
+    "fewshot_bf16": dict(kernel="extend_attention", src_hash="c2ec9c6c03996513",
+                         fetch_kib=204789.90625, write_kib=102977.171875),
     "decode_bf16": dict(kernel="decode_attention", src_hash="1c25a75dd0c3e5a3",
                         fetch_kib=5097152.96875, write_kib=47959.75),
-    "longctx_fp8": dict(kernel="extend_attention", src_hash="ea8dda4ddfe97d66",
-                        fetch_kib=1705922.59375, write_kib=262144.109375),
+    "longctx_fp8": dict(kernel="extend_attention", src_hash="c2ec9c6c03996513",
+                        fetch_kib=1702728.09375, write_kib=262144.03125),
 }
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 KERNEL_SOURCES = {"extend_attention": ["extend_attention.hip", "device.h"],
