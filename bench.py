@@ -50,6 +50,11 @@ TRAFFIC = {
                         fetch_kib=1702728.09375, write_kib=262144.03125),
 }
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
+# (warmup, timed) steps when not given: a few hundred ms of warmup for sub-millisecond steps,
+# a handful of steps for the ones that run tens of milliseconds (one job, or a long-context
+# extend with 64 decode steps)
+DEFAULT_WARMUP_STEPS = {"fewshot_bf16": (200, 300), "decode_bf16": (40, 80), "longctx_fp8": (4, 10),
+                        "multiturn_bf16": (5, 20), "tot_bf16": (5, 20)}
 KERNEL_SOURCES = {"extend_attention": ["extend_attention.hip", "device.h"],
                   "decode_attention": ["decode_attention.hip", "device.h"]}
 
@@ -74,8 +79,11 @@ def traffic_bytes(workload: str, kernel: str):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default per workload: enough for a stable mean, a second or less)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps first (default per workload: long enough for the GPU to leave its "
+                         "idle clocks; a few milliseconds of warmup under-reports a sub-millisecond step)")
     ap.add_argument("--workload", default="fewshot_bf16",
                     choices=["fewshot_bf16", "decode_bf16", "longctx_fp8", "multiturn_bf16", "tot_bf16"])
     ap.add_argument("--schedule", default="lpm", choices=["fcfs", "lpm"],
@@ -102,6 +110,7 @@ class Timer:
     def __init__(self, torch, pool=4096):
         self.torch = torch
         self.free = [torch.cuda.Event(enable_timing=True) for _ in range(pool)]
+        self.stream = torch.cuda.current_stream()
         self.acc = {}
         self.pending = []
 
@@ -113,10 +122,10 @@ class Timer:
                 if len(t.free) < 2:
                     t.collect()
                 s.a, s.b = t.free.pop(), t.free.pop()
-                s.a.record()
+                s.a.record(t.stream)
 
             def __exit__(s, *exc):
-                s.b.record()
+                s.b.record(t.stream)
                 t.pending.append((name, s.a, s.b))
         return _S()
 
@@ -207,13 +216,6 @@ class PathBench:
         self.do = torch.empty_like(self.dq[0]) if n_dec else None
         if n_dec:
             self.ws, self.chunk = eng.decode_workspace(B, self.max_len)
-        # two pinned staging buffers for the per-step slots / lengths, each guarded by an event, so
-        # the host can prepare step i+1 while the GPU still copies step i's values
-        self.stage = [(torch.empty(B, dtype=torch.int32).pin_memory(), torch.empty(B, dtype=torch.int32).pin_memory(),
-                       torch.cuda.Event()) for _ in range(2)]
-        self.stage_i = 0
-        self.dec_slots_dev = torch.empty(B, dtype=torch.int32, device=dev)
-        self.seq_dev = torch.empty(B, dtype=torch.int32, device=dev)
         self.last_tables = None
         self.host_prepare_s = 0.0
 
@@ -234,20 +236,12 @@ class PathBench:
         """rt_decode_step -> H2D (slots, lengths) -> append to the device table -> kv_scatter -> decode."""
         import prefix_shared_kv_match_amd as pkv
         torch, eng, T = self.torch, self.eng, self.timer
-        slots = eng.decode_alloc(hb)
-        sh, lh, ev = self.stage[self.stage_i]
-        self.stage_i ^= 1
-        ev.synchronize()                      # the copies that last read this staging buffer are done
-        sh.numpy()[:] = slots
-        lh.numpy()[:] = hb.seq_lens
-        self.dec_slots_dev.copy_(sh, non_blocking=True)
-        self.seq_dev.copy_(lh, non_blocking=True)
-        ev.record()
-        pkv.pkv_append_slots(r2t_dev, self.seq_dev, self.dec_slots_dev)
+        slots_dev, seq_dev = eng.upload_decode(eng.decode_alloc(hb), hb.seq_lens)   # side-stream copy
+        pkv.pkv_append_slots(r2t_dev, seq_dev, slots_dev)
         with T.span("kv_scatter_decode"):
-            eng.scatter(self.dec_slots_dev, self.dk[i], self.dv[i])
+            eng.scatter(slots_dev, self.dk[i], self.dv[i])
         with T.span("decode_attention"):
-            eng.decode(self.dq[i], r2t_dev, self.seq_dev, self.max_len, self.ws, self.chunk, self.do)
+            eng.decode(self.dq[i], r2t_dev, seq_dev, self.max_len, self.ws, self.chunk, self.do)
 
     def step(self):
         import prefix_shared_kv_match_amd as pkv
@@ -341,8 +335,6 @@ class JobBench:
             self.ws, self.chunk = eng.decode_workspace(B, self.max_len)
             self.full_tokens = [np.concatenate([r.tokens, wl.decode_tokens[:, i]]) for i, r in enumerate(last)]
             self.prompt_lens = [len(r.tokens) for r in last]
-            self.dec_slots_dev = torch.empty(B, dtype=torch.int32, device="cuda")
-            self.seq_dev = torch.empty(B, dtype=torch.int32, device="cuda")
         torch.cuda.synchronize()
         self.flops = 0.0
         self.ext_tokens = 0
@@ -428,14 +420,12 @@ class JobBench:
             hb = self._last_hb
             r2t = self._last_dt["req_to_token"]
             for i in range(self.steps_dec):
-                slots = eng.decode_alloc(hb)
-                self.dec_slots_dev.copy_(torch_from(self.torch, slots))
-                self.seq_dev.copy_(torch_from(self.torch, hb.seq_lens))
-                pkv.pkv_append_slots(r2t, self.seq_dev, self.dec_slots_dev)
+                slots_dev, seq_dev = eng.upload_decode(eng.decode_alloc(hb), hb.seq_lens)
+                pkv.pkv_append_slots(r2t, seq_dev, slots_dev)
                 with T.span("kv_scatter_decode"):
-                    eng.scatter(self.dec_slots_dev, self.dk[i], self.dv[i])
+                    eng.scatter(slots_dev, self.dk[i], self.dv[i])
                 with T.span("decode_attention"):
-                    eng.decode(self.dq[i], r2t, self.seq_dev, self.max_len, self.ws, self.chunk, self.do)
+                    eng.decode(self.dq[i], r2t, seq_dev, self.max_len, self.ws, self.chunk, self.do)
             eng.finish(hb, self.full_tokens, self.prompt_lens)
             n += self.steps_dec * hb.n
         pkv.rt_evict(eng.tree, pkv.rt_evictable_size(eng.tree) - self.root_len)
@@ -459,10 +449,6 @@ class JobBench:
                 out[f"{order}/{pol}"] = {"all": round(cached / self.prompt_tokens, 4),
                                          "priority_class": round(prio_c / max(prio_t, 1), 4)}
         return out
-
-
-def torch_from(torch, a):
-    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
 
 
 def practical_hbm_gbps(torch, mib=1024, reps=5):
@@ -571,6 +557,9 @@ def main():
         print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported (the library runs one GPU per "
               f"process and has no multi-GPU path)", file=sys.stderr)
         return 2
+    dw, ds = DEFAULT_WARMUP_STEPS[a.workload]
+    a.warmup = dw if a.warmup is None else a.warmup
+    a.steps = ds if a.steps is None else a.steps
     import torch
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)

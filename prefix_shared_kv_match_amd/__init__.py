@@ -301,9 +301,13 @@ def _dev(t, name, dtype=None, ndim=None):
 
 
 def _stream(stream):
+    """The HIP stream handle a call is issued on: the given torch stream, else torch's current
+    stream on the current device (read as a raw handle; building a Stream object per call
+    costs more host time than a small launch)."""
     torch = _torch()
-    s = torch.cuda.current_stream() if stream is None else stream
-    return C.c_void_p(s.cuda_stream)
+    if stream is not None:
+        return C.c_void_p(stream.cuda_stream)
+    return C.c_void_p(torch._C._cuda_getCurrentRawStream(torch._C._cuda_getDevice()))
 
 
 def pkv_kv_scatter(k_src, v_src, slots, k_pool, v_pool, k_inv_scale=None, v_inv_scale=None, stream=None) -> None:

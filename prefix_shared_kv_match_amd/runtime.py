@@ -74,6 +74,69 @@ def prepare(tree, token_lists, stride: int, r2t: Optional[np.ndarray] = None) ->
     return HostBatch(n, r2t[:n], pl[:n], el[:n], qo, new[:n_new], last[:n], seq)
 
 
+class StagedUpload:
+    """Host -> device upload of int32 tables without stalling the launch stream.
+
+    Two pinned host buffers and two device buffers alternate.  send() copies the current
+    pair on a side stream (default priority) and makes the caller's current stream wait for
+    that copy, so the copy runs while earlier kernels still execute instead of between them.
+    Reuse is safe because the copy into a device buffer first waits for a marker recorded on
+    the current stream at the previous send(): everything launched before that call, which
+    includes every reader of the buffer's previous contents when readers are launched before
+    the next send(), has finished.  host() waits for the last copy out of the host buffer."""
+
+    def __init__(self, torch, device):
+        self.torch = torch
+        self.device = device
+        self.stream = torch.cuda.Stream(device=device)
+        self.bufs = [dict(host=None, np=None, dev=None, copied=torch.cuda.Event()) for _ in range(2)]
+        self.marks = [torch.cuda.Event(), torch.cuda.Event()]
+        self.i = 0
+        self.seq = 0          # number of send() calls so far
+        self.waited = -1      # bufs[i] host side already synchronized for this send
+
+    def host(self, need: int, keep: bool = False) -> np.ndarray:
+        """The int32 pinned buffer the next send() copies from, holding at least `need`
+        values, once the copy that last read it is done.  keep=True preserves what the buffer
+        holds if it has to grow."""
+        torch = self.torch
+        b = self.bufs[self.i]
+        if self.waited != self.seq:
+            b["copied"].synchronize()
+            self.waited = self.seq
+        if b["host"] is None or b["host"].numel() < need:
+            old = b["np"]
+            b["host"] = torch.empty(max(need * 2, 64), dtype=torch.int32).pin_memory()
+            b["np"] = b["host"].numpy()
+            if keep and old is not None:
+                b["np"][:old.size] = old
+        return b["np"]
+
+    def send(self, total: int):
+        """Copy the first `total` values of the current host buffer to its device buffer on
+        the side stream; returns the device view (int32 [total])."""
+        torch = self.torch
+        b = self.bufs[self.i]
+        if b["host"] is None or b["host"].numel() < total:
+            raise ValueError("send() without a large enough host() buffer")
+        main = torch.cuda.current_stream(self.device)
+        mark = self.marks[self.seq & 1]
+        prev = self.marks[(self.seq & 1) ^ 1]
+        mark.record(main)                  # all work launched so far on the current stream
+        if b["dev"] is None or b["dev"].numel() < total:
+            b["dev"] = torch.empty(max(total * 2, 64), dtype=torch.int32, device=self.device)
+            b["dev"].record_stream(self.stream)
+        if self.seq > 0:
+            self.stream.wait_event(prev)   # readers of this device buffer's previous contents are done
+        with torch.cuda.stream(self.stream):
+            b["dev"][:total].copy_(b["host"][:total], non_blocking=True)
+            b["copied"].record(self.stream)
+        main.wait_event(b["copied"])
+        self.i ^= 1
+        self.seq += 1
+        return b["dev"][:total]
+
+
 class Engine:
     """One radix tree plus its device KV pools."""
 
@@ -112,75 +175,67 @@ class Engine:
     def to_dev(self, a: np.ndarray):
         return self.torch.from_numpy(np.ascontiguousarray(a)).to(self.device, non_blocking=False)
 
-    def _next_stage(self, need: int):
-        """The pinned staging buffer the next staged upload uses, once the copy that last read
-        it is done, holding at least `need` int32."""
-        torch = self.torch
-        if not hasattr(self, "_stage"):
-            self._stage = [dict(host=None, np=None, event=torch.cuda.Event()) for _ in range(2)]
-            self._stage_i = 0
-            self._dev_pack = None
-        st = self._stage[self._stage_i]
-        st["event"].synchronize()          # the copy that last read this pinned buffer is done
-        if st["host"] is None or st["host"].numel() < need:
-            old = st["np"]
-            st["host"] = torch.empty(max(need * 2, 64), dtype=torch.int32).pin_memory()
-            st["np"] = st["host"].numpy()
-            if old is not None:
-                st["np"][:old.size] = old
-        return st
+    def _uploader(self, name: str) -> "StagedUpload":
+        up = getattr(self, name, None)
+        if up is None:
+            up = StagedUpload(self.torch, self.device)
+            setattr(self, name, up)
+        return up
 
     def prepare_staged(self, token_lists, stride: int) -> HostBatch:
         """prepare() whose slot rows are written straight into the pinned buffer the next
-        device_tables(staged=True) call uploads (no host copy of the table).  The rows stay
-        valid until the second staged upload after that one; entries past a request's length
-        are unspecified."""
+        device_tables(staged=True) call uploads (no host copy of the table).  Entries past a
+        request's length are unspecified."""
         toks, indptr = token_lists if isinstance(token_lists, tuple) else flatten(token_lists)
         n = max(int(indptr.size - 1), 1)
-        st = self._next_stage(n * stride + 4 * n + 2 * int(indptr[-1]) + 1024)
-        hb = prepare(self.tree, (toks, indptr), stride, r2t=st["np"][:n * stride].reshape(n, stride))
-        hb.staged_in = st
+        up = self._uploader("_tables_up")
+        hn = up.host(n * stride + 4 * n + 2 * int(indptr[-1]) + 1024)
+        hb = prepare(self.tree, (toks, indptr), stride, r2t=hn[:n * stride].reshape(n, stride))
+        hb.staged_in = (up, up.seq)
         return hb
 
     def device_tables(self, hb: HostBatch, staged: bool = False):
         """Copy one batch's tables (and its extend plan) to the device.
 
-        staged=True copies through two alternating pinned host buffers with asynchronous
-        copies on the current stream, so the host can prepare the next batch while the GPU
-        still works on this one; the returned device tensors are reused by the next staged
-        call (stream order keeps that safe).  A batch from prepare_staged already has its slot
-        rows in place."""
+        staged=True packs them into one pinned buffer and copies it on a side stream
+        (StagedUpload): the copy overlaps the work already queued, and the current stream
+        waits for it before anything launched after this call.  The returned device views
+        may be read by work launched on the current stream until the next staged call; a
+        batch from prepare_staged already has its slot rows in place."""
         work = pkv_extend_plan(hb.prefix_lens, hb.extend_lens, self.tile).reshape(-1, 2)
         arrays = dict(req_to_token=hb.req_to_token, prefix_lens=hb.prefix_lens, extend_lens=hb.extend_lens,
                       qo_indptr=hb.qo_indptr, new_slots=hb.new_slots, work=work)
         if not staged:
             return {k: self.to_dev(v) for k, v in arrays.items()}
-        # all tables packed into one pinned buffer (the slot rows first, each array 256-byte
-        # aligned) and moved with one asynchronous copy; two such buffers alternate so the host
-        # can fill the next batch's while the GPU still copies this one.  The device views stay
-        # valid until the next staged call (stream order keeps the reuse safe).
-        torch = self.torch
+        # all tables in one buffer, the slot rows first, each array 256-byte aligned
         offs, total = {}, 0
         for k, a in arrays.items():
             offs[k] = total
             total += (a.size + 63) // 64 * 64
         total = max(total, 64)
-        inplace = getattr(hb, "staged_in", None) is not None and hb.staged_in is self._stage[self._stage_i] \
-            if hasattr(self, "_stage") else False
-        st = self._next_stage(total)
-        self._stage_i ^= 1
-        if self._dev_pack is None or self._dev_pack.numel() < total:
-            self._dev_pack = torch.empty(total * 2, dtype=torch.int32, device=self.device)
-        hn = st["np"]
+        up = self._uploader("_tables_up")
+        inplace = getattr(hb, "staged_in", None) == (up, up.seq)
+        hn = up.host(total, keep=inplace)
         for k, a in arrays.items():
             if inplace and k == "req_to_token":
                 continue                   # written there by rt_prepare_extend
             hn[offs[k]:offs[k] + a.size] = a.reshape(-1)
         if inplace:
             hb.staged_in = None
-        self._dev_pack[:total].copy_(st["host"][:total], non_blocking=True)
-        st["event"].record()
-        return {k: self._dev_pack[offs[k]:offs[k] + a.size].view(a.shape) for k, a in arrays.items()}
+        dev = up.send(total)
+        return {k: dev[offs[k]:offs[k] + a.size].view(a.shape) for k, a in arrays.items()}
+
+    def upload_decode(self, slots: np.ndarray, seq_lens: np.ndarray):
+        """One decode step's new slots and sequence lengths on the device (int32 [n] each),
+        through a staged upload of their own; valid for work launched on the current stream
+        until the next call."""
+        n = int(slots.size)
+        up = self._uploader("_decode_up")
+        hn = up.host(2 * n)
+        hn[:n] = slots
+        hn[n:2 * n] = seq_lens
+        dev = up.send(2 * n)
+        return dev[:n], dev[n:2 * n]
 
     # -- steps ---------------------------------------------------------------------------
     def prepare(self, token_lists, stride: int) -> HostBatch:

@@ -128,3 +128,78 @@ def test_staged_tables_match_plain_upload():
         torch.cuda.synchronize()
         assert torch.equal(plain, staged), bi
         eng.release(hb)
+
+
+def test_prepare_staged_rows_upload_like_plain_tables():
+    """Slot rows written by prepare_staged straight into the pinned upload buffer give the
+    same device tables (over each row's length) and the same extend output as prepare plus a
+    plain upload, over three consecutive batches (both staging buffers, buffer reuse)."""
+    log("prepare_staged")
+    wl = workloads.multiturn_bf16(n_conv=12, turns=3, turn_range=(16, 80), batch=6, pool_slots=20000,
+                                  capacity=12000)
+    eng = make_engine(wl)
+    twin = make_engine(wl)
+    for bi, batch in enumerate(wl.batches[:3]):
+        toks = [r.tokens for r in batch]
+        hs = eng.prepare_staged(toks, wl.max_len())
+        hp = twin.prepare(toks, wl.max_len())
+        assert hs.prefix_lens.tolist() == hp.prefix_lens.tolist() and hs.new_slots.tolist() == hp.new_slots.tolist()
+        rows = np.concatenate([r.rows[p:] for r, p in zip(batch, hp.prefix_lens)])
+        for e in (eng, twin):
+            h = hs if e is eng else hp
+            sl = torch.from_numpy(np.ascontiguousarray(h.new_slots, dtype=np.int32)).cuda()
+            e.scatter(sl, src_tensor(torch, wl.values.k(rows), wl.shape, "cuda"),
+                      src_tensor(torch, wl.values.v(rows), wl.shape, "cuda"))
+        q = src_tensor(torch, wl.values.q(rows), wl.shape, "cuda")
+        ds, dp = eng.device_tables(hs, staged=True), twin.device_tables(hp)
+        for i, r in enumerate(batch):
+            n = len(r.tokens)
+            assert torch.equal(ds["req_to_token"][i, :n].cpu(), dp["req_to_token"][i, :n].cpu()), (bi, i)
+        a, b = eng.extend(ds, q), twin.extend(dp, q)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b), bi
+        eng.release(hs)
+        twin.release(hp)
+
+
+
+def test_staged_uploads_queued_without_host_sync():
+    """Twelve staged table uploads over three batches and eight decode uploads queued
+    back-to-back with no host synchronisation: the side-stream copies may run ahead of the
+    kernels reading earlier uploads, and every kernel must still see its own tables (extend
+    outputs bit-equal to the plain-upload ones; decode slots / lengths read back intact)."""
+    log("staged uploads queued without host sync")
+    wl = workloads.multiturn_bf16(n_conv=12, turns=3, turn_range=(16, 80), batch=6, pool_slots=20000,
+                                  capacity=12000)
+    eng = make_engine(wl)
+    hbs, qs, refs = [], [], []
+    for batch in wl.batches[:3]:
+        hb = eng.prepare([r.tokens for r in batch], wl.max_len())
+        rows = np.concatenate([r.rows[p:] for r, p in zip(batch, hb.prefix_lens)])
+        sl = torch.from_numpy(np.ascontiguousarray(hb.new_slots, dtype=np.int32)).cuda()
+        eng.scatter(sl, src_tensor(torch, wl.values.k(rows), wl.shape, "cuda"),
+                    src_tensor(torch, wl.values.v(rows), wl.shape, "cuda"))
+        q = src_tensor(torch, wl.values.q(rows), wl.shape, "cuda")
+        refs.append(eng.extend(eng.device_tables(hb), q))
+        hbs.append(hb)
+        qs.append(q)
+    torch.cuda.synchronize()
+    outs = []
+    for rep in range(4):
+        for k in range(3):
+            outs.append((k, eng.extend(eng.device_tables(hbs[k], staged=True), qs[k])))
+    rng = np.random.default_rng(5)
+    dec = []
+    for i in range(8):
+        s = rng.integers(0, 1 << 20, size=37).astype(np.int32)
+        n = rng.integers(1, 4000, size=37).astype(np.int32)
+        sd, nd = eng.upload_decode(s, n)
+        dec.append((s, n, torch.stack([sd * 1, nd * 1])))    # read on the current stream
+    torch.cuda.synchronize()
+    for k, o in outs:
+        assert torch.equal(o, refs[k]), k
+    for s, n, got in dec:
+        g = got.cpu().numpy()
+        assert np.array_equal(g[0], s) and np.array_equal(g[1], n)
+    for hb in hbs:
+        eng.release(hb)
