@@ -94,6 +94,8 @@ def parse():
     ap.add_argument("--chunk-budget", type=int, default=0,
                     help="fewshot_bf16: chunked prefill with at most this many new tokens per extend launch "
                          "(times the whole chunked job; 0 = the default one-batch step)")
+    ap.add_argument("--plain-decode", action="store_true",
+                    help="decode without the shared-prefix plan (every sequence gathers its whole context)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=64, help="requests in the oracle's timed sample")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -163,7 +165,7 @@ class PathBench:
 
     CHUNK_ROWS = 65536   # setup scatter in chunks, so host memory stays bounded
 
-    def __init__(self, torch, wl_name="fewshot_bf16", total_steps=64):
+    def __init__(self, torch, wl_name="fewshot_bf16", total_steps=64, shared_decode=True):
         import workloads
         from prefix_shared_kv_match_amd.runtime import Engine
         self.torch = torch
@@ -216,6 +218,12 @@ class PathBench:
         self.do = torch.empty_like(self.dq[0]) if n_dec else None
         if n_dec:
             self.ws, self.chunk = eng.decode_workspace(B, self.max_len)
+        # shared-prefix decode: which chunks the batch's sequences hold in common (made from the
+        # host rows after the first decode slot is taken; valid while the sequences only grow)
+        self.shared_decode = shared_decode
+        self.plan = None
+        if self.decode_only and shared_decode:
+            self.plan = eng.decode_plan(self.hb.req_to_token, self.hb.seq_lens, self.chunk)
         self.last_tables = None
         self.host_prepare_s = 0.0
 
@@ -237,11 +245,13 @@ class PathBench:
         import prefix_shared_kv_match_amd as pkv
         torch, eng, T = self.torch, self.eng, self.timer
         slots_dev, seq_dev = eng.upload_decode(eng.decode_alloc(hb), hb.seq_lens)   # side-stream copy
+        if i == 0 and self.shared_decode and not self.decode_only:
+            self.plan = eng.decode_plan(hb.req_to_token, hb.seq_lens, self.chunk)    # host, then side stream
         pkv.pkv_append_slots(r2t_dev, seq_dev, slots_dev)
         with T.span("kv_scatter_decode"):
             eng.scatter(slots_dev, self.dk[i], self.dv[i])
         with T.span("decode_attention"):
-            eng.decode(self.dq[i], r2t_dev, seq_dev, self.max_len, self.ws, self.chunk, self.do)
+            eng.decode(self.dq[i], r2t_dev, seq_dev, self.max_len, self.ws, self.chunk, self.do, plan=self.plan)
 
     def step(self):
         import prefix_shared_kv_match_amd as pkv
@@ -419,13 +429,16 @@ class JobBench:
         if self.steps_dec:
             hb = self._last_hb
             r2t = self._last_dt["req_to_token"]
+            plan = None
             for i in range(self.steps_dec):
                 slots_dev, seq_dev = eng.upload_decode(eng.decode_alloc(hb), hb.seq_lens)
+                if i == 0 and not self.a.plain_decode:
+                    plan = eng.decode_plan(hb.req_to_token, hb.seq_lens, self.chunk)
                 pkv.pkv_append_slots(r2t, seq_dev, slots_dev)
                 with T.span("kv_scatter_decode"):
                     eng.scatter(slots_dev, self.dk[i], self.dv[i])
                 with T.span("decode_attention"):
-                    eng.decode(self.dq[i], r2t, seq_dev, self.max_len, self.ws, self.chunk, self.do)
+                    eng.decode(self.dq[i], r2t, seq_dev, self.max_len, self.ws, self.chunk, self.do, plan=plan)
             eng.finish(hb, self.full_tokens, self.prompt_lens)
             n += self.steps_dec * hb.n
         pkv.rt_evict(eng.tree, pkv.rt_evictable_size(eng.tree) - self.root_len)
@@ -568,7 +581,7 @@ def main():
     pkv.lib()
     if a.workload in ("multiturn_bf16", "tot_bf16") or (a.workload == "fewshot_bf16" and a.chunk_budget > 0):
         return main_job(a, torch)
-    b = PathBench(torch, a.workload, a.warmup + a.steps)
+    b = PathBench(torch, a.workload, a.warmup + a.steps, shared_decode=not a.plain_decode)
     wl = b.wl
     if a.copy_calib_mib:
         n = a.copy_calib_mib * (1 << 20) // 4

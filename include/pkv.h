@@ -304,6 +304,49 @@ int pkv_decode_attention(const void* q, void* o, int32_t qo_dtype, const void* k
                          int32_t max_seq_len, int32_t hq, int32_t hkv, int32_t d, float sm_scale, int32_t chunk,
                          void* workspace, size_t ws_bytes, void* stream);
 
+/* Shared-prefix decode.  The radix tree gives every request that matches a cached prefix the
+ * slots of that prefix [RadixAttention: prefix matching and KV cache reuse], so the decode
+ * sequences of a batch that share a prefix hold its K/V rows in the same slots.  A chunk of
+ * such rows can be read once for all of them: their newest tokens are stacked as the query
+ * rows of one MFMA tile (up to pkv_decode_shared_rows rows per kv head) and the chunk's split
+ * partial is written for every one of them; the split phase then skips those chunks.
+ *
+ * pkv_decode_shared_plan (host): from the HOST slot rows req_to_token [batch, stride] and
+ * seq_lens [batch] (each in [1, stride]), partition the sequences chunk by chunk: at chunk k
+ * the sequences of a group (all equal on chunks 0..k-1) whose chunk k (whole, inside their
+ * context) is slot for slot equal form a job (members, k), which is partitioned again at
+ * k + 1; a sequence left alone stops sharing at k.  Outputs (caller-owned host arrays):
+ *   members [batch]  sequence indices, each job's members contiguous;
+ *   skip [batch]     chunks 0..skip[b]-1 of sequence b are covered by jobs;
+ *   items [cap, 3]   (index of the first member in `members`, member count <= rows, chunk),
+ *                    a job cut into items of at most `rows` members.
+ * chunk: the split chunk the decode will use (a multiple of 64).  rows_from_tree = 1 when
+ * the rows come from one radix tree (as rt_prepare_extend / rt_decode_step write them, while
+ * the batch holds its locks): a slot then belongs to one node at one depth, so rows that hold
+ * the same slot at a position agree on every earlier position and only each chunk's last
+ * slot is compared; 0 compares every slot.  Returns the number of items, PKV_ERR_INVAL on
+ * bad sizes or when items_cap is too small (the message gives the count).  The plan stays
+ * valid while the sequences only grow (new tokens are private). */
+int64_t pkv_decode_shared_plan(const int32_t* req_to_token, int64_t stride, const int32_t* seq_lens, int32_t batch,
+                               int32_t chunk, int32_t rows, int32_t rows_from_tree, int32_t* members, int32_t* skip,
+                               int32_t* items, int64_t items_cap);
+/* Query rows (member sequences) per shared-prefix item for a shape: 128 / (hq / hkv), or
+ * PKV_ERR_UNSUPPORTED (shared-prefix decode needs BF16 q/o, a BF16 or FP8_E4M3 pool, d = 128,
+ * hq / hkv in {1, 2, 4, 8}). */
+int32_t pkv_decode_shared_rows(int32_t qo_dtype, int32_t pool_dtype, int32_t hq, int32_t hkv, int32_t d);
+/* pkv_decode_attention with a shared-prefix plan: members, skip, items are DEVICE copies of
+ * pkv_decode_shared_plan's outputs (n_items of them) for the same slot rows and the same
+ * (nonzero) chunk.  Items whose members or chunk fall outside the batch or the workspace are
+ * ignored (their partials are then left unwritten, so the result is wrong but no access
+ * leaves the buffers).  Same result as pkv_decode_attention up to float32 summation order;
+ * n_items = 0 is pkv_decode_attention. */
+int pkv_decode_attention_shared(const void* q, void* o, int32_t qo_dtype, const void* k_pool, const void* v_pool,
+                                int32_t pool_dtype, int64_t num_slots, const float* k_scale, const float* v_scale,
+                                const int32_t* req_to_token, int64_t stride, const int32_t* seq_lens, int32_t batch,
+                                int32_t max_seq_len, int32_t hq, int32_t hkv, int32_t d, float sm_scale, int32_t chunk,
+                                const int32_t* members, const int32_t* skip, const int32_t* items, int64_t n_items,
+                                void* workspace, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -23,6 +23,7 @@ __all__ = [
     "rt_free_size", "rt_clock", "rt_copy_free_list", "rt_dump", "rt_prepare_extend", "rt_release",
     "rt_decode_step", "rt_finish", "pkv_kv_scatter", "pkv_append_slots", "pkv_extend_tile", "pkv_extend_plan",
     "pkv_extend_attention", "pkv_decode_chunk", "pkv_decode_workspace_bytes", "pkv_decode_attention",
+    "pkv_decode_shared_rows", "pkv_decode_shared_plan", "pkv_decode_attention_shared",
 ]
 
 import ctypes as C
@@ -389,3 +390,49 @@ def pkv_decode_attention(q, o, k_pool, v_pool, req_to_token, seq_lens, max_seq_l
             float(sm_scale), int(chunk), _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
             _stream(stream))
     check(lib().pkv_decode_attention(*args))
+
+
+def pkv_decode_shared_rows(qo_dtype: int, pool_dtype: int, hq: int, hkv: int, d: int) -> int:
+    """Member sequences per shared-prefix item for a shape (negative: not supported)."""
+    return int(lib().pkv_decode_shared_rows(qo_dtype, pool_dtype, hq, hkv, d))
+
+
+def pkv_decode_shared_plan(req_to_token: np.ndarray, seq_lens, chunk: int, rows: int, rows_from_tree: bool = False):
+    """Host plan of the shared-prefix decode over host slot rows: (members [batch],
+    skip [batch], items [n, 3]) as int32 arrays.  rows_from_tree: the rows come from one
+    radix tree, so each chunk's last slot decides it (otherwise every slot is compared)."""
+    r2t = _i32(req_to_token)
+    sl = _i32(seq_lens)
+    b = int(sl.size)
+    if r2t.ndim != 2 or r2t.shape[0] < b:
+        raise ValueError("decode plan: req_to_token must be [>= batch, stride]")
+    members = np.empty(max(b, 1), dtype=np.int32)
+    skip = np.empty(max(b, 1), dtype=np.int32)
+    cap = max(b * (r2t.shape[1] // max(int(chunk), 1)) // 2 + 1, 1)   # jobs hold two members or more
+    items = np.empty((cap, 3), dtype=np.int32)
+    n = int(check(lib().pkv_decode_shared_plan(_ptr(r2t), r2t.shape[1], _ptr(sl), b, int(chunk), int(rows),
+                                               int(bool(rows_from_tree)), _ptr(members), _ptr(skip), _ptr(items),
+                                               cap)))
+    return members[:b], skip[:b], items[:n]
+
+
+def pkv_decode_attention_shared(q, o, k_pool, v_pool, req_to_token, seq_lens, max_seq_len, sm_scale, workspace,
+                                chunk: int, members, skip, items, k_scale=None, v_scale=None, stream=None) -> None:
+    """pkv_decode_attention with a shared-prefix plan (device int32 members [b], skip [b],
+    items [n, 3] from pkv_decode_shared_plan for the same rows and chunk)."""
+    torch = _torch()
+    b, hq, d = q.shape
+    ns, hkv, d2 = k_pool.shape
+    if o.shape != q.shape or v_pool.shape != k_pool.shape or d2 != d or seq_lens.shape != (b,) \
+            or req_to_token.dim() != 2 or req_to_token.shape[0] < b:
+        raise ValueError("decode: shape mismatch")
+    if members.shape != (b,) or skip.shape != (b,) or items.dim() != 2 or items.shape[1] != 3:
+        raise ValueError("decode: plan shape mismatch")
+    args = (_dev(q, "q"), _dev(o, "o", q.dtype), _dtype_code(q), _dev(k_pool, "k_pool"),
+            _dev(v_pool, "v_pool", k_pool.dtype), _dtype_code(k_pool), ns, _dev(k_scale, "k_scale", torch.float32),
+            _dev(v_scale, "v_scale", torch.float32), _dev(req_to_token, "req_to_token", torch.int32),
+            req_to_token.shape[1], _dev(seq_lens, "seq_lens", torch.int32), b, int(max_seq_len), hq, hkv, d,
+            float(sm_scale), int(chunk), _dev(members, "members", torch.int32), _dev(skip, "skip", torch.int32),
+            _dev(items, "items", torch.int32), items.shape[0], _dev(workspace, "workspace"),
+            workspace.numel() * workspace.element_size(), _stream(stream))
+    check(lib().pkv_decode_attention_shared(*args))

@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpkv.so")
 
-HOST_SOURCES = ["common.cpp", "radix_tree.cpp"]
+HOST_SOURCES = ["common.cpp", "radix_tree.cpp", "decode_plan.cpp"]
 HIP_SOURCES = ["kv_scatter.hip", "extend_attention.hip", "decode_attention.hip"]
 
 ARCH = "gfx950"

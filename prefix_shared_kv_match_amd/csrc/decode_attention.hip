@@ -114,7 +114,7 @@ __global__ __launch_bounds__(256) void decode_split(const QT* __restrict__ q, co
                                                     const int32_t* __restrict__ r2t, int64_t stride,
                                                     const int32_t* __restrict__ seq_lens, int hkv, int chunk,
                                                     int max_splits, float qk_scale_log2, float* __restrict__ ws_ml,
-                                                    float* __restrict__ ws_acc) {
+                                                    float* __restrict__ ws_acc, const int32_t* __restrict__ skip) {
   constexpr int VEC = D / 16;
   using Chunk = RowChunk<POOL, VEC>;
   constexpr int ROWB = D * Chunk::kBytes / VEC;  // bytes of one (slot, head) row
@@ -128,6 +128,7 @@ __global__ __launch_bounds__(256) void decode_split(const QT* __restrict__ q, co
   const int L = seq_lens[b];
   const int t0 = s * chunk;
   if (t0 >= L) return;  // the whole workgroup leaves together
+  if (skip && s < skip[b]) return;  // chunk computed by the shared-prefix pass
   const int t1 = min(t0 + chunk, L);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int grp = lane >> 4, li = lane & 15;
@@ -269,7 +270,7 @@ __global__ __launch_bounds__(256, (G >= 8 ? 2 : 3)) void decode_split_slot(const
                                                          const int32_t* __restrict__ seq_lens, int chunk,
                                                          int max_splits, float qk_scale_log2,
                                                          float* __restrict__ ws_ml, float* __restrict__ ws_acc,
-                                                         int hkv_total) {
+                                                         int hkv_total, const int32_t* __restrict__ skip) {
   constexpr int VEC = D / 16;
   constexpr int STREAMS = 16 / HKV;
   using Chunk = RowChunk<POOL, VEC>;
@@ -285,6 +286,7 @@ __global__ __launch_bounds__(256, (G >= 8 ? 2 : 3)) void decode_split_slot(const
   const int L = seq_lens[b];
   const int t0 = s * chunk;
   if (t0 >= L) return;  // the whole workgroup leaves together
+  if (skip && s < skip[b]) return;  // chunk computed by the shared-prefix pass
   const int t1 = min(t0 + chunk, L);
   const int r = threadIdx.x >> 4, li = threadIdx.x & 15;
   const int gl = r % HKV, stream = r / HKV;   // this row's head within the group, token stream
@@ -482,12 +484,12 @@ __global__ __launch_bounds__(256) void decode_reduce(const float* __restrict__ w
 template <typename QT, int POOL, int D, int HKV>
 int launch_slot(int G, dim3 grid, hipStream_t st, const void* q, const void* kp, const void* vp, const float* ks,
                 const float* vs, const int32_t* r2t, int64_t stride, const int32_t* lens, int chunk, int max_splits,
-                float sc, float* ml, float* acc, int hkv_total) {
+                float sc, float* ml, float* acc, int hkv_total, const int32_t* skip) {
 #define PKV_SLOT_CASE(GG)                                                                                        \
   case GG:                                                                                                       \
     hipLaunchKernelGGL((decode_split_slot<QT, POOL, D, GG, HKV>), grid, dim3(256), 0, st, (const QT*)q,          \
                        (const uint8_t*)kp, (const uint8_t*)vp, ks, vs, r2t, stride, lens, chunk, max_splits, sc, \
-                       ml, acc, hkv_total);                                                                      \
+                       ml, acc, hkv_total, skip);                                                                \
     return PKV_OK;
   switch (G) {
     PKV_SLOT_CASE(1)
@@ -503,24 +505,24 @@ int launch_slot(int G, dim3 grid, hipStream_t st, const void* q, const void* kp,
 template <typename QT, int POOL, int D>
 int launch_split(int G, dim3 grid, hipStream_t st, const void* q, const void* kp, const void* vp, const float* ks,
                  const float* vs, const int32_t* r2t, int64_t stride, const int32_t* lens, int hkv, int chunk,
-                 int max_splits, float sc, float* ml, float* acc) {
+                 int max_splits, float sc, float* ml, float* acc, const int32_t* skip) {
 #define PKV_DECODE_CASE(GG)                                                                                    \
   case GG:                                                                                                     \
     hipLaunchKernelGGL((decode_split<QT, POOL, D, GG>), grid, dim3(256), 0, st, (const QT*)q, (const uint8_t*)kp, \
-                       (const uint8_t*)vp, ks, vs, r2t, stride, lens, hkv, chunk, max_splits, sc, ml, acc);     \
+                       (const uint8_t*)vp, ks, vs, r2t, stride, lens, hkv, chunk, max_splits, sc, ml, acc, skip); \
     return PKV_OK;
   // all heads of a slot row per workgroup for 2, 4 or 8 kv heads; groups of 8 heads for
   // any multiple of 8 (multi-head attention)
   const dim3 slot_grid(grid.x / hkv);
   if (hkv == 8) return launch_slot<QT, POOL, D, 8>(G, slot_grid, st, q, kp, vp, ks, vs, r2t, stride, lens, chunk,
-                                                  max_splits, sc, ml, acc, hkv);
+                                                  max_splits, sc, ml, acc, hkv, skip);
   if (hkv == 4) return launch_slot<QT, POOL, D, 4>(G, slot_grid, st, q, kp, vp, ks, vs, r2t, stride, lens, chunk,
-                                                  max_splits, sc, ml, acc, hkv);
+                                                  max_splits, sc, ml, acc, hkv, skip);
   if (hkv == 2) return launch_slot<QT, POOL, D, 2>(G, slot_grid, st, q, kp, vp, ks, vs, r2t, stride, lens, chunk,
-                                                  max_splits, sc, ml, acc, hkv);
+                                                  max_splits, sc, ml, acc, hkv, skip);
   if (hkv % 8 == 0)
     return launch_slot<QT, POOL, D, 8>(G, dim3(grid.x / 8), st, q, kp, vp, ks, vs, r2t, stride, lens, chunk,
-                                       max_splits, sc, ml, acc, hkv);
+                                       max_splits, sc, ml, acc, hkv, skip);
   switch (G) {
     PKV_DECODE_CASE(1)
     PKV_DECODE_CASE(2)
@@ -555,11 +557,22 @@ extern "C" size_t pkv_decode_workspace_bytes(int32_t batch, int32_t hq, int32_t 
   return parts * (2 + (size_t)d) * sizeof(float);
 }
 
-extern "C" int pkv_decode_attention(const void* q, void* o, int32_t qo_dtype, const void* k_pool, const void* v_pool,
-                                    int32_t pool_dtype, int64_t num_slots, const float* k_scale, const float* v_scale,
-                                    const int32_t* req_to_token, int64_t stride, const int32_t* seq_lens,
-                                    int32_t batch, int32_t max_seq_len, int32_t hq, int32_t hkv, int32_t d,
-                                    float sm_scale, int32_t chunk, void* workspace, size_t ws_bytes, void* stream) {
+extern "C" int32_t pkv_decode_shared_rows(int32_t qo_dtype, int32_t pool_dtype, int32_t hq, int32_t hkv, int32_t d) {
+  if (hq <= 0 || hkv <= 0 || hq % hkv) return PKV_ERR_INVAL;
+  const int G = hq / hkv;
+  if (qo_dtype == PKV_BF16 && (pool_dtype == PKV_BF16 || pool_dtype == PKV_FP8_E4M3) && d == 128 &&
+      (G == 1 || G == 2 || G == 4 || G == 8) && hkv * (pool_dtype == PKV_FP8_E4M3 ? 128 : 256) <= 16383)
+    return 128 / G;
+  return PKV_ERR_UNSUPPORTED;
+}
+
+namespace {
+
+int decode_impl(const void* q, void* o, int32_t qo_dtype, const void* k_pool, const void* v_pool, int32_t pool_dtype,
+                int64_t num_slots, const float* k_scale, const float* v_scale, const int32_t* req_to_token,
+                int64_t stride, const int32_t* seq_lens, int32_t batch, int32_t max_seq_len, int32_t hq, int32_t hkv,
+                int32_t d, float sm_scale, int32_t chunk, const int32_t* members, const int32_t* skip,
+                const int32_t* items, int64_t n_items, void* workspace, size_t ws_bytes, void* stream) {
   if (batch < 0 || hq <= 0 || hkv <= 0 || hq % hkv || max_seq_len <= 0 || max_seq_len > stride || num_slots <= 0)
     return fail(PKV_ERR_INVAL, "decode: bad sizes (batch %d hq %d hkv %d max_seq_len %d stride %lld)", batch, hq,
                 hkv, max_seq_len, (long long)stride);
@@ -581,21 +594,26 @@ extern "C" int pkv_decode_attention(const void* q, void* o, int32_t qo_dtype, co
   int rc;
   if (qo_dtype == PKV_F32 && pool_dtype == PKV_F32 && d == 64)
     rc = launch_split<float, PKV_F32, 64>(G, grid, st, q, k_pool, v_pool, k_scale, v_scale, req_to_token, stride,
-                                          seq_lens, hkv, chunk, max_splits, sc, ml, acc);
+                                          seq_lens, hkv, chunk, max_splits, sc, ml, acc, skip);
   else if (qo_dtype == PKV_F32 && pool_dtype == PKV_F32 && d == 128)
     rc = launch_split<float, PKV_F32, 128>(G, grid, st, q, k_pool, v_pool, k_scale, v_scale, req_to_token, stride,
-                                           seq_lens, hkv, chunk, max_splits, sc, ml, acc);
+                                           seq_lens, hkv, chunk, max_splits, sc, ml, acc, skip);
   else if (qo_dtype == PKV_BF16 && pool_dtype == PKV_BF16 && d == 128)
     rc = launch_split<bf16, PKV_BF16, 128>(G, grid, st, q, k_pool, v_pool, k_scale, v_scale, req_to_token, stride,
-                                           seq_lens, hkv, chunk, max_splits, sc, ml, acc);
+                                           seq_lens, hkv, chunk, max_splits, sc, ml, acc, skip);
   else if (qo_dtype == PKV_BF16 && pool_dtype == PKV_FP8_E4M3 && d == 128)
     rc = launch_split<bf16, PKV_FP8_E4M3, 128>(G, grid, st, q, k_pool, v_pool, k_scale, v_scale, req_to_token,
-                                               stride, seq_lens, hkv, chunk, max_splits, sc, ml, acc);
+                                               stride, seq_lens, hkv, chunk, max_splits, sc, ml, acc, skip);
   else
     return fail(PKV_ERR_UNSUPPORTED, "decode: qo dtype %d, pool dtype %d, d %d", qo_dtype, pool_dtype, d);
   if (rc < 0) return rc;
   rc = hip_check(hipGetLastError(), "decode split launch");
   if (rc < 0) return rc;
+  if (n_items > 0) {
+    rc = launch_decode_shared(q, pool_dtype, k_pool, v_pool, k_scale, v_scale, num_slots, req_to_token, stride, batch,
+                              members, items, n_items, chunk, max_splits, hq, hkv, sc, ml, acc, st);
+    if (rc < 0) return rc;
+  }
   const dim3 rgrid((unsigned)(((int64_t)batch * hq + kWaves - 1) / kWaves));
   if (qo_dtype == PKV_F32 && d == 64)
     hipLaunchKernelGGL((decode_reduce<float, 64>), rgrid, dim3(256), 0, st, ml, acc, seq_lens, batch, hq, chunk,
@@ -607,4 +625,37 @@ extern "C" int pkv_decode_attention(const void* q, void* o, int32_t qo_dtype, co
     hipLaunchKernelGGL((decode_reduce<bf16, 128>), rgrid, dim3(256), 0, st, ml, acc, seq_lens, batch, hq, chunk,
                        max_splits, (bf16*)o);
   return hip_check(hipGetLastError(), "decode reduce launch");
+}
+
+}  // namespace
+
+extern "C" int pkv_decode_attention(const void* q, void* o, int32_t qo_dtype, const void* k_pool, const void* v_pool,
+                                    int32_t pool_dtype, int64_t num_slots, const float* k_scale, const float* v_scale,
+                                    const int32_t* req_to_token, int64_t stride, const int32_t* seq_lens,
+                                    int32_t batch, int32_t max_seq_len, int32_t hq, int32_t hkv, int32_t d,
+                                    float sm_scale, int32_t chunk, void* workspace, size_t ws_bytes, void* stream) {
+  return decode_impl(q, o, qo_dtype, k_pool, v_pool, pool_dtype, num_slots, k_scale, v_scale, req_to_token, stride,
+                     seq_lens, batch, max_seq_len, hq, hkv, d, sm_scale, chunk, nullptr, nullptr, nullptr, 0,
+                     workspace, ws_bytes, stream);
+}
+
+extern "C" int pkv_decode_attention_shared(const void* q, void* o, int32_t qo_dtype, const void* k_pool,
+                                           const void* v_pool, int32_t pool_dtype, int64_t num_slots,
+                                           const float* k_scale, const float* v_scale, const int32_t* req_to_token,
+                                           int64_t stride, const int32_t* seq_lens, int32_t batch,
+                                           int32_t max_seq_len, int32_t hq, int32_t hkv, int32_t d, float sm_scale,
+                                           int32_t chunk, const int32_t* members, const int32_t* skip,
+                                           const int32_t* items, int64_t n_items, void* workspace, size_t ws_bytes,
+                                           void* stream) {
+  if (n_items < 0) return fail(PKV_ERR_INVAL, "decode: n_items %lld", (long long)n_items);
+  if (n_items > 0 && batch > 0) {
+    if (!members || !skip || !items) return fail(PKV_ERR_INVAL, "decode: null shared-prefix plan");
+    if (chunk <= 0) return fail(PKV_ERR_INVAL, "decode: a shared-prefix plan needs the chunk it was made for");
+    if (pkv_decode_shared_rows(qo_dtype, pool_dtype, hq, hkv, d) < 0)
+      return fail(PKV_ERR_UNSUPPORTED, "decode: no shared-prefix kernel for qo dtype %d, pool dtype %d, hq %d, hkv %d, d %d",
+                  qo_dtype, pool_dtype, hq, hkv, d);
+  }
+  return decode_impl(q, o, qo_dtype, k_pool, v_pool, pool_dtype, num_slots, k_scale, v_scale, req_to_token, stride,
+                     seq_lens, batch, max_seq_len, hq, hkv, d, sm_scale, chunk, members, n_items > 0 ? skip : nullptr,
+                     items, n_items, workspace, ws_bytes, stream);
 }

@@ -1,0 +1,106 @@
+// Host-side plan of the shared-prefix decode: which leading context chunks several sequences
+// of a decode batch hold in the same pool slots.
+//
+// The radix tree hands every request that matches a cached prefix the slots of that prefix
+// (RadixAttention, "prefix matching" / "KV cache reuse"): sequences that share a prefix
+// share its K/V rows in the pool, slot for slot.  Their decode steps then read the same
+// rows; a chunk of such rows can be streamed once for all of them, with the query rows of
+// every sharing sequence stacked into one dense product (a multi-query tile).
+//
+// The plan is computed from the slot rows alone.  Sequences are partitioned chunk by chunk:
+// at level k the members of a group (which all agree on chunks 0 .. k-1) are sorted by the
+// first slot of chunk k, and members whose whole chunk k equals that of the first member of
+// their run form a sub-group.  A sub-group of two or more sequences is a job (members,
+// chunk k) and is partitioned again at level k + 1; a sequence left alone stops sharing at
+// chunk k.  Only whole chunks inside a sequence's context take part.  Jobs are cut into
+// items of at most `rows` members, the query rows one kernel workgroup holds per kv head.
+//
+// Rows that come from one radix tree need no whole-chunk comparison: a slot belongs to one
+// node at one depth, so two rows holding the same slot at a position hold the same slots at
+// every earlier position too, and comparing a chunk's last slot decides the whole chunk.
+// With rows_from_tree = 0 every chunk is compared slot for slot.
+
+#include <algorithm>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "common.h"
+
+using namespace pkv;
+
+extern "C" int64_t pkv_decode_shared_plan(const int32_t* req_to_token, int64_t stride, const int32_t* seq_lens,
+                                          int32_t batch, int32_t chunk, int32_t rows, int32_t rows_from_tree,
+                                          int32_t* members, int32_t* skip, int32_t* items, int64_t items_cap) {
+  if (batch < 0 || stride <= 0 || chunk < 64 || chunk % 64 || rows <= 0 || items_cap < 0)
+    return fail(PKV_ERR_INVAL, "decode plan: bad sizes (batch %d stride %lld chunk %d rows %d)", batch,
+                (long long)stride, chunk, rows);
+  if (batch == 0) return 0;
+  if (!req_to_token || !seq_lens || !members || !skip || (items_cap > 0 && !items))
+    return fail(PKV_ERR_INVAL, "decode plan: null pointer");
+  std::vector<int32_t> full((size_t)batch);   // whole chunks inside each context
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t L = seq_lens[b];
+    if (L < 1 || L > stride) return fail(PKV_ERR_INVAL, "decode plan: seq_lens[%d] = %lld", b, (long long)L);
+    full[b] = (int32_t)(L / chunk);
+    members[b] = b;
+    skip[b] = 0;
+  }
+  const size_t chunk_bytes = (size_t)chunk * sizeof(int32_t);
+  auto row = [&](int32_t b, int32_t k) { return req_to_token + (int64_t)b * stride + (int64_t)k * chunk; };
+  int64_t n_items = 0;
+  bool overflow = false;
+  struct Range {
+    int32_t lo, hi, k;   // members[lo, hi) agree on chunks 0 .. k-1
+  };
+  std::vector<Range> todo{Range{0, batch, 0}};
+  while (!todo.empty()) {
+    const Range r = todo.back();
+    todo.pop_back();
+    int32_t* m = members + r.lo;
+    const int32_t n = r.hi - r.lo;
+    // members whose context holds chunk k first, ordered by the chunk's first slot (then by
+    // sequence, so the plan is deterministic); the others stop sharing here
+    int32_t* mid = std::stable_partition(m, m + n, [&](int32_t b) { return full[b] > r.k; });
+    for (int32_t* p = mid; p < m + n; ++p) skip[*p] = r.k;
+    std::stable_sort(m, mid, [&](int32_t a, int32_t b) {
+      const int32_t sa = row(a, r.k)[0], sb = row(b, r.k)[0];
+      return sa != sb ? sa < sb : a < b;
+    });
+    // runs of equal first slot, each split into the members equal to the run's first one
+    // over the whole chunk (moved to the front) and the rest, which stop sharing here
+    std::vector<Range> next;
+    for (int32_t* a = m; a < mid;) {
+      int32_t* e = a + 1;
+      while (e < mid && row(*e, r.k)[0] == row(*a, r.k)[0]) ++e;
+      const int32_t* ref = row(*a, r.k);
+      int32_t* same_end = std::stable_partition(a + 1, e, [&](int32_t b) {
+        return rows_from_tree ? row(b, r.k)[chunk - 1] == ref[chunk - 1]
+                              : std::memcmp(row(b, r.k), ref, chunk_bytes) == 0;
+      });
+      for (int32_t* p = same_end; p < e; ++p) skip[*p] = r.k;
+      const int32_t cnt = (int32_t)(same_end - a);
+      if (cnt >= 2) {
+        const int32_t lo = (int32_t)(a - members);
+        for (int32_t i = 0; i < cnt; i += rows) {
+          if (n_items < items_cap) {
+            items[3 * n_items] = lo + i;
+            items[3 * n_items + 1] = std::min(rows, cnt - i);
+            items[3 * n_items + 2] = r.k;
+          } else {
+            overflow = true;
+          }
+          ++n_items;
+        }
+        next.push_back(Range{lo, lo + cnt, r.k + 1});
+      } else {
+        skip[*a] = r.k;
+      }
+      a = e;
+    }
+    // depth first, lowest members first
+    for (auto it = next.rbegin(); it != next.rend(); ++it) todo.push_back(*it);
+  }
+  if (overflow) return fail(PKV_ERR_INVAL, "decode plan: needs %lld items", (long long)n_items);
+  return n_items;
+}

@@ -22,12 +22,13 @@
 //    The S^T row order inside each 16-row MFMA block is permuted so that each lane's four
 //    S^T values of two neighbouring blocks are 8 consecutive kv tokens, which is exactly the
 //    B-operand slice of P^T for the PV product.  Tiles are double-buffered in LDS (one barrier
-//    per tile).  extend_dma stages them with buffer-to-LDS loads (no registers, no vector ALU
-//    work) in a token-row layout and reads V^T with the transposing LDS read of gfx950;
+//    per tile).  extend_dma stages them with global-to-LDS loads (no registers, no LDS store
+//    instructions) in a token-row layout and reads V^T with the transposing LDS read of gfx950;
 //    extend_mfma gathers fp8 codes into registers, decodes them to bf16 (exact) and stores
 //    K row-major and V transposed; the per-head scales are folded into the float32 logits and
 //    output.  The slot table is read with buffer loads one tile ahead of the K/V records it
-//    addresses, so a gathered row costs no address arithmetic and no dependent-load stall.
+//    addresses, so a gathered row waits on no dependent load; rows are addressed in 64 bits
+//    (slot * slot bytes), so pools beyond 4 GiB work.
 //  - extend_f32 (f32 q/o, f32 pool, d 64 or 128): one wave per (tile, q head), VALU only;
 //    it serves the small fp32 case.
 
@@ -151,23 +152,16 @@ __device__ __forceinline__ int sigma(int mb, int rho) {
   return 32 * (mb >> 1) + 8 * (rho >> 2) + 4 * (mb & 1) + (rho & 3);
 }
 
-// Buffer loads.  The K/V pools are read as structured buffers (record = one slot of
-// hkv*d values, record index = slot), and the slot table as a raw buffer, so a gathered
-// row costs no address arithmetic: the slot loaded from the table is the record index,
-// the per-thread column offset is fixed, and out-of-range records read as zero.
-__device__ u32x4 buf_load_rec_x4(__amdgpu_buffer_rsrc_t rsrc, int rec, int voffset, int soffset,
-                                 int aux) __asm("llvm.amdgcn.struct.ptr.buffer.load.v4i32");
-__device__ u32x2 buf_load_rec_x2(__amdgpu_buffer_rsrc_t rsrc, int rec, int voffset, int soffset,
-                                 int aux) __asm("llvm.amdgcn.struct.ptr.buffer.load.v2i32");
+// Buffer loads of the slot table: a raw buffer with range checking (the table stays below
+// 2 GB), so an entry past the table reads as slot 0.  K/V rows of a bf16 pool of at most
+// 2 GiB are gathered as structured-buffer records (PoolGather below); larger pools, and the
+// fp8 path, use 64-bit addresses (slot * slot bytes + column), since a buffer offset is 32 bits.
 __device__ u32x4 buf_load_raw_x4(__amdgpu_buffer_rsrc_t rsrc, int voffset, int soffset,
                                  int aux) __asm("llvm.amdgcn.raw.ptr.buffer.load.v4i32");
 __device__ u32x2 buf_load_raw_x2(__amdgpu_buffer_rsrc_t rsrc, int voffset, int soffset,
                                  int aux) __asm("llvm.amdgcn.raw.ptr.buffer.load.v2i32");
 constexpr int kBufWord3 = 0x00020000;   // 32-bit data format, no swizzle
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t pool_rsrc(const void* p, int slot_bytes, int num_slots) {
-  return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)slot_bytes, num_slots, kBufWord3);
-}
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t table_rsrc(const void* p, int table_bytes) {
   return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, table_bytes, kBufWord3);
 }
@@ -206,6 +200,42 @@ struct WaveAttn {
       vis[nb] = min(qpos0 + qt[nb], ctx - 1);   // padded rows see the whole context
       const bool ok = qt[nb] < nq;
       const bf16* qp = q + ((qrow0 + (ok ? qt[nb] : 0)) * hq + qh[nb]) * kD + 8 * lg;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const u32x4 v = ok ? *(const u32x4*)(qp + 32 * ks) : u32x4{0u, 0u, 0u, 0u};
+        qf[nb][ks] = __builtin_bit_cast(bf16x8, v);
+      }
+      lsum[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int db = 0; db < 8; ++db) oacc[nb][db] = floatx4{0.f, 0.f, 0.f, 0.f};
+      m[nb] = -INFINITY;
+    }
+    const bf16 one = (bf16)(ln == 0 ? 1.f : 0.f);
+    ones_row = bf16x8{one, one, one, one, one, one, one, one};
+  }
+
+  // Rows of a shared-prefix decode item instead of extend rows: row r of the workgroup is the
+  // newest token of sequence members[m0 + r % BT] at head g * G + r / BT (nm real members);
+  // every row sees the whole chunk, so no tile is masked.
+  __device__ __forceinline__ void init_shared(const bf16* q, const int32_t* members, int m0, int nm, int batch, int hq,
+                                              int g, int wave, int lane, float scale) {
+    ln = lane & 15;
+    lg = lane >> 4;
+    sc = scale;
+    qpos0 = 0x3FFFFFFF;   // beyond every tile: the mask branch is never taken
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int r0 = 32 * wave + 16 * nb;
+      qh[nb] = g * G + r0 / BT;
+      qt[nb] = r0 % BT + ln;
+      vis[nb] = qpos0;
+      int b = qt[nb] < nm ? members[m0 + qt[nb]] : -1;
+      const bool ok = b >= 0 && b < batch;   // a member index outside the batch is a padding row
+      if (!ok) {
+        b = 0;
+        qt[nb] = BT;   // never stored
+      }
+      const bf16* qp = q + ((int64_t)b * hq + qh[nb]) * kD + 8 * lg;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const u32x4 v = ok ? *(const u32x4*)(qp + 32 * ks) : u32x4{0u, 0u, 0u, 0u};
@@ -322,6 +352,23 @@ struct WaveAttn {
     __builtin_amdgcn_s_setprio(0);
   }
 
+  // Split partials of a shared-prefix decode item, in the split phase's layout: for member b
+  // and head h, partial p = (b * hq + h) * max_splits + s holds (reference max, row sum) at
+  // ws_ml[2p], ws_ml[2p + 1] and the unnormalised output row (times omul) at ws_acc[p * d].
+  __device__ __forceinline__ void store_partial(float* ws_ml, float* ws_acc, const int32_t* members, int m0, int nm,
+                                                int hq, int max_splits, int s, float omul) const {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const float lt = __shfl(lsum[nb][0], ln);   // row sum sits in lane ln (row 0 of the block)
+      if (qt[nb] >= nm) continue;
+      const int64_t part = ((int64_t)members[m0 + qt[nb]] * hq + qh[nb]) * max_splits + s;
+      float* ap = ws_acc + part * kD + 4 * lg;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) *(floatx4*)(ap + 16 * db) = oacc[nb][db] * omul;
+      if (lg == 0) *(float2*)(ws_ml + 2 * part) = float2{m[nb], lt};
+    }
+  }
+
   // O = O^T / row sum (times the V scale for fp8 pools), bf16, for the item's real rows
   __device__ __forceinline__ void store(bf16* o, int64_t qrow0, int hq, int nq, float omul) const {
 #pragma unroll
@@ -341,12 +388,12 @@ struct WaveAttn {
 };
 
 // ------------------------------------------------------------------------------------------
-// bf16 pools: tiles staged by buffer-to-LDS loads
+// bf16 pools: tiles staged by global-to-LDS loads
 // ------------------------------------------------------------------------------------------
 //
 // LDS layout of a 64-token K (or V) tile: 16 blocks of 4 token rows (256 B each), block
 // stride 1040 B, so block j starts 4 banks after block j - 1.  Token t (bits t0..t5) sits in
-// block 2 t0 + 4 t1 + t4 + 8 t3, row t2 + 2 t5.  A buffer-to-LDS load writes 16 bytes per lane
+// block 2 t0 + 4 t1 + t4 + 8 t3, row t2 + 2 t5.  A global-to-LDS load writes 16 bytes per lane
 // at consecutive addresses, so one load fills one block, 16 lanes per token row, which keeps
 // the global reads of a row contiguous.  The 16 tokens of one S^T operand read differ in bits
 // t0, t1, t3, t4 and so lie in 16 different blocks (16 different bank groups), and the 4
@@ -367,6 +414,7 @@ __device__ __forceinline__ int kv_tok(int j, int r) {
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glob_void;
 
 // Eight bf16 of one column of a row-major tile: two transposing reads.  In each 16-lane
 // group, ds_read_b64_tr_b16 hands lane i element i of the 4 rows addressed by lanes
@@ -378,7 +426,39 @@ __device__ __forceinline__ bf16x8 lds_read_tr2(const char* p0, const char* p1) {
   return __builtin_bit_cast(bf16x8, ab);
 }
 
-template <int G>
+// Gathers of one tile's rows into LDS (16 bytes per lane, one 4-row block per load).  NARROW:
+// the pool is read as a structured buffer (record = slot, so a gathered row costs no address
+// arithmetic and a slot past the pool reads zero); its 32-bit offsets reach 2 GiB of pool.
+// Otherwise 64-bit addresses (slot * slot bytes), a slot past the pool clamped to the last.
+template <bool NARROW>
+struct PoolGather {
+  const uint8_t *kcol, *vcol;   // pool + this lane's byte column
+  __amdgpu_buffer_rsrc_t kp, vp;
+  uint32_t slot_bytes, max_slot;
+  int col;
+  __device__ __forceinline__ PoolGather(const uint8_t* kpool, const uint8_t* vpool, int hkv, int num_slots, int col_)
+      : kcol(kpool + col_), vcol(vpool + col_), slot_bytes((uint32_t)(hkv * 2 * kD)),
+        max_slot((uint32_t)(num_slots - 1)), col(col_) {
+    if constexpr (NARROW) {
+      kp = __builtin_amdgcn_make_buffer_rsrc((void*)kpool, (short)(hkv * 2 * kD), num_slots, kBufWord3);
+      vp = __builtin_amdgcn_make_buffer_rsrc((void*)vpool, (short)(hkv * 2 * kD), num_slots, kBufWord3);
+    }
+  }
+  __device__ __forceinline__ void operator()(uint32_t slot, char* kd, char* vd) const {
+    if constexpr (NARROW) {
+      __builtin_amdgcn_struct_ptr_buffer_load_lds(kp, (lds_void*)kd, 16, (int)slot, col, 0, 0, 0);
+      __builtin_amdgcn_struct_ptr_buffer_load_lds(vp, (lds_void*)vd, 16, (int)slot, col, 0, 0, 0);
+    } else {
+      const uint64_t off = (uint64_t)min(slot, max_slot) * slot_bytes;
+      __builtin_amdgcn_global_load_lds((glob_void*)(kcol + off), (lds_void*)kd, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((glob_void*)(vcol + off), (lds_void*)vd, 16, 0, 0);
+    }
+  }
+};
+// pools up to this size are gathered through buffer offsets
+constexpr int64_t kNarrowPoolBytes = (int64_t)1 << 31;
+
+template <int G, bool NARROW>
 __global__ __launch_bounds__(256, 2) void extend_dma(const bf16* __restrict__ q, bf16* __restrict__ o,
                                                      const uint8_t* __restrict__ kpool,
                                                      const uint8_t* __restrict__ vpool,
@@ -403,8 +483,6 @@ __global__ __launch_bounds__(256, 2) void extend_dma(const bf16* __restrict__ q,
   const int ctx = p + j0 + nq;
   const int hq = hkv * G;
   const int64_t qrow0 = (int64_t)qo_indptr[req] + j0;
-  const __amdgpu_buffer_rsrc_t kp = pool_rsrc(kpool, hkv * 2 * kD, num_slots);
-  const __amdgpu_buffer_rsrc_t vp = pool_rsrc(vpool, hkv * 2 * kD, num_slots);
   const __amdgpu_buffer_rsrc_t tab = table_rsrc(r2t, table_bytes);
   const int row_bytes = (int)((int64_t)req * stride * 4);
 
@@ -418,14 +496,10 @@ __global__ __launch_bounds__(256, 2) void extend_dma(const bf16* __restrict__ q,
     sl[0] = buf_load_raw_x2(tab, row_bytes + 4 * (kv0 + tok0), 0, 0);
     sl[1] = buf_load_raw_x2(tab, row_bytes + 4 * (kv0 + tok0 + 16), 0, 0);
   };
+  const PoolGather<NARROW> gather(kpool, vpool, hkv, num_slots, col);
   auto stage = [&](char* kd, char* vd, const u32x2* sl) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int j = 4 * wave + i;
-      const int slot = (int)sl[i & 1][i >> 1];
-      __builtin_amdgcn_struct_ptr_buffer_load_lds(kp, (lds_void*)(kd + kBlk * j), 16, slot, col, 0, 0, 0);
-      __builtin_amdgcn_struct_ptr_buffer_load_lds(vp, (lds_void*)(vd + kBlk * j), 16, slot, col, 0, 0, 0);
-    }
+    for (int i = 0; i < 4; ++i) gather(sl[i & 1][i >> 1], kd + kBlk * (4 * wave + i), vd + kBlk * (4 * wave + i));
   };
 
   WaveAttn<G> wa;
@@ -448,7 +522,7 @@ __global__ __launch_bounds__(256, 2) void extend_dma(const bf16* __restrict__ q,
   slots(0, sl);
   stage(k0s, v0s, sl);
   slots(min(1, last) * kBN, sl);
-  // this wave's buffer-to-LDS loads are complete (vmcnt(0): the table loads issued after them
+  // this wave's global-to-LDS loads are complete (vmcnt(0): the table loads issued after them
   // are waited for too); then the barrier publishes the tile to the other waves
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
@@ -515,15 +589,19 @@ struct Fp8Stage {
     const int tb = row_bytes + 4 * kv0;
     return Slots{buf_load_raw_x2(tab, tb + 8 * (tid >> 3), 0, 0), buf_load_raw_x4(tab, tb + 16 * (tid & 15), 0, 0)};
   }
-  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t kp, __amdgpu_buffer_rsrc_t vp, const Slots& sl, int g,
-                                       int tid) {
-    const int kc = g * kD + (tid & 7) * 16, vc = g * kD + (tid >> 4) * 8;
-    k0 = buf_load_rec_x4(kp, (int)sl.k[0], kc, 0, 0);
-    k1 = buf_load_rec_x4(kp, (int)sl.k[1], kc, 0, 0);
-    v0 = buf_load_rec_x2(vp, (int)sl.v[0], vc, 0, 0);
-    v1 = buf_load_rec_x2(vp, (int)sl.v[1], vc, 0, 0);
-    v2 = buf_load_rec_x2(vp, (int)sl.v[2], vc, 0, 0);
-    v3 = buf_load_rec_x2(vp, (int)sl.v[3], vc, 0, 0);
+  // K/V records by 64-bit address (a pool may exceed 4 GiB); a slot past the pool (an entry
+  // past the context) reads the last slot instead, masked later
+  __device__ __forceinline__ void load(const uint8_t* kpool, const uint8_t* vpool, uint32_t slot_bytes,
+                                       uint32_t max_slot, const Slots& sl, int g, int tid) {
+    const uint8_t* kc = kpool + g * kD + (tid & 7) * 16;
+    const uint8_t* vc = vpool + g * kD + (tid >> 4) * 8;
+    auto off = [&](uint32_t slot) { return (uint64_t)min(slot, max_slot) * slot_bytes; };
+    k0 = *(const u32x4*)(kc + off(sl.k[0]));
+    k1 = *(const u32x4*)(kc + off(sl.k[1]));
+    v0 = *(const u32x2*)(vc + off(sl.v[0]));
+    v1 = *(const u32x2*)(vc + off(sl.v[1]));
+    v2 = *(const u32x2*)(vc + off(sl.v[2]));
+    v3 = *(const u32x2*)(vc + off(sl.v[3]));
   }
   static __device__ __forceinline__ void store_k(bf16* dst, u32x4 c) {
     *(u32x4*)dst = dec4(u32x2{c[0], c[1]});
@@ -580,9 +658,8 @@ __global__ __launch_bounds__(256, 2) void extend_mfma(const bf16* __restrict__ q
   const int ctx = p + j0 + nq;
   const int hq = hkv * G;
   const int64_t qrow0 = (int64_t)qo_indptr[req] + j0;
-  const __amdgpu_buffer_rsrc_t kp = pool_rsrc(kpool, hkv * kD, num_slots);
-  const __amdgpu_buffer_rsrc_t vp = pool_rsrc(vpool, hkv * kD, num_slots);
   const __amdgpu_buffer_rsrc_t tab = table_rsrc(r2t, table_bytes);
+  const uint32_t slot_bytes = (uint32_t)(hkv * kD), max_slot = (uint32_t)(num_slots - 1);
   const int row_bytes = (int)((int64_t)req * stride * 4);
 
   WaveAttn<G> wa;
@@ -591,9 +668,9 @@ __global__ __launch_bounds__(256, 2) void extend_mfma(const bf16* __restrict__ q
 
   Fp8Stage stage;
   const int n_tiles = (ctx + kBN - 1) / kBN;
-  stage.load(kp, vp, Fp8Stage::slots(tab, row_bytes, 0, tid), g, tid);
+  stage.load(kpool, vpool, slot_bytes, max_slot, Fp8Stage::slots(tab, row_bytes, 0, tid), g, tid);
   stage.store(Ks[0], Vt[0], tid);
-  stage.load(kp, vp, Fp8Stage::slots(tab, row_bytes, min(1, n_tiles - 1) * kBN, tid), g, tid);
+  stage.load(kpool, vpool, slot_bytes, max_slot, Fp8Stage::slots(tab, row_bytes, min(1, n_tiles - 1) * kBN, tid), g, tid);
   // slot-table entries run one tile ahead of the K/V records they address
   auto nslots = Fp8Stage::slots(tab, row_bytes, min(2, n_tiles - 1) * kBN, tid);
   __syncthreads();
@@ -605,7 +682,7 @@ __global__ __launch_bounds__(256, 2) void extend_mfma(const bf16* __restrict__ q
     // Branch-free, so it interleaves with the S^T products: past the last tile the last tile
     // is fetched again (from L2) and stored to a buffer nobody reads any more.
     stage.store(Ks[(kt + 1) & 1], Vt[(kt + 1) & 1], tid);
-    stage.load(kp, vp, nslots, g, tid);
+    stage.load(kpool, vpool, slot_bytes, max_slot, nslots, g, tid);
     nslots = Fp8Stage::slots(tab, row_bytes, min(kt + 3, n_tiles - 1) * kBN, tid);
     if (active)
       wa.tile(
@@ -617,9 +694,194 @@ __global__ __launch_bounds__(256, 2) void extend_mfma(const bf16* __restrict__ q
   wa.store(o, qrow0, hq, nq, vscale[g]);
 }
 
+// ------------------------------------------------------------------------------------------
+// Shared-prefix decode: one chunk of context held in the same slots by several sequences
+// ------------------------------------------------------------------------------------------
+//
+// A decode step reads each sequence's whole context once for a single query token.  Where
+// several sequences of the batch hold a chunk of context in the same slots (a prefix the
+// radix tree shares), their newest tokens are stacked as the query rows of one extend-style
+// workgroup: the chunk's K/V tiles are staged once and multiplied against up to 128 query
+// rows with MFMA, instead of being gathered once per sequence by the split phase.  An item
+// (host plan) is (first member, member count <= 128 / G, chunk s); one workgroup per (item,
+// kv head), blockIdx.x = item * hkv + g; the chunk's slots are read from the first member's
+// row.  The output is the split phase's partial for chunk s of every member, which the
+// reduce then merges with the other chunks.  Same tile pipeline as extend_dma / extend_mfma.
+
+template <int G, bool NARROW>
+__global__ __launch_bounds__(256, 2) void decode_shared_dma(const bf16* __restrict__ q,
+                                                            const uint8_t* __restrict__ kpool,
+                                                            const uint8_t* __restrict__ vpool,
+                                                            const int32_t* __restrict__ r2t, int64_t stride,
+                                                            const int32_t* __restrict__ members,
+                                                            const int32_t* __restrict__ items, int chunk,
+                                                            int max_splits, int hkv, float scale_log2, int num_slots,
+                                                            int table_bytes, int batch, float* __restrict__ ws_ml,
+                                                            float* __restrict__ ws_acc) {
+  __shared__ __attribute__((aligned(16))) char k0s[kTileBytes], v0s[kTileBytes], k1s[kTileBytes], v1s[kTileBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ln = lane & 15, lg = lane >> 4;
+  const int g = blockIdx.x % hkv;
+  const int it = blockIdx.x / hkv;
+  const int m0 = items[3 * it], nm = items[3 * it + 1], s = items[3 * it + 2];
+  // an item outside the batch or the workspace is ignored (the whole workgroup leaves)
+  if (m0 < 0 || nm <= 0 || nm > WaveAttn<G>::BT || m0 > batch - nm || s < 0 || s >= max_splits) return;
+  const int hq = hkv * G;
+  const __amdgpu_buffer_rsrc_t tab = table_rsrc(r2t, table_bytes);
+  const int row_bytes = (int)((int64_t)members[m0] * stride * 4);
+  const int kv_begin = s * chunk;
+
+  const int tok0 = kv_tok(4 * wave, lg);
+  const int col = g * kD * 2 + 16 * ln;
+  auto slots = [&](int kv0, u32x2* sl) {
+    sl[0] = buf_load_raw_x2(tab, row_bytes + 4 * (kv0 + tok0), 0, 0);
+    sl[1] = buf_load_raw_x2(tab, row_bytes + 4 * (kv0 + tok0 + 16), 0, 0);
+  };
+  const PoolGather<NARROW> gather(kpool, vpool, hkv, num_slots, col);
+  auto stage = [&](char* kd, char* vd, const u32x2* sl) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) gather(sl[i & 1][i >> 1], kd + kBlk * (4 * wave + i), vd + kBlk * (4 * wave + i));
+  };
+
+  WaveAttn<G> wa;
+  wa.init_shared(q, members, m0, nm, batch, hq, g, wave, lane, scale_log2);
+  const bool active = G != 1 || 32 * wave < nm;
+  int kb[4], vb[2][2];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) kb[mb] = kv_off(sigma(mb, ln)) + 16 * lg;
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) vb[kk][h] = kv_off(32 * kk + 8 * lg + 4 * h + (ln >> 2)) + 8 * (ln & 3);
+
+  const int n_tiles = chunk / kBN;
+  const int last = n_tiles - 1;
+  u32x2 sl[2];
+  slots(kv_begin, sl);
+  stage(k0s, v0s, sl);
+  slots(kv_begin + min(1, last) * kBN, sl);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+  auto step = [&](int kt, const char* K, const char* V, char* Kn, char* Vn) {
+    stage(Kn, Vn, sl);
+    slots(kv_begin + min(kt + 2, last) * kBN, sl);
+    if (active)
+      wa.tile(
+          kv_begin + kt * kBN, [&](int mb, int ks) { return *(const bf16x8*)(K + kb[mb] + 64 * ks); },
+          [&](int kk, int db) { return lds_read_tr2(V + vb[kk][0] + 32 * db, V + vb[kk][1] + 32 * db); });
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+  };
+  int kt = 0;
+  for (; kt + 1 < n_tiles; kt += 2) {
+    step(kt, k0s, v0s, k1s, v1s);
+    step(kt + 1, k1s, v1s, k0s, v0s);
+  }
+  if (kt < n_tiles) step(kt, k0s, v0s, k1s, v1s);
+
+  wa.store_partial(ws_ml, ws_acc, members, m0, nm, hq, max_splits, s, 1.f);
+}
+
+template <int G>
+__global__ __launch_bounds__(256, 2) void decode_shared_fp8(const bf16* __restrict__ q,
+                                                            const uint8_t* __restrict__ kpool,
+                                                            const uint8_t* __restrict__ vpool,
+                                                            const float* __restrict__ kscale,
+                                                            const float* __restrict__ vscale,
+                                                            const int32_t* __restrict__ r2t, int64_t stride,
+                                                            const int32_t* __restrict__ members,
+                                                            const int32_t* __restrict__ items, int chunk,
+                                                            int max_splits, int hkv, float scale_log2, int num_slots,
+                                                            int table_bytes, int batch, float* __restrict__ ws_ml,
+                                                            float* __restrict__ ws_acc) {
+  __shared__ __attribute__((aligned(16))) bf16 Ks[2][kBN * kKStride];
+  __shared__ __attribute__((aligned(16))) bf16 Vt[2][kD * kVStride];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int ln = lane & 15, lg = lane >> 4;
+  const int g = blockIdx.x % hkv;
+  const int it = blockIdx.x / hkv;
+  const int m0 = items[3 * it], nm = items[3 * it + 1], s = items[3 * it + 2];
+  // an item outside the batch or the workspace is ignored (the whole workgroup leaves)
+  if (m0 < 0 || nm <= 0 || nm > WaveAttn<G>::BT || m0 > batch - nm || s < 0 || s >= max_splits) return;
+  const int hq = hkv * G;
+  const __amdgpu_buffer_rsrc_t tab = table_rsrc(r2t, table_bytes);
+  const uint32_t slot_bytes = (uint32_t)(hkv * kD), max_slot = (uint32_t)(num_slots - 1);
+  const int row_bytes = (int)((int64_t)members[m0] * stride * 4);
+  const int kv_begin = s * chunk;
+
+  WaveAttn<G> wa;
+  wa.init_shared(q, members, m0, nm, batch, hq, g, wave, lane, scale_log2 * kscale[g]);
+  const bool active = G != 1 || 32 * wave < nm;
+
+  Fp8Stage stage;
+  const int n_tiles = chunk / kBN;
+  stage.load(kpool, vpool, slot_bytes, max_slot, Fp8Stage::slots(tab, row_bytes, kv_begin, tid), g, tid);
+  stage.store(Ks[0], Vt[0], tid);
+  stage.load(kpool, vpool, slot_bytes, max_slot, Fp8Stage::slots(tab, row_bytes, kv_begin + min(1, n_tiles - 1) * kBN, tid), g, tid);
+  auto nslots = Fp8Stage::slots(tab, row_bytes, kv_begin + min(2, n_tiles - 1) * kBN, tid);
+  __syncthreads();
+  for (int kt = 0; kt < n_tiles; ++kt) {
+    const bf16* K = Ks[kt & 1];
+    const bf16* V = Vt[kt & 1];
+    stage.store(Ks[(kt + 1) & 1], Vt[(kt + 1) & 1], tid);
+    stage.load(kpool, vpool, slot_bytes, max_slot, nslots, g, tid);
+    nslots = Fp8Stage::slots(tab, row_bytes, kv_begin + min(kt + 3, n_tiles - 1) * kBN, tid);
+    if (active)
+      wa.tile(
+          kv_begin + kt * kBN,
+          [&](int mb, int ks) { return *(const bf16x8*)(K + krow(sigma(mb, ln)) * kKStride + 32 * ks + 8 * lg); },
+          [&](int kk, int db) { return *(const bf16x8*)(V + (16 * db + ln) * kVStride + 32 * kk + 8 * lg); });
+    __syncthreads();
+  }
+  wa.store_partial(ws_ml, ws_acc, members, m0, nm, hq, max_splits, s, vscale[g]);
+}
+
 int mfma_tile(int G) { return kRows / G; }
 
 }  // namespace
+
+int launch_decode_shared(const void* q, int32_t pool_dtype, const void* k_pool, const void* v_pool,
+                         const float* k_scale, const float* v_scale, int64_t num_slots, const int32_t* r2t,
+                         int64_t stride, int32_t batch, const int32_t* members, const int32_t* items, int64_t n_items,
+                         int chunk, int max_splits, int hq, int hkv, float sc_log2, float* ws_ml, float* ws_acc,
+                         hipStream_t st) {
+  const int G = hq / hkv;
+  const int64_t slot_bytes = (int64_t)hkv * (pool_dtype == PKV_FP8_E4M3 ? 128 : 256);
+  const int64_t table_bytes = (int64_t)batch * stride * 4;
+  if (slot_bytes > 16383) return fail(PKV_ERR_UNSUPPORTED, "decode: a slot of %lld bytes is too wide", (long long)slot_bytes);
+  if (table_bytes > 0x7FFFFFFFLL || num_slots > 0x7FFFFFFFLL)
+    return fail(PKV_ERR_UNSUPPORTED, "decode: slot table or pool too large for 32-bit buffer offsets");
+  if (n_items * hkv > 0x7FFFFFFFLL) return fail(PKV_ERR_INVAL, "decode: too many shared items");
+  const dim3 grid((unsigned)(n_items * hkv));
+  const bool narrow = num_slots * slot_bytes <= kNarrowPoolBytes;
+#define PKV_SHARED_CASE(GG)                                                                                      \
+  if (G == GG) {                                                                                                 \
+    if (pool_dtype == PKV_BF16 && narrow)                                                                        \
+      hipLaunchKernelGGL((decode_shared_dma<GG, true>), grid, dim3(256), 0, st, (const bf16*)q,                 \
+                         (const uint8_t*)k_pool, (const uint8_t*)v_pool, r2t, stride, members, items, chunk,     \
+                         max_splits, hkv, sc_log2, (int)num_slots, (int)table_bytes, batch, ws_ml, ws_acc);      \
+    else if (pool_dtype == PKV_BF16)                                                                             \
+      hipLaunchKernelGGL((decode_shared_dma<GG, false>), grid, dim3(256), 0, st, (const bf16*)q,                \
+                         (const uint8_t*)k_pool, (const uint8_t*)v_pool, r2t, stride, members, items, chunk,     \
+                         max_splits, hkv, sc_log2, (int)num_slots, (int)table_bytes, batch, ws_ml, ws_acc);      \
+    else                                                                                                         \
+      hipLaunchKernelGGL((decode_shared_fp8<GG>), grid, dim3(256), 0, st, (const bf16*)q, (const uint8_t*)k_pool, \
+                         (const uint8_t*)v_pool, k_scale, v_scale, r2t, stride, members, items, chunk,           \
+                         max_splits, hkv, sc_log2, (int)num_slots, (int)table_bytes, batch, ws_ml, ws_acc);      \
+    return hip_check(hipGetLastError(), "decode_shared launch");                                                 \
+  }
+  PKV_SHARED_CASE(1)
+  PKV_SHARED_CASE(2)
+  PKV_SHARED_CASE(4)
+  PKV_SHARED_CASE(8)
+#undef PKV_SHARED_CASE
+  return fail(PKV_ERR_UNSUPPORTED, "decode: no shared-prefix kernel for group %d", G);
+}
+
 }  // namespace pkv
 
 using namespace pkv;
@@ -719,11 +981,17 @@ extern "C" int pkv_extend_attention(const void* q, void* o, int32_t qo_dtype, co
                        prefix_lens, extend_lens, qo_indptr, work, hkv, sc, (int)num_slots, (int)table_bytes);     \
     return hip_check(hipGetLastError(), "extend_mfma launch");                                                   \
   }
+  const bool narrow = num_slots * slot_bytes <= kNarrowPoolBytes;
 #define PKV_EXTEND_DMA(GG)                                                                                       \
   if (pool_dtype == PKV_BF16 && G == GG) {                                                                       \
-    hipLaunchKernelGGL((extend_dma<GG>), grid, dim3(256), 0, st, (const bf16*)q, (bf16*)o, (const uint8_t*)k_pool, \
-                       (const uint8_t*)v_pool, req_to_token, stride, prefix_lens, extend_lens, qo_indptr, work, hkv, sc, \
-                       (int)num_slots, (int)table_bytes);                                                        \
+    if (narrow)                                                                                                  \
+      hipLaunchKernelGGL((extend_dma<GG, true>), grid, dim3(256), 0, st, (const bf16*)q, (bf16*)o,               \
+                         (const uint8_t*)k_pool, (const uint8_t*)v_pool, req_to_token, stride, prefix_lens,      \
+                         extend_lens, qo_indptr, work, hkv, sc, (int)num_slots, (int)table_bytes);               \
+    else                                                                                                         \
+      hipLaunchKernelGGL((extend_dma<GG, false>), grid, dim3(256), 0, st, (const bf16*)q, (bf16*)o,              \
+                         (const uint8_t*)k_pool, (const uint8_t*)v_pool, req_to_token, stride, prefix_lens,      \
+                         extend_lens, qo_indptr, work, hkv, sc, (int)num_slots, (int)table_bytes);               \
     return hip_check(hipGetLastError(), "extend_dma launch");                                                    \
   }
   PKV_EXTEND_DMA(1)

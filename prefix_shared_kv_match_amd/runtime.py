@@ -19,7 +19,8 @@ from typing import List, Optional, Sequence
 
 import numpy as np
 
-from . import (PKV_BF16, PKV_F32, PKV_FP8_E4M3, pkv_decode_attention, pkv_decode_chunk, rt_set_eviction_log,
+from . import (PKV_BF16, PKV_F32, PKV_FP8_E4M3, pkv_decode_attention, pkv_decode_attention_shared,
+               pkv_decode_chunk, pkv_decode_shared_plan, pkv_decode_shared_rows, rt_set_eviction_log,
                pkv_decode_workspace_bytes, pkv_extend_attention, pkv_extend_plan, pkv_extend_tile, pkv_kv_scatter,
                rt_create, rt_create_policy, rt_dec_lock_ref, rt_decode_step, rt_destroy, rt_finish, rt_peek_prefix,
                rt_prepare_extend, rt_prepare_extend_prio, rt_release, rt_schedule_longest_prefix)
@@ -77,18 +78,21 @@ def prepare(tree, token_lists, stride: int, r2t: Optional[np.ndarray] = None) ->
 class StagedUpload:
     """Host -> device upload of int32 tables without stalling the launch stream.
 
-    Two pinned host buffers and two device buffers alternate.  send() copies the current
-    pair on a side stream (default priority) and makes the caller's current stream wait for
-    that copy, so the copy runs while earlier kernels still execute instead of between them.
-    Reuse is safe because the copy into a device buffer first waits for a marker recorded on
-    the current stream at the previous send(): everything launched before that call, which
-    includes every reader of the buffer's previous contents when readers are launched before
-    the next send(), has finished.  host() waits for the last copy out of the host buffer."""
+    Two pinned host buffers and two device buffers alternate.  With side=True, send() copies
+    the current pair on a side stream (default priority) and makes the caller's current
+    stream wait for that copy, so a large copy runs while earlier kernels still execute
+    instead of between them.  Reuse is safe because the copy into a device buffer first waits
+    for a marker recorded on the current stream at the previous send(): everything launched
+    before that call, which includes every reader of the buffer's previous contents when
+    readers are launched before the next send(), has finished.  With side=False (small
+    tables, where the side stream's host cost outweighs the copy) the copy goes on the
+    current stream, which orders it after those readers by itself.  host() waits for the last
+    copy out of the host buffer."""
 
-    def __init__(self, torch, device):
+    def __init__(self, torch, device, side: bool = True):
         self.torch = torch
         self.device = device
-        self.stream = torch.cuda.Stream(device=device)
+        self.stream = torch.cuda.Stream(device=device) if side else None
         self.bufs = [dict(host=None, np=None, dev=None, copied=torch.cuda.Event()) for _ in range(2)]
         self.marks = [torch.cuda.Event(), torch.cuda.Event()]
         self.i = 0
@@ -120,18 +124,23 @@ class StagedUpload:
         if b["host"] is None or b["host"].numel() < total:
             raise ValueError("send() without a large enough host() buffer")
         main = torch.cuda.current_stream(self.device)
-        mark = self.marks[self.seq & 1]
-        prev = self.marks[(self.seq & 1) ^ 1]
-        mark.record(main)                  # all work launched so far on the current stream
         if b["dev"] is None or b["dev"].numel() < total:
             b["dev"] = torch.empty(max(total * 2, 64), dtype=torch.int32, device=self.device)
-            b["dev"].record_stream(self.stream)
-        if self.seq > 0:
-            self.stream.wait_event(prev)   # readers of this device buffer's previous contents are done
-        with torch.cuda.stream(self.stream):
+            if self.stream is not None:
+                b["dev"].record_stream(self.stream)
+        if self.stream is None:
             b["dev"][:total].copy_(b["host"][:total], non_blocking=True)
-            b["copied"].record(self.stream)
-        main.wait_event(b["copied"])
+            b["copied"].record(main)
+        else:
+            mark = self.marks[self.seq & 1]
+            prev = self.marks[(self.seq & 1) ^ 1]
+            mark.record(main)                  # all work launched so far on the current stream
+            if self.seq > 0:
+                self.stream.wait_event(prev)   # readers of this device buffer's previous contents are done
+            with torch.cuda.stream(self.stream):
+                b["dev"][:total].copy_(b["host"][:total], non_blocking=True)
+                b["copied"].record(self.stream)
+            main.wait_event(b["copied"])
         self.i ^= 1
         self.seq += 1
         return b["dev"][:total]
@@ -175,10 +184,10 @@ class Engine:
     def to_dev(self, a: np.ndarray):
         return self.torch.from_numpy(np.ascontiguousarray(a)).to(self.device, non_blocking=False)
 
-    def _uploader(self, name: str) -> "StagedUpload":
+    def _uploader(self, name: str, side: bool = True) -> "StagedUpload":
         up = getattr(self, name, None)
         if up is None:
-            up = StagedUpload(self.torch, self.device)
+            up = StagedUpload(self.torch, self.device, side)
             setattr(self, name, up)
         return up
 
@@ -230,7 +239,7 @@ class Engine:
         through a staged upload of their own; valid for work launched on the current stream
         until the next call."""
         n = int(slots.size)
-        up = self._uploader("_decode_up")
+        up = self._uploader("_decode_up", side=False)
         hn = up.host(2 * n)
         hn[:n] = slots
         hn[n:2 * n] = seq_lens
@@ -265,11 +274,43 @@ class Engine:
         nbytes = pkv_decode_workspace_bytes(batch, self.hq, self.d, max_seq_len, chunk)
         return self.torch.empty(nbytes // 4 + 1, dtype=self.torch.float32, device=self.device), chunk
 
-    def decode(self, q, r2t_dev, seq_lens_dev, max_seq_len: int, workspace, chunk: int, o=None):
+    def decode_plan(self, req_to_token: np.ndarray, seq_lens: np.ndarray, chunk: int):
+        """The shared-prefix plan of a decode batch (host slot rows and current lengths) on the
+        device: a dict of int32 views (members, skip, items) valid for work launched before the
+        next call, or None when no chunk is shared or the shape has no shared-prefix kernel.
+        Computed once, it serves every later decode step of the same sequences (new tokens are
+        private, so the shared chunks do not change)."""
+        rows = pkv_decode_shared_rows(self.qo_code, self.pool_code, self.hq, self.hkv, self.d)
+        if rows <= 0:
+            return None
+        # the rows come from this engine's tree (its locks keep them), so each chunk's last
+        # slot decides whether two rows share it
+        members, skip, items = pkv_decode_shared_plan(req_to_token, seq_lens, chunk, rows, rows_from_tree=True)
+        if items.shape[0] == 0:
+            return None
+        b, n = members.size, items.size
+        up = self._uploader("_plan_up", side=False)
+        hn = up.host(2 * b + n)
+        hn[:b] = members
+        hn[b:2 * b] = skip
+        hn[2 * b:2 * b + n] = items.reshape(-1)
+        dev = up.send(2 * b + n)
+        return dict(members=dev[:b], skip=dev[b:2 * b], items=dev[2 * b:2 * b + n].view(-1, 3), chunk=int(chunk))
+
+    def decode(self, q, r2t_dev, seq_lens_dev, max_seq_len: int, workspace, chunk: int, o=None, plan=None):
+        """One decode step; with a plan from decode_plan (same chunk), the shared chunks are
+        read once per group of sequences."""
         if o is None:
             o = self.torch.empty_like(q)
-        pkv_decode_attention(q, o, self.k_pool, self.v_pool, r2t_dev, seq_lens_dev, max_seq_len, self.sm_scale,
-                             workspace, chunk, self.k_scale, self.v_scale)
+        if plan is not None:
+            if plan["chunk"] != chunk:
+                raise ValueError("decode: the plan was made for another chunk")
+            pkv_decode_attention_shared(q, o, self.k_pool, self.v_pool, r2t_dev, seq_lens_dev, max_seq_len,
+                                        self.sm_scale, workspace, chunk, plan["members"], plan["skip"], plan["items"],
+                                        self.k_scale, self.v_scale)
+        else:
+            pkv_decode_attention(q, o, self.k_pool, self.v_pool, r2t_dev, seq_lens_dev, max_seq_len, self.sm_scale,
+                                 workspace, chunk, self.k_scale, self.v_scale)
         return o
 
     def finish(self, hb: HostBatch, full_token_lists, prompt_lens):

@@ -74,6 +74,8 @@ class Run:
         self.check_pool = check_pool
         self.req_stride = req_stride      # check every req_stride-th request of a batch
         self.stats: List[Dict] = []
+        self.plan = None
+        self.shared_items = 0
         self.oracle_log = od.run_workload_host(wl) if oracle_host else None
 
     def scatter(self, slots: np.ndarray, rows: np.ndarray):
@@ -174,14 +176,24 @@ class Run:
             r2t = torch.from_numpy(np.ascontiguousarray(hb.req_to_token)).to(self.dev)
             sl = torch.from_numpy(hb.seq_lens.copy()).to(self.dev)
             o = eng.decode(q, r2t, sl, max_len, ws, chunk)
+            # the shared-prefix decode too, with the plan made at the first step (it stays valid
+            # as the sequences grow), wherever the batch shares whole chunks
+            if s == 0:
+                self.plan = eng.decode_plan(hb.req_to_token, hb.seq_lens, chunk)
+                if self.plan is not None:
+                    self.shared_items = int(self.plan["items"].shape[0])
+            outs = [("plain", o)]
+            if self.plan is not None:
+                outs.append(("shared", eng.decode(q, r2t, sl, max_len, ws, chunk, plan=self.plan)))
             torch.cuda.synchronize()
             if decode_sample is None or s == steps - 1 or s % max(1, steps // 2) == 0:
                 seqs = range(B) if decode_sample is None else \
                     sorted(self.rng.choice(B, size=min(B, decode_sample), replace=False).tolist())
-                got = o.float().cpu().numpy()
                 ref = np.stack([oa.decode_row(wl, np.array(rows[i])) for i in seqs])
-                st = compare(got[list(seqs)], ref, wl.shape.qo_dtype, f"decode step {s}")
-                st.update(kind="decode", step=s)
-                self.stats.append(st)
+                for how, out in outs:
+                    got = out.float().cpu().numpy()
+                    st = compare(got[list(seqs)], ref, wl.shape.qo_dtype, f"decode step {s} ({how})")
+                    st.update(kind="decode", step=s, path=how)
+                    self.stats.append(st)
         full = [np.concatenate([r.tokens, wl.decode_tokens[:, i]]) for i, r in enumerate(wl.batches[-1])]
         eng.finish(hb, full, [len(r.tokens) for r in wl.batches[-1]])

@@ -1,0 +1,135 @@
+"""The shared-prefix decode plan (pkv_decode_shared_plan) on the CPU, against brute force over
+pairs of slot rows: members is a permutation, every item's members hold its chunk whole and
+slot for slot equal, each sequence's chunks 0 .. skip-1 are covered exactly once, and the
+plan is maximal (two sequences that agree on chunks 0..k, whole in both contexts, both share
+chunk k).  On rows built the way the radix tree builds them, the last-slot shortcut
+(rows_from_tree) gives the same plan."""
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+import prefix_shared_kv_match_amd as pkv
+
+
+def rows_from_paths(rng, paths, lens, chunk, stride):
+    """Slot rows of sequences that follow paths in a tree of chunks: equal path prefixes give
+    equal slots (as the radix tree hands them out), the rest is private."""
+    r2t = np.full((len(paths), stride), -1, dtype=np.int32)
+    node_slots = {}
+    nxt = 0
+    for b, (path, L) in enumerate(zip(paths, lens)):
+        for k in range((L + chunk - 1) // chunk):
+            key = tuple(path[:k + 1]) if k < len(path) else ("private", b, k)
+            if key not in node_slots:
+                node_slots[key] = np.arange(nxt, nxt + chunk, dtype=np.int32)
+                nxt += chunk
+            hi = min(L, (k + 1) * chunk)
+            r2t[b, k * chunk:hi] = node_slots[key][:hi - k * chunk]
+    perm = rng.permutation(nxt).astype(np.int32)        # slots are not in any particular order
+    return np.where(r2t >= 0, perm[np.maximum(r2t, 0)], -1).astype(np.int32)
+
+
+def check_plan(r2t, lens, chunk, rows, members, skip, items):
+    b = len(lens)
+    assert sorted(members.tolist()) == list(range(b))
+    full = [L // chunk for L in lens]
+    covered = {i: [] for i in range(b)}
+    for m0, nm, k in items.tolist():
+        assert 1 <= nm <= rows and 0 <= m0 and m0 + nm <= b
+        mem = members[m0:m0 + nm].tolist()
+        for i in mem:
+            assert full[i] > k
+            covered[i].append(k)
+        for i in mem[1:]:
+            assert np.array_equal(r2t[i, :(k + 1) * chunk], r2t[mem[0], :(k + 1) * chunk])
+    for i in range(b):
+        assert sorted(covered[i]) == list(range(skip[i])), (i, covered[i], skip[i])
+    # every chunk listed for a sequence is shared with another one: jobs have >= 2 members
+    job_sizes = {}
+    for m0, nm, k in items.tolist():
+        job_sizes.setdefault((k, tuple(r2t[members[m0], :(k + 1) * chunk])), 0)
+        job_sizes[(k, tuple(r2t[members[m0], :(k + 1) * chunk]))] += nm
+    assert all(v >= 2 for v in job_sizes.values())
+    # maximal: agreement on chunks 0..k (whole in both) means both cover chunk k
+    for i in range(b):
+        for j in range(i + 1, b):
+            k = 0
+            while k < min(full[i], full[j]) and np.array_equal(r2t[i, k * chunk:(k + 1) * chunk],
+                                                               r2t[j, k * chunk:(k + 1) * chunk]):
+                k += 1
+            assert skip[i] >= k and skip[j] >= k, (i, j, k, skip[i], skip[j])
+
+
+def test_fewshot_like_one_group():
+    rng = np.random.default_rng(0)
+    chunk, stride = 64, 640
+    lens = [int(x) for x in rng.integers(450, 640, size=20)]
+    paths = [[0, 1, 2, 3, 4, 5] for _ in lens]            # a 384-token common prefix (6 chunks)
+    r2t = rows_from_paths(rng, paths, lens, chunk, stride)
+    members, skip, items = pkv.pkv_decode_shared_plan(r2t, lens, chunk, 8)
+    check_plan(r2t, lens, chunk, 8, members, skip, items)
+    assert skip.tolist() == [6] * 20
+    assert len(items) == 6 * 3                            # 20 members in items of <= 8
+    assert items[:3, 2].tolist() == [0, 0, 0] and items[:3, 1].tolist() == [8, 8, 4]
+
+
+def test_tree_shaped_sharing_and_singletons():
+    rng = np.random.default_rng(1)
+    chunk, stride = 64, 512
+    paths = [[0, 1, 2], [0, 1, 3], [0, 4], [0, 4], [5], [0, 1, 2], [6, 7]]
+    lens = [300, 300, 250, 130, 200, 190, 500]
+    r2t = rows_from_paths(rng, paths, lens, chunk, stride)
+    members, skip, items = pkv.pkv_decode_shared_plan(r2t, lens, chunk, 16)
+    check_plan(r2t, lens, chunk, 16, members, skip, items)
+    # 0 and 5 share 3 chunks but 5 holds only 2 whole (190 tokens); 0, 1 share 2; 2, 3 share 2
+    # (3 holds 2 whole); chunk 0 is shared by 0, 1, 2, 3, 5
+    assert skip.tolist() == [2, 2, 2, 2, 0, 2, 0]
+
+
+def test_no_sharing_and_short_contexts():
+    rng = np.random.default_rng(2)
+    lens = [1, 63, 64, 65, 200]
+    r2t = rows_from_paths(rng, [[i] for i in range(5)], lens, 64, 256)
+    members, skip, items = pkv.pkv_decode_shared_plan(r2t, lens, 64, 32)
+    assert len(items) == 0 and skip.tolist() == [0] * 5
+    members, skip, items = pkv.pkv_decode_shared_plan(r2t[:0], [], 64, 32)
+    assert len(items) == 0 and members.size == 0
+
+
+def test_same_first_slot_different_chunk_does_not_share():
+    """Rows that agree on a chunk's first slot but not on the rest of it (not something the tree
+    produces) are not grouped."""
+    r2t = np.arange(4 * 128, dtype=np.int32).reshape(4, 128)
+    r2t[1] = r2t[0]
+    r2t[1, 5] = 999
+    r2t[2] = r2t[0]
+    lens = [128, 128, 128, 100]
+    members, skip, items = pkv.pkv_decode_shared_plan(r2t, lens, 64, 32)
+    check_plan(r2t, lens, 64, 32, members, skip, items)
+    assert skip.tolist() == [2, 0, 2, 0]
+
+
+def test_rejects_bad_arguments():
+    r2t = np.zeros((2, 128), dtype=np.int32)
+    with pytest.raises(pkv.PkvError):
+        pkv.pkv_decode_shared_plan(r2t, [10, 10], 100, 8)      # chunk not a multiple of 64
+    with pytest.raises(pkv.PkvError):
+        pkv.pkv_decode_shared_plan(r2t, [10, 129], 64, 8)      # longer than the row
+    with pytest.raises(pkv.PkvError):
+        pkv.pkv_decode_shared_plan(r2t, [0, 10], 64, 8)        # empty sequence
+
+
+@settings(max_examples=150, deadline=None)
+@given(seed=st.integers(0, 10_000), n=st.integers(1, 24), depth=st.integers(1, 6), branch=st.integers(1, 3),
+       rows=st.sampled_from([1, 2, 16, 128]))
+def test_random_trees_against_brute_force(seed, n, depth, branch, rows):
+    rng = np.random.default_rng(seed)
+    chunk, stride = 64, 64 * 8
+    paths = [[int(x) for x in rng.integers(0, branch, size=depth)] for _ in range(n)]
+    lens = [int(x) for x in rng.integers(1, stride + 1, size=n)]
+    r2t = rows_from_paths(rng, paths, lens, chunk, stride)
+    members, skip, items = pkv.pkv_decode_shared_plan(r2t, lens, chunk, rows)
+    check_plan(r2t, lens, chunk, rows, members, skip, items)
+    # rows built like the tree builds them: the last-slot shortcut gives the same plan
+    m2, s2, i2 = pkv.pkv_decode_shared_plan(r2t, lens, chunk, rows, rows_from_tree=True)
+    assert np.array_equal(m2, members) and np.array_equal(s2, skip) and np.array_equal(i2, items)

@@ -110,7 +110,9 @@ def test_decode_small_every_row():
     log("decode small")
     wl = workloads.decode_bf16(n_seq=24, n_prefix=4, prefix_len=256, ctx_range=(300, 1500), steps=3,
                                pool_slots=60000)
-    stats = Run(wl, check_pool=True).run()
+    r = Run(wl, check_pool=True)
+    stats = r.run()
+    assert r.shared_items > 0, "the shared-prefix decode did not run"
     report("decode small", stats)
 
 
@@ -119,14 +121,18 @@ def test_decode_two_long_sequences_many_splits():
     # two sequences only: the automatic chunk drops to 128 tokens, about 110 splits each
     wl = workloads.decode_bf16(n_seq=2, n_prefix=1, prefix_len=1024, ctx_range=(12000, 15000), steps=2,
                                pool_slots=40000)
-    stats = Run(wl).run()
+    r = Run(wl)
+    stats = r.run()
+    assert r.shared_items == 8         # one item per shared 128-token chunk of the 1,024-token prefix
     report("decode two long sequences", stats)
 
 
 def test_longctx_small_every_row():
     log("longctx small")
     wl = workloads.longctx_fp8(prefix_len=2048, suffix_len=200, n_req=4, steps=3, pool_slots=8192)
-    stats = Run(wl, check_pool=True).run()
+    r = Run(wl, check_pool=True)
+    stats = r.run()
+    assert r.shared_items > 0, "the shared-prefix decode did not run"
     report("longctx small", stats)
 
 
@@ -203,6 +209,26 @@ def test_edge_cases(qo):
     report(f"edge {qo}", stats)
 
 
+@pytest.mark.parametrize("pool", ["bf16", "fp8_e4m3"])
+def test_pool_beyond_4gib_high_slots(pool):
+    """A pool of more than 4 GiB per tensor with the allocator handing out its highest slots
+    first: every gathered row lies beyond byte offset 2^32 of its pool, so the gathers must
+    address it with 64-bit arithmetic (extend, decode and the shared-prefix decode)."""
+    log(f"pool beyond 4 GiB ({pool})")
+    if pool == "bf16":
+        wl = workloads.fewshot_bf16(n_req=6, prefix_len=300, suffix_range=(40, 200), decode_steps=2)
+    else:
+        wl = workloads.longctx_fp8(prefix_len=640, suffix_len=150, n_req=4, steps=2, pool_slots=8192)
+    row = wl.shape.hkv * wl.shape.d * (2 if pool == "bf16" else 1)
+    wl.pool_slots = (1 << 32) // row + 65536                 # 2^32 bytes and then some
+    wl.free_order = np.arange(wl.pool_slots - 1, wl.pool_slots - 1 - 40000, -1, dtype=np.int32)
+    assert int(wl.free_order.min()) * row >= 1 << 32
+    r = Run(wl, check_pool=True)
+    stats = r.run()
+    assert r.shared_items > 0
+    report(f"pool beyond 4 GiB ({pool})", stats)
+
+
 def test_decode_split_invariance_and_extend_agreement():
     """Decode over one context with several chunk sizes agrees with itself and with extend's last row."""
     log("decode split invariance")
@@ -227,6 +253,10 @@ def test_decode_split_invariance_and_extend_agreement():
     for chunk in (64, 128, 256, 1024):
         ws, _ = eng.decode_workspace(hb.n, max_len, chunk)
         outs.append(eng.decode(q, r2t, sl, max_len, ws, chunk).float().cpu().numpy())
+        plan = eng.decode_plan(hb.req_to_token, hb.seq_lens, chunk)
+        assert plan is not None or chunk > 900          # the 900-token prefix holds no whole 1,024 chunk
+        if plan is not None:
+            outs.append(eng.decode(q, r2t, sl, max_len, ws, chunk, plan=plan).float().cpu().numpy())
     for o in outs[1:]:
         assert np.abs(o - outs[0]).max() <= 2 * 2.0 ** -8 * np.abs(outs[0]).max()
     ref = np.stack([oa.decode_row(wl, x.rows) for x in reqs])
