@@ -336,7 +336,8 @@ int64_t pkv_decode_shared_plan(const int32_t* req_to_token, int64_t stride, cons
 int32_t pkv_decode_shared_rows(int32_t qo_dtype, int32_t pool_dtype, int32_t hq, int32_t hkv, int32_t d);
 /* pkv_decode_attention with a shared-prefix plan: members, skip, items are DEVICE copies of
  * pkv_decode_shared_plan's outputs (n_items of them) for the same slot rows and the same
- * (nonzero) chunk.  Items whose members or chunk fall outside the batch or the workspace are
+ * (nonzero) chunk; first_split: the smallest skip[b] (0 is always correct), the split phase
+ * launches chunks first_split and later only.  Items whose members or chunk fall outside the batch or the workspace are
  * ignored (their partials are then left unwritten, so the result is wrong but no access
  * leaves the buffers).  Same result as pkv_decode_attention up to float32 summation order;
  * n_items = 0 is pkv_decode_attention. */
@@ -345,7 +346,7 @@ int pkv_decode_attention_shared(const void* q, void* o, int32_t qo_dtype, const 
                                 const int32_t* req_to_token, int64_t stride, const int32_t* seq_lens, int32_t batch,
                                 int32_t max_seq_len, int32_t hq, int32_t hkv, int32_t d, float sm_scale, int32_t chunk,
                                 const int32_t* members, const int32_t* skip, const int32_t* items, int64_t n_items,
-                                void* workspace, size_t ws_bytes, void* stream);
+                                int32_t first_split, void* workspace, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

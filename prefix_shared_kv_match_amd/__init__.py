@@ -417,9 +417,11 @@ def pkv_decode_shared_plan(req_to_token: np.ndarray, seq_lens, chunk: int, rows:
 
 
 def pkv_decode_attention_shared(q, o, k_pool, v_pool, req_to_token, seq_lens, max_seq_len, sm_scale, workspace,
-                                chunk: int, members, skip, items, k_scale=None, v_scale=None, stream=None) -> None:
+                                chunk: int, members, skip, items, first_split: int = 0, k_scale=None, v_scale=None,
+                                stream=None) -> None:
     """pkv_decode_attention with a shared-prefix plan (device int32 members [b], skip [b],
-    items [n, 3] from pkv_decode_shared_plan for the same rows and chunk)."""
+    items [n, 3] from pkv_decode_shared_plan for the same rows and chunk; first_split = the
+    smallest skip, or 0)."""
     torch = _torch()
     b, hq, d = q.shape
     ns, hkv, d2 = k_pool.shape
@@ -433,6 +435,6 @@ def pkv_decode_attention_shared(q, o, k_pool, v_pool, req_to_token, seq_lens, ma
             _dev(v_scale, "v_scale", torch.float32), _dev(req_to_token, "req_to_token", torch.int32),
             req_to_token.shape[1], _dev(seq_lens, "seq_lens", torch.int32), b, int(max_seq_len), hq, hkv, d,
             float(sm_scale), int(chunk), _dev(members, "members", torch.int32), _dev(skip, "skip", torch.int32),
-            _dev(items, "items", torch.int32), items.shape[0], _dev(workspace, "workspace"),
+            _dev(items, "items", torch.int32), items.shape[0], int(first_split), _dev(workspace, "workspace"),
             workspace.numel() * workspace.element_size(), _stream(stream))
     check(lib().pkv_decode_attention_shared(*args))

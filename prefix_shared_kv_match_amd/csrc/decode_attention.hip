@@ -16,12 +16,20 @@
 // HBM-bound (about 4 FLOP per gathered byte for bf16 GQA-4), so no MFMA is used.
 //  - decode_split_slot (hkv 2, 4 or 8, or any multiple of 8 in groups of 8 heads, e.g.
 //    multi-head attention): one workgroup per (sequence, chunk, head group), so a token's
-//    slot row (or its 8-head part) is read at once; blockIdx.x = (b * max_splits + s) *
-//    groups + group.
-//  - decode_split (other hkv): one workgroup per (sequence, chunk, kv head); blockIdx.x =
-//    (b * max_splits + s) * hkv + g, so consecutive workgroups cycle through the kv heads.
+//    slot row (or its 8-head part) is read at once; blockIdx.x = (b * ns_odd + s - s0) *
+//    groups + group over chunks s0 .. s0 + ns - 1 (s0 > 0 when a shared-prefix pass has
+//    covered every sequence's first s0 chunks).  The chunk count per sequence is padded to an
+//    odd number (the extra workgroup leaves at once): with the XCD of a workgroup being
+//    blockIdx.x mod 8, chunk s of consecutive sequences then lands on different XCDs, and the
+//    XCDs get equal work whatever the spread of context lengths (an even count would pin a
+//    chunk index to one or a few XCDs, and only long sequences have late chunks).
+//  - decode_split (other hkv, and the short private tails left after a shared-prefix pass):
+//    one workgroup per (sequence, chunk, kv head), 16 token streams; blockIdx.x =
+//    (b * ns + s - s0) * hkv + g, so consecutive workgroups cycle through the kv heads.
 
 #include <math.h>
+
+#include <algorithm>
 
 #include "device.h"
 
@@ -114,7 +122,8 @@ __global__ __launch_bounds__(256) void decode_split(const QT* __restrict__ q, co
                                                     const int32_t* __restrict__ r2t, int64_t stride,
                                                     const int32_t* __restrict__ seq_lens, int hkv, int chunk,
                                                     int max_splits, float qk_scale_log2, float* __restrict__ ws_ml,
-                                                    float* __restrict__ ws_acc, const int32_t* __restrict__ skip) {
+                                                    float* __restrict__ ws_acc, const int32_t* __restrict__ skip,
+                                                    int s0, int ns) {
   constexpr int VEC = D / 16;
   using Chunk = RowChunk<POOL, VEC>;
   constexpr int ROWB = D * Chunk::kBytes / VEC;  // bytes of one (slot, head) row
@@ -123,8 +132,8 @@ __global__ __launch_bounds__(256) void decode_split(const QT* __restrict__ q, co
 
   const int g = blockIdx.x % hkv;
   const int rest = blockIdx.x / hkv;
-  const int s = rest % max_splits;
-  const int b = rest / max_splits;
+  const int s = s0 + rest % ns;
+  const int b = rest / ns;
   const int L = seq_lens[b];
   const int t0 = s * chunk;
   if (t0 >= L) return;  // the whole workgroup leaves together
@@ -260,7 +269,8 @@ __global__ __launch_bounds__(256) void decode_split(const QT* __restrict__ q, co
 // fetched by different workgroups at different times.  Each stream keeps the next group of
 // kUnroll tokens in flight (two register buffers) while it consumes the current one; with a
 // bf16 pool the q.k products are packed bf16 dot products.  Streams of one head are merged
-// in LDS at the end.  blockIdx.x = b * max_splits + s.
+// in LDS at the end.  blockIdx.x = (b * ns_odd + s - s0) * groups + group (chunks s0 .. s0 + ns - 1,
+// ns_odd = ns rounded up to an odd count).
 template <typename QT, int POOL, int D, int G, int HKV>
 __global__ __launch_bounds__(256, (G >= 8 ? 2 : 3)) void decode_split_slot(const QT* __restrict__ q, const uint8_t* __restrict__ kpool,
                                                          const uint8_t* __restrict__ vpool,
@@ -270,7 +280,8 @@ __global__ __launch_bounds__(256, (G >= 8 ? 2 : 3)) void decode_split_slot(const
                                                          const int32_t* __restrict__ seq_lens, int chunk,
                                                          int max_splits, float qk_scale_log2,
                                                          float* __restrict__ ws_ml, float* __restrict__ ws_acc,
-                                                         int hkv_total, const int32_t* __restrict__ skip) {
+                                                         int hkv_total, const int32_t* __restrict__ skip, int s0,
+                                                         int ns, int ns_odd) {
   constexpr int VEC = D / 16;
   constexpr int STREAMS = 16 / HKV;
   using Chunk = RowChunk<POOL, VEC>;
@@ -278,11 +289,13 @@ __global__ __launch_bounds__(256, (G >= 8 ? 2 : 3)) void decode_split_slot(const
   __shared__ float sm_ml[(STREAMS - 1) * HKV][G][2];
   __shared__ float sm_acc[(STREAMS - 1) * HKV][G][D];
 
-  // kv heads in groups of HKV: blockIdx.x = (b * max_splits + s) * groups + group
+  // kv heads in groups of HKV: blockIdx.x = (b * ns_odd + s - s0) * groups + group
   const int groups = hkv_total / HKV;
   const int group = blockIdx.x % groups;
-  const int s = (blockIdx.x / groups) % max_splits;
-  const int b = blockIdx.x / groups / max_splits;
+  const int j = (blockIdx.x / groups) % ns_odd;
+  const int b = blockIdx.x / groups / ns_odd;
+  if (j >= ns) return;  // the padding chunk of an even count
+  const int s = s0 + j;
   const int L = seq_lens[b];
   const int t0 = s * chunk;
   if (t0 >= L) return;  // the whole workgroup leaves together
@@ -482,14 +495,16 @@ __global__ __launch_bounds__(256) void decode_reduce(const float* __restrict__ w
 }
 
 template <typename QT, int POOL, int D, int HKV>
-int launch_slot(int G, dim3 grid, hipStream_t st, const void* q, const void* kp, const void* vp, const float* ks,
-                const float* vs, const int32_t* r2t, int64_t stride, const int32_t* lens, int chunk, int max_splits,
-                float sc, float* ml, float* acc, int hkv_total, const int32_t* skip) {
+int launch_slot(int G, int batch, int s0, int ns, hipStream_t st, const void* q, const void* kp, const void* vp,
+                const float* ks, const float* vs, const int32_t* r2t, int64_t stride, const int32_t* lens, int chunk,
+                int max_splits, float sc, float* ml, float* acc, int hkv_total, const int32_t* skip) {
+  const int ns_odd = ns | 1;
+  const dim3 grid((unsigned)((int64_t)batch * ns_odd * (hkv_total / HKV)));
 #define PKV_SLOT_CASE(GG)                                                                                        \
   case GG:                                                                                                       \
     hipLaunchKernelGGL((decode_split_slot<QT, POOL, D, GG, HKV>), grid, dim3(256), 0, st, (const QT*)q,          \
                        (const uint8_t*)kp, (const uint8_t*)vp, ks, vs, r2t, stride, lens, chunk, max_splits, sc, \
-                       ml, acc, hkv_total, skip);                                                                \
+                       ml, acc, hkv_total, skip, s0, ns, ns_odd);                                                \
     return PKV_OK;
   switch (G) {
     PKV_SLOT_CASE(1)
@@ -503,26 +518,29 @@ int launch_slot(int G, dim3 grid, hipStream_t st, const void* q, const void* kp,
 }
 
 template <typename QT, int POOL, int D>
-int launch_split(int G, dim3 grid, hipStream_t st, const void* q, const void* kp, const void* vp, const float* ks,
-                 const float* vs, const int32_t* r2t, int64_t stride, const int32_t* lens, int hkv, int chunk,
-                 int max_splits, float sc, float* ml, float* acc, const int32_t* skip) {
+int launch_split(int G, int batch, int s0, int ns, bool per_head, hipStream_t st, const void* q, const void* kp,
+                 const void* vp, const float* ks, const float* vs, const int32_t* r2t, int64_t stride,
+                 const int32_t* lens, int hkv, int chunk, int max_splits, float sc, float* ml, float* acc,
+                 const int32_t* skip) {
 #define PKV_DECODE_CASE(GG)                                                                                    \
   case GG:                                                                                                     \
-    hipLaunchKernelGGL((decode_split<QT, POOL, D, GG>), grid, dim3(256), 0, st, (const QT*)q, (const uint8_t*)kp, \
-                       (const uint8_t*)vp, ks, vs, r2t, stride, lens, hkv, chunk, max_splits, sc, ml, acc, skip); \
+    hipLaunchKernelGGL((decode_split<QT, POOL, D, GG>), dim3((unsigned)((int64_t)batch * ns * hkv)), dim3(256), 0, \
+                       st, (const QT*)q, (const uint8_t*)kp, (const uint8_t*)vp, ks, vs, r2t, stride, lens, hkv,  \
+                       chunk, max_splits, sc, ml, acc, skip, s0, ns);                                          \
     return PKV_OK;
   // all heads of a slot row per workgroup for 2, 4 or 8 kv heads; groups of 8 heads for
   // any multiple of 8 (multi-head attention)
-  const dim3 slot_grid(grid.x / hkv);
-  if (hkv == 8) return launch_slot<QT, POOL, D, 8>(G, slot_grid, st, q, kp, vp, ks, vs, r2t, stride, lens, chunk,
-                                                  max_splits, sc, ml, acc, hkv, skip);
-  if (hkv == 4) return launch_slot<QT, POOL, D, 4>(G, slot_grid, st, q, kp, vp, ks, vs, r2t, stride, lens, chunk,
-                                                  max_splits, sc, ml, acc, hkv, skip);
-  if (hkv == 2) return launch_slot<QT, POOL, D, 2>(G, slot_grid, st, q, kp, vp, ks, vs, r2t, stride, lens, chunk,
-                                                  max_splits, sc, ml, acc, hkv, skip);
-  if (hkv % 8 == 0)
-    return launch_slot<QT, POOL, D, 8>(G, dim3(grid.x / 8), st, q, kp, vp, ks, vs, r2t, stride, lens, chunk,
-                                       max_splits, sc, ml, acc, hkv, skip);
+  if (!per_head) {
+    if (hkv == 8) return launch_slot<QT, POOL, D, 8>(G, batch, s0, ns, st, q, kp, vp, ks, vs, r2t, stride, lens, chunk,
+                                                    max_splits, sc, ml, acc, hkv, skip);
+    if (hkv == 4) return launch_slot<QT, POOL, D, 4>(G, batch, s0, ns, st, q, kp, vp, ks, vs, r2t, stride, lens, chunk,
+                                                    max_splits, sc, ml, acc, hkv, skip);
+    if (hkv == 2) return launch_slot<QT, POOL, D, 2>(G, batch, s0, ns, st, q, kp, vp, ks, vs, r2t, stride, lens, chunk,
+                                                    max_splits, sc, ml, acc, hkv, skip);
+    if (hkv % 8 == 0)
+      return launch_slot<QT, POOL, D, 8>(G, batch, s0, ns, st, q, kp, vp, ks, vs, r2t, stride, lens, chunk,
+                                         max_splits, sc, ml, acc, hkv, skip);
+  }
   switch (G) {
     PKV_DECODE_CASE(1)
     PKV_DECODE_CASE(2)
@@ -572,7 +590,8 @@ int decode_impl(const void* q, void* o, int32_t qo_dtype, const void* k_pool, co
                 int64_t num_slots, const float* k_scale, const float* v_scale, const int32_t* req_to_token,
                 int64_t stride, const int32_t* seq_lens, int32_t batch, int32_t max_seq_len, int32_t hq, int32_t hkv,
                 int32_t d, float sm_scale, int32_t chunk, const int32_t* members, const int32_t* skip,
-                const int32_t* items, int64_t n_items, void* workspace, size_t ws_bytes, void* stream) {
+                const int32_t* items, int64_t n_items, int32_t first_split, void* workspace, size_t ws_bytes,
+                void* stream) {
   if (batch < 0 || hq <= 0 || hkv <= 0 || hq % hkv || max_seq_len <= 0 || max_seq_len > stride || num_slots <= 0)
     return fail(PKV_ERR_INVAL, "decode: bad sizes (batch %d hq %d hkv %d max_seq_len %d stride %lld)", batch, hq,
                 hkv, max_seq_len, (long long)stride);
@@ -586,23 +605,31 @@ int decode_impl(const void* q, void* o, int32_t qo_dtype, const void* k_pool, co
   if (pool_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale)) return fail(PKV_ERR_INVAL, "decode: fp8 pool needs scales");
   const int G = hq / hkv;
   const int max_splits = splits_for(max_seq_len, chunk);
+  if ((int64_t)batch * (max_splits | 1) * hkv > 0x7FFFFFFFLL)
+    return fail(PKV_ERR_UNSUPPORTED, "decode: %d sequences x %d chunks x %d kv heads is beyond one launch", batch,
+                max_splits, hkv);
   float* ml = (float*)workspace;
   float* acc = ml + (size_t)batch * hq * max_splits * 2;
-  const dim3 grid((unsigned)((int64_t)batch * max_splits * hkv));
   hipStream_t st = (hipStream_t)stream;
   const float sc = sm_scale * kLog2e;
+  // split phase over chunks s0 .. max_splits - 1.  After a shared-prefix pass only short
+  // private tails may be left: when the all-heads kernel would then launch too few
+  // workgroups to fill the GPU, the per-head kernel (16 token streams each) takes them.
+  const int s0 = skip ? std::min(std::max(first_split, 0), max_splits - 1) : 0;
+  const int ns = max_splits - s0;
+  const bool per_head = skip && (int64_t)batch * ns < 1024;
   int rc;
   if (qo_dtype == PKV_F32 && pool_dtype == PKV_F32 && d == 64)
-    rc = launch_split<float, PKV_F32, 64>(G, grid, st, q, k_pool, v_pool, k_scale, v_scale, req_to_token, stride,
+    rc = launch_split<float, PKV_F32, 64>(G, batch, s0, ns, per_head, st, q, k_pool, v_pool, k_scale, v_scale, req_to_token, stride,
                                           seq_lens, hkv, chunk, max_splits, sc, ml, acc, skip);
   else if (qo_dtype == PKV_F32 && pool_dtype == PKV_F32 && d == 128)
-    rc = launch_split<float, PKV_F32, 128>(G, grid, st, q, k_pool, v_pool, k_scale, v_scale, req_to_token, stride,
+    rc = launch_split<float, PKV_F32, 128>(G, batch, s0, ns, per_head, st, q, k_pool, v_pool, k_scale, v_scale, req_to_token, stride,
                                            seq_lens, hkv, chunk, max_splits, sc, ml, acc, skip);
   else if (qo_dtype == PKV_BF16 && pool_dtype == PKV_BF16 && d == 128)
-    rc = launch_split<bf16, PKV_BF16, 128>(G, grid, st, q, k_pool, v_pool, k_scale, v_scale, req_to_token, stride,
+    rc = launch_split<bf16, PKV_BF16, 128>(G, batch, s0, ns, per_head, st, q, k_pool, v_pool, k_scale, v_scale, req_to_token, stride,
                                            seq_lens, hkv, chunk, max_splits, sc, ml, acc, skip);
   else if (qo_dtype == PKV_BF16 && pool_dtype == PKV_FP8_E4M3 && d == 128)
-    rc = launch_split<bf16, PKV_FP8_E4M3, 128>(G, grid, st, q, k_pool, v_pool, k_scale, v_scale, req_to_token,
+    rc = launch_split<bf16, PKV_FP8_E4M3, 128>(G, batch, s0, ns, per_head, st, q, k_pool, v_pool, k_scale, v_scale, req_to_token,
                                                stride, seq_lens, hkv, chunk, max_splits, sc, ml, acc, skip);
   else
     return fail(PKV_ERR_UNSUPPORTED, "decode: qo dtype %d, pool dtype %d, d %d", qo_dtype, pool_dtype, d);
@@ -635,7 +662,7 @@ extern "C" int pkv_decode_attention(const void* q, void* o, int32_t qo_dtype, co
                                     int32_t batch, int32_t max_seq_len, int32_t hq, int32_t hkv, int32_t d,
                                     float sm_scale, int32_t chunk, void* workspace, size_t ws_bytes, void* stream) {
   return decode_impl(q, o, qo_dtype, k_pool, v_pool, pool_dtype, num_slots, k_scale, v_scale, req_to_token, stride,
-                     seq_lens, batch, max_seq_len, hq, hkv, d, sm_scale, chunk, nullptr, nullptr, nullptr, 0,
+                     seq_lens, batch, max_seq_len, hq, hkv, d, sm_scale, chunk, nullptr, nullptr, nullptr, 0, 0,
                      workspace, ws_bytes, stream);
 }
 
@@ -645,8 +672,8 @@ extern "C" int pkv_decode_attention_shared(const void* q, void* o, int32_t qo_dt
                                            int64_t stride, const int32_t* seq_lens, int32_t batch,
                                            int32_t max_seq_len, int32_t hq, int32_t hkv, int32_t d, float sm_scale,
                                            int32_t chunk, const int32_t* members, const int32_t* skip,
-                                           const int32_t* items, int64_t n_items, void* workspace, size_t ws_bytes,
-                                           void* stream) {
+                                           const int32_t* items, int64_t n_items, int32_t first_split,
+                                           void* workspace, size_t ws_bytes, void* stream) {
   if (n_items < 0) return fail(PKV_ERR_INVAL, "decode: n_items %lld", (long long)n_items);
   if (n_items > 0 && batch > 0) {
     if (!members || !skip || !items) return fail(PKV_ERR_INVAL, "decode: null shared-prefix plan");
@@ -657,5 +684,5 @@ extern "C" int pkv_decode_attention_shared(const void* q, void* o, int32_t qo_dt
   }
   return decode_impl(q, o, qo_dtype, k_pool, v_pool, pool_dtype, num_slots, k_scale, v_scale, req_to_token, stride,
                      seq_lens, batch, max_seq_len, hq, hkv, d, sm_scale, chunk, members, n_items > 0 ? skip : nullptr,
-                     items, n_items, workspace, ws_bytes, stream);
+                     items, n_items, first_split, workspace, ws_bytes, stream);
 }

@@ -295,7 +295,8 @@ class Engine:
         hn[b:2 * b] = skip
         hn[2 * b:2 * b + n] = items.reshape(-1)
         dev = up.send(2 * b + n)
-        return dict(members=dev[:b], skip=dev[b:2 * b], items=dev[2 * b:2 * b + n].view(-1, 3), chunk=int(chunk))
+        return dict(members=dev[:b], skip=dev[b:2 * b], items=dev[2 * b:2 * b + n].view(-1, 3), chunk=int(chunk),
+                    first_split=int(skip.min()))
 
     def decode(self, q, r2t_dev, seq_lens_dev, max_seq_len: int, workspace, chunk: int, o=None, plan=None):
         """One decode step; with a plan from decode_plan (same chunk), the shared chunks are
@@ -307,7 +308,7 @@ class Engine:
                 raise ValueError("decode: the plan was made for another chunk")
             pkv_decode_attention_shared(q, o, self.k_pool, self.v_pool, r2t_dev, seq_lens_dev, max_seq_len,
                                         self.sm_scale, workspace, chunk, plan["members"], plan["skip"], plan["items"],
-                                        self.k_scale, self.v_scale)
+                                        plan["first_split"], self.k_scale, self.v_scale)
         else:
             pkv_decode_attention(q, o, self.k_pool, self.v_pool, r2t_dev, seq_lens_dev, max_seq_len, self.sm_scale,
                                  workspace, chunk, self.k_scale, self.v_scale)
