@@ -481,17 +481,35 @@ __global__ __launch_bounds__(256) void decode_reduce(const float* __restrict__ w
   float lsum = 0.f;
   for (int s = lane; s < ns; s += 64) lsum += exp2f(ml[2 * s] - M) * ml[2 * s + 1];
   lsum = wave_sum(lsum);
-  float out[PER];
+  // partials in groups of 8 with independent accumulators, so 8 partials' loads are in
+  // flight at once (the loop is bound by load latency, not bandwidth, when there are many)
+  constexpr int U = 8;
+  float out[U][PER];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) out[i] = 0.f;
-  for (int s = 0; s < ns; ++s) {
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int i = 0; i < PER; ++i) out[u][i] = 0.f;
+  int s = 0;
+  for (; s + U <= ns; s += U) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float w = exp2f(ml[2 * (s + u)] - M);
+#pragma unroll
+      for (int i = 0; i < PER; ++i) out[u][i] = fmaf(w, acc[(int64_t)(s + u) * D + lane * PER + i], out[u][i]);
+    }
+  }
+  for (; s < ns; ++s) {
     const float w = exp2f(ml[2 * s] - M);
 #pragma unroll
-    for (int i = 0; i < PER; ++i) out[i] = fmaf(w, acc[(int64_t)s * D + lane * PER + i], out[i]);
+    for (int i = 0; i < PER; ++i) out[0][i] = fmaf(w, acc[(int64_t)s * D + lane * PER + i], out[0][i]);
   }
+#pragma unroll
+  for (int u = 1; u < U; ++u)
+#pragma unroll
+    for (int i = 0; i < PER; ++i) out[0][i] += out[u][i];
   const float inv = 1.f / lsum;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) store_o<OT>(o + (int64_t)idx * D + lane * PER + i, out[i] * inv);
+  for (int i = 0; i < PER; ++i) store_o<OT>(o + (int64_t)idx * D + lane * PER + i, out[0][i] * inv);
 }
 
 template <typename QT, int POOL, int D, int HKV>
