@@ -42,12 +42,12 @@ CSRC = os.path.join(ROOT, "prefix_shared_kv_match_amd", "csrc")
 # what the same counters read for a plain 1 GiB device copy (FETCH x2.0, WRITE x1.0).  Each
 # entry holds the hash of the kernel sources it was taken on; a changed kernel reports null.
 TRAFFIC = {
-    "fewshot_bf16": dict(kernel="extend_attention", src_hash="c2ec9c6c03996513",
-                         fetch_kib=204789.90625, write_kib=102977.171875),
-    "decode_bf16": dict(kernel="decode_attention", src_hash="1c25a75dd0c3e5a3",
-                        fetch_kib=5097152.96875, write_kib=47959.75),
-    "longctx_fp8": dict(kernel="extend_attention", src_hash="c2ec9c6c03996513",
-                        fetch_kib=1702728.09375, write_kib=262144.03125),
+    "fewshot_bf16": dict(kernel="extend_attention", src_hash="ac3bea050f040e4d",
+                         fetch_kib=204812.0, write_kib=102975.0),
+    "decode_bf16": dict(kernel="decode_attention", src_hash="",
+                        fetch_kib=0.0, write_kib=0.0),
+    "longctx_fp8": dict(kernel="extend_attention", src_hash="ac3bea050f040e4d",
+                        fetch_kib=1704359.0, write_kib=262144.0),
 }
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 # (warmup, timed) steps when not given: a few hundred ms of warmup for sub-millisecond steps,
@@ -55,8 +55,10 @@ FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 # extend with 64 decode steps)
 DEFAULT_WARMUP_STEPS = {"fewshot_bf16": (200, 300), "decode_bf16": (40, 80), "longctx_fp8": (4, 10),
                         "multiturn_bf16": (5, 20), "tot_bf16": (5, 20)}
+# the decode span is the split phase, the shared-prefix pass (in extend_attention.hip) and the
+# reduce; its traffic entry is the sum over the three kernels per decode step
 KERNEL_SOURCES = {"extend_attention": ["extend_attention.hip", "device.h"],
-                  "decode_attention": ["decode_attention.hip", "device.h"]}
+                  "decode_attention": ["decode_attention.hip", "extend_attention.hip", "device.h"]}
 
 
 def kernel_src_hash(kernel: str) -> str:

@@ -84,10 +84,12 @@ class StagedUpload:
     instead of between them.  Reuse is safe because the copy into a device buffer first waits
     for a marker recorded on the current stream at the previous send(): everything launched
     before that call, which includes every reader of the buffer's previous contents when
-    readers are launched before the next send(), has finished.  With side=False (small
-    tables, where the side stream's host cost outweighs the copy) the copy goes on the
-    current stream, which orders it after those readers by itself.  host() waits for the last
-    copy out of the host buffer."""
+    readers are launched before the next send(), has finished.  Small copies (below
+    SIDE_MIN_BYTES, or every copy with side=False) go on the current stream, which orders them
+    after those readers by itself: there the side stream's host bookkeeping (~20 µs) costs
+    more than the copy.  host() waits for the last copy out of the host buffer."""
+
+    SIDE_MIN_BYTES = 256 << 10
 
     def __init__(self, torch, device, side: bool = True):
         self.torch = torch
@@ -128,15 +130,16 @@ class StagedUpload:
             b["dev"] = torch.empty(max(total * 2, 64), dtype=torch.int32, device=self.device)
             if self.stream is not None:
                 b["dev"].record_stream(self.stream)
-        if self.stream is None:
+        if self.stream is not None:
+            self.marks[self.seq & 1].record(main)    # all work launched so far on the current stream
+        if self.stream is None or total * 4 < self.SIDE_MIN_BYTES:
             b["dev"][:total].copy_(b["host"][:total], non_blocking=True)
             b["copied"].record(main)
         else:
-            mark = self.marks[self.seq & 1]
-            prev = self.marks[(self.seq & 1) ^ 1]
-            mark.record(main)                  # all work launched so far on the current stream
             if self.seq > 0:
-                self.stream.wait_event(prev)   # readers of this device buffer's previous contents are done
+                # readers of this device buffer's previous contents were launched before the
+                # previous send(), whose marker covers them
+                self.stream.wait_event(self.marks[(self.seq & 1) ^ 1])
             with torch.cuda.stream(self.stream):
                 b["dev"][:total].copy_(b["host"][:total], non_blocking=True)
                 b["copied"].record(self.stream)

@@ -163,15 +163,20 @@ def test_prepare_staged_rows_upload_like_plain_tables():
 
 
 
-def test_staged_uploads_queued_without_host_sync():
+@pytest.mark.parametrize("side_min_bytes", [0, None])
+def test_staged_uploads_queued_without_host_sync(side_min_bytes):
     """Twelve staged table uploads over three batches and eight decode uploads queued
     back-to-back with no host synchronisation: the side-stream copies may run ahead of the
     kernels reading earlier uploads, and every kernel must still see its own tables (extend
-    outputs bit-equal to the plain-upload ones; decode slots / lengths read back intact)."""
-    log("staged uploads queued without host sync")
+    outputs bit-equal to the plain-upload ones; decode slots / lengths read back intact).
+    side_min_bytes 0 sends every table on the side stream; None keeps the size rule (these
+    small tables then go on the launch stream)."""
+    log(f"staged uploads queued without host sync (side stream from {side_min_bytes} bytes)")
     wl = workloads.multiturn_bf16(n_conv=12, turns=3, turn_range=(16, 80), batch=6, pool_slots=20000,
                                   capacity=12000)
     eng = make_engine(wl)
+    if side_min_bytes is not None:
+        eng._uploader("_tables_up").SIDE_MIN_BYTES = side_min_bytes
     hbs, qs, refs = [], [], []
     for batch in wl.batches[:3]:
         hb = eng.prepare([r.tokens for r in batch], wl.max_len())
