@@ -105,11 +105,21 @@ def parse():
     return ap.parse_args()
 
 
+class _NoSpan:
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        return False
+
+
 class Timer:
     """HIP events on torch's current stream (the stream every library call is given).
 
     Events are created once, up front, and recycled: creating timing events inside the
-    timed loop costs far more host time than the kernels it measures."""
+    timed loop costs far more host time than the kernels it measures.  A timing event is
+    not free on the GPU either (a few µs of queue time per record), so the timed loop records
+    only the spans named in `live` (None: all)."""
 
     def __init__(self, torch, pool=4096):
         self.torch = torch
@@ -117,9 +127,12 @@ class Timer:
         self.stream = torch.cuda.current_stream()
         self.acc = {}
         self.pending = []
+        self.live = None
 
     def span(self, name):
         t = self
+        if self.live is not None and name not in self.live:
+            return _NoSpan()
 
         class _S:
             def __enter__(s):
@@ -244,12 +257,19 @@ class PathBench:
 
     def _decode_step(self, hb, r2t_dev, i):
         """rt_decode_step -> H2D (slots, lengths) -> append to the device table -> kv_scatter -> decode."""
-        import prefix_shared_kv_match_amd as pkv
         torch, eng, T = self.torch, self.eng, self.timer
-        slots_dev, seq_dev = eng.upload_decode(eng.decode_alloc(hb), hb.seq_lens)   # side-stream copy
-        if i == 0 and self.shared_decode and not self.decode_only:
-            self.plan = eng.decode_plan(hb.req_to_token, hb.seq_lens, self.chunk)    # host, then side stream
-        pkv.pkv_append_slots(r2t_dev, seq_dev, slots_dev)
+        slots = eng.decode_alloc(hb)
+        if self.decode_only or not self.shared_decode:
+            slots_dev, seq_dev = eng.upload_decode(slots, hb.seq_lens)                # async copy
+        else:
+            if i == 0:      # the batch's shared chunks (host); sent with every step's slots
+                self.plan_host = eng.decode_plan(hb.req_to_token, hb.seq_lens, self.chunk, upload=False)
+            if self.plan_host is None:
+                slots_dev, seq_dev = eng.upload_decode(slots, hb.seq_lens)
+                self.plan = None
+            else:
+                slots_dev, seq_dev, self.plan = eng.upload_decode(slots, hb.seq_lens, self.plan_host)
+        eng.append_slots(r2t_dev, seq_dev, slots_dev)
         with T.span("kv_scatter_decode"):
             eng.scatter(slots_dev, self.dk[i], self.dv[i])
         with T.span("decode_attention"):
@@ -436,7 +456,7 @@ class JobBench:
                 slots_dev, seq_dev = eng.upload_decode(eng.decode_alloc(hb), hb.seq_lens)
                 if i == 0 and not self.a.plain_decode:
                     plan = eng.decode_plan(hb.req_to_token, hb.seq_lens, self.chunk)
-                pkv.pkv_append_slots(r2t, seq_dev, slots_dev)
+                eng.append_slots(r2t, seq_dev, slots_dev)
                 with T.span("kv_scatter_decode"):
                     eng.scatter(slots_dev, self.dk[i], self.dv[i])
                 with T.span("decode_attention"):
@@ -489,6 +509,7 @@ def main_job(a, torch):
     import prefix_shared_kv_match_amd as pkv
     b = JobBench(torch, a)
     wl, s = b.wl, b.wl.shape
+    b.timer.live = {"extend_attention"}      # the only span recorded in the timed loop
     for _ in range(a.warmup):
         b.step()
     b.timer.reset()
@@ -500,6 +521,14 @@ def main_job(a, torch):
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     b.timer.collect()
+    live_acc = dict(b.timer.acc)
+    extra = min(3, a.steps) if b.steps_dec else 0     # untimed jobs for the decode spans
+    b.timer.live = None
+    b.timer.reset()
+    for _ in range(extra):
+        b.step()
+    b.timer.collect()
+    b.timer.acc.update(live_acc)
     ext_ms, n_ext = b.timer.acc.get("extend_attention", (0.0, 0))
     ext_ms_job = ext_ms / a.steps
     kernels = {"extend_attention": {"ms_per_job": ext_ms_job, "launches_per_job": n_ext // a.steps,
@@ -583,7 +612,8 @@ def main():
     pkv.lib()
     if a.workload in ("multiturn_bf16", "tot_bf16") or (a.workload == "fewshot_bf16" and a.chunk_budget > 0):
         return main_job(a, torch)
-    b = PathBench(torch, a.workload, a.warmup + a.steps, shared_decode=not a.plain_decode)
+    extra = min(30, a.steps)      # untimed steps after the timed ones, for the other kernels' spans
+    b = PathBench(torch, a.workload, a.warmup + a.steps + extra, shared_decode=not a.plain_decode)
     wl = b.wl
     if a.copy_calib_mib:
         n = a.copy_calib_mib * (1 << 20) // 4
@@ -592,6 +622,9 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    # the timed loop records events around the dominant kernel only
+    dominant = "extend_attention" if wl.extend_attention else "decode_attention"
+    b.timer.live = {dominant}
     for _ in range(a.warmup):
         b.step()
     b.timer.reset()
@@ -604,8 +637,25 @@ def main():
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     b.timer.collect()
+    live_acc = dict(b.timer.acc)
+    # the tables the timed steps ran on (the extra steps below overwrite the staging buffers
+    # and, for the decode workload, grow the contexts)
+    import dataclasses
+    lt = b.last_tables
+    timed_tables = dataclasses.replace(lt, req_to_token=lt.req_to_token.copy(), seq_lens=lt.seq_lens.copy(),
+                                       prefix_lens=lt.prefix_lens.copy(), extend_lens=lt.extend_lens.copy())
+    timed_step_i = b.step_i if b.decode_only else 0
+    # then a few untimed steps with every span, for the other kernels' durations
+    b.timer.live = None
+    b.timer.reset()
+    host_prepare_s = b.host_prepare_s
+    for _ in range(extra):
+        b.step()
+    b.timer.collect()
+    b.timer.acc.update(live_acc)
+    b.host_prepare_s = host_prepare_s
     hbm_practical = practical_hbm_gbps(torch)
-    hb = b.last_tables
+    hb = timed_tables
     s = wl.shape
     flops, pairs = extend_flops(s.d, s.hq, hb.prefix_lens, hb.extend_lens)
     kv_tok = kv_row_bytes(s)
@@ -652,11 +702,13 @@ def main():
         "roofline": {"bound": bound, "kernel": dom, "achieved": achieved, "peak": peak, "unit": unit,
                      "frac": achieved / peak, "traffic": traffic_bytes(wl.name, dom)},
         "kernels": kernels,
+        "kernel_timing": f"{dom}: HIP events in every timed step (the only span recorded there); the other "
+                         f"kernels: HIP events over {extra} untimed steps after the timed ones",
         "hbm_practical_gbps": hbm_practical,
         "library": os.path.relpath(pkv._capi.LIB_PATH, ROOT),
     }
     if not a.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, hb, a.cpu_sample, b.decode_only, b.step_i if b.decode_only else 0)
+        out["cpu_baseline"] = cpu_baseline(wl, hb, a.cpu_sample, b.decode_only, timed_step_i)
     print(json.dumps(out), flush=True)
     return 0
 

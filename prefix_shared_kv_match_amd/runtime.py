@@ -19,7 +19,7 @@ from typing import List, Optional, Sequence
 
 import numpy as np
 
-from . import (PKV_BF16, PKV_F32, PKV_FP8_E4M3, pkv_decode_attention, pkv_decode_attention_shared,
+from . import (PKV_BF16, PKV_F32, PKV_FP8_E4M3, check, lib, pkv_decode_attention, pkv_decode_attention_shared,
                pkv_decode_chunk, pkv_decode_shared_plan, pkv_decode_shared_rows, rt_set_eviction_log,
                pkv_decode_workspace_bytes, pkv_extend_attention, pkv_extend_plan, pkv_extend_tile, pkv_kv_scatter,
                rt_create, rt_create_policy, rt_dec_lock_ref, rt_decode_step, rt_destroy, rt_finish, rt_peek_prefix,
@@ -171,6 +171,18 @@ class Engine:
         self.k_inv_scale, self.v_inv_scale = f(k_inv_scale), f(v_inv_scale)
         self.sm_scale = float(sm_scale if sm_scale is not None else d ** -0.5)
         self.tile = pkv_extend_tile(self.qo_code, self.pool_code, hq, hkv, d)
+        self.shared_rows = pkv_decode_shared_rows(self.qo_code, self.pool_code, hq, hkv, d)
+        # the step calls below go to the C ABI directly: the pools, scales and shapes are the
+        # engine's own (their addresses fixed for its life) and the per-call tensors are its
+        # device tables or are checked by shape here; the public binding's per-argument checks
+        # cost more host time than a small launch
+        ptr = lambda t: 0 if t is None else t.data_ptr()
+        self._lib = lib()
+        self._pools = (ptr(self.k_pool), ptr(self.v_pool))
+        self._scales = (ptr(self.k_scale), ptr(self.v_scale))
+        self._inv_scales = (ptr(self.k_inv_scale), ptr(self.v_inv_scale))
+        self._cur_stream = torch._C._cuda_getCurrentRawStream
+        self._cur_device = torch._C._cuda_getDevice
 
     def close(self):
         if self.tree is not None:
@@ -237,32 +249,85 @@ class Engine:
         dev = up.send(total)
         return {k: dev[offs[k]:offs[k] + a.size].view(a.shape) for k, a in arrays.items()}
 
-    def upload_decode(self, slots: np.ndarray, seq_lens: np.ndarray):
+    def upload_decode(self, slots: np.ndarray, seq_lens: np.ndarray, plan=None):
         """One decode step's new slots and sequence lengths on the device (int32 [n] each),
         through a staged upload of their own; valid for work launched on the current stream
-        until the next call."""
+        until the next call.  With a host plan (decode_plan(..., upload=False)) it travels in
+        the same copy and a third value, the device plan, is returned."""
         n = int(slots.size)
+        extra = 0 if plan is None else 2 * n + plan["items"].size
         up = self._uploader("_decode_up", side=False)
-        hn = up.host(2 * n)
+        hn = up.host(2 * n + extra)
         hn[:n] = slots
         hn[n:2 * n] = seq_lens
-        dev = up.send(2 * n)
-        return dev[:n], dev[n:2 * n]
+        if plan is None:
+            dev = up.send(2 * n)
+            return dev[:n], dev[n:2 * n]
+        m = plan["items"].size
+        hn[2 * n:3 * n] = plan["members"]
+        hn[3 * n:4 * n] = plan["skip"]
+        hn[4 * n:4 * n + m] = plan["items"].reshape(-1)
+        dev = up.send(4 * n + m)
+        return dev[:n], dev[n:2 * n], dict(members=dev[2 * n:3 * n], skip=dev[3 * n:4 * n],
+                                           items=dev[4 * n:4 * n + m].view(-1, 3), chunk=plan["chunk"],
+                                           first_split=plan["first_split"])
 
     # -- steps ---------------------------------------------------------------------------
     def prepare(self, token_lists, stride: int) -> HostBatch:
         return prepare(self.tree, token_lists, stride)
 
+    def _stream(self):
+        return self._cur_stream(self._cur_device())
+
+    def _rows(self, t, n, what):
+        """A contiguous device tensor of n rows of [hkv, d]."""
+        if t.shape != (n, self.hkv, self.d) or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{what}: expected a contiguous device tensor [{n}, {self.hkv}, {self.d}]")
+        return t.data_ptr()
+
+    def _src_code(self, t):
+        if t.dtype == self.torch.bfloat16:
+            return PKV_BF16
+        if t.dtype == self.torch.float32:
+            return PKV_F32
+        raise TypeError(f"unsupported source dtype {t.dtype}")
+
     def scatter(self, slots_dev, k_new, v_new):
-        pkv_kv_scatter(k_new, v_new, slots_dev, self.k_pool, self.v_pool, self.k_inv_scale, self.v_inv_scale)
+        n = int(slots_dev.shape[0])
+        if slots_dev.dtype != self.torch.int32 or not slots_dev.is_contiguous() or v_new.dtype != k_new.dtype:
+            raise ValueError("scatter: slots must be contiguous int32, k and v of one dtype")
+        check(self._lib.pkv_kv_scatter(self._rows(k_new, n, "k_new"), self._rows(v_new, n, "v_new"),
+                                       self._src_code(k_new), slots_dev.data_ptr(), n, *self._pools,
+                                       self.pool_code, self.num_slots, self.hkv, self.d, *self._inv_scales,
+                                       self._stream()))
 
     def extend(self, dt, q, o=None):
         if o is None:
             o = self.torch.empty_like(q)
-        pkv_extend_attention(q, o, self.k_pool, self.v_pool, dt["req_to_token"], dt["prefix_lens"],
-                             dt["extend_lens"], dt["qo_indptr"], dt["work"], self.sm_scale, self.k_scale,
-                             self.v_scale)
+        n = int(q.shape[0])
+        if q.shape != (n, self.hq, self.d) or o.shape != q.shape or q.dtype != self.qo_torch \
+                or o.dtype != q.dtype or not (q.is_contiguous() and o.is_contiguous()):
+            raise ValueError("extend: q and o must be contiguous [rows, hq, d] in the engine's dtype")
+        r2t = dt["req_to_token"]
+        work = dt["work"]
+        if r2t.dtype != self.torch.int32 or work.dtype != self.torch.int32:
+            raise ValueError("extend: tables must be int32 (Engine.device_tables)")
+        check(self._lib.pkv_extend_attention(q.data_ptr(), o.data_ptr(), self.qo_code, *self._pools, self.pool_code,
+                                             self.num_slots, *self._scales, r2t.data_ptr(), r2t.shape[1],
+                                             dt["prefix_lens"].data_ptr(), dt["extend_lens"].data_ptr(),
+                                             dt["qo_indptr"].data_ptr(), dt["prefix_lens"].shape[0],
+                                             work.data_ptr(), work.shape[0], self.hq, self.hkv, self.d,
+                                             self.sm_scale, self._stream()))
         return o
+
+    def append_slots(self, r2t_dev, seq_lens_dev, slots_dev):
+        """Device side of a decode step's table emit (pkv_append_slots) on the engine's tables."""
+        b = int(slots_dev.shape[0])
+        if seq_lens_dev.shape != (b,) or r2t_dev.dim() != 2 or r2t_dev.shape[0] < b \
+                or r2t_dev.dtype != self.torch.int32:
+            raise ValueError("append_slots: shape mismatch")
+        check(self._lib.pkv_append_slots(r2t_dev.data_ptr(), r2t_dev.shape[1], seq_lens_dev.data_ptr(),
+                                         slots_dev.data_ptr(), b, self._stream()))
 
     def release(self, hb: HostBatch):
         rt_release(self.tree, hb.last_nodes)
@@ -277,13 +342,14 @@ class Engine:
         nbytes = pkv_decode_workspace_bytes(batch, self.hq, self.d, max_seq_len, chunk)
         return self.torch.empty(nbytes // 4 + 1, dtype=self.torch.float32, device=self.device), chunk
 
-    def decode_plan(self, req_to_token: np.ndarray, seq_lens: np.ndarray, chunk: int):
+    def decode_plan(self, req_to_token: np.ndarray, seq_lens: np.ndarray, chunk: int, upload: bool = True):
         """The shared-prefix plan of a decode batch (host slot rows and current lengths) on the
         device: a dict of int32 views (members, skip, items) valid for work launched before the
         next call, or None when no chunk is shared or the shape has no shared-prefix kernel.
         Computed once, it serves every later decode step of the same sequences (new tokens are
-        private, so the shared chunks do not change)."""
-        rows = pkv_decode_shared_rows(self.qo_code, self.pool_code, self.hq, self.hkv, self.d)
+        private, so the shared chunks do not change).  upload=False returns the host arrays,
+        for upload_decode to send with a step's slots."""
+        rows = self.shared_rows
         if rows <= 0:
             return None
         # the rows come from this engine's tree (its locks keep them), so each chunk's last
@@ -291,6 +357,8 @@ class Engine:
         members, skip, items = pkv_decode_shared_plan(req_to_token, seq_lens, chunk, rows, rows_from_tree=True)
         if items.shape[0] == 0:
             return None
+        if not upload:
+            return dict(members=members, skip=skip, items=items, chunk=int(chunk), first_split=int(skip.min()))
         b, n = members.size, items.size
         up = self._uploader("_plan_up", side=False)
         hn = up.host(2 * b + n)
@@ -306,15 +374,24 @@ class Engine:
         read once per group of sequences."""
         if o is None:
             o = self.torch.empty_like(q)
+        b = int(q.shape[0])
+        if q.shape != (b, self.hq, self.d) or o.shape != q.shape or q.dtype != self.qo_torch \
+                or o.dtype != q.dtype or not (q.is_contiguous() and o.is_contiguous()) \
+                or seq_lens_dev.shape != (b,) or r2t_dev.dim() != 2 or r2t_dev.shape[0] < b \
+                or r2t_dev.dtype != self.torch.int32 or seq_lens_dev.dtype != self.torch.int32:
+            raise ValueError("decode: shape mismatch")
+        head = (q.data_ptr(), o.data_ptr(), self.qo_code, *self._pools, self.pool_code, self.num_slots,
+                *self._scales, r2t_dev.data_ptr(), r2t_dev.shape[1], seq_lens_dev.data_ptr(), b, int(max_seq_len),
+                self.hq, self.hkv, self.d, self.sm_scale, int(chunk))
+        ws = (workspace.data_ptr(), workspace.numel() * workspace.element_size(), self._stream())
         if plan is not None:
-            if plan["chunk"] != chunk:
-                raise ValueError("decode: the plan was made for another chunk")
-            pkv_decode_attention_shared(q, o, self.k_pool, self.v_pool, r2t_dev, seq_lens_dev, max_seq_len,
-                                        self.sm_scale, workspace, chunk, plan["members"], plan["skip"], plan["items"],
-                                        plan["first_split"], self.k_scale, self.v_scale)
+            if plan["chunk"] != chunk or plan["members"].shape != (b,):
+                raise ValueError("decode: the plan was made for another chunk or batch")
+            items = plan["items"]
+            check(self._lib.pkv_decode_attention_shared(*head, plan["members"].data_ptr(), plan["skip"].data_ptr(),
+                                                        items.data_ptr(), items.shape[0], plan["first_split"], *ws))
         else:
-            pkv_decode_attention(q, o, self.k_pool, self.v_pool, r2t_dev, seq_lens_dev, max_seq_len, self.sm_scale,
-                                 workspace, chunk, self.k_scale, self.v_scale)
+            check(self._lib.pkv_decode_attention(*head, *ws))
         return o
 
     def finish(self, hb: HostBatch, full_token_lists, prompt_lens):
