@@ -33,6 +33,17 @@ def decode(**kw):
                                           a["ws_bytes"], a["stream"])
 
 
+def decode_shared(**kw):
+    a = dict(q=P, o=P, qo=PKV_BF16, kp=P, vp=P, pool=PKV_BF16, num_slots=1024, ks=None, vs=None, r2t=P, stride=4096,
+             lens=P, batch=4, max_len=4096, hq=32, hkv=8, d=128, sm=0.088, chunk=256, members=P, skip=P, items=P,
+             n_items=3, first_split=0, ws=P, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return pkv.lib().pkv_decode_attention_shared(
+        a["q"], a["o"], a["qo"], a["kp"], a["vp"], a["pool"], a["num_slots"], a["ks"], a["vs"], a["r2t"], a["stride"],
+        a["lens"], a["batch"], a["max_len"], a["hq"], a["hkv"], a["d"], a["sm"], a["chunk"], a["members"], a["skip"],
+        a["items"], a["n_items"], a["first_split"], a["ws"], a["ws_bytes"], a["stream"])
+
+
 def scatter(**kw):
     a = dict(ks=P, vs=P, src=PKV_BF16, slots=P, n=16, kp=P, vp=P, pool=PKV_BF16, num_slots=1024, hkv=8, d=128,
              kinv=None, vinv=None, stream=None)
@@ -78,6 +89,35 @@ def test_decode_rejects(kw, code):
 
 def test_decode_empty_batch_is_a_no_op():
     assert decode(batch=0) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(members=None), INVAL),                # a plan without its arrays
+    (dict(items=None), INVAL),
+    (dict(chunk=0), INVAL),                     # a plan is made for one chunk size
+    (dict(n_items=-1), INVAL),
+    (dict(qo=PKV_F32, pool=PKV_F32), UNSUP),    # no shared-prefix kernel for fp32
+    (dict(hq=24, hkv=8), UNSUP),                # group size 3: no shared-prefix kernel
+    (dict(max_len=8192), INVAL),                # longer than the table stride, as without a plan
+])
+def test_decode_shared_rejects(kw, code):
+    assert decode_shared(**kw) == code
+    assert pkv.lib().pkv_last_error()
+
+
+def test_decode_shared_without_items_is_plain_decode_validation():
+    # no items: the same checks as pkv_decode_attention (and no launch for an empty batch)
+    assert decode_shared(n_items=0, members=None, skip=None, items=None, batch=0) == 0
+    assert decode_shared(n_items=0, members=None, skip=None, items=None, ws=None) == INVAL
+
+
+def test_decode_shared_rows():
+    lib = pkv.lib()
+    assert lib.pkv_decode_shared_rows(PKV_BF16, PKV_BF16, 32, 8, 128) == 32
+    assert lib.pkv_decode_shared_rows(PKV_BF16, PKV_FP8_E4M3, 64, 8, 128) == 16
+    assert lib.pkv_decode_shared_rows(PKV_BF16, PKV_BF16, 32, 32, 128) == 128
+    assert lib.pkv_decode_shared_rows(PKV_F32, PKV_F32, 8, 8, 64) == UNSUP
+    assert lib.pkv_decode_shared_rows(PKV_BF16, PKV_BF16, 30, 8, 128) == INVAL
 
 
 @pytest.mark.parametrize("kw,code", [
