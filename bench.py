@@ -98,6 +98,8 @@ def parse():
                          "(times the whole chunked job; 0 = the default one-batch step)")
     ap.add_argument("--plain-decode", action="store_true",
                     help="decode without the shared-prefix plan (every sequence gathers its whole context)")
+    ap.add_argument("--decode-chunk", type=int, default=0,
+                    help="tokens per decode split (a multiple of 64; 0 = the library's automatic choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=64, help="requests in the oracle's timed sample")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -180,7 +182,7 @@ class PathBench:
 
     CHUNK_ROWS = 65536   # setup scatter in chunks, so host memory stays bounded
 
-    def __init__(self, torch, wl_name="fewshot_bf16", total_steps=64, shared_decode=True):
+    def __init__(self, torch, wl_name="fewshot_bf16", total_steps=64, shared_decode=True, decode_chunk=0):
         import workloads
         from prefix_shared_kv_match_amd.runtime import Engine
         self.torch = torch
@@ -232,7 +234,7 @@ class PathBench:
         self.dq = [self._src(wl.values.q(wl.decode_rows[i])) for i in range(n_dec)]
         self.do = torch.empty_like(self.dq[0]) if n_dec else None
         if n_dec:
-            self.ws, self.chunk = eng.decode_workspace(B, self.max_len)
+            self.ws, self.chunk = eng.decode_workspace(B, self.max_len, decode_chunk)
         # shared-prefix decode: which chunks the batch's sequences hold in common (made from the
         # host rows after the first decode slot is taken; valid while the sequences only grow)
         self.shared_decode = shared_decode
@@ -613,7 +615,8 @@ def main():
     if a.workload in ("multiturn_bf16", "tot_bf16") or (a.workload == "fewshot_bf16" and a.chunk_budget > 0):
         return main_job(a, torch)
     extra = min(30, a.steps)      # untimed steps after the timed ones, for the other kernels' spans
-    b = PathBench(torch, a.workload, a.warmup + a.steps + extra, shared_decode=not a.plain_decode)
+    b = PathBench(torch, a.workload, a.warmup + a.steps + extra, shared_decode=not a.plain_decode,
+                  decode_chunk=a.decode_chunk)
     wl = b.wl
     if a.copy_calib_mib:
         n = a.copy_calib_mib * (1 << 20) // 4

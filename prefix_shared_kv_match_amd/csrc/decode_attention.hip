@@ -632,10 +632,12 @@ int decode_impl(const void* q, void* o, int32_t qo_dtype, const void* k_pool, co
   const float sc = sm_scale * kLog2e;
   // split phase over chunks s0 .. max_splits - 1.  After a shared-prefix pass only short
   // private tails may be left: when the all-heads kernel would then launch too few
-  // workgroups to fill the GPU, the per-head kernel (16 token streams each) takes them.
+  // workgroups to fill the GPU (counting its head groups), the per-head kernel (16 token
+  // streams each) takes them.
   const int s0 = skip ? std::min(std::max(first_split, 0), max_splits - 1) : 0;
   const int ns = max_splits - s0;
-  const bool per_head = skip && (int64_t)batch * ns < 1024;
+  const int slot_groups = (hkv == 2 || hkv == 4 || hkv == 8) ? 1 : (hkv % 8 == 0 ? hkv / 8 : 0);
+  const bool per_head = skip && (int64_t)batch * ns * slot_groups < 1024;
   int rc;
   if (qo_dtype == PKV_F32 && pool_dtype == PKV_F32 && d == 64)
     rc = launch_split<float, PKV_F32, 64>(G, batch, s0, ns, per_head, st, q, k_pool, v_pool, k_scale, v_scale, req_to_token, stride,
