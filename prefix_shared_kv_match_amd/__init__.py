@@ -408,7 +408,9 @@ def pkv_decode_shared_plan(req_to_token: np.ndarray, seq_lens, chunk: int, rows:
         raise ValueError("decode plan: req_to_token must be [>= batch, stride]")
     members = np.empty(max(b, 1), dtype=np.int32)
     skip = np.empty(max(b, 1), dtype=np.int32)
-    cap = max(b * (r2t.shape[1] // max(int(chunk), 1)) // 2 + 1, 1)   # jobs hold two members or more
+    # a job holds two members or more, so it makes at most members / 2 items when an item
+    # takes two or more rows (members per item); with one row per item, one item per member
+    cap = max(b * (r2t.shape[1] // max(int(chunk), 1)) // (2 if rows >= 2 else 1) + 1, 1)
     items = np.empty((cap, 3), dtype=np.int32)
     n = int(check(lib().pkv_decode_shared_plan(_ptr(r2t), r2t.shape[1], _ptr(sl), b, int(chunk), int(rows),
                                                int(bool(rows_from_tree)), _ptr(members), _ptr(skip), _ptr(items),
