@@ -100,6 +100,9 @@ def parse():
                     help="decode without the shared-prefix plan (every sequence gathers its whole context)")
     ap.add_argument("--decode-chunk", type=int, default=0,
                     help="tokens per decode split (a multiple of 64; 0 = the library's automatic choice)")
+    ap.add_argument("--shared-min-workgroups", type=int, default=0,
+                    help="shared-prefix decode: merge chunks into longer items while this many workgroups remain "
+                         "(0 = the engine's default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=64, help="requests in the oracle's timed sample")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -617,6 +620,8 @@ def main():
     extra = min(30, a.steps)      # untimed steps after the timed ones, for the other kernels' spans
     b = PathBench(torch, a.workload, a.warmup + a.steps + extra, shared_decode=not a.plain_decode,
                   decode_chunk=a.decode_chunk)
+    if a.shared_min_workgroups:
+        b.eng.SHARED_MIN_WORKGROUPS = a.shared_min_workgroups
     wl = b.wl
     if a.copy_calib_mib:
         n = a.copy_calib_mib * (1 << 20) // 4

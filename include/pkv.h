@@ -315,11 +315,13 @@ int pkv_decode_attention(const void* q, void* o, int32_t qo_dtype, const void* k
  * seq_lens [batch] (each in [1, stride]), partition the sequences chunk by chunk: at chunk k
  * the sequences of a group (all equal on chunks 0..k-1) whose chunk k (whole, inside their
  * context) is slot for slot equal form a job (members, k), which is partitioned again at
- * k + 1; a sequence left alone stops sharing at k.  Outputs (caller-owned host arrays):
+ * k + 1; a sequence left alone stops sharing at k.  The jobs of one member set at
+ * consecutive chunks are merged into spans of at most max_span chunks (one workgroup then
+ * reads the whole span and writes one partial).  Outputs (caller-owned host arrays):
  *   members [batch]  sequence indices, each job's members contiguous;
  *   skip [batch]     chunks 0..skip[b]-1 of sequence b are covered by jobs;
- *   items [cap, 3]   (index of the first member in `members`, member count <= rows, chunk),
- *                    a job cut into items of at most `rows` members.
+ *   items [cap, 4]   (index of the first member in `members`, member count <= rows, first
+ *                    chunk, span in chunks), a span cut into items of at most `rows` members.
  * chunk: the split chunk the decode will use (a multiple of 64).  rows_from_tree = 1 when
  * the rows come from one radix tree (as rt_prepare_extend / rt_decode_step write them, while
  * the batch holds its locks): a slot then belongs to one node at one depth, so rows that hold
@@ -328,8 +330,8 @@ int pkv_decode_attention(const void* q, void* o, int32_t qo_dtype, const void* k
  * bad sizes or when items_cap is too small (the message gives the count).  The plan stays
  * valid while the sequences only grow (new tokens are private). */
 int64_t pkv_decode_shared_plan(const int32_t* req_to_token, int64_t stride, const int32_t* seq_lens, int32_t batch,
-                               int32_t chunk, int32_t rows, int32_t rows_from_tree, int32_t* members, int32_t* skip,
-                               int32_t* items, int64_t items_cap);
+                               int32_t chunk, int32_t rows, int32_t max_span, int32_t rows_from_tree,
+                               int32_t* members, int32_t* skip, int32_t* items, int64_t items_cap);
 /* Query rows (member sequences) per shared-prefix item for a shape: 128 / (hq / hkv), or
  * PKV_ERR_UNSUPPORTED (shared-prefix decode needs BF16 q/o, a BF16 or FP8_E4M3 pool, d = 128,
  * hq / hkv in {1, 2, 4, 8}). */

@@ -397,10 +397,12 @@ def pkv_decode_shared_rows(qo_dtype: int, pool_dtype: int, hq: int, hkv: int, d:
     return int(lib().pkv_decode_shared_rows(qo_dtype, pool_dtype, hq, hkv, d))
 
 
-def pkv_decode_shared_plan(req_to_token: np.ndarray, seq_lens, chunk: int, rows: int, rows_from_tree: bool = False):
+def pkv_decode_shared_plan(req_to_token: np.ndarray, seq_lens, chunk: int, rows: int, rows_from_tree: bool = False,
+                           max_span: int = 1):
     """Host plan of the shared-prefix decode over host slot rows: (members [batch],
-    skip [batch], items [n, 3]) as int32 arrays.  rows_from_tree: the rows come from one
-    radix tree, so each chunk's last slot decides it (otherwise every slot is compared)."""
+    skip [batch], items [n, 4]) as int32 arrays.  rows_from_tree: the rows come from one
+    radix tree, so each chunk's last slot decides it (otherwise every slot is compared);
+    max_span: chunks one item may span."""
     r2t = _i32(req_to_token)
     sl = _i32(seq_lens)
     b = int(sl.size)
@@ -411,10 +413,10 @@ def pkv_decode_shared_plan(req_to_token: np.ndarray, seq_lens, chunk: int, rows:
     # a job holds two members or more, so it makes at most members / 2 items when an item
     # takes two or more rows (members per item); with one row per item, one item per member
     cap = max(b * (r2t.shape[1] // max(int(chunk), 1)) // (2 if rows >= 2 else 1) + 1, 1)
-    items = np.empty((cap, 3), dtype=np.int32)
+    items = np.empty((cap, 4), dtype=np.int32)
     n = int(check(lib().pkv_decode_shared_plan(_ptr(r2t), r2t.shape[1], _ptr(sl), b, int(chunk), int(rows),
-                                               int(bool(rows_from_tree)), _ptr(members), _ptr(skip), _ptr(items),
-                                               cap)))
+                                               int(max_span), int(bool(rows_from_tree)), _ptr(members), _ptr(skip),
+                                               _ptr(items), cap)))
     return members[:b], skip[:b], items[:n]
 
 
@@ -422,7 +424,7 @@ def pkv_decode_attention_shared(q, o, k_pool, v_pool, req_to_token, seq_lens, ma
                                 chunk: int, members, skip, items, first_split: int = 0, k_scale=None, v_scale=None,
                                 stream=None) -> None:
     """pkv_decode_attention with a shared-prefix plan (device int32 members [b], skip [b],
-    items [n, 3] from pkv_decode_shared_plan for the same rows and chunk; first_split = the
+    items [n, 4] from pkv_decode_shared_plan for the same rows and chunk; first_split = the
     smallest skip, or 0)."""
     torch = _torch()
     b, hq, d = q.shape
@@ -430,7 +432,7 @@ def pkv_decode_attention_shared(q, o, k_pool, v_pool, req_to_token, seq_lens, ma
     if o.shape != q.shape or v_pool.shape != k_pool.shape or d2 != d or seq_lens.shape != (b,) \
             or req_to_token.dim() != 2 or req_to_token.shape[0] < b:
         raise ValueError("decode: shape mismatch")
-    if members.shape != (b,) or skip.shape != (b,) or items.dim() != 2 or items.shape[1] != 3:
+    if members.shape != (b,) or skip.shape != (b,) or items.dim() != 2 or items.shape[1] != 4:
         raise ValueError("decode: plan shape mismatch")
     args = (_dev(q, "q"), _dev(o, "o", q.dtype), _dtype_code(q), _dev(k_pool, "k_pool"),
             _dev(v_pool, "v_pool", k_pool.dtype), _dtype_code(k_pool), ns, _dev(k_scale, "k_scale", torch.float32),

@@ -475,11 +475,16 @@ __global__ __launch_bounds__(256) void decode_reduce(const float* __restrict__ w
   const int ns = (seq_lens[b] + chunk - 1) / chunk;
   const float* ml = ws_ml + (int64_t)idx * max_splits * 2;
   const float* acc = ws_acc + (int64_t)idx * max_splits * D;
+  // a partial with running max -inf is empty (a later chunk of a shared-prefix span): its
+  // weight is 0 and its output row, never written, is not read
   float M = -INFINITY;
   for (int s = lane; s < ns; s += 64) M = fmaxf(M, ml[2 * s]);
   M = wave_max(M);
   float lsum = 0.f;
-  for (int s = lane; s < ns; s += 64) lsum += exp2f(ml[2 * s] - M) * ml[2 * s + 1];
+  for (int s = lane; s < ns; s += 64) {
+    const float m = ml[2 * s];
+    if (m != -INFINITY) lsum += exp2f(m - M) * ml[2 * s + 1];
+  }
   lsum = wave_sum(lsum);
   // partials in groups of 8 with independent accumulators, so 8 partials' loads are in
   // flight at once (the loop is bound by load latency, not bandwidth, when there are many)
@@ -491,17 +496,32 @@ __global__ __launch_bounds__(256) void decode_reduce(const float* __restrict__ w
     for (int i = 0; i < PER; ++i) out[u][i] = 0.f;
   int s = 0;
   for (; s + U <= ns; s += U) {
+    // all eight partials' loads first, then the arithmetic, so the loads are in flight
+    // together; an empty partial's row (whatever the workspace holds) is replaced by 0
+    float mv[U], av[U][PER];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const float w = exp2f(ml[2 * (s + u)] - M);
+      mv[u] = ml[2 * (s + u)];
 #pragma unroll
-      for (int i = 0; i < PER; ++i) out[u][i] = fmaf(w, acc[(int64_t)(s + u) * D + lane * PER + i], out[u][i]);
+      for (int i = 0; i < PER; ++i) av[u][i] = acc[(int64_t)(s + u) * D + lane * PER + i];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool used = mv[u] != -INFINITY;
+      const float w = used ? exp2f(mv[u] - M) : 0.f;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) out[u][i] = fmaf(w, used ? av[u][i] : 0.f, out[u][i]);
     }
   }
   for (; s < ns; ++s) {
-    const float w = exp2f(ml[2 * s] - M);
+    const float m = ml[2 * s];
+    const bool used = m != -INFINITY;
+    const float w = used ? exp2f(m - M) : 0.f;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) out[0][i] = fmaf(w, acc[(int64_t)s * D + lane * PER + i], out[0][i]);
+    for (int i = 0; i < PER; ++i) {
+      const float a = acc[(int64_t)s * D + lane * PER + i];
+      out[0][i] = fmaf(w, used ? a : 0.f, out[0][i]);
+    }
   }
 #pragma unroll
   for (int u = 1; u < U; ++u)

@@ -12,8 +12,11 @@
 // first slot of chunk k, and members whose whole chunk k equals that of the first member of
 // their run form a sub-group.  A sub-group of two or more sequences is a job (members,
 // chunk k) and is partitioned again at level k + 1; a sequence left alone stops sharing at
-// chunk k.  Only whole chunks inside a sequence's context take part.  Jobs are cut into
-// items of at most `rows` members, the query rows one kernel workgroup holds per kv head.
+// chunk k.  Only whole chunks inside a sequence's context take part.  The jobs of one member
+// set at consecutive levels (a group that does not split) are merged into spans of up to
+// max_span chunks, so a long shared prefix is read by fewer, longer workgroups that write one
+// partial per span instead of one per chunk; spans are cut into items of at most `rows`
+// members, the query rows one kernel workgroup holds per kv head.
 //
 // Rows that come from one radix tree need no whole-chunk comparison: a slot belongs to one
 // node at one depth, so two rows holding the same slot at a position hold the same slots at
@@ -30,11 +33,12 @@
 using namespace pkv;
 
 extern "C" int64_t pkv_decode_shared_plan(const int32_t* req_to_token, int64_t stride, const int32_t* seq_lens,
-                                          int32_t batch, int32_t chunk, int32_t rows, int32_t rows_from_tree,
-                                          int32_t* members, int32_t* skip, int32_t* items, int64_t items_cap) {
-  if (batch < 0 || stride <= 0 || chunk < 64 || chunk % 64 || rows <= 0 || items_cap < 0)
-    return fail(PKV_ERR_INVAL, "decode plan: bad sizes (batch %d stride %lld chunk %d rows %d)", batch,
-                (long long)stride, chunk, rows);
+                                          int32_t batch, int32_t chunk, int32_t rows, int32_t max_span,
+                                          int32_t rows_from_tree, int32_t* members, int32_t* skip, int32_t* items,
+                                          int64_t items_cap) {
+  if (batch < 0 || stride <= 0 || chunk < 64 || chunk % 64 || rows <= 0 || max_span <= 0 || items_cap < 0)
+    return fail(PKV_ERR_INVAL, "decode plan: bad sizes (batch %d stride %lld chunk %d rows %d span %d)", batch,
+                (long long)stride, chunk, rows, max_span);
   if (batch == 0) return 0;
   if (!req_to_token || !seq_lens || !members || !skip || (items_cap > 0 && !items))
     return fail(PKV_ERR_INVAL, "decode plan: null pointer");
@@ -48,8 +52,10 @@ extern "C" int64_t pkv_decode_shared_plan(const int32_t* req_to_token, int64_t s
   }
   const size_t chunk_bytes = (size_t)chunk * sizeof(int32_t);
   auto row = [&](int32_t b, int32_t k) { return req_to_token + (int64_t)b * stride + (int64_t)k * chunk; };
-  int64_t n_items = 0;
-  bool overflow = false;
+  struct Job {
+    int32_t lo, cnt, k;   // members[lo, lo + cnt) share chunk k
+  };
+  std::vector<Job> jobs;
   struct Range {
     int32_t lo, hi, k;   // members[lo, hi) agree on chunks 0 .. k-1
   };
@@ -82,16 +88,7 @@ extern "C" int64_t pkv_decode_shared_plan(const int32_t* req_to_token, int64_t s
       const int32_t cnt = (int32_t)(same_end - a);
       if (cnt >= 2) {
         const int32_t lo = (int32_t)(a - members);
-        for (int32_t i = 0; i < cnt; i += rows) {
-          if (n_items < items_cap) {
-            items[3 * n_items] = lo + i;
-            items[3 * n_items + 1] = std::min(rows, cnt - i);
-            items[3 * n_items + 2] = r.k;
-          } else {
-            overflow = true;
-          }
-          ++n_items;
-        }
+        jobs.push_back(Job{lo, cnt, r.k});
         next.push_back(Range{lo, lo + cnt, r.k + 1});
       } else {
         skip[*a] = r.k;
@@ -101,6 +98,39 @@ extern "C" int64_t pkv_decode_shared_plan(const int32_t* req_to_token, int64_t s
     // depth first, lowest members first
     for (auto it = next.rbegin(); it != next.rend(); ++it) todo.push_back(*it);
   }
-  if (overflow) return fail(PKV_ERR_INVAL, "decode plan: needs %lld items", (long long)n_items);
+  // spans: the jobs of one member set (same range of `members`) at consecutive chunks, up to
+  // max_span chunks each, in order of first chunk; then items of at most `rows` members
+  std::stable_sort(jobs.begin(), jobs.end(), [](const Job& x, const Job& y) {
+    return x.lo != y.lo ? x.lo < y.lo : (x.cnt != y.cnt ? x.cnt > y.cnt : x.k < y.k);
+  });
+  struct Span {
+    int32_t lo, cnt, k, span;
+  };
+  std::vector<Span> spans;
+  for (const Job& j : jobs) {
+    if (!spans.empty()) {
+      Span& last = spans.back();
+      if (last.lo == j.lo && last.cnt == j.cnt && last.k + last.span == j.k && last.span < max_span) {
+        ++last.span;
+        continue;
+      }
+    }
+    spans.push_back(Span{j.lo, j.cnt, j.k, 1});
+  }
+  std::stable_sort(spans.begin(), spans.end(),
+                   [](const Span& x, const Span& y) { return x.k != y.k ? x.k < y.k : x.lo < y.lo; });
+  int64_t n_items = 0;
+  for (const Span& sp : spans)
+    for (int32_t i = 0; i < sp.cnt; i += rows) {
+      if (n_items < items_cap) {
+        int32_t* it = items + 4 * n_items;
+        it[0] = sp.lo + i;
+        it[1] = std::min(rows, sp.cnt - i);
+        it[2] = sp.k;
+        it[3] = sp.span;
+      }
+      ++n_items;
+    }
+  if (n_items > items_cap) return fail(PKV_ERR_INVAL, "decode plan: needs %lld items", (long long)n_items);
   return n_items;
 }

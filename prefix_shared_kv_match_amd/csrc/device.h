@@ -105,8 +105,9 @@ inline int hip_check(hipError_t e, const char* what) {
 }
 
 // Shared-prefix decode items (extend_attention.hip): for each item (first member, member
-// count, chunk s) of the host plan, the split partial of chunk s for every member, written
-// into the split phase's workspace layout.  bf16 q with a bf16 or fp8 E4M3 pool, d = 128,
+// count, first chunk s, span) of the host plan, the split partial of chunks s .. s + span - 1
+// for every member, written at chunk s of the split phase's workspace layout (the other
+// chunks of the span marked empty).  bf16 q with a bf16 or fp8 E4M3 pool, d = 128,
 // group size 1, 2, 4 or 8.
 int launch_decode_shared(const void* q, int32_t pool_dtype, const void* k_pool, const void* v_pool,
                          const float* k_scale, const float* v_scale, int64_t num_slots, const int32_t* r2t,

@@ -355,8 +355,10 @@ struct WaveAttn {
   // Split partials of a shared-prefix decode item, in the split phase's layout: for member b
   // and head h, partial p = (b * hq + h) * max_splits + s holds (reference max, row sum) at
   // ws_ml[2p], ws_ml[2p + 1] and the unnormalised output row (times omul) at ws_acc[p * d].
+  // An item spanning chunks s .. s + span - 1 marks the later ones empty (max -inf, sum 0;
+  // the reduce skips them without reading their output row).
   __device__ __forceinline__ void store_partial(float* ws_ml, float* ws_acc, const int32_t* members, int m0, int nm,
-                                                int hq, int max_splits, int s, float omul) const {
+                                                int hq, int max_splits, int s, int span, float omul) const {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       const float lt = __shfl(lsum[nb][0], ln);   // row sum sits in lane ln (row 0 of the block)
@@ -366,6 +368,7 @@ struct WaveAttn {
 #pragma unroll
       for (int db = 0; db < 8; ++db) *(floatx4*)(ap + 16 * db) = oacc[nb][db] * omul;
       if (lg == 0) *(float2*)(ws_ml + 2 * part) = float2{m[nb], lt};
+      for (int j = 1 + lg; j < span; j += 4) *(float2*)(ws_ml + 2 * (part + j)) = float2{-INFINITY, 0.f};
     }
   }
 
@@ -703,10 +706,11 @@ __global__ __launch_bounds__(256, 2) void extend_mfma(const bf16* __restrict__ q
 // radix tree shares), their newest tokens are stacked as the query rows of one extend-style
 // workgroup: the chunk's K/V tiles are staged once and multiplied against up to 128 query
 // rows with MFMA, instead of being gathered once per sequence by the split phase.  An item
-// (host plan) is (first member, member count <= 128 / G, chunk s); one workgroup per (item,
-// kv head), blockIdx.x = item * hkv + g; the chunk's slots are read from the first member's
-// row.  The output is the split phase's partial for chunk s of every member, which the
-// reduce then merges with the other chunks.  Same tile pipeline as extend_dma / extend_mfma.
+// (host plan) is (first member, member count <= 128 / G, first chunk s, span): one workgroup
+// per (item, kv head), blockIdx.x = item * hkv + g, reads chunks s .. s + span - 1 (their
+// slots from the first member's row).  The output is the split phase's partial at chunk s of
+// every member (chunks s + 1 .. marked empty), which the reduce then merges with the other
+// chunks.  Same tile pipeline as extend_dma / extend_mfma.
 
 template <int G, bool NARROW>
 __global__ __launch_bounds__(256, 2) void decode_shared_dma(const bf16* __restrict__ q,
@@ -725,9 +729,10 @@ __global__ __launch_bounds__(256, 2) void decode_shared_dma(const bf16* __restri
   const int ln = lane & 15, lg = lane >> 4;
   const int g = blockIdx.x % hkv;
   const int it = blockIdx.x / hkv;
-  const int m0 = items[3 * it], nm = items[3 * it + 1], s = items[3 * it + 2];
+  const int m0 = items[4 * it], nm = items[4 * it + 1], s = items[4 * it + 2], span = items[4 * it + 3];
   // an item outside the batch or the workspace is ignored (the whole workgroup leaves)
-  if (m0 < 0 || nm <= 0 || nm > WaveAttn<G>::BT || m0 > batch - nm || s < 0 || s >= max_splits) return;
+  if (m0 < 0 || nm <= 0 || nm > WaveAttn<G>::BT || m0 > batch - nm || s < 0 || span <= 0 || s > max_splits - span)
+    return;
   const int hq = hkv * G;
   const __amdgpu_buffer_rsrc_t tab = table_rsrc(r2t, table_bytes);
   const int row_bytes = (int)((int64_t)members[m0] * stride * 4);
@@ -756,7 +761,7 @@ __global__ __launch_bounds__(256, 2) void decode_shared_dma(const bf16* __restri
 #pragma unroll
     for (int h = 0; h < 2; ++h) vb[kk][h] = kv_off(32 * kk + 8 * lg + 4 * h + (ln >> 2)) + 8 * (ln & 3);
 
-  const int n_tiles = chunk / kBN;
+  const int n_tiles = span * chunk / kBN;
   const int last = n_tiles - 1;
   u32x2 sl[2];
   slots(kv_begin, sl);
@@ -781,7 +786,7 @@ __global__ __launch_bounds__(256, 2) void decode_shared_dma(const bf16* __restri
   }
   if (kt < n_tiles) step(kt, k0s, v0s, k1s, v1s);
 
-  wa.store_partial(ws_ml, ws_acc, members, m0, nm, hq, max_splits, s, 1.f);
+  wa.store_partial(ws_ml, ws_acc, members, m0, nm, hq, max_splits, s, span, 1.f);
 }
 
 template <int G>
@@ -804,9 +809,10 @@ __global__ __launch_bounds__(256, 2) void decode_shared_fp8(const bf16* __restri
   const int ln = lane & 15, lg = lane >> 4;
   const int g = blockIdx.x % hkv;
   const int it = blockIdx.x / hkv;
-  const int m0 = items[3 * it], nm = items[3 * it + 1], s = items[3 * it + 2];
+  const int m0 = items[4 * it], nm = items[4 * it + 1], s = items[4 * it + 2], span = items[4 * it + 3];
   // an item outside the batch or the workspace is ignored (the whole workgroup leaves)
-  if (m0 < 0 || nm <= 0 || nm > WaveAttn<G>::BT || m0 > batch - nm || s < 0 || s >= max_splits) return;
+  if (m0 < 0 || nm <= 0 || nm > WaveAttn<G>::BT || m0 > batch - nm || s < 0 || span <= 0 || s > max_splits - span)
+    return;
   const int hq = hkv * G;
   const __amdgpu_buffer_rsrc_t tab = table_rsrc(r2t, table_bytes);
   const uint32_t slot_bytes = (uint32_t)(hkv * kD), max_slot = (uint32_t)(num_slots - 1);
@@ -818,7 +824,7 @@ __global__ __launch_bounds__(256, 2) void decode_shared_fp8(const bf16* __restri
   const bool active = G != 1 || 32 * wave < nm;
 
   Fp8Stage stage;
-  const int n_tiles = chunk / kBN;
+  const int n_tiles = span * chunk / kBN;
   stage.load(kpool, vpool, slot_bytes, max_slot, Fp8Stage::slots(tab, row_bytes, kv_begin, tid), g, tid);
   stage.store(Ks[0], Vt[0], tid);
   stage.load(kpool, vpool, slot_bytes, max_slot, Fp8Stage::slots(tab, row_bytes, kv_begin + min(1, n_tiles - 1) * kBN, tid), g, tid);
@@ -837,7 +843,7 @@ __global__ __launch_bounds__(256, 2) void decode_shared_fp8(const bf16* __restri
           [&](int kk, int db) { return *(const bf16x8*)(V + (16 * db + ln) * kVStride + 32 * kk + 8 * lg); });
     __syncthreads();
   }
-  wa.store_partial(ws_ml, ws_acc, members, m0, nm, hq, max_splits, s, vscale[g]);
+  wa.store_partial(ws_ml, ws_acc, members, m0, nm, hq, max_splits, s, span, vscale[g]);
 }
 
 int mfma_tile(int G) { return kRows / G; }

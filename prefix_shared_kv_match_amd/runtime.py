@@ -152,6 +152,8 @@ class StagedUpload:
 class Engine:
     """One radix tree plus its device KV pools."""
 
+    SHARED_MIN_WORKGROUPS = 512
+
     def __init__(self, num_slots: int, hq: int, hkv: int, d: int, qo_dtype: str, pool_dtype: str,
                  free_order: Optional[np.ndarray] = None, device: str = "cuda", k_scale=None, v_scale=None,
                  k_inv_scale=None, v_inv_scale=None, sm_scale: Optional[float] = None, policy: str = "lru"):
@@ -269,7 +271,7 @@ class Engine:
         hn[4 * n:4 * n + m] = plan["items"].reshape(-1)
         dev = up.send(4 * n + m)
         return dev[:n], dev[n:2 * n], dict(members=dev[2 * n:3 * n], skip=dev[3 * n:4 * n],
-                                           items=dev[4 * n:4 * n + m].view(-1, 3), chunk=plan["chunk"],
+                                           items=dev[4 * n:4 * n + m].view(-1, 4), chunk=plan["chunk"],
                                            first_split=plan["first_split"])
 
     # -- steps ---------------------------------------------------------------------------
@@ -357,6 +359,12 @@ class Engine:
         members, skip, items = pkv_decode_shared_plan(req_to_token, seq_lens, chunk, rows, rows_from_tree=True)
         if items.shape[0] == 0:
             return None
+        # a long shared prefix: items spanning several chunks, as long as about 512
+        # workgroups (items x kv heads) remain, write fewer partials
+        span = items.shape[0] * self.hkv // self.SHARED_MIN_WORKGROUPS
+        if span >= 2:
+            members, skip, items = pkv_decode_shared_plan(req_to_token, seq_lens, chunk, rows, rows_from_tree=True,
+                                                          max_span=span)
         if not upload:
             return dict(members=members, skip=skip, items=items, chunk=int(chunk), first_split=int(skip.min()))
         b, n = members.size, items.size
@@ -366,7 +374,7 @@ class Engine:
         hn[b:2 * b] = skip
         hn[2 * b:2 * b + n] = items.reshape(-1)
         dev = up.send(2 * b + n)
-        return dict(members=dev[:b], skip=dev[b:2 * b], items=dev[2 * b:2 * b + n].view(-1, 3), chunk=int(chunk),
+        return dict(members=dev[:b], skip=dev[b:2 * b], items=dev[2 * b:2 * b + n].view(-1, 4), chunk=int(chunk),
                     first_split=int(skip.min()))
 
     def decode(self, q, r2t_dev, seq_lens_dev, max_seq_len: int, workspace, chunk: int, o=None, plan=None):

@@ -29,26 +29,27 @@ def rows_from_paths(rng, paths, lens, chunk, stride):
     return np.where(r2t >= 0, perm[np.maximum(r2t, 0)], -1).astype(np.int32)
 
 
-def check_plan(r2t, lens, chunk, rows, members, skip, items):
+def check_plan(r2t, lens, chunk, rows, members, skip, items, max_span=1):
     b = len(lens)
+    assert items.shape[1:] == (4,)
     assert sorted(members.tolist()) == list(range(b))
     full = [L // chunk for L in lens]
     covered = {i: [] for i in range(b)}
-    for m0, nm, k in items.tolist():
-        assert 1 <= nm <= rows and 0 <= m0 and m0 + nm <= b
+    job_sizes = {}
+    for m0, nm, k0, span in items.tolist():
+        assert 1 <= nm <= rows and 0 <= m0 and m0 + nm <= b and 1 <= span <= max_span
         mem = members[m0:m0 + nm].tolist()
-        for i in mem:
-            assert full[i] > k
-            covered[i].append(k)
-        for i in mem[1:]:
-            assert np.array_equal(r2t[i, :(k + 1) * chunk], r2t[mem[0], :(k + 1) * chunk])
+        for k in range(k0, k0 + span):
+            for i in mem:
+                assert full[i] > k
+                covered[i].append(k)
+            for i in mem[1:]:
+                assert np.array_equal(r2t[i, :(k + 1) * chunk], r2t[mem[0], :(k + 1) * chunk])
+            key = (k, tuple(r2t[mem[0], :(k + 1) * chunk]))
+            job_sizes[key] = job_sizes.get(key, 0) + nm
     for i in range(b):
         assert sorted(covered[i]) == list(range(skip[i])), (i, covered[i], skip[i])
     # every chunk listed for a sequence is shared with another one: jobs have >= 2 members
-    job_sizes = {}
-    for m0, nm, k in items.tolist():
-        job_sizes.setdefault((k, tuple(r2t[members[m0], :(k + 1) * chunk])), 0)
-        job_sizes[(k, tuple(r2t[members[m0], :(k + 1) * chunk]))] += nm
     assert all(v >= 2 for v in job_sizes.values())
     # maximal: agreement on chunks 0..k (whole in both) means both cover chunk k
     for i in range(b):
@@ -71,6 +72,11 @@ def test_fewshot_like_one_group():
     assert skip.tolist() == [6] * 20
     assert len(items) == 6 * 3                            # 20 members in items of <= 8
     assert items[:3, 2].tolist() == [0, 0, 0] and items[:3, 1].tolist() == [8, 8, 4]
+    assert items[:, 3].tolist() == [1] * 18
+    # spans of up to 4 chunks: chunks 0-3 and 4-5, three items each
+    members, skip, items = pkv.pkv_decode_shared_plan(r2t, lens, chunk, 8, max_span=4)
+    check_plan(r2t, lens, chunk, 8, members, skip, items, max_span=4)
+    assert items[:, 2:].tolist() == [[0, 4]] * 3 + [[4, 2]] * 3
 
 
 def test_tree_shaped_sharing_and_singletons():
@@ -117,19 +123,21 @@ def test_rejects_bad_arguments():
         pkv.pkv_decode_shared_plan(r2t, [10, 129], 64, 8)      # longer than the row
     with pytest.raises(pkv.PkvError):
         pkv.pkv_decode_shared_plan(r2t, [0, 10], 64, 8)        # empty sequence
+    with pytest.raises(pkv.PkvError):
+        pkv.pkv_decode_shared_plan(r2t, [10, 10], 64, 8, max_span=0)
 
 
 @settings(max_examples=150, deadline=None)
 @given(seed=st.integers(0, 10_000), n=st.integers(1, 24), depth=st.integers(1, 6), branch=st.integers(1, 3),
-       rows=st.sampled_from([1, 2, 16, 128]))
-def test_random_trees_against_brute_force(seed, n, depth, branch, rows):
+       rows=st.sampled_from([1, 2, 16, 128]), max_span=st.sampled_from([1, 2, 3, 8]))
+def test_random_trees_against_brute_force(seed, n, depth, branch, rows, max_span):
     rng = np.random.default_rng(seed)
     chunk, stride = 64, 64 * 8
     paths = [[int(x) for x in rng.integers(0, branch, size=depth)] for _ in range(n)]
     lens = [int(x) for x in rng.integers(1, stride + 1, size=n)]
     r2t = rows_from_paths(rng, paths, lens, chunk, stride)
-    members, skip, items = pkv.pkv_decode_shared_plan(r2t, lens, chunk, rows)
-    check_plan(r2t, lens, chunk, rows, members, skip, items)
+    members, skip, items = pkv.pkv_decode_shared_plan(r2t, lens, chunk, rows, max_span=max_span)
+    check_plan(r2t, lens, chunk, rows, members, skip, items, max_span)
     # rows built like the tree builds them: the last-slot shortcut gives the same plan
-    m2, s2, i2 = pkv.pkv_decode_shared_plan(r2t, lens, chunk, rows, rows_from_tree=True)
+    m2, s2, i2 = pkv.pkv_decode_shared_plan(r2t, lens, chunk, rows, rows_from_tree=True, max_span=max_span)
     assert np.array_equal(m2, members) and np.array_equal(s2, skip) and np.array_equal(i2, items)

@@ -229,6 +229,25 @@ def test_pool_beyond_4gib_high_slots(pool):
     report(f"pool beyond 4 GiB ({pool})", stats)
 
 
+@pytest.mark.parametrize("case", ["longctx", "decode", "fewshot"])
+def test_decode_shared_spans(case):
+    """The shared-prefix pass with items spanning several chunks (a low workgroup target makes
+    the plan merge chunks): every decode row against the oracle, both paths."""
+    log(f"decode shared spans ({case})")
+    if case == "longctx":
+        wl = workloads.longctx_fp8(prefix_len=2048, suffix_len=200, n_req=4, steps=2, pool_slots=8192)
+    elif case == "decode":
+        wl = workloads.decode_bf16(n_seq=24, n_prefix=4, prefix_len=512, ctx_range=(600, 1500), steps=2,
+                                   pool_slots=60000)
+    else:
+        wl = workloads.fewshot_bf16(n_req=6, prefix_len=900, suffix_range=(40, 120), decode_steps=2)
+    r = Run(wl)
+    r.eng.SHARED_MIN_WORKGROUPS = 16
+    stats = r.run()
+    assert r.plan is not None and int(r.plan["items"][:, 3].max()) >= 2, "no item spans two chunks"
+    report(f"decode shared spans ({case})", stats)
+
+
 def test_decode_split_invariance_and_extend_agreement():
     """Decode over one context with several chunk sizes agrees with itself and with extend's last row."""
     log("decode split invariance")
