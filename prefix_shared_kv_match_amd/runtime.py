@@ -19,11 +19,11 @@ from typing import List, Optional, Sequence
 
 import numpy as np
 
-from . import (PKV_BF16, PKV_F32, PKV_FP8_E4M3, check, lib, pkv_decode_attention, pkv_decode_attention_shared,
-               pkv_decode_chunk, pkv_decode_shared_plan, pkv_decode_shared_rows, rt_set_eviction_log,
-               pkv_decode_workspace_bytes, pkv_extend_attention, pkv_extend_plan, pkv_extend_tile, pkv_kv_scatter,
-               rt_create, rt_create_policy, rt_dec_lock_ref, rt_decode_step, rt_destroy, rt_finish, rt_peek_prefix,
-               rt_prepare_extend, rt_prepare_extend_prio, rt_release, rt_schedule_longest_prefix)
+from . import (PKV_BF16, PKV_F32, PKV_FP8_E4M3, check, lib, pkv_decode_chunk, pkv_decode_shared_plan,
+               pkv_decode_shared_rows, pkv_decode_workspace_bytes, pkv_extend_plan, pkv_extend_tile,
+               rt_create_policy, rt_dec_lock_ref, rt_decode_step, rt_destroy, rt_finish, rt_peek_prefix,
+               rt_prepare_extend, rt_prepare_extend_prio, rt_release, rt_schedule_longest_prefix,
+               rt_set_eviction_log)
 
 _DT = {"f32": PKV_F32, "bf16": PKV_BF16, "fp8_e4m3": PKV_FP8_E4M3}
 
