@@ -331,6 +331,8 @@ class JobBench:
         s = wl.shape
         self.eng = eng = Engine(wl.pool_slots, s.hq, s.hkv, s.d, s.qo_dtype, s.pool_dtype, wl.free_order, "cuda",
                                 sm_scale=s.sm_scale, policy=a.policy)
+        if a.shared_min_workgroups:
+            eng.SHARED_MIN_WORKGROUPS = a.shared_min_workgroups
         self.stride = wl.max_len()
         self.timer = Timer(torch)
         self.decode_only = False
@@ -369,7 +371,7 @@ class JobBench:
             self.dq = [self.Q.index_select(0, dr[i]) for i in range(self.steps_dec)]
             self.do = torch.empty_like(self.dq[0])
             self.max_len = max(len(r.tokens) for r in last) + self.steps_dec
-            self.ws, self.chunk = eng.decode_workspace(B, self.max_len)
+            self.ws, self.chunk = eng.decode_workspace(B, self.max_len, a.decode_chunk)
             self.full_tokens = [np.concatenate([r.tokens, wl.decode_tokens[:, i]]) for i, r in enumerate(last)]
             self.prompt_lens = [len(r.tokens) for r in last]
         torch.cuda.synchronize()
