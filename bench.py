@@ -685,10 +685,15 @@ def main():
     if b.steps_dec:
         ctx = hb.seq_lens.astype(np.float64)
         dec_bytes = float(ctx.sum()) * kv_tok
+        # the distinct K/V rows of the step: the bytes HBM must deliver at least once (the
+        # gathered bytes count a shared prefix once per sequence)
+        uniq = float(np.unique(np.concatenate([hb.req_to_token[i, :hb.seq_lens[i]] for i in range(hb.n)])).size)
         kernels["decode_attention"] = {
             "ms": dec_ms, "kv_gathered_gbps": dec_bytes / dec_ms / 1e6,
             "frac_hbm": dec_bytes / dec_ms / 1e6 / PEAK_HBM_GBPS, "bytes": dec_bytes,
             "frac_hbm_practical": dec_bytes / dec_ms / 1e6 / hbm_practical,
+            "unique_kv_bytes": uniq * kv_tok, "unique_gbps": uniq * kv_tok / dec_ms / 1e6,
+            "frac_hbm_unique": uniq * kv_tok / dec_ms / 1e6 / PEAK_HBM_GBPS,
             "tflops": 4.0 * s.d * s.hq * float(ctx.sum()) / dec_ms / 1e9}
     sc_name = "kv_scatter_decode" if b.decode_only else "kv_scatter"
     sc_ms = b.timer.avg_ms(sc_name)
