@@ -208,3 +208,48 @@ def test_staged_uploads_queued_without_host_sync(side_min_bytes):
         assert np.array_equal(g[0], s) and np.array_equal(g[1], n)
     for hb in hbs:
         eng.release(hb)
+
+
+def test_decode_shared_identical_and_boundary_contexts():
+    """Shared-prefix decode on contexts built to hit the plan's edges: two identical requests
+    (a full hit: they share every whole chunk but the newest token's), a context of exactly two
+    chunks, one cut inside a shared chunk, one shorter than a chunk, one private; every row
+    equals the plain decode's within float32 summation order (the plain path is checked against
+    the oracle by the parity tests)."""
+    from prefix_shared_kv_match_amd.runtime import Engine
+    log("decode shared: identical and boundary contexts")
+    rng = np.random.default_rng(11)
+    hq, hkv, d, chunk = 32, 8, 128, 128
+    eng = Engine(4096, hq, hkv, d, "bf16", "bf16", None, "cuda")
+    base = rng.integers(0, 50_000, size=400).astype(np.int32)
+    other = rng.integers(50_000, 100_000, size=400).astype(np.int32)
+    reqs = [base[:300], base[:300], base[:256], base[:200], base[:100],
+            np.concatenate([base[:128], other[:150]]), other[:333]]
+    stride = 512
+    hb = eng.prepare(reqs, stride)
+    n_new = hb.n_new
+    k = torch.randn(n_new, hkv, d).to(torch.bfloat16).cuda()
+    v = torch.randn(n_new, hkv, d).to(torch.bfloat16).cuda()
+    eng.scatter(torch.from_numpy(hb.new_slots.astype(np.int32)).cuda(), k, v)
+    slots = eng.decode_alloc(hb)
+    b = hb.n
+    eng.scatter(torch.from_numpy(slots).cuda(), torch.randn(b, hkv, d).to(torch.bfloat16).cuda(),
+                torch.randn(b, hkv, d).to(torch.bfloat16).cuda())
+    q = torch.randn(b, hq, d).to(torch.bfloat16).cuda()
+    r2t = torch.from_numpy(np.ascontiguousarray(hb.req_to_token)).cuda()
+    sl = torch.from_numpy(hb.seq_lens.copy()).cuda()
+    max_len = int(hb.seq_lens.max())
+    ws, _ = eng.decode_workspace(b, max_len, chunk)
+    plan = eng.decode_plan(hb.req_to_token, hb.seq_lens, chunk)
+    assert plan is not None
+    skip = plan["skip"].cpu().tolist()
+    # 0, 1 identical (301 tokens: chunks 0, 1 whole and shared); 2 (257) shares both; 3 (201)
+    # shares chunk 0 only; 4 (101) holds no whole chunk; 5 shares chunk 0 (its own 128 tokens);
+    # 6 is private
+    assert skip == [2, 2, 2, 1, 0, 1, 0], skip
+    plain = eng.decode(q, r2t, sl, max_len, ws, chunk).float()
+    shared = eng.decode(q, r2t, sl, max_len, ws, chunk, plan=plan).float()
+    torch.cuda.synchronize()
+    diff = (plain - shared).abs().max().item()
+    assert diff <= 2.0 ** -7 * plain.abs().max().item(), diff
+    eng.release(hb)
