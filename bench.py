@@ -458,11 +458,15 @@ class JobBench:
         if self.steps_dec:
             hb = self._last_hb
             r2t = self._last_dt["req_to_token"]
-            plan = None
+            plan_host = plan = None
             for i in range(self.steps_dec):
-                slots_dev, seq_dev = eng.upload_decode(eng.decode_alloc(hb), hb.seq_lens)
-                if i == 0 and not self.a.plain_decode:
-                    plan = eng.decode_plan(hb.req_to_token, hb.seq_lens, self.chunk)
+                slots = eng.decode_alloc(hb)
+                if i == 0 and not self.a.plain_decode:     # the batch's shared chunks, on the host
+                    plan_host = eng.decode_plan(hb.req_to_token, hb.seq_lens, self.chunk, upload=False)
+                if plan_host is None:
+                    slots_dev, seq_dev = eng.upload_decode(slots, hb.seq_lens)
+                else:                                       # sent with every step's slots
+                    slots_dev, seq_dev, plan = eng.upload_decode(slots, hb.seq_lens, plan_host)
                 eng.append_slots(r2t, seq_dev, slots_dev)
                 with T.span("kv_scatter_decode"):
                     eng.scatter(slots_dev, self.dk[i], self.dv[i])

@@ -326,20 +326,28 @@ int pkv_decode_attention(const void* q, void* o, int32_t qo_dtype, const void* k
  * the rows come from one radix tree (as rt_prepare_extend / rt_decode_step write them, while
  * the batch holds its locks): a slot then belongs to one node at one depth, so rows that hold
  * the same slot at a position agree on every earlier position and only each chunk's last
- * slot is compared; 0 compares every slot.  Returns the number of items, PKV_ERR_INVAL on
- * bad sizes or when items_cap is too small (the message gives the count).  The plan stays
- * valid while the sequences only grow (new tokens are private). */
+ * slot is compared; 0 compares every slot.  private_items = 1 appends, after the shared
+ * items, one-member items (spans of at most max_span chunks) over each sequence's remaining
+ * chunks up to the one holding its newest token, and sets skip[b] = ceil(seq_lens[b] / chunk):
+ * the shared-prefix kernel then takes the whole step (the kernel masks positions past each
+ * member's newest token), which pays when those tails are few and short.  Returns the number
+ * of items, PKV_ERR_INVAL on bad sizes or when items_cap is too small (the message gives the
+ * count).  The plan stays valid while the sequences only grow (new tokens are private; a
+ * sequence that grows into a chunk past skip[b] has it done by the split phase). */
 int64_t pkv_decode_shared_plan(const int32_t* req_to_token, int64_t stride, const int32_t* seq_lens, int32_t batch,
                                int32_t chunk, int32_t rows, int32_t max_span, int32_t rows_from_tree,
-                               int32_t* members, int32_t* skip, int32_t* items, int64_t items_cap);
+                               int32_t private_items, int32_t* members, int32_t* skip, int32_t* items,
+                               int64_t items_cap);
 /* Query rows (member sequences) per shared-prefix item for a shape: 128 / (hq / hkv), or
  * PKV_ERR_UNSUPPORTED (shared-prefix decode needs BF16 q/o, a BF16 or FP8_E4M3 pool, d = 128,
  * hq / hkv in {1, 2, 4, 8}). */
 int32_t pkv_decode_shared_rows(int32_t qo_dtype, int32_t pool_dtype, int32_t hq, int32_t hkv, int32_t d);
 /* pkv_decode_attention with a shared-prefix plan: members, skip, items are DEVICE copies of
  * pkv_decode_shared_plan's outputs (n_items of them) for the same slot rows and the same
- * (nonzero) chunk; first_split: the smallest skip[b] (0 is always correct), the split phase
- * launches chunks first_split and later only.  Items whose members or chunk fall outside the batch or the workspace are
+ * (nonzero) chunk; first_split: the smallest skip[b] over the sequences whose context reaches
+ * past chunk skip[b] (0 is always correct); the split phase launches chunks first_split and
+ * later only, and not at all when first_split >= ceil(max_seq_len / chunk).  Items whose
+ * members or chunk fall outside the batch or the workspace are
  * ignored (their partials are then left unwritten, so the result is wrong but no access
  * leaves the buffers).  Same result as pkv_decode_attention up to float32 summation order;
  * n_items = 0 is pkv_decode_attention. */

@@ -398,11 +398,12 @@ def pkv_decode_shared_rows(qo_dtype: int, pool_dtype: int, hq: int, hkv: int, d:
 
 
 def pkv_decode_shared_plan(req_to_token: np.ndarray, seq_lens, chunk: int, rows: int, rows_from_tree: bool = False,
-                           max_span: int = 1):
+                           max_span: int = 1, private_items: bool = False):
     """Host plan of the shared-prefix decode over host slot rows: (members [batch],
     skip [batch], items [n, 4]) as int32 arrays.  rows_from_tree: the rows come from one
     radix tree, so each chunk's last slot decides it (otherwise every slot is compared);
-    max_span: chunks one item may span."""
+    max_span: chunks one item may span; private_items: one-member items also cover every
+    sequence's remaining chunks (skip then reaches each context's end)."""
     r2t = _i32(req_to_token)
     sl = _i32(seq_lens)
     b = int(sl.size)
@@ -413,10 +414,12 @@ def pkv_decode_shared_plan(req_to_token: np.ndarray, seq_lens, chunk: int, rows:
     # a job holds two members or more, so it makes at most members / 2 items when an item
     # takes two or more rows (members per item); with one row per item, one item per member
     cap = max(b * (r2t.shape[1] // max(int(chunk), 1)) // (2 if rows >= 2 else 1) + 1, 1)
+    if private_items and chunk > 0:     # at most one private item per chunk of each context
+        cap += int(((sl.astype(np.int64) + chunk - 1) // chunk).sum())
     items = np.empty((cap, 4), dtype=np.int32)
     n = int(check(lib().pkv_decode_shared_plan(_ptr(r2t), r2t.shape[1], _ptr(sl), b, int(chunk), int(rows),
-                                               int(max_span), int(bool(rows_from_tree)), _ptr(members), _ptr(skip),
-                                               _ptr(items), cap)))
+                                               int(max_span), int(bool(rows_from_tree)), int(bool(private_items)),
+                                               _ptr(members), _ptr(skip), _ptr(items), cap)))
     return members[:b], skip[:b], items[:n]
 
 

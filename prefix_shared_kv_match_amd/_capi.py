@@ -67,7 +67,7 @@ SIGNATURES = {
     "pkv_decode_chunk": (_i32, [_i32, _i32, _i32]),
     "pkv_decode_attention": (C.c_int, [_p, _p, _i32, _p, _p, _i32, _i64, _p, _p, _p, _i64, _p, _i32, _i32, _i32,
                                        _i32, _i32, _f32, _i32, _p, _sz, _p]),
-    "pkv_decode_shared_plan": (_i64, [_p, _i64, _p, _i32, _i32, _i32, _i32, _i32, _p, _p, _p, _i64]),
+    "pkv_decode_shared_plan": (_i64, [_p, _i64, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p, _p, _i64]),
     "pkv_decode_shared_rows": (_i32, [_i32, _i32, _i32, _i32, _i32]),
     "pkv_decode_attention_shared": (C.c_int, [_p, _p, _i32, _p, _p, _i32, _i64, _p, _p, _p, _i64, _p, _i32, _i32,
                                               _i32, _i32, _i32, _f32, _i32, _p, _p, _p, _i64, _i32, _p, _sz, _p]),

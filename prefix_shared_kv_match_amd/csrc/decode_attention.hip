@@ -654,12 +654,16 @@ int decode_impl(const void* q, void* o, int32_t qo_dtype, const void* k_pool, co
   // private tails may be left: when the all-heads kernel would then launch too few
   // workgroups to fill the GPU (counting its head groups), the per-head kernel (16 token
   // streams each) takes them.
+  // A plan whose items cover every chunk (first_split >= max_splits) leaves no split phase.
   const int s0 = skip ? std::min(std::max(first_split, 0), max_splits - 1) : 0;
   const int ns = max_splits - s0;
   const int slot_groups = (hkv == 2 || hkv == 4 || hkv == 8) ? 1 : (hkv % 8 == 0 ? hkv / 8 : 0);
   const bool per_head = skip && (int64_t)batch * ns * slot_groups < 1024;
-  int rc;
-  if (qo_dtype == PKV_F32 && pool_dtype == PKV_F32 && d == 64)
+  const bool split_phase = !skip || first_split < max_splits;
+  int rc = PKV_OK;
+  if (!split_phase)
+    rc = PKV_OK;
+  else if (qo_dtype == PKV_F32 && pool_dtype == PKV_F32 && d == 64)
     rc = launch_split<float, PKV_F32, 64>(G, batch, s0, ns, per_head, st, q, k_pool, v_pool, k_scale, v_scale, req_to_token, stride,
                                           seq_lens, hkv, chunk, max_splits, sc, ml, acc, skip);
   else if (qo_dtype == PKV_F32 && pool_dtype == PKV_F32 && d == 128)
@@ -674,11 +678,13 @@ int decode_impl(const void* q, void* o, int32_t qo_dtype, const void* k_pool, co
   else
     return fail(PKV_ERR_UNSUPPORTED, "decode: qo dtype %d, pool dtype %d, d %d", qo_dtype, pool_dtype, d);
   if (rc < 0) return rc;
-  rc = hip_check(hipGetLastError(), "decode split launch");
-  if (rc < 0) return rc;
+  if (split_phase) {
+    rc = hip_check(hipGetLastError(), "decode split launch");
+    if (rc < 0) return rc;
+  }
   if (n_items > 0) {
     rc = launch_decode_shared(q, pool_dtype, k_pool, v_pool, k_scale, v_scale, num_slots, req_to_token, stride, batch,
-                              members, items, n_items, chunk, max_splits, hq, hkv, sc, ml, acc, st);
+                              seq_lens, members, items, n_items, chunk, max_splits, hq, hkv, sc, ml, acc, st);
     if (rc < 0) return rc;
   }
   const dim3 rgrid((unsigned)(((int64_t)batch * hq + kWaves - 1) / kWaves));

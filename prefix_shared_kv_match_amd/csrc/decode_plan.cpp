@@ -18,6 +18,12 @@
 // partial per span instead of one per chunk; spans are cut into items of at most `rows`
 // members, the query rows one kernel workgroup holds per kv head.
 //
+// With private_items, every sequence's remaining chunks (from skip[b] to the chunk holding
+// its newest token) become one-member items too, spans of up to max_span chunks, and skip[b]
+// moves past them: the MFMA kernel then takes the whole step and the split phase has nothing
+// left (worth it when those tails are short and few, where the split phase's workgroups are
+// latency-bound; the kernel masks the positions past each member's newest token).
+//
 // Rows that come from one radix tree need no whole-chunk comparison: a slot belongs to one
 // node at one depth, so two rows holding the same slot at a position hold the same slots at
 // every earlier position too, and comparing a chunk's last slot decides the whole chunk.
@@ -34,8 +40,8 @@ using namespace pkv;
 
 extern "C" int64_t pkv_decode_shared_plan(const int32_t* req_to_token, int64_t stride, const int32_t* seq_lens,
                                           int32_t batch, int32_t chunk, int32_t rows, int32_t max_span,
-                                          int32_t rows_from_tree, int32_t* members, int32_t* skip, int32_t* items,
-                                          int64_t items_cap) {
+                                          int32_t rows_from_tree, int32_t private_items, int32_t* members,
+                                          int32_t* skip, int32_t* items, int64_t items_cap) {
   if (batch < 0 || stride <= 0 || chunk < 64 || chunk % 64 || rows <= 0 || max_span <= 0 || items_cap < 0)
     return fail(PKV_ERR_INVAL, "decode plan: bad sizes (batch %d stride %lld chunk %d rows %d span %d)", batch,
                 (long long)stride, chunk, rows, max_span);
@@ -120,17 +126,26 @@ extern "C" int64_t pkv_decode_shared_plan(const int32_t* req_to_token, int64_t s
   std::stable_sort(spans.begin(), spans.end(),
                    [](const Span& x, const Span& y) { return x.k != y.k ? x.k < y.k : x.lo < y.lo; });
   int64_t n_items = 0;
-  for (const Span& sp : spans)
-    for (int32_t i = 0; i < sp.cnt; i += rows) {
-      if (n_items < items_cap) {
-        int32_t* it = items + 4 * n_items;
-        it[0] = sp.lo + i;
-        it[1] = std::min(rows, sp.cnt - i);
-        it[2] = sp.k;
-        it[3] = sp.span;
-      }
-      ++n_items;
+  auto emit = [&](int32_t m0, int32_t nm, int32_t k, int32_t span) {
+    if (n_items < items_cap) {
+      int32_t* it = items + 4 * n_items;
+      it[0] = m0;
+      it[1] = nm;
+      it[2] = k;
+      it[3] = span;
     }
+    ++n_items;
+  };
+  for (const Span& sp : spans)
+    for (int32_t i = 0; i < sp.cnt; i += rows) emit(sp.lo + i, std::min(rows, sp.cnt - i), sp.k, sp.span);
+  if (private_items) {
+    for (int32_t i = 0; i < batch; ++i) {
+      const int32_t b = members[i];
+      const int32_t last = (int32_t)((seq_lens[b] - 1) / chunk);   // the chunk of the newest token
+      for (int32_t k = skip[b]; k <= last; k += max_span) emit(i, 1, k, std::min(max_span, last - k + 1));
+      skip[b] = last + 1;
+    }
+  }
   if (n_items > items_cap) return fail(PKV_ERR_INVAL, "decode plan: needs %lld items", (long long)n_items);
   return n_items;
 }

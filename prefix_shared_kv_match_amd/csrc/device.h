@@ -111,7 +111,8 @@ inline int hip_check(hipError_t e, const char* what) {
 // group size 1, 2, 4 or 8.
 int launch_decode_shared(const void* q, int32_t pool_dtype, const void* k_pool, const void* v_pool,
                          const float* k_scale, const float* v_scale, int64_t num_slots, const int32_t* r2t,
-                         int64_t stride, int32_t batch, const int32_t* members, const int32_t* items, int64_t n_items,
+                         int64_t stride, int32_t batch, const int32_t* seq_lens, const int32_t* members,
+                         const int32_t* items, int64_t n_items,
                          int chunk, int max_splits, int hq, int hkv, float sc_log2, float* ws_ml, float* ws_acc,
                          hipStream_t st);
 

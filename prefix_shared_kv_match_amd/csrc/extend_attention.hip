@@ -214,26 +214,29 @@ struct WaveAttn {
     ones_row = bf16x8{one, one, one, one, one, one, one, one};
   }
 
-  // Rows of a shared-prefix decode item instead of extend rows: row r of the workgroup is the
-  // newest token of sequence members[m0 + r % BT] at head g * G + r / BT (nm real members);
-  // every row sees the whole chunk, so no tile is masked.
-  __device__ __forceinline__ void init_shared(const bf16* q, const int32_t* members, int m0, int nm, int batch, int hq,
-                                              int g, int wave, int lane, float scale) {
+  // Rows of a decode item instead of extend rows: row r of the workgroup is the newest token
+  // of sequence members[m0 + r % BT] at head g * G + r / BT (nm real members), which sees
+  // positions 0 .. seq_lens[b] - 1.  A shared item's chunks lie inside every member's context,
+  // so its tiles never reach the mask; a one-member item over a sequence's own last chunk
+  // masks the positions past its newest token.
+  __device__ __forceinline__ void init_shared(const bf16* q, const int32_t* members, const int32_t* seq_lens, int m0,
+                                              int nm, int batch, int hq, int g, int wave, int lane, float scale) {
     ln = lane & 15;
     lg = lane >> 4;
     sc = scale;
-    qpos0 = 0x3FFFFFFF;   // beyond every tile: the mask branch is never taken
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       const int r0 = 32 * wave + 16 * nb;
       qh[nb] = g * G + r0 / BT;
       qt[nb] = r0 % BT + ln;
-      vis[nb] = qpos0;
+      vis[nb] = 0x3FFFFFFF;   // padding rows see everything
       int b = qt[nb] < nm ? members[m0 + qt[nb]] : -1;
       const bool ok = b >= 0 && b < batch;   // a member index outside the batch is a padding row
       if (!ok) {
         b = 0;
         qt[nb] = BT;   // never stored
+      } else {
+        vis[nb] = seq_lens[b] - 1;
       }
       const bf16* qp = q + ((int64_t)b * hq + qh[nb]) * kD + 8 * lg;
 #pragma unroll
@@ -246,6 +249,11 @@ struct WaveAttn {
       for (int db = 0; db < 8; ++db) oacc[nb][db] = floatx4{0.f, 0.f, 0.f, 0.f};
       m[nb] = -INFINITY;
     }
+    // the wave's earliest newest-token position: tiles ending at or before it need no mask
+    int v = min(vis[0], vis[1]);
+#pragma unroll
+    for (int off = 32; off >= 1; off /= 2) v = min(v, __shfl_xor(v, off));
+    qpos0 = v;
     const bf16 one = (bf16)(ln == 0 ? 1.f : 0.f);
     ones_row = bf16x8{one, one, one, one, one, one, one, one};
   }
@@ -718,6 +726,7 @@ __global__ __launch_bounds__(256, 2) void decode_shared_dma(const bf16* __restri
                                                             const uint8_t* __restrict__ vpool,
                                                             const int32_t* __restrict__ r2t, int64_t stride,
                                                             const int32_t* __restrict__ members,
+                                                            const int32_t* __restrict__ seq_lens,
                                                             const int32_t* __restrict__ items, int chunk,
                                                             int max_splits, int hkv, float scale_log2, int num_slots,
                                                             int table_bytes, int batch, float* __restrict__ ws_ml,
@@ -751,7 +760,7 @@ __global__ __launch_bounds__(256, 2) void decode_shared_dma(const bf16* __restri
   };
 
   WaveAttn<G> wa;
-  wa.init_shared(q, members, m0, nm, batch, hq, g, wave, lane, scale_log2);
+  wa.init_shared(q, members, seq_lens, m0, nm, batch, hq, g, wave, lane, scale_log2);
   const bool active = G != 1 || 32 * wave < nm;
   int kb[4], vb[2][2];
 #pragma unroll
@@ -797,6 +806,7 @@ __global__ __launch_bounds__(256, 2) void decode_shared_fp8(const bf16* __restri
                                                             const float* __restrict__ vscale,
                                                             const int32_t* __restrict__ r2t, int64_t stride,
                                                             const int32_t* __restrict__ members,
+                                                            const int32_t* __restrict__ seq_lens,
                                                             const int32_t* __restrict__ items, int chunk,
                                                             int max_splits, int hkv, float scale_log2, int num_slots,
                                                             int table_bytes, int batch, float* __restrict__ ws_ml,
@@ -820,7 +830,7 @@ __global__ __launch_bounds__(256, 2) void decode_shared_fp8(const bf16* __restri
   const int kv_begin = s * chunk;
 
   WaveAttn<G> wa;
-  wa.init_shared(q, members, m0, nm, batch, hq, g, wave, lane, scale_log2 * kscale[g]);
+  wa.init_shared(q, members, seq_lens, m0, nm, batch, hq, g, wave, lane, scale_log2 * kscale[g]);
   const bool active = G != 1 || 32 * wave < nm;
 
   Fp8Stage stage;
@@ -852,7 +862,8 @@ int mfma_tile(int G) { return kRows / G; }
 
 int launch_decode_shared(const void* q, int32_t pool_dtype, const void* k_pool, const void* v_pool,
                          const float* k_scale, const float* v_scale, int64_t num_slots, const int32_t* r2t,
-                         int64_t stride, int32_t batch, const int32_t* members, const int32_t* items, int64_t n_items,
+                         int64_t stride, int32_t batch, const int32_t* seq_lens, const int32_t* members,
+                         const int32_t* items, int64_t n_items,
                          int chunk, int max_splits, int hq, int hkv, float sc_log2, float* ws_ml, float* ws_acc,
                          hipStream_t st) {
   const int G = hq / hkv;
@@ -868,15 +879,15 @@ int launch_decode_shared(const void* q, int32_t pool_dtype, const void* k_pool, 
   if (G == GG) {                                                                                                 \
     if (pool_dtype == PKV_BF16 && narrow)                                                                        \
       hipLaunchKernelGGL((decode_shared_dma<GG, true>), grid, dim3(256), 0, st, (const bf16*)q,                 \
-                         (const uint8_t*)k_pool, (const uint8_t*)v_pool, r2t, stride, members, items, chunk,     \
+                         (const uint8_t*)k_pool, (const uint8_t*)v_pool, r2t, stride, members, seq_lens, items, chunk, \
                          max_splits, hkv, sc_log2, (int)num_slots, (int)table_bytes, batch, ws_ml, ws_acc);      \
     else if (pool_dtype == PKV_BF16)                                                                             \
       hipLaunchKernelGGL((decode_shared_dma<GG, false>), grid, dim3(256), 0, st, (const bf16*)q,                \
-                         (const uint8_t*)k_pool, (const uint8_t*)v_pool, r2t, stride, members, items, chunk,     \
+                         (const uint8_t*)k_pool, (const uint8_t*)v_pool, r2t, stride, members, seq_lens, items, chunk, \
                          max_splits, hkv, sc_log2, (int)num_slots, (int)table_bytes, batch, ws_ml, ws_acc);      \
     else                                                                                                         \
       hipLaunchKernelGGL((decode_shared_fp8<GG>), grid, dim3(256), 0, st, (const bf16*)q, (const uint8_t*)k_pool, \
-                         (const uint8_t*)v_pool, k_scale, v_scale, r2t, stride, members, items, chunk,           \
+                         (const uint8_t*)v_pool, k_scale, v_scale, r2t, stride, members, seq_lens, items, chunk, \
                          max_splits, hkv, sc_log2, (int)num_slots, (int)table_bytes, batch, ws_ml, ws_acc);      \
     return hip_check(hipGetLastError(), "decode_shared launch");                                                 \
   }

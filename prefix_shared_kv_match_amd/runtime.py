@@ -153,6 +153,10 @@ class Engine:
     """One radix tree plus its device KV pools."""
 
     SHARED_MIN_WORKGROUPS = 512
+    # shared-prefix plans whose items and private tails together need at most this many
+    # workgroups (items x kv heads) also give the tails to the shared-prefix kernel
+    PRIVATE_MAX_WORKGROUPS = 4096
+    NO_SPLIT_PHASE = 1 << 30
 
     def __init__(self, num_slots: int, hq: int, hkv: int, d: int, qo_dtype: str, pool_dtype: str,
                  free_order: Optional[np.ndarray] = None, device: str = "cuda", k_scale=None, v_scale=None,
@@ -270,9 +274,12 @@ class Engine:
         hn[3 * n:4 * n] = plan["skip"]
         hn[4 * n:4 * n + m] = plan["items"].reshape(-1)
         dev = up.send(4 * n + m)
+        # the split phase starts at the first chunk a sequence still needs (none: no launch)
+        skip, c = plan["skip"], plan["chunk"]
+        need = (np.asarray(seq_lens, dtype=np.int64) + c - 1) // c > skip
+        first = int(skip[need].min()) if need.any() else self.NO_SPLIT_PHASE
         return dev[:n], dev[n:2 * n], dict(members=dev[2 * n:3 * n], skip=dev[3 * n:4 * n],
-                                           items=dev[4 * n:4 * n + m].view(-1, 4), chunk=plan["chunk"],
-                                           first_split=plan["first_split"])
+                                           items=dev[4 * n:4 * n + m].view(-1, 4), chunk=c, first_split=first)
 
     # -- steps ---------------------------------------------------------------------------
     def prepare(self, token_lists, stride: int) -> HostBatch:
@@ -359,12 +366,17 @@ class Engine:
         members, skip, items = pkv_decode_shared_plan(req_to_token, seq_lens, chunk, rows, rows_from_tree=True)
         if items.shape[0] == 0:
             return None
+        # few, short private tails: one-member items take them too and the split phase (whose
+        # workgroups would then be latency-bound) is not launched
+        lens = np.asarray(seq_lens, dtype=np.int64)
+        tails = int(((lens + chunk - 1) // chunk - skip).sum())
+        private = (items.shape[0] + tails) * self.hkv <= self.PRIVATE_MAX_WORKGROUPS
         # a long shared prefix: items spanning several chunks, as long as about 512
         # workgroups (items x kv heads) remain, write fewer partials
-        span = items.shape[0] * self.hkv // self.SHARED_MIN_WORKGROUPS
-        if span >= 2:
+        span = (items.shape[0] + (tails if private else 0)) * self.hkv // self.SHARED_MIN_WORKGROUPS
+        if span >= 2 or private:
             members, skip, items = pkv_decode_shared_plan(req_to_token, seq_lens, chunk, rows, rows_from_tree=True,
-                                                          max_span=span)
+                                                          max_span=max(span, 1), private_items=private)
         if not upload:
             return dict(members=members, skip=skip, items=items, chunk=int(chunk), first_split=int(skip.min()))
         b, n = members.size, items.size

@@ -180,6 +180,7 @@ class Run:
             # as the sequences grow), wherever the batch shares whole chunks
             if s == 0:
                 self.plan = eng.decode_plan(hb.req_to_token, hb.seq_lens, chunk)
+                self.plan_lens = hb.seq_lens.copy()
                 if self.plan is not None:
                     self.shared_items = int(self.plan["items"].shape[0])
             outs = [("plain", o)]

@@ -3,7 +3,8 @@ pairs of slot rows: members is a permutation, every item's members hold its chun
 slot for slot equal, each sequence's chunks 0 .. skip-1 are covered exactly once, and the
 plan is maximal (two sequences that agree on chunks 0..k, whole in both contexts, both share
 chunk k).  On rows built the way the radix tree builds them, the last-slot shortcut
-(rows_from_tree) gives the same plan."""
+(rows_from_tree) gives the same plan.  With private_items the same shared items come first and
+one-member items then cover every sequence's remaining chunks, once each."""
 import numpy as np
 import pytest
 from hypothesis import given, settings, strategies as st
@@ -61,6 +62,24 @@ def check_plan(r2t, lens, chunk, rows, members, skip, items, max_span=1):
             assert skip[i] >= k and skip[j] >= k, (i, j, k, skip[i], skip[j])
 
 
+def check_private(r2t, lens, chunk, rows, max_span, rows_from_tree=False):
+    """The private-items plan: the shared plan's members and items first, then one-member items
+    of at most max_span chunks covering chunks skip[b] .. ceil(L / chunk) - 1 of each sequence
+    exactly once; skip[b] = ceil(L / chunk)."""
+    m0, s0, i0 = pkv.pkv_decode_shared_plan(r2t, lens, chunk, rows, rows_from_tree, max_span)
+    m, s, it = pkv.pkv_decode_shared_plan(r2t, lens, chunk, rows, rows_from_tree, max_span, private_items=True)
+    n0 = len(i0)
+    assert np.array_equal(m, m0) and np.array_equal(it[:n0], i0)
+    ends = [(L + chunk - 1) // chunk for L in lens]
+    assert s.tolist() == ends
+    covered = {b: [] for b in range(len(lens))}
+    for m_0, nm, k0, span in it[n0:].tolist():
+        assert nm == 1 and 1 <= span <= max_span and 0 <= m_0 < len(lens)
+        covered[int(m[m_0])] += list(range(k0, k0 + span))
+    for b in range(len(lens)):
+        assert sorted(covered[b]) == list(range(s0[b], ends[b])), (b, covered[b], s0[b], ends[b])
+
+
 def test_fewshot_like_one_group():
     rng = np.random.default_rng(0)
     chunk, stride = 64, 640
@@ -77,6 +96,11 @@ def test_fewshot_like_one_group():
     members, skip, items = pkv.pkv_decode_shared_plan(r2t, lens, chunk, 8, max_span=4)
     check_plan(r2t, lens, chunk, 8, members, skip, items, max_span=4)
     assert items[:, 2:].tolist() == [[0, 4]] * 3 + [[4, 2]] * 3
+    # private items: every sequence's chunks from 6 to the one holding its newest token
+    check_private(r2t, lens, chunk, 8, 4)
+    # shared: 3 spans of 2 chunks x 3 items, then the private ones
+    m, s, it = pkv.pkv_decode_shared_plan(r2t, lens, chunk, 8, max_span=2, private_items=True)
+    assert all(nm == 1 for nm in it[9:, 1]) and len(it) == 9 + sum(((L + 63) // 64 - 6 + 1) // 2 for L in lens)
 
 
 def test_tree_shaped_sharing_and_singletons():
@@ -141,3 +165,4 @@ def test_random_trees_against_brute_force(seed, n, depth, branch, rows, max_span
     # rows built like the tree builds them: the last-slot shortcut gives the same plan
     m2, s2, i2 = pkv.pkv_decode_shared_plan(r2t, lens, chunk, rows, rows_from_tree=True, max_span=max_span)
     assert np.array_equal(m2, members) and np.array_equal(s2, skip) and np.array_equal(i2, items)
+    check_private(r2t, lens, chunk, rows, max_span, rows_from_tree=seed % 2 == 0)

@@ -122,6 +122,7 @@ def test_decode_two_long_sequences_many_splits():
     wl = workloads.decode_bf16(n_seq=2, n_prefix=1, prefix_len=1024, ctx_range=(12000, 15000), steps=2,
                                pool_slots=40000)
     r = Run(wl)
+    r.eng.PRIVATE_MAX_WORKGROUPS = 0   # the private tails stay with the split phase
     stats = r.run()
     assert r.shared_items == 8         # one item per shared 128-token chunk of the 1,024-token prefix
     report("decode two long sequences", stats)
@@ -229,11 +230,13 @@ def test_pool_beyond_4gib_high_slots(pool):
     report(f"pool beyond 4 GiB ({pool})", stats)
 
 
+@pytest.mark.parametrize("private", [False, True], ids=["shared", "private"])
 @pytest.mark.parametrize("case", ["longctx", "decode", "fewshot"])
-def test_decode_shared_spans(case):
+def test_decode_shared_spans(case, private):
     """The shared-prefix pass with items spanning several chunks (a low workgroup target makes
-    the plan merge chunks): every decode row against the oracle, both paths."""
-    log(f"decode shared spans ({case})")
+    the plan merge chunks), with and without one-member items over the private tails: every
+    decode row against the oracle, both paths."""
+    log(f"decode shared spans ({case}, {'private items' if private else 'shared items only'})")
     if case == "longctx":
         wl = workloads.longctx_fp8(prefix_len=2048, suffix_len=200, n_req=4, steps=2, pool_slots=8192)
     elif case == "decode":
@@ -243,9 +246,13 @@ def test_decode_shared_spans(case):
         wl = workloads.fewshot_bf16(n_req=6, prefix_len=900, suffix_range=(40, 120), decode_steps=2)
     r = Run(wl)
     r.eng.SHARED_MIN_WORKGROUPS = 16
+    r.eng.PRIVATE_MAX_WORKGROUPS = 1 << 20 if private else 0
     stats = r.run()
     assert r.plan is not None and int(r.plan["items"][:, 3].max()) >= 2, "no item spans two chunks"
-    report(f"decode shared spans ({case})", stats)
+    skip = r.plan["skip"].cpu().numpy()
+    ends = (r.plan_lens + r.plan["chunk"] - 1) // r.plan["chunk"]
+    assert np.array_equal(skip, ends) if private else (skip < ends).any()
+    report(f"decode shared spans ({case}, private {private})", stats)
 
 
 def test_decode_split_invariance_and_extend_agreement():

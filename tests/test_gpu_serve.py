@@ -213,9 +213,12 @@ def test_staged_uploads_queued_without_host_sync(side_min_bytes):
 def test_decode_shared_identical_and_boundary_contexts():
     """Shared-prefix decode on contexts built to hit the plan's edges: two identical requests
     (a full hit: they share every whole chunk but the newest token's), a context of exactly two
-    chunks, one cut inside a shared chunk, one shorter than a chunk, one private; every row
-    equals the plain decode's within float32 summation order (the plain path is checked against
-    the oracle by the parity tests)."""
+    chunks, one cut inside a shared chunk, one shorter than a chunk, one private, one that
+    fills two chunks and then grows into a third; every row equals the plain decode's within
+    float32 summation order (the plain path is checked against the oracle by the parity
+    tests).  Both plans: shared chunks only, and with the private tails as one-member items
+    (made at the first step and kept while the sequences grow, the split phase launched from
+    the first chunk a sequence still needs, or not at all)."""
     from prefix_shared_kv_match_amd.runtime import Engine
     log("decode shared: identical and boundary contexts")
     rng = np.random.default_rng(11)
@@ -224,32 +227,42 @@ def test_decode_shared_identical_and_boundary_contexts():
     base = rng.integers(0, 50_000, size=400).astype(np.int32)
     other = rng.integers(50_000, 100_000, size=400).astype(np.int32)
     reqs = [base[:300], base[:300], base[:256], base[:200], base[:100],
-            np.concatenate([base[:128], other[:150]]), other[:333]]
+            np.concatenate([base[:128], other[:150]]), other[:333], base[:255]]
     stride = 512
     hb = eng.prepare(reqs, stride)
     n_new = hb.n_new
     k = torch.randn(n_new, hkv, d).to(torch.bfloat16).cuda()
     v = torch.randn(n_new, hkv, d).to(torch.bfloat16).cuda()
     eng.scatter(torch.from_numpy(hb.new_slots.astype(np.int32)).cuda(), k, v)
-    slots = eng.decode_alloc(hb)
     b = hb.n
-    eng.scatter(torch.from_numpy(slots).cuda(), torch.randn(b, hkv, d).to(torch.bfloat16).cuda(),
-                torch.randn(b, hkv, d).to(torch.bfloat16).cuda())
-    q = torch.randn(b, hq, d).to(torch.bfloat16).cuda()
-    r2t = torch.from_numpy(np.ascontiguousarray(hb.req_to_token)).cuda()
-    sl = torch.from_numpy(hb.seq_lens.copy()).cuda()
-    max_len = int(hb.seq_lens.max())
+    max_len = int(hb.seq_lens.max()) + 3
     ws, _ = eng.decode_workspace(b, max_len, chunk)
-    plan = eng.decode_plan(hb.req_to_token, hb.seq_lens, chunk)
-    assert plan is not None
-    skip = plan["skip"].cpu().tolist()
-    # 0, 1 identical (301 tokens: chunks 0, 1 whole and shared); 2 (257) shares both; 3 (201)
-    # shares chunk 0 only; 4 (101) holds no whole chunk; 5 shares chunk 0 (its own 128 tokens);
-    # 6 is private
-    assert skip == [2, 2, 2, 1, 0, 1, 0], skip
-    plain = eng.decode(q, r2t, sl, max_len, ws, chunk).float()
-    shared = eng.decode(q, r2t, sl, max_len, ws, chunk, plan=plan).float()
-    torch.cuda.synchronize()
-    diff = (plain - shared).abs().max().item()
-    assert diff <= 2.0 ** -7 * plain.abs().max().item(), diff
+    plans = {}
+    for step in range(3):
+        slots = eng.decode_alloc(hb)
+        eng.scatter(torch.from_numpy(slots).cuda(), torch.randn(b, hkv, d).to(torch.bfloat16).cuda(),
+                    torch.randn(b, hkv, d).to(torch.bfloat16).cuda())
+        q = torch.randn(b, hq, d).to(torch.bfloat16).cuda()
+        r2t = torch.from_numpy(np.ascontiguousarray(hb.req_to_token)).cuda()
+        sl = torch.from_numpy(hb.seq_lens.copy()).cuda()
+        if step == 0:
+            eng.PRIVATE_MAX_WORKGROUPS = 0
+            plans["shared"] = eng.decode_plan(hb.req_to_token, hb.seq_lens, chunk, upload=False)
+            eng.PRIVATE_MAX_WORKGROUPS = Engine.PRIVATE_MAX_WORKGROUPS
+            plans["private"] = eng.decode_plan(hb.req_to_token, hb.seq_lens, chunk, upload=False)
+            # 0, 1 identical (301 tokens: chunks 0, 1 whole and shared); 2 (257) shares both; 3
+            # (201) shares chunk 0 only; 4 (101) holds no whole chunk; 5 shares chunk 0 (its own
+            # 128 tokens); 6 is private; 7 (256: its newest token ends chunk 1) shares chunk 0
+            assert plans["shared"]["skip"].tolist() == [2, 2, 2, 1, 0, 1, 0, 1]
+            assert plans["private"]["skip"].tolist() == [3, 3, 3, 2, 1, 3, 3, 2]
+        plain = eng.decode(q, r2t, sl, max_len, ws, chunk).float()
+        for name, host_plan in plans.items():
+            _, _, plan = eng.upload_decode(slots, hb.seq_lens, host_plan)
+            if name == "private":
+                # every chunk is an item at the first step; then sequence 7 grows into chunk 2
+                assert plan["first_split"] == (Engine.NO_SPLIT_PHASE if step == 0 else 2), (step, plan["first_split"])
+            shared = eng.decode(q, r2t, sl, max_len, ws, chunk, plan=plan).float()
+            torch.cuda.synchronize()
+            diff = (plain - shared).abs().max().item()
+            assert diff <= 2.0 ** -7 * plain.abs().max().item(), (step, name, diff)
     eng.release(hb)
