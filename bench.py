@@ -42,12 +42,12 @@ CSRC = os.path.join(ROOT, "prefix_shared_kv_match_amd", "csrc")
 # what the same counters read for a plain 1 GiB device copy (FETCH x2.0, WRITE x1.0).  Each
 # entry holds the hash of the kernel sources it was taken on; a changed kernel reports null.
 TRAFFIC = {
-    "fewshot_bf16": dict(kernel="extend_attention", src_hash="67016657fb84bcee",
-                         fetch_kib=204737.0, write_kib=102974.0),
-    "decode_bf16": dict(kernel="decode_attention", src_hash="28f461d287ea8bb5",
-                        fetch_kib=4214605.0 + 35174.0 + 23302.0, write_kib=39256.0 + 8704.0 + 4096.0),
-    "longctx_fp8": dict(kernel="extend_attention", src_hash="67016657fb84bcee",
-                        fetch_kib=1704811.0, write_kib=262144.0),
+    "fewshot_bf16": dict(kernel="extend_attention", src_hash="331a9425f55b6f4a",
+                         fetch_kib=204946.0, write_kib=102979.0),
+    "decode_bf16": dict(kernel="decode_attention", src_hash="d2553de404a13387",
+                        fetch_kib=4214637.0 + 35187.0 + 23302.0, write_kib=39256.0 + 8704.0 + 4096.0),
+    "longctx_fp8": dict(kernel="extend_attention", src_hash="331a9425f55b6f4a",
+                        fetch_kib=1704504.0, write_kib=262145.0),
 }
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 # (warmup, timed) steps when not given: a few hundred ms of warmup for sub-millisecond steps,
