@@ -274,12 +274,19 @@ class Engine:
         hn[3 * n:4 * n] = plan["skip"]
         hn[4 * n:4 * n + m] = plan["items"].reshape(-1)
         dev = up.send(4 * n + m)
-        # the split phase starts at the first chunk a sequence still needs (none: no launch)
-        skip, c = plan["skip"], plan["chunk"]
-        need = (np.asarray(seq_lens, dtype=np.int64) + c - 1) // c > skip
-        first = int(skip[need].min()) if need.any() else self.NO_SPLIT_PHASE
+        first = self.first_split(plan["skip"], seq_lens, plan["chunk"])
         return dev[:n], dev[n:2 * n], dict(members=dev[2 * n:3 * n], skip=dev[3 * n:4 * n],
-                                           items=dev[4 * n:4 * n + m].view(-1, 4), chunk=c, first_split=first)
+                                           items=dev[4 * n:4 * n + m].view(-1, 4), chunk=plan["chunk"],
+                                           first_split=first)
+
+    @classmethod
+    def first_split(cls, skip: np.ndarray, seq_lens: np.ndarray, chunk: int) -> int:
+        """The first chunk the split phase must launch for a plan's skip at the current
+        lengths: the smallest skip[b] of a sequence whose context reaches past chunk skip[b],
+        or NO_SPLIT_PHASE when the plan's items cover every sequence's context."""
+        skip = np.asarray(skip, dtype=np.int64)
+        need = (np.asarray(seq_lens, dtype=np.int64) + chunk - 1) // chunk > skip
+        return int(skip[need].min()) if need.any() else cls.NO_SPLIT_PHASE
 
     # -- steps ---------------------------------------------------------------------------
     def prepare(self, token_lists, stride: int) -> HostBatch:

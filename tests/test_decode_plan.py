@@ -166,3 +166,21 @@ def test_random_trees_against_brute_force(seed, n, depth, branch, rows, max_span
     m2, s2, i2 = pkv.pkv_decode_shared_plan(r2t, lens, chunk, rows, rows_from_tree=True, max_span=max_span)
     assert np.array_equal(m2, members) and np.array_equal(s2, skip) and np.array_equal(i2, items)
     check_private(r2t, lens, chunk, rows, max_span, rows_from_tree=seed % 2 == 0)
+
+
+def test_first_split_at_current_lengths():
+    """The split phase's first chunk for a plan kept while the sequences grow: none while the
+    items cover every context, then the skip of the first sequence that grows past them."""
+    from prefix_shared_kv_match_amd.runtime import Engine
+    rng = np.random.default_rng(3)
+    chunk, stride = 64, 512
+    paths = [[0, 1, 2], [0, 1, 2], [0, 1, 3], [4]]
+    lens = np.array([200, 256, 190, 100])
+    r2t = rows_from_paths(rng, paths, lens.tolist(), chunk, stride)
+    m, skip, it = pkv.pkv_decode_shared_plan(r2t, lens, chunk, 16, private_items=True)
+    assert skip.tolist() == [4, 4, 3, 2]
+    assert Engine.first_split(skip, lens, chunk) == Engine.NO_SPLIT_PHASE
+    assert Engine.first_split(skip, lens + 1, chunk) == 4          # sequence 1 reaches chunk 4
+    assert Engine.first_split(skip, lens + 3, chunk) == 3          # sequence 2 reaches chunk 3
+    _, s0, _ = pkv.pkv_decode_shared_plan(r2t, lens, chunk, 16)   # shared chunks only
+    assert s0.tolist() == [3, 3, 2, 0] and Engine.first_split(s0, lens, chunk) == 0
