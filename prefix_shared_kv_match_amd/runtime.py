@@ -363,8 +363,13 @@ class Engine:
         device: a dict of int32 views (members, skip, items) valid for work launched before the
         next call, or None when no chunk is shared or the shape has no shared-prefix kernel.
         Computed once, it serves every later decode step of the same sequences (new tokens are
-        private, so the shared chunks do not change).  upload=False returns the host arrays,
-        for upload_decode to send with a step's slots."""
+        private, so the shared chunks do not change; a chunk a sequence grows into is left to
+        the split phase).  When the shared items and the private tails together need at most
+        PRIVATE_MAX_WORKGROUPS workgroups, the tails become one-member items too and the split
+        phase has nothing left at this step.  The device plan's first_split is the smallest
+        skip (right at any later step); upload=False returns the host arrays, for
+        upload_decode to send with a step's slots and to set first_split from that step's
+        lengths."""
         rows = self.shared_rows
         if rows <= 0:
             return None
