@@ -255,7 +255,15 @@ def test_decode_shared_identical_and_boundary_contexts():
             # 128 tokens); 6 is private; 7 (256: its newest token ends chunk 1) shares chunk 0
             assert plans["shared"]["skip"].tolist() == [2, 2, 2, 1, 0, 1, 0, 1]
             assert plans["private"]["skip"].tolist() == [3, 3, 3, 2, 1, 3, 3, 2]
+            # the same private plan on the device, made once: its split phase starts at the
+            # smallest skip at every step
+            device_plan = eng.decode_plan(hb.req_to_token, hb.seq_lens, chunk)
+            assert device_plan["first_split"] == 1
         plain = eng.decode(q, r2t, sl, max_len, ws, chunk).float()
+        shared = eng.decode(q, r2t, sl, max_len, ws, chunk, plan=device_plan).float()
+        torch.cuda.synchronize()
+        diff = (plain - shared).abs().max().item()
+        assert diff <= 2.0 ** -7 * plain.abs().max().item(), (step, "device plan", diff)
         for name, host_plan in plans.items():
             _, _, plan = eng.upload_decode(slots, hb.seq_lens, host_plan)
             if name == "private":
