@@ -103,6 +103,9 @@ def parse():
     ap.add_argument("--shared-min-workgroups", type=int, default=0,
                     help="shared-prefix decode: merge chunks into longer items while this many workgroups remain "
                          "(0 = the engine's default)")
+    ap.add_argument("--private-max-workgroups", type=int, default=-1,
+                    help="shared-prefix decode: give the private tails to the shared-prefix kernel too when items "
+                         "and tails need at most this many workgroups (-1 = the engine's default, 0 = never)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=64, help="requests in the oracle's timed sample")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -333,6 +336,8 @@ class JobBench:
                                 sm_scale=s.sm_scale, policy=a.policy)
         if a.shared_min_workgroups:
             eng.SHARED_MIN_WORKGROUPS = a.shared_min_workgroups
+        if a.private_max_workgroups >= 0:
+            eng.PRIVATE_MAX_WORKGROUPS = a.private_max_workgroups
         self.stride = wl.max_len()
         self.timer = Timer(torch)
         self.decode_only = False
@@ -626,8 +631,13 @@ def main():
     extra = min(30, a.steps)      # untimed steps after the timed ones, for the other kernels' spans
     b = PathBench(torch, a.workload, a.warmup + a.steps + extra, shared_decode=not a.plain_decode,
                   decode_chunk=a.decode_chunk)
-    if a.shared_min_workgroups:
-        b.eng.SHARED_MIN_WORKGROUPS = a.shared_min_workgroups
+    if a.shared_min_workgroups or a.private_max_workgroups >= 0:
+        if a.shared_min_workgroups:
+            b.eng.SHARED_MIN_WORKGROUPS = a.shared_min_workgroups
+        if a.private_max_workgroups >= 0:
+            b.eng.PRIVATE_MAX_WORKGROUPS = a.private_max_workgroups
+        if b.plan is not None:      # a decode-only batch planned at construction: plan again
+            b.plan = b.eng.decode_plan(b.hb.req_to_token, b.hb.seq_lens, b.chunk)
     wl = b.wl
     if a.copy_calib_mib:
         n = a.copy_calib_mib * (1 << 20) // 4
