@@ -392,3 +392,27 @@ def test_peek_changes_nothing():
     before = (t.dump(), t.dump_stats(), t.clock)
     assert t.peek([1, 2, 3, 9]) == 3 and t.peek([1, 2]) == 2 and t.peek([8]) == 0 and t.peek([7, 7]) == 1
     assert (t.dump(), t.dump_stats(), t.clock) == before
+
+
+def test_priority_raised_by_walking_inserts_hand_example():
+    """Priority field ([RC] "삽입: _insert_helper" passes a priority down the walk): an insert
+    raises every node it walks over to max(old, its priority), a cut raises only the upper part
+    (the part holding walked positions), a new node takes the insert's priority.  Expected values
+    derived by hand below."""
+    t = _three_leaves("priority")          # A=[1,1] prio 2, B=[2,2] prio 0, C=[3,3] prio 1 (ids 1, 2, 3)
+    prio = {tuple(t.path_tokens(nid)): p for nid, _, _, p in t.dump_stats()}
+    assert prio == {(1, 1): 2, (2, 2): 0, (3, 3): 1}
+    # insert [2, 7] at priority 5: B is cut after its first position; upper [2] is walked (5),
+    # lower [2] keeps 0, the new node [7] takes 5
+    bt = driver.prepare_batch(t, [[2, 7]])
+    t.insert([2, 7], bt.rows[0], priority=5)
+    driver.release(t, bt.last_nodes)
+    prio = {tuple(t.path_tokens(nid)): p for nid, _, _, p in t.dump_stats()}
+    assert prio == {(1, 1): 2, (2,): 5, (2, 2): 0, (2, 7): 5, (3, 3): 1}
+    # priority order: lowest first, ties by access time: (2,2) prio 0, then C prio 1, then A prio 2;
+    # [2] is not a leaf until both children are gone
+    got = []
+    for _ in range(3):
+        t.evict(1)
+        got += [list(s) for _, s in t.take_evlog()]
+    assert got == [[3], [4, 5], [0, 1]]    # lower half of B (its second slot), C, A

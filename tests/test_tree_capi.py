@@ -300,3 +300,71 @@ def test_workload_tot_host():
     fam = ob.batches[3]
     for f in range(0, 256, 4):
         assert all(fam.prefix_lens[f + c] == fam.prefix_lens[f] + 8 for c in range(1, 4))
+
+
+def test_finish_duplicate_release_through_capi():
+    """rt_finish's duplicate branch (the caller's slots of positions the final insert finds
+    cached go back to the free list): the hand-derived example of
+    tests/golden/finish_duplicates.json, bit-exact through the C ABI (tables, decode slots,
+    end nodes, free list, counters, clock, every node) and against the oracle."""
+    with open(os.path.join(GOLDEN, "finish_duplicates.json")) as f:
+        g = json.load(f)
+    t = pkv.rt_create(g["pool_slots"])
+    o = OracleTree(g["pool_slots"])
+    try:
+        stride = 8
+        hb = runtime.prepare(t, [np.array(p) for p in g["prompts"]], stride)
+        ob = driver.prepare_batch(o, g["prompts"])
+        assert hb.prefix_lens.tolist() == g["prefix_lens"] == ob.prefix_lens
+        assert hb.extend_lens.tolist() == g["extend_lens"]
+        assert hb.new_slots.tolist() == g["new_slots"]
+        assert hb.last_nodes.tolist() == g["last_nodes"]
+        rows = [list(r) for r in ob.rows]
+        for s, want in enumerate(g["decode_slots"]):
+            out = np.empty(hb.n, dtype=np.int32)
+            pkv.rt_decode_step(t, hb.req_to_token, hb.seq_lens, out)
+            assert out.tolist() == want == driver.decode_alloc(o, rows), s
+        full = [np.array(p + d) for p, d in zip(g["prompts"], g["decode_tokens"])]
+        toks, indptr = runtime.flatten(full)
+        ends = pkv.rt_finish(t, toks, indptr, hb.req_to_token, [len(p) for p in g["prompts"]], hb.last_nodes)
+        oends = driver.finish(o, [f.tolist() for f in full], rows, [len(p) for p in g["prompts"]], ob.last_nodes)
+        assert ends.tolist() == g["ends"] == oends
+        assert pkv.rt_copy_free_list(t).tolist() == g["free_after_finish"] == list(o.free)
+        assert pkv.rt_evictable_size(t) == g["evictable"] and pkv.rt_protected_size(t) == g["protected"]
+        assert pkv.rt_clock(t) == g["clock_after_finish"]
+        assert [list(x[:4]) + [list(x[4]), list(x[5])] for x in pkv.rt_dump(t)] == g["dump_after_finish"]
+        assert pkv.rt_dump(t) == o.dump()
+        m, slots, node = pkv.rt_match_prefix(t, g["followup_query"])
+        assert (m, slots.tolist(), node) == (g["followup_match_len"], g["followup_match_slots"], g["followup_node"])
+    finally:
+        pkv.rt_destroy(t)
+
+
+@settings(max_examples=60, deadline=None)
+@given(prompts=st.lists(st.lists(st.integers(0, 2), min_size=1, max_size=5), min_size=1, max_size=5),
+       dec=st.lists(st.lists(st.integers(0, 2), min_size=1, max_size=5), min_size=1, max_size=4))
+def test_finish_with_duplicates_matches_oracle(prompts, dec):
+    """Random batches over a 3-token vocabulary whose decoded tokens often repeat another
+    sequence's: rt_finish bit-exact against the oracle's finish (free list, dump, counters)."""
+    steps = len(dec[0])
+    dtoks = [(dec[i % len(dec)] * steps)[:steps] for i in range(len(prompts))]
+    t = pkv.rt_create(64)
+    o = OracleTree(64)
+    try:
+        hb = runtime.prepare(t, [np.array(p) for p in prompts], 16)
+        ob = driver.prepare_batch(o, prompts)
+        rows = [list(r) for r in ob.rows]
+        for _ in range(steps):
+            out = np.empty(hb.n, dtype=np.int32)
+            pkv.rt_decode_step(t, hb.req_to_token, hb.seq_lens, out)
+            assert out.tolist() == driver.decode_alloc(o, rows)
+        full = [p + d for p, d in zip(prompts, dtoks)]
+        toks, indptr = runtime.flatten([np.array(f) for f in full])
+        ends = pkv.rt_finish(t, toks, indptr, hb.req_to_token, [len(p) for p in prompts], hb.last_nodes)
+        assert ends.tolist() == driver.finish(o, full, rows, [len(p) for p in prompts], ob.last_nodes)
+        assert pkv.rt_dump(t) == o.dump()
+        assert pkv.rt_copy_free_list(t).tolist() == list(o.free)
+        assert (pkv.rt_evictable_size(t), pkv.rt_protected_size(t)) == (o.evictable, o.protected)
+        assert pkv.rt_free_size(t) + o.cached_tokens() == 64
+    finally:
+        pkv.rt_destroy(t)
