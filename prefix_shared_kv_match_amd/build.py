@@ -1,9 +1,20 @@
 """Builds libpkv.so in-tree: host C++ (radix tree, allocator, C ABI) plus HIP kernels for gfx950.
 
-    python -m prefix_shared_kv_match_amd.build [--debug]
+    python -m prefix_shared_kv_match_amd.build [--debug] [--sanitize]
 
 The host sources are compiled with g++, the .hip sources with hipcc for gfx950 only,
 and everything is linked by hipcc into prefix_shared_kv_match_amd/libpkv.so.
+
+--debug defines PKV_DEBUG (kv_scatter then checks its slot list on the host before each
+launch) and adds debug info.  --sanitize builds the host sources (radix tree, plans, C ABI
+argument checks) with AddressSanitizer and UndefinedBehaviorSanitizer into
+_build/sanitize/libpkv.so, leaving the in-tree library alone; the CPU tests run against it
+with
+
+    PKV_LIBRARY=_build/sanitize/libpkv.so LD_PRELOAD=$(g++ -print-file-name=libasan.so) \
+        ASAN_OPTIONS=detect_leaks=0 python -m pytest tests -m "not gpu"
+
+(the GPU code is not instrumented; the sanitizers cover the host library only).
 """
 from __future__ import annotations
 
@@ -62,19 +73,24 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def build(debug: bool = False, verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-omit-frame-pointer", "-fno-sanitize-recover=undefined"]
+
+
+def build(debug: bool = False, verbose: bool = False, sanitize: bool = False) -> str:
+    out_dir = os.path.join(BUILD, "sanitize") if sanitize else BUILD
+    os.makedirs(out_dir, exist_ok=True)
     hc = hipcc()
     extra = ["-DPKV_DEBUG=1", "-g"] if debug else []
     extra = extra + [f'-DPKV_SOURCE_HASH="{source_hash()}"']
     jobs = []
     objs = []
     for s in HOST_SOURCES:
-        o = os.path.join(BUILD, s + ".o")
+        o = os.path.join(out_dir, s + ".o")
         objs.append(o)
-        jobs.append(["g++", *HOST_FLAGS, *extra, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, s), "-o", o])
+        jobs.append(["g++", *HOST_FLAGS, *(SANITIZE_FLAGS + ["-g"] if sanitize else []), *extra, "-I", INCLUDE,
+                     "-I", CSRC, "-c", os.path.join(CSRC, s), "-o", o])
     for s in HIP_SOURCES:
-        o = os.path.join(BUILD, s + ".o")
+        o = os.path.join(out_dir, s + ".o")
         objs.append(o)
         jobs.append([hc, *HIP_FLAGS, *HIP_FILE_FLAGS.get(s, []), *extra, "-I", INCLUDE, "-I", CSRC, "-c",
                      os.path.join(CSRC, s), "-o", o])
@@ -84,18 +100,23 @@ def build(debug: bool = False, verbose: bool = False) -> str:
         for o in outs:
             if o.strip():
                 print(o)
-    tmp = LIB + ".tmp"
-    _run([hc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp])
-    os.replace(tmp, LIB)
-    return LIB
+    lib_path = os.path.join(out_dir, "libpkv.so") if sanitize else LIB
+    tmp = lib_path + ".tmp"
+    # the sanitizer runtimes of the host compiler, linked as plain libraries
+    _run([hc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, *(["-lasan", "-lubsan"] if sanitize else []),
+          "-o", tmp])
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--debug", action="store_true")
+    ap.add_argument("--sanitize", action="store_true",
+                    help="host sources with ASan/UBSan into _build/sanitize/libpkv.so")
     ap.add_argument("-v", "--verbose", action="store_true")
     a = ap.parse_args(argv)
-    print(build(a.debug, a.verbose))
+    print(build(a.debug, a.verbose, a.sanitize))
 
 
 if __name__ == "__main__":

@@ -123,7 +123,7 @@ __global__ __launch_bounds__(256) void decode_split(const QT* __restrict__ q, co
                                                     const int32_t* __restrict__ seq_lens, int hkv, int chunk,
                                                     int max_splits, float qk_scale_log2, float* __restrict__ ws_ml,
                                                     float* __restrict__ ws_acc, const int32_t* __restrict__ skip,
-                                                    int s0, int ns) {
+                                                    int s0, int ns, uint32_t max_slot) {
   constexpr int VEC = D / 16;
   using Chunk = RowChunk<POOL, VEC>;
   constexpr int ROWB = D * Chunk::kBytes / VEC;  // bytes of one (slot, head) row
@@ -173,7 +173,7 @@ __global__ __launch_bounds__(256) void decode_split(const QT* __restrict__ q, co
     for (int u = 0; u < kUnroll; ++u) {
       const int t = base + 16 * u;
       valid[u] = t < t1;
-      const int64_t slot = row[valid[u] ? t : t0];
+      const int64_t slot = min((uint32_t)row[valid[u] ? t : t0], max_slot);   // a slot past the pool reads the last one
       kc[u].load(kpool + slot * slot_bytes + head_off);
       vc[u].load(vpool + slot * slot_bytes + head_off);
     }
@@ -281,7 +281,7 @@ __global__ __launch_bounds__(256, (G >= 8 ? 2 : 3)) void decode_split_slot(const
                                                          int max_splits, float qk_scale_log2,
                                                          float* __restrict__ ws_ml, float* __restrict__ ws_acc,
                                                          int hkv_total, const int32_t* __restrict__ skip, int s0,
-                                                         int ns, int ns_odd) {
+                                                         int ns, int ns_odd, uint32_t max_slot) {
   constexpr int VEC = D / 16;
   constexpr int STREAMS = 16 / HKV;
   using Chunk = RowChunk<POOL, VEC>;
@@ -343,7 +343,7 @@ __global__ __launch_bounds__(256, (G >= 8 ? 2 : 3)) void decode_split_slot(const
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int t = base + STREAMS * u;
-      const int64_t slot = row[t < t1 ? t : t0];
+      const int64_t slot = min((uint32_t)row[t < t1 ? t : t0], max_slot);   // a slot past the pool reads the last one
       kc[u].load(kpool + slot * slot_bytes + head_off);
       vc[u].load(vpool + slot * slot_bytes + head_off);
     }
@@ -535,14 +535,15 @@ __global__ __launch_bounds__(256) void decode_reduce(const float* __restrict__ w
 template <typename QT, int POOL, int D, int HKV>
 int launch_slot(int G, int batch, int s0, int ns, hipStream_t st, const void* q, const void* kp, const void* vp,
                 const float* ks, const float* vs, const int32_t* r2t, int64_t stride, const int32_t* lens, int chunk,
-                int max_splits, float sc, float* ml, float* acc, int hkv_total, const int32_t* skip) {
+                int max_splits, float sc, float* ml, float* acc, int hkv_total, const int32_t* skip,
+                uint32_t max_slot) {
   const int ns_odd = ns | 1;
   const dim3 grid((unsigned)((int64_t)batch * ns_odd * (hkv_total / HKV)));
 #define PKV_SLOT_CASE(GG)                                                                                        \
   case GG:                                                                                                       \
     hipLaunchKernelGGL((decode_split_slot<QT, POOL, D, GG, HKV>), grid, dim3(256), 0, st, (const QT*)q,          \
                        (const uint8_t*)kp, (const uint8_t*)vp, ks, vs, r2t, stride, lens, chunk, max_splits, sc, \
-                       ml, acc, hkv_total, skip, s0, ns, ns_odd);                                                \
+                       ml, acc, hkv_total, skip, s0, ns, ns_odd, max_slot);                                      \
     return PKV_OK;
   switch (G) {
     PKV_SLOT_CASE(1)
@@ -559,25 +560,25 @@ template <typename QT, int POOL, int D>
 int launch_split(int G, int batch, int s0, int ns, bool per_head, hipStream_t st, const void* q, const void* kp,
                  const void* vp, const float* ks, const float* vs, const int32_t* r2t, int64_t stride,
                  const int32_t* lens, int hkv, int chunk, int max_splits, float sc, float* ml, float* acc,
-                 const int32_t* skip) {
+                 const int32_t* skip, uint32_t max_slot) {
 #define PKV_DECODE_CASE(GG)                                                                                    \
   case GG:                                                                                                     \
     hipLaunchKernelGGL((decode_split<QT, POOL, D, GG>), dim3((unsigned)((int64_t)batch * ns * hkv)), dim3(256), 0, \
                        st, (const QT*)q, (const uint8_t*)kp, (const uint8_t*)vp, ks, vs, r2t, stride, lens, hkv,  \
-                       chunk, max_splits, sc, ml, acc, skip, s0, ns);                                          \
+                       chunk, max_splits, sc, ml, acc, skip, s0, ns, max_slot);                                \
     return PKV_OK;
   // all heads of a slot row per workgroup for 2, 4 or 8 kv heads; groups of 8 heads for
   // any multiple of 8 (multi-head attention)
   if (!per_head) {
     if (hkv == 8) return launch_slot<QT, POOL, D, 8>(G, batch, s0, ns, st, q, kp, vp, ks, vs, r2t, stride, lens, chunk,
-                                                    max_splits, sc, ml, acc, hkv, skip);
+                                                    max_splits, sc, ml, acc, hkv, skip, max_slot);
     if (hkv == 4) return launch_slot<QT, POOL, D, 4>(G, batch, s0, ns, st, q, kp, vp, ks, vs, r2t, stride, lens, chunk,
-                                                    max_splits, sc, ml, acc, hkv, skip);
+                                                    max_splits, sc, ml, acc, hkv, skip, max_slot);
     if (hkv == 2) return launch_slot<QT, POOL, D, 2>(G, batch, s0, ns, st, q, kp, vp, ks, vs, r2t, stride, lens, chunk,
-                                                    max_splits, sc, ml, acc, hkv, skip);
+                                                    max_splits, sc, ml, acc, hkv, skip, max_slot);
     if (hkv % 8 == 0)
       return launch_slot<QT, POOL, D, 8>(G, batch, s0, ns, st, q, kp, vp, ks, vs, r2t, stride, lens, chunk,
-                                         max_splits, sc, ml, acc, hkv, skip);
+                                         max_splits, sc, ml, acc, hkv, skip, max_slot);
   }
   switch (G) {
     PKV_DECODE_CASE(1)
@@ -660,21 +661,23 @@ int decode_impl(const void* q, void* o, int32_t qo_dtype, const void* k_pool, co
   const int slot_groups = (hkv == 2 || hkv == 4 || hkv == 8) ? 1 : (hkv % 8 == 0 ? hkv / 8 : 0);
   const bool per_head = skip && (int64_t)batch * ns * slot_groups < 1024;
   const bool split_phase = !skip || first_split < max_splits;
+  if (num_slots > 0x7FFFFFFFLL) return fail(PKV_ERR_INVAL, "decode: num_slots beyond int32");
+  const uint32_t mslot = (uint32_t)(num_slots - 1);
   int rc = PKV_OK;
   if (!split_phase)
     rc = PKV_OK;
   else if (qo_dtype == PKV_F32 && pool_dtype == PKV_F32 && d == 64)
     rc = launch_split<float, PKV_F32, 64>(G, batch, s0, ns, per_head, st, q, k_pool, v_pool, k_scale, v_scale, req_to_token, stride,
-                                          seq_lens, hkv, chunk, max_splits, sc, ml, acc, skip);
+                                          seq_lens, hkv, chunk, max_splits, sc, ml, acc, skip, mslot);
   else if (qo_dtype == PKV_F32 && pool_dtype == PKV_F32 && d == 128)
     rc = launch_split<float, PKV_F32, 128>(G, batch, s0, ns, per_head, st, q, k_pool, v_pool, k_scale, v_scale, req_to_token, stride,
-                                           seq_lens, hkv, chunk, max_splits, sc, ml, acc, skip);
+                                           seq_lens, hkv, chunk, max_splits, sc, ml, acc, skip, mslot);
   else if (qo_dtype == PKV_BF16 && pool_dtype == PKV_BF16 && d == 128)
     rc = launch_split<bf16, PKV_BF16, 128>(G, batch, s0, ns, per_head, st, q, k_pool, v_pool, k_scale, v_scale, req_to_token, stride,
-                                           seq_lens, hkv, chunk, max_splits, sc, ml, acc, skip);
+                                           seq_lens, hkv, chunk, max_splits, sc, ml, acc, skip, mslot);
   else if (qo_dtype == PKV_BF16 && pool_dtype == PKV_FP8_E4M3 && d == 128)
     rc = launch_split<bf16, PKV_FP8_E4M3, 128>(G, batch, s0, ns, per_head, st, q, k_pool, v_pool, k_scale, v_scale, req_to_token,
-                                               stride, seq_lens, hkv, chunk, max_splits, sc, ml, acc, skip);
+                                               stride, seq_lens, hkv, chunk, max_splits, sc, ml, acc, skip, mslot);
   else
     return fail(PKV_ERR_UNSUPPORTED, "decode: qo dtype %d, pool dtype %d, d %d", qo_dtype, pool_dtype, d);
   if (rc < 0) return rc;

@@ -68,7 +68,7 @@ __global__ __launch_bounds__(64) void extend_f32(const float* __restrict__ q, fl
                                                  const int32_t* __restrict__ extend_lens,
                                                  const int32_t* __restrict__ qo_indptr,
                                                  const int32_t* __restrict__ work, int hq, int hkv,
-                                                 float scale_log2) {
+                                                 float scale_log2, uint32_t max_slot) {
   constexpr int PER = D / 64;
   __shared__ float qs[kF32Tile][D];
   __shared__ float ps[kF32Kv];
@@ -99,7 +99,7 @@ __global__ __launch_bounds__(64) void extend_f32(const float* __restrict__ q, fl
   for (int kv0 = 0; kv0 < ctx; kv0 += kF32Kv) {
     const int k = kv0 + lane;
     const bool kin = k < ctx;
-    const int64_t slot = row[kin ? k : 0];
+    const int64_t slot = min((uint32_t)row[kin ? k : 0], max_slot);   // a slot past the pool reads the last one
     sl[lane] = (int32_t)slot;
     const float* krow = kpool + (slot * hkv + g) * D;
     __syncthreads();
@@ -974,15 +974,17 @@ extern "C" int pkv_extend_attention(const void* q, void* o, int32_t qo_dtype, co
   const float sc = sm_scale * kLog2e;
   const int G = hq / hkv;
   if (qo_dtype == PKV_F32) {
+    if (num_slots > 0x7FFFFFFFLL) return fail(PKV_ERR_UNSUPPORTED, "extend: pool beyond int32 slots");
+    const uint32_t mslot = (uint32_t)(num_slots - 1);
     const dim3 grid((unsigned)(n_work * hq));
     if (d == 64)
       hipLaunchKernelGGL((extend_f32<64>), grid, dim3(64), 0, st, (const float*)q, (float*)o, (const float*)k_pool,
                          (const float*)v_pool, req_to_token, stride, prefix_lens, extend_lens, qo_indptr, work, hq,
-                         hkv, sc);
+                         hkv, sc, mslot);
     else
       hipLaunchKernelGGL((extend_f32<128>), grid, dim3(64), 0, st, (const float*)q, (float*)o, (const float*)k_pool,
                          (const float*)v_pool, req_to_token, stride, prefix_lens, extend_lens, qo_indptr, work, hq,
-                         hkv, sc);
+                         hkv, sc, mslot);
     return hip_check(hipGetLastError(), "extend_f32 launch");
   }
   const int64_t slot_bytes = (int64_t)hkv * (pool_dtype == PKV_FP8_E4M3 ? 128 : 256);

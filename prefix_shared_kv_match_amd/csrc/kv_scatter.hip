@@ -10,6 +10,12 @@
 // quantises with the per-head inverse scale (OCP E4M3, round to nearest even,
 // saturating), writing 8 bytes per thread.  HBM-bound: per token it reads
 // 2*hkv*d*src_bytes and writes 2*hkv*d*pool_bytes.
+//
+// A slot outside [0, num_slots) is skipped (its token is not written), so a bad slot list
+// cannot write past the pools.  Builds with PKV_DEBUG also copy the slot list to the host
+// before the launch and reject out-of-range or repeated slots with PKV_ERR_SLOT.
+
+#include <vector>
 
 #include "device.h"
 
@@ -19,12 +25,15 @@ namespace {
 // Copy: each thread moves one 16-byte chunk of K and the same chunk of V.
 __global__ __launch_bounds__(256) void scatter_copy(const uint4* __restrict__ ksrc, const uint4* __restrict__ vsrc,
                                                     const int32_t* __restrict__ slots, int64_t n, int chunks_per_row,
-                                                    uint4* __restrict__ kpool, uint4* __restrict__ vpool) {
+                                                    uint32_t num_slots, uint4* __restrict__ kpool,
+                                                    uint4* __restrict__ vpool) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n * chunks_per_row) return;
   const int64_t tok = i / chunks_per_row;
   const int c = (int)(i - tok * chunks_per_row);
-  const int64_t dst = (int64_t)slots[tok] * chunks_per_row + c;
+  const uint32_t slot = (uint32_t)slots[tok];
+  if (slot >= num_slots) return;
+  const int64_t dst = (int64_t)slot * chunks_per_row + c;
   const uint4 k = ksrc[i];
   const uint4 v = vsrc[i];
   kpool[dst] = k;
@@ -39,15 +48,17 @@ __device__ __forceinline__ uint32_t pack4_e4m3(uint32_t w0, uint32_t w1, float s
 // bf16 -> fp8: each thread reads 8 bf16 (16 B) of K and of V and writes 8 codes (8 B) each.
 __global__ __launch_bounds__(256) void scatter_fp8(const uint4* __restrict__ ksrc, const uint4* __restrict__ vsrc,
                                                    const int32_t* __restrict__ slots, int64_t n, int chunks_per_row,
-                                                   int chunks_per_head, const float* __restrict__ kinv,
-                                                   const float* __restrict__ vinv, uint2* __restrict__ kpool,
-                                                   uint2* __restrict__ vpool) {
+                                                   int chunks_per_head, uint32_t num_slots,
+                                                   const float* __restrict__ kinv, const float* __restrict__ vinv,
+                                                   uint2* __restrict__ kpool, uint2* __restrict__ vpool) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n * chunks_per_row) return;
   const int64_t tok = i / chunks_per_row;
   const int c = (int)(i - tok * chunks_per_row);
   const int h = c / chunks_per_head;
-  const int64_t dst = (int64_t)slots[tok] * chunks_per_row + c;
+  const uint32_t slot = (uint32_t)slots[tok];
+  if (slot >= num_slots) return;
+  const int64_t dst = (int64_t)slot * chunks_per_row + c;
   const uint4 k = ksrc[i];
   const uint4 v = vsrc[i];
   const float ks = kinv[h], vs = vinv[h];
@@ -87,21 +98,37 @@ extern "C" int pkv_kv_scatter(const void* k_src, const void* v_src, int32_t src_
   if (n == 0) return PKV_OK;
   if (!k_src || !v_src || !slots || !k_pool || !v_pool) return fail(PKV_ERR_INVAL, "kv_scatter: null pointer");
   if (d != 64 && d != 128) return fail(PKV_ERR_UNSUPPORTED, "kv_scatter: d=%d", d);
+  if (num_slots > (int64_t)INT32_MAX) return fail(PKV_ERR_INVAL, "kv_scatter: num_slots beyond int32");
   hipStream_t st = (hipStream_t)stream;
+#ifdef PKV_DEBUG
+  {
+    // debug builds: every slot in range and none twice (a repeated slot would race)
+    std::vector<int32_t> h((size_t)n);
+    if (int rc = hip_check(hipMemcpyAsync(h.data(), slots, (size_t)n * 4, hipMemcpyDeviceToHost, st), "kv_scatter slots"))
+      return rc;
+    if (int rc = hip_check(hipStreamSynchronize(st), "kv_scatter slots")) return rc;
+    std::vector<uint8_t> seen((size_t)num_slots, 0);
+    for (int64_t i = 0; i < n; ++i) {
+      if (h[i] < 0 || h[i] >= num_slots) return fail(PKV_ERR_SLOT, "kv_scatter: slot %d of token %lld out of range", h[i], (long long)i);
+      if (seen[h[i]]++) return fail(PKV_ERR_SLOT, "kv_scatter: slot %d written twice", h[i]);
+    }
+  }
+#endif
   const int threads = 256;
   if ((src_dtype == PKV_F32 && pool_dtype == PKV_F32) || (src_dtype == PKV_BF16 && pool_dtype == PKV_BF16)) {
     const int esz = src_dtype == PKV_F32 ? 4 : 2;
     const int chunks = hkv * d * esz / 16;
     const int64_t total = n * chunks;
     hipLaunchKernelGGL(scatter_copy, dim3((unsigned)((total + threads - 1) / threads)), dim3(threads), 0, st,
-                       (const uint4*)k_src, (const uint4*)v_src, slots, n, chunks, (uint4*)k_pool, (uint4*)v_pool);
+                       (const uint4*)k_src, (const uint4*)v_src, slots, n, chunks, (uint32_t)num_slots, (uint4*)k_pool,
+                       (uint4*)v_pool);
   } else if (src_dtype == PKV_BF16 && pool_dtype == PKV_FP8_E4M3) {
     if (!k_inv_scale || !v_inv_scale) return fail(PKV_ERR_INVAL, "kv_scatter: fp8 pool needs inverse scales");
     const int chunks = hkv * d / 8;
     const int64_t total = n * chunks;
     hipLaunchKernelGGL(scatter_fp8, dim3((unsigned)((total + threads - 1) / threads)), dim3(threads), 0, st,
-                       (const uint4*)k_src, (const uint4*)v_src, slots, n, chunks, d / 8, k_inv_scale, v_inv_scale,
-                       (uint2*)k_pool, (uint2*)v_pool);
+                       (const uint4*)k_src, (const uint4*)v_src, slots, n, chunks, d / 8, (uint32_t)num_slots,
+                       k_inv_scale, v_inv_scale, (uint2*)k_pool, (uint2*)v_pool);
   } else {
     return fail(PKV_ERR_UNSUPPORTED, "kv_scatter: src dtype %d -> pool dtype %d", src_dtype, pool_dtype);
   }

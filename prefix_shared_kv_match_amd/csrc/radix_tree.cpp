@@ -673,9 +673,11 @@ int64_t rt_prepare_extend_prio(rt_tree* t, int32_t num_reqs, const int32_t* toke
         t->dec_lock(a);
         return tm;
       }
-      if (tm != m)
+      if (tm != m) {
+        t->dec_lock(a);   // request r leaves no lock behind (its new tokens stay cached, unlocked)
         return pkv::fail(PKV_ERR_INTERNAL, "insert found %lld cached tokens after a match of %lld", (long long)tm,
                          (long long)m);
+      }
       t->inc_lock(last);
       t->dec_lock(a);
       prefix_lens[r] = (int32_t)m;
