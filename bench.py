@@ -281,7 +281,8 @@ class PathBench:
         with T.span("kv_scatter_decode"):
             eng.scatter(slots_dev, self.dk[i], self.dv[i])
         with T.span("decode_attention"):
-            eng.decode(self.dq[i], r2t_dev, seq_dev, self.max_len, self.ws, self.chunk, self.do, plan=self.plan)
+            eng.decode(self.dq[i], r2t_dev, seq_dev, self.max_len, self.ws, self.chunk, self.do, plan=self.plan,
+                       seq_lens_host=hb.seq_lens)
 
     def step(self):
         import prefix_shared_kv_match_amd as pkv

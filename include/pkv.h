@@ -149,15 +149,23 @@ int64_t rt_evict(rt_tree* t, int64_t num_tokens);
 
 /* Hand out n slots from the free list's head (first in, first out).  If fewer than n
  * are free it first evicts (n - free) tokens; if still short, returns PKV_ERR_OOM
- * (evictions already done stay done).  Slots become in flight.  Returns n. */
+ * (evictions already done stay done).  Slots become in flight.  Returns n.
+ * [RC "Eviction 전략": eviction exists to give KV indices back to the pool's allocator
+ * when new tokens need room; OV "Architectural Deep Dive" flowchart: compute the missing
+ * KV, evicting least recently used entries under memory pressure.]  out: caller-owned host
+ * array of n int32. */
 int64_t rt_alloc(rt_tree* t, int64_t n, int32_t* out);
 
-/* Return in-flight slots to the free list's tail, in the order given. */
+/* Return in-flight slots to the free list's tail, in the order given [RC "Eviction 전략":
+ * freed KV indices go back to the pool allocator; "삽입: _insert_helper": the caller frees
+ * the duplicate indices an insert reports].  A slot that is free already, cached by a node
+ * or outside [0, num_slots) fails with PKV_ERR_SLOT and nothing is freed. */
 int rt_free(rt_tree* t, const int32_t* slots, int64_t n);
 
 /* Eviction log since the last take: node ids, their lengths, and the freed slots in
- * eviction order.  rt_eviction_log_size reports the sizes; rt_take_eviction_log copies
- * and clears (PKV_ERR_INVAL, nothing cleared, if a capacity is too small). */
+ * eviction order (the nodes [RC "Eviction 전략"] removes, one record per popped leaf).
+ * rt_eviction_log_size reports the sizes; rt_take_eviction_log copies into caller-owned
+ * host arrays and clears (PKV_ERR_INVAL, nothing cleared, if a capacity is too small). */
 int rt_eviction_log_size(const rt_tree* t, int64_t* n_nodes, int64_t* n_slots);
 int rt_take_eviction_log(rt_tree* t, int64_t* node_ids, int64_t* node_lens, int64_t nodes_cap,
                          int32_t* slots, int64_t slots_cap);
@@ -167,6 +175,9 @@ int rt_take_eviction_log(rt_tree* t, int64_t* node_ids, int64_t* node_lens, int6
  * off also drops what it holds. */
 int rt_set_eviction_log(rt_tree* t, int32_t enabled);
 
+/* Token counters [RC "삽입: _insert_helper" (a new leaf's tokens count as evictable) and
+ * "참조 카운트: lock_ref" (tokens move between evictable and protected on 0 <-> 1)]; the
+ * free count is the allocator's [RC "Eviction 전략"].  PKV_ERR_INVAL for a null tree. */
 int64_t rt_evictable_size(const rt_tree* t);   /* tokens in unlocked nodes  */
 int64_t rt_protected_size(const rt_tree* t);   /* tokens in locked nodes    */
 int64_t rt_free_size(const rt_tree* t);        /* slots on the free list    */
@@ -182,7 +193,10 @@ int64_t rt_dump(const rt_tree* t, int64_t* out, int64_t cap);
  * is large enough. */
 int64_t rt_dump_stats(const rt_tree* t, int64_t* out, int64_t cap);
 
-/* Batch driver: the hot path's host steps for one batch of requests, in order.
+/* Batch driver: the hot path's host steps for one batch of requests, in order [OV
+ * "Architectural Deep Dive" flowchart: prefix match, reuse the matched KV, compute the
+ * missing KV, insert; RC "프리픽스 매칭", "참조 카운트", "삽입"; EX "プレフィックスマッチング
+ * アルゴリズム": only the part after the matched prefix is prefilled].
  * For request r (tokens[tok_indptr[r] .. tok_indptr[r+1])), length L_r:
  *   match (split, stamp) -> lock the matched node -> allocate L_r - m_r slots (evicting
  *   on shortfall) -> insert (tokens, matched slots ++ new slots) -> lock the new end
@@ -207,12 +221,18 @@ int64_t rt_prepare_extend_prio(rt_tree* t, int32_t num_reqs, const int32_t* toke
                                int32_t* prefix_lens, int32_t* extend_lens, int32_t* qo_indptr,
                                int32_t* new_slots, int64_t new_cap, rt_node* out_last);
 
-/* Unlock out_last entries of a prepared batch (entries < 0 are skipped). */
+/* Unlock out_last entries of a prepared batch (entries < 0 are skipped) once its kernels
+ * have been enqueued [RC "참조 카운트: lock_ref": a request's nodes are protected from
+ * eviction only while it uses them].  An entry already at lock 0 fails with PKV_ERR_LOCK
+ * (the entries before it stay released). */
 int rt_release(rt_tree* t, const rt_node* nodes, int32_t n);
 
-/* One decode step for `batch` sequences: allocate `batch` slots in one call (evicting on
- * shortfall); slot b is written to req_to_token[b*stride + seq_lens[b]] and to
- * out_slots[b], and seq_lens[b] is incremented.  Requires seq_lens[b] < stride. */
+/* One decode step for `batch` sequences [OV "Architectural Deep Dive": each generated
+ * token gets KV of its own, which later feeds back into insertion]: allocate `batch` slots
+ * in one call (evicting on shortfall, RC "Eviction 전략"); slot b is written to
+ * req_to_token[b*stride + seq_lens[b]] and to out_slots[b], and seq_lens[b] is incremented.
+ * Host arrays, caller-owned.  Requires seq_lens[b] < stride (else PKV_ERR_INVAL, nothing
+ * allocated); PKV_ERR_OOM if the pool cannot supply `batch` slots. */
 int64_t rt_decode_step(rt_tree* t, int32_t batch, int32_t* req_to_token, int64_t stride, int32_t* seq_lens,
                        int32_t* out_slots);
 
@@ -224,20 +244,36 @@ int rt_finish(rt_tree* t, int32_t n, const int32_t* tokens, const int64_t* tok_i
               const int32_t* req_to_token, int64_t stride, const int32_t* prompt_lens,
               const rt_node* prompt_last, rt_node* out_end);
 
+/* One launch of chunked prefill (a cap of `budget` new tokens per extend launch) [the
+ * deployment-tuning page's chunked-prefill option; requests keep their order]: from request
+ * `head` on, each request contributes min(its tokens not yet prefilled, budget left) and the
+ * walk stops when the budget is spent, so only the last request taken may be cut.  A
+ * request's tokens not yet prefilled start at done[r] when done[r] >= 0 (it is under way:
+ * its earlier chunks are cached and locked) and otherwise after its cached prefix
+ * (rt_peek_prefix, read-only).  Writes the requests taken to out_reqs and the end position of
+ * each one's chunk to out_ends (caller-owned, capacity num_reqs - head); the caller prepares
+ * the launch as the truncated token lists [0, end).  Returns the number taken;
+ * PKV_ERR_INVAL on bad arguments. */
+int32_t rt_chunk_launch(const rt_tree* t, int32_t num_reqs, const int32_t* tokens, const int64_t* tok_indptr,
+                        const int64_t* done, int32_t head, int64_t budget, int32_t* out_reqs, int64_t* out_ends);
+
 /* ----------------------------------------------------------------------------------
  * Kernels (device)
  * -------------------------------------------------------------------------------- */
 
 typedef enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_FP8_E4M3 = 2 } pkv_dtype;
 
-/* Write new tokens' K/V into their pool slots:
+/* Write new tokens' K/V into their pool slots [RC "핵심 자료구조: TreeNode": a node's value
+ * holds one KV-pool index per token; OV flowchart: the missing KV is computed and stored]:
  *   k_pool[slots[i], h, :] = cvt(k_src[i, h, :]),  same for V,  i < n, h < hkv.
  * Layouts: k_src/v_src [n, hkv, d] row-major in src_dtype; pools [num_slots, hkv, d]
  * row-major in pool_dtype; slots device int32 [n].
  * Supported: (F32 -> F32), (BF16 -> BF16) copies, and (BF16 -> FP8_E4M3) quantisation
  * code = round-to-nearest-even(float32(x * inv_scale[h])) saturated to +-448 (OCP
  * E4M3, sign kept), with k_inv_scale/v_inv_scale device float32 [hkv].
- * Slots must be distinct and in [0, num_slots) (duplicates race).  d in {64, 128}. */
+ * Slots must be distinct (duplicates race); a slot outside [0, num_slots) is skipped (its
+ * token is not written; a PKV_DEBUG build rejects such a list, and repeated slots, with
+ * PKV_ERR_SLOT before launching).  d in {64, 128}. */
 int pkv_kv_scatter(const void* k_src, const void* v_src, int32_t src_dtype, const int32_t* slots, int64_t n,
                    void* k_pool, void* v_pool, int32_t pool_dtype, int64_t num_slots, int32_t hkv, int32_t d,
                    const float* k_inv_scale, const float* v_inv_scale, void* stream);
@@ -282,8 +318,10 @@ int pkv_extend_attention(const void* q, void* o, int32_t qo_dtype, const void* k
                          const int32_t* work, int64_t n_work, int32_t hq, int32_t hkv, int32_t d,
                          float sm_scale, void* stream);
 
-/* Decode: one query token per sequence, the newest one (position seq_lens[b] - 1, its
- * own K/V included).  Split-K: the context is cut into chunks of `chunk` tokens; one
+/* Decode [OV "Architectural Deep Dive": the generation step; EX: the matched prefix's KV is
+ * reused, not recomputed]: one query token per sequence, the newest one (position
+ * seq_lens[b] - 1, its own K/V included), over its whole cached context (textbook scaled
+ * dot-product attention; the pages do not state the formula).  Split-K: the context is cut into chunks of `chunk` tokens; one
  * partial (running max, running sum, unnormalised output) per (sequence, q head, chunk)
  * goes to the workspace, then a reduce merges the chunks by log-sum-exp:
  *   M = max_s m_s,  o = sum_s exp(m_s - M) acc_s / sum_s exp(m_s - M) l_s.
@@ -291,7 +329,12 @@ int pkv_extend_attention(const void* q, void* o, int32_t qo_dtype, const void* k
  * seq_lens device int32 [batch], each in [1, max_seq_len].  chunk: tokens per split, a
  * multiple of 64, or 0 for automatic.  workspace: device memory of at least
  * pkv_decode_workspace_bytes(batch, hq, d, max_seq_len, chunk) bytes.
- * Supported shapes as for pkv_extend_attention. */
+ * Supported shapes as for pkv_extend_attention.  Slots past the pool read the pool's last
+ * slot (no access leaves the pools).  Errors: PKV_ERR_INVAL (sizes, null pointers, a
+ * workspace too small), PKV_ERR_UNSUPPORTED (shape), PKV_ERR_HIP (launch).
+ * pkv_decode_workspace_bytes: the caller-owned device workspace the split phase needs for
+ * this decode (one partial per (sequence, q head, chunk): running max, running sum and d
+ * output values, float32); 0 for bad sizes. */
 size_t pkv_decode_workspace_bytes(int32_t batch, int32_t hq, int32_t d, int32_t max_seq_len, int32_t chunk);
 /* The automatic chunk: 1024 tokens, halved (not below 128) while the split phase would launch
  * fewer than 2048 workgroups (one per (sequence, chunk) when hkv is 2, 4 or 8, one per
@@ -357,6 +400,30 @@ int pkv_decode_attention_shared(const void* q, void* o, int32_t qo_dtype, const 
                                 int32_t max_seq_len, int32_t hq, int32_t hkv, int32_t d, float sm_scale, int32_t chunk,
                                 const int32_t* members, const int32_t* skip, const int32_t* items, int64_t n_items,
                                 int32_t first_split, void* workspace, size_t ws_bytes, void* stream);
+
+/* first_split value meaning "no split phase at all". */
+#define PKV_NO_SPLIT_PHASE (1 << 30)
+/* The first chunk the split phase must launch for a plan's skip [batch] at the current
+ * lengths seq_lens [batch] (host arrays): the smallest skip[b] over the sequences whose
+ * context holds a chunk at or past skip[b], or PKV_NO_SPLIT_PHASE when the plan's items
+ * cover every context.  A plan made at one step stays valid while the sequences grow; this
+ * is recomputed at each step from that step's lengths.  PKV_ERR_INVAL on bad arguments. */
+int32_t pkv_decode_first_split(const int32_t* skip, const int32_t* seq_lens, int32_t batch, int32_t chunk);
+/* Item capacity pkv_decode_plan (and pkv_decode_shared_plan with any max_span and
+ * private_items) may need for these lengths, stride, chunk and rows per item. */
+int64_t pkv_decode_plan_items_cap(const int32_t* seq_lens, int32_t batch, int64_t stride, int32_t chunk, int32_t rows);
+/* The shared-prefix plan with its choices made [the radix tree gives sequences that share a
+ * prefix the same slots: RC "프리픽스 매칭"; EX: matched KV is reused]: pkv_decode_shared_plan
+ * over rows from one radix tree; when the shared items and the private tails together need
+ * at most private_max_workgroups workgroups (items x hkv), the tails become one-member items
+ * too; when that many items x hkv reach 2 x shared_min_workgroups, items span several chunks
+ * (as many as keep about shared_min_workgroups workgroups).  Outputs as for
+ * pkv_decode_shared_plan, plus *first_split = pkv_decode_first_split at these lengths.
+ * Returns the number of items (0: nothing is shared, decode without a plan; *first_split 0). */
+int64_t pkv_decode_plan(const int32_t* req_to_token, int64_t stride, const int32_t* seq_lens, int32_t batch,
+                        int32_t chunk, int32_t rows, int32_t hkv, int32_t shared_min_workgroups,
+                        int32_t private_max_workgroups, int32_t* members, int32_t* skip, int32_t* items,
+                        int64_t items_cap, int32_t* first_split);
 
 #ifdef __cplusplus
 }

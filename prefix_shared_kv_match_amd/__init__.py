@@ -11,7 +11,7 @@ from typing import List, Optional, Sequence, Tuple
 
 import numpy as np
 
-from ._capi import PKV_BF16, PKV_F32, PKV_FP8_E4M3, PkvError, check, lib
+from ._capi import PKV_BF16, PKV_F32, PKV_FP8_E4M3, PKV_NO_SPLIT_PHASE, PkvError, check, lib
 
 __all__ = [
     "PKV_F32", "PKV_BF16", "PKV_FP8_E4M3", "PkvError", "lib",
@@ -266,6 +266,23 @@ def rt_finish(t, tokens: np.ndarray, tok_indptr: np.ndarray, req_to_token: np.nd
     return ends[:n]
 
 
+def rt_chunk_launch(t, tokens: np.ndarray, tok_indptr: np.ndarray, done, head: int, budget: int):
+    """One chunked-prefill launch from request `head` on: (requests taken, end position of each
+    one's chunk).  done[r] >= 0: request r is under way with done[r] tokens prefilled; -1: not
+    started (its cached prefix is skipped)."""
+    ip = np.ascontiguousarray(tok_indptr, dtype=np.int64)
+    n = int(ip.size - 1)
+    dn = np.ascontiguousarray(done, dtype=np.int64)
+    if dn.size != n:
+        raise ValueError("rt_chunk_launch: done must hold one entry per request")
+    toks = _i32(tokens)
+    reqs = np.empty(max(n - int(head), 1), dtype=np.int32)
+    ends = np.empty(max(n - int(head), 1), dtype=np.int64)
+    k = int(check(lib().rt_chunk_launch(t, n, _ptr(toks), _ptr(ip), _ptr(dn), int(head), int(budget), _ptr(reqs),
+                                        _ptr(ends))))
+    return reqs[:k], ends[:k]
+
+
 # ------------------------------------------------------------------------------------------
 # kernels (device); tensors must live on the ROCm device
 # ------------------------------------------------------------------------------------------
@@ -421,6 +438,38 @@ def pkv_decode_shared_plan(req_to_token: np.ndarray, seq_lens, chunk: int, rows:
                                                int(max_span), int(bool(rows_from_tree)), int(bool(private_items)),
                                                _ptr(members), _ptr(skip), _ptr(items), cap)))
     return members[:b], skip[:b], items[:n]
+
+
+def pkv_decode_first_split(skip, seq_lens, chunk: int) -> int:
+    """First chunk the split phase must launch for a plan's skip at the current lengths, or
+    PKV_NO_SPLIT_PHASE."""
+    sk, sl = _i32(skip), _i32(seq_lens)
+    if sk.size != sl.size:
+        raise ValueError("first split: skip and seq_lens differ in length")
+    return int(check(lib().pkv_decode_first_split(_ptr(sk), _ptr(sl), sl.size, int(chunk))))
+
+
+def pkv_decode_plan(req_to_token: np.ndarray, seq_lens, chunk: int, rows: int, hkv: int,
+                    shared_min_workgroups: int, private_max_workgroups: int):
+    """The shared-prefix plan with the library's choices (spans, private items) over host slot
+    rows from one radix tree: (members, skip, items [n, 4], first_split), or None when nothing
+    is shared."""
+    r2t = _i32(req_to_token)
+    sl = _i32(seq_lens)
+    b = int(sl.size)
+    if r2t.ndim != 2 or r2t.shape[0] < b:
+        raise ValueError("decode plan: req_to_token must be [>= batch, stride]")
+    cap = int(check(lib().pkv_decode_plan_items_cap(_ptr(sl), b, r2t.shape[1], int(chunk), int(rows))))
+    members = np.empty(max(b, 1), dtype=np.int32)
+    skip = np.empty(max(b, 1), dtype=np.int32)
+    items = np.empty((max(cap, 1), 4), dtype=np.int32)
+    first = C.c_int32()
+    n = int(check(lib().pkv_decode_plan(_ptr(r2t), r2t.shape[1], _ptr(sl), b, int(chunk), int(rows), int(hkv),
+                                        int(shared_min_workgroups), int(private_max_workgroups), _ptr(members),
+                                        _ptr(skip), _ptr(items), cap, C.byref(first))))
+    if n == 0:
+        return None
+    return members[:b], skip[:b], items[:n], int(first.value)
 
 
 def pkv_decode_attention_shared(q, o, k_pool, v_pool, req_to_token, seq_lens, max_seq_len, sm_scale, workspace,

@@ -9,6 +9,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("PKV_LIBRARY") or os.path.join(_HERE, "libpkv.so")
 
 PKV_F32, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2
+PKV_NO_SPLIT_PHASE = 1 << 30
 ERRORS = {-1: "PKV_ERR_INVAL", -2: "PKV_ERR_OOM", -3: "PKV_ERR_LOCK", -4: "PKV_ERR_SLOT", -5: "PKV_ERR_NODE",
           -6: "PKV_ERR_HIP", -7: "PKV_ERR_UNSUPPORTED", -8: "PKV_ERR_INTERNAL"}
 
@@ -56,6 +57,7 @@ SIGNATURES = {
     "rt_release": (C.c_int, [_p, _p, _i32]),
     "rt_decode_step": (_i64, [_p, _i32, _p, _i64, _p, _p]),
     "rt_finish": (C.c_int, [_p, _i32, _p, _p, _p, _i64, _p, _p, _p]),
+    "rt_chunk_launch": (_i32, [_p, _i32, _p, _p, _p, _i32, _i64, _p, _p]),
     "pkv_kv_scatter": (C.c_int, [_p, _p, _i32, _p, _i64, _p, _p, _i32, _i64, _i32, _i32, _p, _p, _p]),
     "pkv_append_slots": (C.c_int, [_p, _i64, _p, _p, _i32, _p]),
     "pkv_extend_plan_size": (_i64, [_p, _i32, _i32]),
@@ -69,6 +71,9 @@ SIGNATURES = {
                                        _i32, _i32, _f32, _i32, _p, _sz, _p]),
     "pkv_decode_shared_plan": (_i64, [_p, _i64, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p, _p, _i64]),
     "pkv_decode_shared_rows": (_i32, [_i32, _i32, _i32, _i32, _i32]),
+    "pkv_decode_first_split": (_i32, [_p, _p, _i32, _i32]),
+    "pkv_decode_plan_items_cap": (_i64, [_p, _i32, _i64, _i32, _i32]),
+    "pkv_decode_plan": (_i64, [_p, _i64, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p, _p, _i64, _pi32]),
     "pkv_decode_attention_shared": (C.c_int, [_p, _p, _i32, _p, _p, _i32, _i64, _p, _p, _p, _i64, _p, _i32, _i32,
                                               _i32, _i32, _i32, _f32, _i32, _p, _p, _p, _i64, _i32, _p, _sz, _p]),
 }

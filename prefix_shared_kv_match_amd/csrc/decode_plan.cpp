@@ -149,3 +149,59 @@ extern "C" int64_t pkv_decode_shared_plan(const int32_t* req_to_token, int64_t s
   if (n_items > items_cap) return fail(PKV_ERR_INVAL, "decode plan: needs %lld items", (long long)n_items);
   return n_items;
 }
+
+extern "C" int32_t pkv_decode_first_split(const int32_t* skip, const int32_t* seq_lens, int32_t batch, int32_t chunk) {
+  if (batch < 0 || chunk <= 0 || (batch > 0 && (!skip || !seq_lens)))
+    return fail(PKV_ERR_INVAL, "first split: bad arguments (batch %d chunk %d)", batch, chunk);
+  int32_t first = PKV_NO_SPLIT_PHASE;
+  for (int32_t b = 0; b < batch; ++b) {
+    if (seq_lens[b] < 1 || skip[b] < 0) return fail(PKV_ERR_INVAL, "first split: sequence %d", b);
+    const int64_t chunks = ((int64_t)seq_lens[b] + chunk - 1) / chunk;   // chunks holding its context
+    if (chunks > skip[b]) first = std::min(first, skip[b]);
+  }
+  return first;
+}
+
+extern "C" int64_t pkv_decode_plan_items_cap(const int32_t* seq_lens, int32_t batch, int64_t stride, int32_t chunk,
+                                             int32_t rows) {
+  if (batch < 0 || stride <= 0 || chunk <= 0 || rows <= 0 || (batch > 0 && !seq_lens))
+    return fail(PKV_ERR_INVAL, "decode plan capacity: bad arguments");
+  // a job holds two members or more, so a chunk level makes at most batch / 2 items when an
+  // item takes two rows or more (one per member with one row per item); private items add at
+  // most one per chunk of each context
+  int64_t cap = (int64_t)batch * (stride / chunk) / (rows >= 2 ? 2 : 1) + 1;
+  for (int32_t b = 0; b < batch; ++b) cap += ((int64_t)seq_lens[b] + chunk - 1) / chunk;
+  return cap;
+}
+
+extern "C" int64_t pkv_decode_plan(const int32_t* req_to_token, int64_t stride, const int32_t* seq_lens, int32_t batch,
+                                   int32_t chunk, int32_t rows, int32_t hkv, int32_t shared_min_workgroups,
+                                   int32_t private_max_workgroups, int32_t* members, int32_t* skip, int32_t* items,
+                                   int64_t items_cap, int32_t* first_split) {
+  if (hkv <= 0 || shared_min_workgroups <= 0 || !first_split)
+    return fail(PKV_ERR_INVAL, "decode plan: bad arguments (hkv %d, shared_min_workgroups %d)", hkv,
+                shared_min_workgroups);
+  *first_split = 0;
+  // rows from one radix tree (the caller holds the batch's locks): each chunk's last slot decides
+  int64_t n = pkv_decode_shared_plan(req_to_token, stride, seq_lens, batch, chunk, rows, 1, 1, 0, members, skip,
+                                     items, items_cap);
+  if (n <= 0) return n;
+  int64_t tails = 0;   // private chunks left to the split phase
+  for (int32_t b = 0; b < batch; ++b) tails += ((int64_t)seq_lens[b] + chunk - 1) / chunk - skip[b];
+  // few, short private tails: one-member items take them too, and the split phase (whose
+  // workgroups would be latency-bound) is not launched
+  const bool priv = (n + tails) * hkv <= (int64_t)private_max_workgroups;
+  // a long shared prefix: items spanning several chunks while about shared_min_workgroups
+  // workgroups (items x kv heads) remain, so fewer partials are written
+  const int64_t span = (n + (priv ? tails : 0)) * hkv / shared_min_workgroups;
+  if (span >= 2 || priv) {
+    n = pkv_decode_shared_plan(req_to_token, stride, seq_lens, batch, chunk, rows,
+                               (int32_t)std::min<int64_t>(std::max<int64_t>(span, 1), 1 << 20), 1, priv ? 1 : 0,
+                               members, skip, items, items_cap);
+    if (n < 0) return n;
+  }
+  const int32_t fs = pkv_decode_first_split(skip, seq_lens, batch, chunk);
+  if (fs < 0) return fs;
+  *first_split = fs;
+  return n;
+}

@@ -511,6 +511,32 @@ int rt_schedule_longest_prefix(const rt_tree* t, int32_t num_reqs, const int32_t
   });
 }
 
+int32_t rt_chunk_launch(const rt_tree* t, int32_t num_reqs, const int32_t* tokens, const int64_t* tok_indptr,
+                        const int64_t* done, int32_t head, int64_t budget, int32_t* out_reqs, int64_t* out_ends) {
+  return guard([&]() -> int32_t {
+    if (!t || num_reqs < 0 || head < 0 || head > num_reqs || budget < 1 ||
+        (num_reqs > 0 && (!tokens || !tok_indptr || !done || !out_reqs || !out_ends)))
+      return pkv::fail(PKV_ERR_INVAL, "bad arguments to rt_chunk_launch");
+    int64_t left = budget;
+    int32_t k = 0;
+    for (int32_t r = head; r < num_reqs && left > 0; ++r) {
+      const int64_t L = tok_indptr[r + 1] - tok_indptr[r];
+      if (L < 0) return pkv::fail(PKV_ERR_INVAL, "request %d has a negative length", r);
+      // a request already under way continues where its last chunk ended; a new one starts
+      // after its cached prefix
+      const int64_t start = done[r] >= 0 ? done[r] : t->peek(tokens + tok_indptr[r], L);
+      if (start > L) return pkv::fail(PKV_ERR_INVAL, "request %d: %lld tokens done of %lld", r, (long long)start,
+                                      (long long)L);
+      const int64_t take = std::min(L - start, left);
+      out_reqs[k] = r;
+      out_ends[k] = start + take;
+      ++k;
+      left -= take;
+    }
+    return k;
+  });
+}
+
 int64_t rt_dump_stats(const rt_tree* t, int64_t* out, int64_t cap) {
   if (!t) return pkv::fail(PKV_ERR_INVAL, "tree is null");
   std::vector<int64_t> ids(t->live.begin(), t->live.end());

@@ -19,11 +19,11 @@ from typing import List, Optional, Sequence
 
 import numpy as np
 
-from . import (PKV_BF16, PKV_F32, PKV_FP8_E4M3, check, lib, pkv_decode_chunk, pkv_decode_shared_plan,
-               pkv_decode_shared_rows, pkv_decode_workspace_bytes, pkv_extend_plan, pkv_extend_tile,
-               rt_create_policy, rt_dec_lock_ref, rt_decode_step, rt_destroy, rt_finish, rt_peek_prefix,
-               rt_prepare_extend, rt_prepare_extend_prio, rt_release, rt_schedule_longest_prefix,
-               rt_set_eviction_log)
+from . import (PKV_BF16, PKV_F32, PKV_FP8_E4M3, PKV_NO_SPLIT_PHASE, check, lib, pkv_decode_chunk,
+               pkv_decode_first_split, pkv_decode_plan, pkv_decode_shared_rows, pkv_decode_workspace_bytes,
+               pkv_extend_plan, pkv_extend_tile, rt_chunk_launch, rt_create_policy, rt_dec_lock_ref, rt_decode_step,
+               rt_destroy, rt_finish, rt_prepare_extend, rt_prepare_extend_prio, rt_release,
+               rt_schedule_longest_prefix, rt_set_eviction_log)
 
 _DT = {"f32": PKV_F32, "bf16": PKV_BF16, "fp8_e4m3": PKV_FP8_E4M3}
 
@@ -152,11 +152,13 @@ class StagedUpload:
 class Engine:
     """One radix tree plus its device KV pools."""
 
+    # the two knobs of the library's decode plan (pkv_decode_plan): items span several chunks
+    # while about SHARED_MIN_WORKGROUPS workgroups remain; plans whose items and private tails
+    # together need at most PRIVATE_MAX_WORKGROUPS workgroups give the tails to the
+    # shared-prefix kernel too
     SHARED_MIN_WORKGROUPS = 512
-    # shared-prefix plans whose items and private tails together need at most this many
-    # workgroups (items x kv heads) also give the tails to the shared-prefix kernel
     PRIVATE_MAX_WORKGROUPS = 4096
-    NO_SPLIT_PHASE = 1 << 30
+    NO_SPLIT_PHASE = PKV_NO_SPLIT_PHASE
 
     def __init__(self, num_slots: int, hq: int, hkv: int, d: int, qo_dtype: str, pool_dtype: str,
                  free_order: Optional[np.ndarray] = None, device: str = "cuda", k_scale=None, v_scale=None,
@@ -279,14 +281,11 @@ class Engine:
                                            items=dev[4 * n:4 * n + m].view(-1, 4), chunk=plan["chunk"],
                                            first_split=first)
 
-    @classmethod
-    def first_split(cls, skip: np.ndarray, seq_lens: np.ndarray, chunk: int) -> int:
+    @staticmethod
+    def first_split(skip: np.ndarray, seq_lens: np.ndarray, chunk: int) -> int:
         """The first chunk the split phase must launch for a plan's skip at the current
-        lengths: the smallest skip[b] of a sequence whose context reaches past chunk skip[b],
-        or NO_SPLIT_PHASE when the plan's items cover every sequence's context."""
-        skip = np.asarray(skip, dtype=np.int64)
-        need = (np.asarray(seq_lens, dtype=np.int64) + chunk - 1) // chunk > skip
-        return int(skip[need].min()) if need.any() else cls.NO_SPLIT_PHASE
+        lengths (pkv_decode_first_split), or NO_SPLIT_PHASE."""
+        return pkv_decode_first_split(skip, seq_lens, chunk)
 
     # -- steps ---------------------------------------------------------------------------
     def prepare(self, token_lists, stride: int) -> HostBatch:
@@ -359,38 +358,25 @@ class Engine:
         return self.torch.empty(nbytes // 4 + 1, dtype=self.torch.float32, device=self.device), chunk
 
     def decode_plan(self, req_to_token: np.ndarray, seq_lens: np.ndarray, chunk: int, upload: bool = True):
-        """The shared-prefix plan of a decode batch (host slot rows and current lengths) on the
-        device: a dict of int32 views (members, skip, items) valid for work launched before the
-        next call, or None when no chunk is shared or the shape has no shared-prefix kernel.
-        Computed once, it serves every later decode step of the same sequences (new tokens are
-        private, so the shared chunks do not change; a chunk a sequence grows into is left to
-        the split phase).  When the shared items and the private tails together need at most
-        PRIVATE_MAX_WORKGROUPS workgroups, the tails become one-member items too and the split
-        phase has nothing left at this step.  The device plan's first_split is the smallest
-        skip (right at any later step); upload=False returns the host arrays, for
-        upload_decode to send with a step's slots and to set first_split from that step's
-        lengths."""
+        """The library's shared-prefix plan of a decode batch (pkv_decode_plan over the host slot
+        rows and current lengths), or None when no chunk is shared or the shape has no
+        shared-prefix kernel.  Computed once, it serves every later decode step of the same
+        sequences (new tokens are private, so the shared chunks do not change; a chunk a
+        sequence grows into is left to the split phase, which decode() launches from the
+        first split at that step's lengths).  upload=True: a dict of device int32 views
+        (members, skip, items) valid for work launched before the next call, plus the host
+        skip; upload=False: the host arrays, for upload_decode to send with a step's slots."""
         rows = self.shared_rows
         if rows <= 0:
             return None
-        # the rows come from this engine's tree (its locks keep them), so each chunk's last
-        # slot decides whether two rows share it
-        members, skip, items = pkv_decode_shared_plan(req_to_token, seq_lens, chunk, rows, rows_from_tree=True)
-        if items.shape[0] == 0:
+        # the rows come from this engine's tree (its locks keep them)
+        plan = pkv_decode_plan(req_to_token, seq_lens, chunk, rows, self.hkv, self.SHARED_MIN_WORKGROUPS,
+                               self.PRIVATE_MAX_WORKGROUPS)
+        if plan is None:
             return None
-        # few, short private tails: one-member items take them too and the split phase (whose
-        # workgroups would then be latency-bound) is not launched
-        lens = np.asarray(seq_lens, dtype=np.int64)
-        tails = int(((lens + chunk - 1) // chunk - skip).sum())
-        private = (items.shape[0] + tails) * self.hkv <= self.PRIVATE_MAX_WORKGROUPS
-        # a long shared prefix: items spanning several chunks, as long as about 512
-        # workgroups (items x kv heads) remain, write fewer partials
-        span = (items.shape[0] + (tails if private else 0)) * self.hkv // self.SHARED_MIN_WORKGROUPS
-        if span >= 2 or private:
-            members, skip, items = pkv_decode_shared_plan(req_to_token, seq_lens, chunk, rows, rows_from_tree=True,
-                                                          max_span=max(span, 1), private_items=private)
+        members, skip, items, first = plan
         if not upload:
-            return dict(members=members, skip=skip, items=items, chunk=int(chunk), first_split=int(skip.min()))
+            return dict(members=members, skip=skip, items=items, chunk=int(chunk), first_split=first)
         b, n = members.size, items.size
         up = self._uploader("_plan_up", side=False)
         hn = up.host(2 * b + n)
@@ -399,11 +385,14 @@ class Engine:
         hn[2 * b:2 * b + n] = items.reshape(-1)
         dev = up.send(2 * b + n)
         return dict(members=dev[:b], skip=dev[b:2 * b], items=dev[2 * b:2 * b + n].view(-1, 4), chunk=int(chunk),
-                    first_split=int(skip.min()))
+                    first_split=first, skip_host=skip.copy())
 
-    def decode(self, q, r2t_dev, seq_lens_dev, max_seq_len: int, workspace, chunk: int, o=None, plan=None):
+    def decode(self, q, r2t_dev, seq_lens_dev, max_seq_len: int, workspace, chunk: int, o=None, plan=None,
+               seq_lens_host=None):
         """One decode step; with a plan from decode_plan (same chunk), the shared chunks are
-        read once per group of sequences."""
+        read once per group of sequences.  seq_lens_host (this step's lengths) sets the split
+        phase's first chunk for a plan made at an earlier step; without it the plan's own
+        first_split (right at the step it was made for) is used."""
         if o is None:
             o = self.torch.empty_like(q)
         b = int(q.shape[0])
@@ -420,8 +409,11 @@ class Engine:
             if plan["chunk"] != chunk or plan["members"].shape != (b,):
                 raise ValueError("decode: the plan was made for another chunk or batch")
             items = plan["items"]
+            first = plan["first_split"]
+            if seq_lens_host is not None and plan.get("skip_host") is not None:
+                first = pkv_decode_first_split(plan["skip_host"], seq_lens_host, chunk)
             check(self._lib.pkv_decode_attention_shared(*head, plan["members"].data_ptr(), plan["skip"].data_ptr(),
-                                                        items.data_ptr(), items.shape[0], plan["first_split"], *ws))
+                                                        items.data_ptr(), items.shape[0], first, *ws))
         else:
             check(self._lib.pkv_decode_attention(*head, *ws))
         return o
@@ -536,22 +528,14 @@ def chunked_prefill(tree, token_lists: Sequence[np.ndarray], budget: int, stride
     if budget < 1:
         raise ValueError("chunk budget must be positive")
     n = len(token_lists)
-    done = [0] * n
+    toks, indptr = flatten(token_lists)
+    done = np.full(n, -1, dtype=np.int64)   # tokens prefilled of a request under way, -1 before it starts
     held = [-1] * n
     out = []
     head = 0
     while head < n:
-        left = budget
-        reqs, ends = [], []
-        r = head
-        while r < n and left > 0:
-            L = len(token_lists[r])
-            start = done[r] if held[r] >= 0 else rt_peek_prefix(tree, token_lists[r])
-            take = min(L - start, left)
-            reqs.append(r)
-            ends.append(start + take)
-            left -= take
-            r += 1
+        reqs, ends = rt_chunk_launch(tree, toks, indptr, done, head, budget)
+        reqs, ends = reqs.tolist(), ends.tolist()
         hb = prepare(tree, [np.asarray(token_lists[i])[:e] for i, e in zip(reqs, ends)], stride)
         for i, e, last in zip(reqs, ends, hb.last_nodes.tolist()):
             if held[i] >= 0:

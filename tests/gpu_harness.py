@@ -185,7 +185,8 @@ class Run:
                     self.shared_items = int(self.plan["items"].shape[0])
             outs = [("plain", o)]
             if self.plan is not None:
-                outs.append(("shared", eng.decode(q, r2t, sl, max_len, ws, chunk, plan=self.plan)))
+                outs.append(("shared", eng.decode(q, r2t, sl, max_len, ws, chunk, plan=self.plan,
+                                                      seq_lens_host=hb.seq_lens)))
             torch.cuda.synchronize()
             if decode_sample is None or s == steps - 1 or s % max(1, steps // 2) == 0:
                 seqs = range(B) if decode_sample is None else \

@@ -184,3 +184,46 @@ def test_first_split_at_current_lengths():
     assert Engine.first_split(skip, lens + 3, chunk) == 3          # sequence 2 reaches chunk 3
     _, s0, _ = pkv.pkv_decode_shared_plan(r2t, lens, chunk, 16)   # shared chunks only
     assert s0.tolist() == [3, 3, 2, 0] and Engine.first_split(s0, lens, chunk) == 0
+
+
+@settings(max_examples=80, deadline=None)
+@given(seed=st.integers(0, 10_000), n=st.integers(1, 40), hkv=st.sampled_from([1, 4, 8, 32]),
+       shared_min=st.sampled_from([1, 16, 512]), private_max=st.sampled_from([0, 64, 4096, 1 << 20]))
+def test_plan_choices_of_the_library(seed, n, hkv, shared_min, private_max):
+    """pkv_decode_plan (the library's choices) equals pkv_decode_shared_plan called the way its
+    documentation states: private items when items plus private tails need at most
+    private_max_workgroups workgroups (times hkv), spans of (items [+ tails]) x hkv /
+    shared_min_workgroups chunks when that reaches 2, and first_split at these lengths."""
+    rng = np.random.default_rng(seed)
+    chunk, stride, rows = 64, 512, 8
+    paths = [[int(x) for x in rng.integers(0, 3, size=4)] for _ in range(n)]
+    lens = [int(x) for x in rng.integers(1, stride + 1, size=n)]
+    r2t = rows_from_paths(rng, paths, lens, chunk, stride)
+    got = pkv.pkv_decode_plan(r2t, lens, chunk, rows, hkv, shared_min, private_max)
+    m, skip, items = pkv.pkv_decode_shared_plan(r2t, lens, chunk, rows, rows_from_tree=True)
+    if items.shape[0] == 0:
+        assert got is None
+        return
+    tails = int(sum((L + chunk - 1) // chunk for L in lens) - skip.sum())
+    priv = (items.shape[0] + tails) * hkv <= private_max
+    span = (items.shape[0] + (tails if priv else 0)) * hkv // shared_min
+    if span >= 2 or priv:
+        m, skip, items = pkv.pkv_decode_shared_plan(r2t, lens, chunk, rows, rows_from_tree=True,
+                                                    max_span=max(span, 1), private_items=priv)
+    gm, gs, gi, first = got
+    assert np.array_equal(gm, m) and np.array_equal(gs, skip) and np.array_equal(gi, items)
+    assert first == pkv.pkv_decode_first_split(skip, lens, chunk)
+    need = [s for s, L in zip(skip.tolist(), lens) if (L + chunk - 1) // chunk > s]
+    assert first == (min(need) if need else pkv.PKV_NO_SPLIT_PHASE)
+
+
+def test_first_split_and_plan_reject_bad_arguments():
+    with pytest.raises(pkv.PkvError):
+        pkv.pkv_decode_first_split([0, 1], [10, 0], 64)        # a sequence of length 0
+    with pytest.raises(pkv.PkvError):
+        pkv.pkv_decode_first_split([0], [10], 0)               # no chunk
+    r2t = np.zeros((2, 128), dtype=np.int32)
+    with pytest.raises(pkv.PkvError):
+        pkv.pkv_decode_plan(r2t, [64, 64], 64, 8, 0, 512, 4096)    # hkv 0
+    with pytest.raises(pkv.PkvError):
+        pkv.pkv_decode_plan(r2t, [64, 64], 64, 8, 8, 0, 4096)      # no workgroup target

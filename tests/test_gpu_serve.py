@@ -215,10 +215,11 @@ def test_decode_shared_identical_and_boundary_contexts():
     (a full hit: they share every whole chunk but the newest token's), a context of exactly two
     chunks, one cut inside a shared chunk, one shorter than a chunk, one private, one that
     fills two chunks and then grows into a third; every row equals the plain decode's within
-    float32 summation order (the plain path is checked against the oracle by the parity
-    tests).  Both plans: shared chunks only, and with the private tails as one-member items
-    (made at the first step and kept while the sequences grow, the split phase launched from
-    the first chunk a sequence still needs, or not at all)."""
+    float32 summation order, and both equal the float64 oracle's attention over each
+    sequence's gathered K/V rows (bf16 tolerances).  Both plans: shared chunks only, and with
+    the private tails as one-member items (made at the first step and kept while the
+    sequences grow, the split phase launched from the first chunk a sequence still needs at
+    that step, or not at all)."""
     from prefix_shared_kv_match_amd.runtime import Engine
     log("decode shared: identical and boundary contexts")
     rng = np.random.default_rng(11)
@@ -231,18 +232,25 @@ def test_decode_shared_identical_and_boundary_contexts():
     stride = 512
     hb = eng.prepare(reqs, stride)
     n_new = hb.n_new
-    k = torch.randn(n_new, hkv, d).to(torch.bfloat16).cuda()
-    v = torch.randn(n_new, hkv, d).to(torch.bfloat16).cuda()
-    eng.scatter(torch.from_numpy(hb.new_slots.astype(np.int32)).cuda(), k, v)
+    k = torch.randn(n_new, hkv, d).to(torch.bfloat16)
+    v = torch.randn(n_new, hkv, d).to(torch.bfloat16)
+    # host copies of what each slot holds, for the oracle
+    kh = np.zeros((4096, hkv, d), dtype=np.float64)
+    vh = np.zeros((4096, hkv, d), dtype=np.float64)
+    kh[hb.new_slots] = k.float().numpy()
+    vh[hb.new_slots] = v.float().numpy()
+    eng.scatter(torch.from_numpy(hb.new_slots.astype(np.int32)).cuda(), k.cuda(), v.cuda())
     b = hb.n
     max_len = int(hb.seq_lens.max()) + 3
     ws, _ = eng.decode_workspace(b, max_len, chunk)
     plans = {}
     for step in range(3):
         slots = eng.decode_alloc(hb)
-        eng.scatter(torch.from_numpy(slots).cuda(), torch.randn(b, hkv, d).to(torch.bfloat16).cuda(),
-                    torch.randn(b, hkv, d).to(torch.bfloat16).cuda())
-        q = torch.randn(b, hq, d).to(torch.bfloat16).cuda()
+        kn, vn = torch.randn(b, hkv, d).to(torch.bfloat16), torch.randn(b, hkv, d).to(torch.bfloat16)
+        kh[slots], vh[slots] = kn.float().numpy(), vn.float().numpy()
+        eng.scatter(torch.from_numpy(slots).cuda(), kn.cuda(), vn.cuda())
+        qh = torch.randn(b, hq, d).to(torch.bfloat16)
+        q = qh.cuda()
         r2t = torch.from_numpy(np.ascontiguousarray(hb.req_to_token)).cuda()
         sl = torch.from_numpy(hb.seq_lens.copy()).cuda()
         if step == 0:
@@ -255,15 +263,21 @@ def test_decode_shared_identical_and_boundary_contexts():
             # 128 tokens); 6 is private; 7 (256: its newest token ends chunk 1) shares chunk 0
             assert plans["shared"]["skip"].tolist() == [2, 2, 2, 1, 0, 1, 0, 1]
             assert plans["private"]["skip"].tolist() == [3, 3, 3, 2, 1, 3, 3, 2]
-            # the same private plan on the device, made once: its split phase starts at the
-            # smallest skip at every step
+            # the same private plan on the device, made once: at this step its items cover every
+            # context; at later steps decode() starts the split phase from the lengths it is given
             device_plan = eng.decode_plan(hb.req_to_token, hb.seq_lens, chunk)
-            assert device_plan["first_split"] == 1
+            assert device_plan["first_split"] == Engine.NO_SPLIT_PHASE
         plain = eng.decode(q, r2t, sl, max_len, ws, chunk).float()
-        shared = eng.decode(q, r2t, sl, max_len, ws, chunk, plan=device_plan).float()
+        shared = eng.decode(q, r2t, sl, max_len, ws, chunk, plan=device_plan, seq_lens_host=hb.seq_lens).float()
         torch.cuda.synchronize()
         diff = (plain - shared).abs().max().item()
         assert diff <= 2.0 ** -7 * plain.abs().max().item(), (step, "device plan", diff)
+        # the float64 oracle over each sequence's gathered rows (position L - 1 sees 0..L-1)
+        ref = np.stack([oa.attend(qh[i:i + 1].float().numpy(), kh[hb.req_to_token[i, :hb.seq_lens[i]]],
+                                  vh[hb.req_to_token[i, :hb.seq_lens[i]]], [hb.seq_lens[i] - 1], 1.0 / np.sqrt(d))[0]
+                        for i in range(b)])
+        compare(plain.cpu().numpy(), ref, "bf16", f"boundary decode step {step} (plain)")
+        compare(shared.cpu().numpy(), ref, "bf16", f"boundary decode step {step} (device plan)")
         for name, host_plan in plans.items():
             _, _, plan = eng.upload_decode(slots, hb.seq_lens, host_plan)
             if name == "private":

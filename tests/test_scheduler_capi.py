@@ -79,3 +79,27 @@ def test_chunked_prefill_matches_oracle(budget):
         assert pkv.rt_protected_size(t) == 0
     finally:
         pkv.rt_destroy(t)
+
+
+def test_chunk_launch_hand_example():
+    """rt_chunk_launch, the cut of one chunked-prefill launch: [1,2,3] cached; requests
+    [1,2,3,4,5] (2 uncached tokens) and [9,9,9] (3) under a budget of 4 -> the first takes its
+    2 tokens (end 5), the second 2 of its 3 (end 2, cut); the next launch from the cut request
+    (2 done) takes its last token (end 3).  The tree is not changed."""
+    t = pkv.rt_create(32)
+    try:
+        hb = runtime.prepare(t, [np.array([1, 2, 3])], 8)
+        pkv.rt_release(t, hb.last_nodes)
+        before = (pkv.rt_dump(t), pkv.rt_clock(t))
+        toks, indptr = runtime.flatten([np.array([1, 2, 3, 4, 5]), np.array([9, 9, 9])])
+        reqs, ends = pkv.rt_chunk_launch(t, toks, indptr, [-1, -1], 0, 4)
+        assert reqs.tolist() == [0, 1] and ends.tolist() == [5, 2]
+        reqs, ends = pkv.rt_chunk_launch(t, toks, indptr, [5, 2], 1, 4)
+        assert reqs.tolist() == [1] and ends.tolist() == [3]
+        assert (pkv.rt_dump(t), pkv.rt_clock(t)) == before
+        with pytest.raises(pkv.PkvError):
+            pkv.rt_chunk_launch(t, toks, indptr, [-1, -1], 0, 0)       # no budget
+        with pytest.raises(pkv.PkvError):
+            pkv.rt_chunk_launch(t, toks, indptr, [9, -1], 0, 4)       # more done than the request holds
+    finally:
+        pkv.rt_destroy(t)
