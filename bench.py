@@ -1,11 +1,17 @@
 """Throughput of the prefix-shared KV hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload fewshot_bf16|decode_bf16|longctx_fp8]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload longctx_fp8|fewshot_bf16|decode_bf16|...]
 
 A step is one pass of the whole hot path over one batch of synthetic input, with the
 inputs (K/V/Q source rows) already resident in HBM:
 
-  fewshot_bf16 (default; 64 requests sharing a 1,800-token prefix that is cached before
+  longctx_fp8 (default; the largest configuration on one GPU): 16 requests sharing a
+  32,768-token prefix cached before the timed region, 1,024-token suffixes, GQA 64/8, d 128,
+  fp8 e4m3 pool with per-head scales:
+    rt_prepare_extend -> H2D tables -> kv_scatter (quantising) -> extend_attention
+    -> 64 decode steps (rt_decode_step -> H2D -> kv_scatter -> decode_attention)
+    -> rt_finish -> rt_evict of the batch's private tokens
+  fewshot_bf16 (64 requests sharing a 1,800-token prefix that is cached before
   the timed region, suffixes U[150, 250], GQA 32/8, d 128, bf16, 200k-slot pool):
     rt_prepare_extend (match with split, lock, allocate, insert, relock for 64 requests)
     -> H2D tables -> kv_scatter of the suffix K/V -> extend_attention
@@ -13,12 +19,15 @@ inputs (K/V/Q source rows) already resident in HBM:
     -> rt_finish (insert prompt + decoded token, unlock) -> rt_evict of the batch's private
        tokens (LRU leaves), so that every step meets the same cached state
   decode_bf16: one decode step of 512 sequences over 2,048-8,192-token contexts
-  longctx_fp8: extend of 16 x 1,024 tokens over a 32,768-token prefix, then 64 decode steps
 
 Prints one JSON line.  `value` is query tokens (extend rows + decode rows) per second of
 the whole step; `roofline` is the dominant kernel's achieved rate from HIP events on the
 stream the library launches on, against MI355X's published peak; `cpu_baseline` is the
-float64 CPU oracle on a bounded sample of the same workload.
+float64 CPU oracle on a bounded sample of the same workload.  Decode rates are reported on
+three byte counts, never as one fraction above 1: the gathered bytes (each sequence's context
+once; "effective" rate, which a shared prefix read once can push past the HBM peak), the
+distinct K/V bytes of the step (a floor on what HBM must deliver) and, where the counters
+were taken on the current kernels, the HBM bytes FETCH_SIZE/WRITE_SIZE measured.
 """
 from __future__ import annotations
 
@@ -86,7 +95,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=None,
                     help="untimed steps first (default per workload: long enough for the GPU to leave its "
                          "idle clocks; a few milliseconds of warmup under-reports a sub-millisecond step)")
-    ap.add_argument("--workload", default="fewshot_bf16",
+    ap.add_argument("--workload", default="longctx_fp8",
                     choices=["fewshot_bf16", "decode_bf16", "longctx_fp8", "multiturn_bf16", "tot_bf16"])
     ap.add_argument("--schedule", default="lpm", choices=["fcfs", "lpm"],
                     help="multiturn_bf16: batch order of the serve loop")
@@ -108,6 +117,9 @@ def parse():
                          "and tails need at most this many workgroups (-1 = the engine's default, 0 = never)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=64, help="requests in the oracle's timed sample")
+    ap.add_argument("--cpu-rows", type=int, default=-1,
+                    help="extend rows per request in the oracle's timed sample (0 = all; -1 = 48 for the "
+                         "long-context case, whose rows each cost ~2 GFLOP in float64, else all)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (reference for HBM byte counters)")
     return ap.parse_args()
@@ -503,23 +515,48 @@ class JobBench:
         return out
 
 
-def practical_hbm_gbps(torch, mib=1024, reps=5):
-    """A plain device-to-device copy of `mib` MiB (read + write), best of `reps`: the HBM rate a
-    streaming kernel reaches on this GPU, next to the published 8 TB/s."""
-    n = mib * (1 << 20) // 4
-    src = torch.ones(n, dtype=torch.float32, device="cuda")
-    dst = torch.empty_like(src)
+def practical_hbm_gbps(torch, mib=4096, reps=5):
+    """The library's streaming-read kernel (pkv_stream_read) over `mib` MiB, far beyond the
+    256 MB last-level cache, best of `reps`: the read rate HBM delivers to a plain kernel on
+    this GPU, next to the published 8 TB/s."""
+    import prefix_shared_kv_match_amd as pkv
+    lib = pkv.lib()
+    buf = torch.ones(mib * (1 << 20) // 4, dtype=torch.float32, device="cuda")
+    out = torch.empty(int(lib.pkv_stream_read_words()), dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
     best = float("inf")
     for _ in range(reps + 1):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        dst.copy_(src)
+        pkv.check(lib.pkv_stream_read(buf.data_ptr(), buf.numel() * 4, out.data_ptr(), st))
         e1.record()
         torch.cuda.synchronize()
         best = min(best, e0.elapsed_time(e1))
-    del src, dst
+    del buf, out
     torch.cuda.empty_cache()
-    return 2.0 * n * 4 / best / 1e6
+    return mib * (1 << 20) / best / 1e6
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def blas_threads() -> int:
+    try:
+        import threadpoolctl
+        info = [x for x in threadpoolctl.threadpool_info() if x.get("user_api") == "blas"]
+        if info:
+            return int(info[0]["num_threads"])
+    except Exception:
+        pass
+    return 1
 
 
 def main_job(a, torch):
@@ -580,16 +617,23 @@ def main_job(a, torch):
     return 0
 
 
-def cpu_baseline(wl, hb, n_req, decode_only=False, steps_done=0, min_seconds=10.0):
+def cpu_baseline(wl, hb, n_req, decode_only=False, steps_done=0, min_seconds=10.0, rows_per_req=0):
     """The float64 oracle on a bounded sample, repeated until at least min_seconds of CPU work:
-    the extend rows of the first n_req requests, or (decode workload) the newest decode row of
-    the first n_req sequences over their whole current context."""
+    the extend rows of the first n_req requests (with rows_per_req > 0, that many rows of each,
+    a seeded sample that holds the first and last), or (decode workload) the newest decode row
+    of the first n_req sequences over their whole current context."""
     from oracle import attention as oa
-    try:
-        cores = len(os.sched_getaffinity(0))
-    except AttributeError:
-        cores = os.cpu_count() or 1
+    threads = blas_threads()
     reqs = wl.batches[-1][:n_req]
+    rng = np.random.default_rng(0)
+    picks = []
+    for i, r in enumerate(reqs):
+        p = int(hb.prefix_lens[i])
+        pos = np.arange(p, len(r.tokens))
+        if rows_per_req and pos.size > rows_per_req:
+            mid = rng.choice(pos[1:-1], size=rows_per_req - 2, replace=False)
+            pos = np.sort(np.concatenate([[pos[0], pos[-1]], mid]))
+        picks.append(pos)
     t0 = time.perf_counter()
     rows, passes = 0, 0
     while True:
@@ -598,18 +642,19 @@ def cpu_baseline(wl, hb, n_req, decode_only=False, steps_done=0, min_seconds=10.
                 oa.decode_row(wl, np.concatenate([r.rows, wl.decode_rows[:steps_done, i]]))
                 rows += 1
             else:
-                p = int(hb.prefix_lens[i])
-                oa.extend_rows(wl, r, p)
-                rows += len(r.tokens) - p
+                oa.extend_rows(wl, r, int(hb.prefix_lens[i]), sample=picks[i])
+                rows += picks[i].size
         passes += 1
         dt = time.perf_counter() - t0
         if dt >= min_seconds:
             break
-    return {"value": rows / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"float64 numpy oracle (BLAS threads = {cores}): "
-                      f"{'newest decode row' if decode_only else 'extend rows'} of the first {len(reqs)} of "
-                      f"{len(wl.batches[-1])} {'sequences' if decode_only else 'requests'} over their full contexts, "
-                      f"{passes} pass(es), {rows} query tokens in {dt:.1f} s"}
+    what = "newest decode row" if decode_only else (
+        f"{rows_per_req} sampled extend rows" if rows_per_req else "extend rows")
+    return {"value": rows / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "sample": f"float64 numpy oracle (BLAS threads = {threads}, {cpu_model()}): {what} of the first "
+                      f"{len(reqs)} of {len(wl.batches[-1])} {'sequences' if decode_only else 'requests'} over "
+                      f"their full contexts, {passes} pass(es), {rows} query tokens in {dt:.1f} s"}
 
 
 def main():
@@ -703,24 +748,38 @@ def main():
         # the distinct K/V rows of the step: the bytes HBM must deliver at least once (the
         # gathered bytes count a shared prefix once per sequence)
         uniq = float(np.unique(np.concatenate([hb.req_to_token[i, :hb.seq_lens[i]] for i in range(hb.n)])).size)
+        hbm = traffic_bytes(wl.name, "decode_attention")
         kernels["decode_attention"] = {
-            "ms": dec_ms, "kv_gathered_gbps": dec_bytes / dec_ms / 1e6,
-            "frac_hbm": dec_bytes / dec_ms / 1e6 / PEAK_HBM_GBPS, "bytes": dec_bytes,
-            "frac_hbm_practical": dec_bytes / dec_ms / 1e6 / hbm_practical,
+            "ms": dec_ms,
+            "gathered_bytes": dec_bytes, "effective_gbps": dec_bytes / dec_ms / 1e6,
             "unique_kv_bytes": uniq * kv_tok, "unique_gbps": uniq * kv_tok / dec_ms / 1e6,
             "frac_hbm_unique": uniq * kv_tok / dec_ms / 1e6 / PEAK_HBM_GBPS,
-            "tflops": 4.0 * s.d * s.hq * float(ctx.sum()) / dec_ms / 1e9}
+            "hbm_bytes": hbm, "hbm_gbps": None if hbm is None else hbm / dec_ms / 1e6,
+            "frac_hbm": None if hbm is None else hbm / dec_ms / 1e6 / PEAK_HBM_GBPS,
+            "frac_hbm_practical": None if hbm is None else hbm / dec_ms / 1e6 / hbm_practical,
+            "tflops": 4.0 * s.d * s.hq * float(ctx.sum()) / dec_ms / 1e9,
+            "note": "effective_gbps counts each sequence's whole context (a shared prefix once per sequence) and "
+                    "can exceed the HBM peak when shared chunks are read once; frac_hbm is on the HBM bytes the "
+                    "counters measured (null until taken on the current kernels); frac_hbm_unique on the "
+                    "distinct K/V bytes, a floor on HBM traffic"}
     sc_name = "kv_scatter_decode" if b.decode_only else "kv_scatter"
     sc_ms = b.timer.avg_ms(sc_name)
     n_new = hb.n if b.decode_only else int(hb.extend_lens.sum())
     src_b = 2 * s.hkv * s.d * (4 if s.qo_dtype == "f32" else 2)
     kernels["kv_scatter"] = {"ms": sc_ms, "gbps": n_new * (src_b + kv_tok) / sc_ms / 1e6}
+    basis = None
     if wl.extend_attention:
         dom, bound = "extend_attention", "mfma"
         achieved, peak, unit = kernels[dom]["tflops"], PEAK_BF16_TFLOPS, "TFLOP/s"
+        basis = "algorithmic FLOPs 4*d*hq*sum(e*p + e(e+1)/2) from the tree's (p, e) / extend time"
     else:
         dom, bound = "decode_attention", "hbm"
-        achieved, peak, unit = kernels[dom]["kv_gathered_gbps"], PEAK_HBM_GBPS, "GB/s"
+        k = kernels[dom]
+        peak, unit = PEAK_HBM_GBPS, "GB/s"
+        if k["hbm_gbps"] is not None:
+            achieved, basis = k["hbm_gbps"], "HBM bytes measured by FETCH_SIZE/WRITE_SIZE / decode time"
+        else:
+            achieved, basis = k["unique_gbps"], "distinct K/V bytes of the step / decode time (counters not taken)"
     out = {
         "metric": "extend+decode attention tokens/s, TFLOP/s & KV GB/s vs MI355X roofline",
         "value": tokens / el, "unit": "tokens/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
@@ -730,15 +789,16 @@ def main():
                    "hq": s.hq, "hkv": s.hkv, "head_dim": s.d, "pool_dtype": s.pool_dtype,
                    "pool_slots": wl.pool_slots, "decode_steps_per_step": 1 if b.decode_only else b.steps_dec},
         "roofline": {"bound": bound, "kernel": dom, "achieved": achieved, "peak": peak, "unit": unit,
-                     "frac": achieved / peak, "traffic": traffic_bytes(wl.name, dom)},
+                     "frac": achieved / peak, "traffic": traffic_bytes(wl.name, dom), "basis": basis},
         "kernels": kernels,
         "kernel_timing": f"{dom}: HIP events in every timed step (the only span recorded there); the other "
                          f"kernels: HIP events over {extra} untimed steps after the timed ones",
-        "hbm_practical_gbps": hbm_practical,
+        "hbm_practical_read_gbps": hbm_practical,
         "library": os.path.relpath(pkv._capi.LIB_PATH, ROOT),
     }
     if not a.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, hb, a.cpu_sample, b.decode_only, timed_step_i)
+        rows = a.cpu_rows if a.cpu_rows >= 0 else (48 if wl.name == "longctx_fp8" else 0)
+        out["cpu_baseline"] = cpu_baseline(wl, hb, a.cpu_sample, b.decode_only, timed_step_i, rows_per_req=rows)
     print(json.dumps(out), flush=True)
     return 0
 

@@ -425,6 +425,18 @@ int64_t pkv_decode_plan(const int32_t* req_to_token, int64_t stride, const int32
                         int32_t private_max_workgroups, int32_t* members, int32_t* skip, int32_t* items,
                         int64_t items_cap, int32_t* first_split);
 
+/* ----------------------------------------------------------------------------------
+ * Measurement helper (device)
+ * -------------------------------------------------------------------------------- */
+
+/* A plain streaming read of `bytes` (a positive multiple of 16) of device memory at `buf`:
+ * the rate a read-only kernel reaches on this GPU's HBM, set beside the published peak when
+ * the HBM-bound kernels are measured.  `out` is caller-owned device memory of
+ * pkv_stream_read_words() uint32 words (written so the loads stay live; the values mean
+ * nothing).  Enqueued on `stream`; PKV_ERR_INVAL on bad arguments. */
+int32_t pkv_stream_read_words(void);
+int pkv_stream_read(const void* buf, int64_t bytes, uint32_t* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

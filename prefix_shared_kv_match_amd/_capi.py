@@ -72,6 +72,8 @@ SIGNATURES = {
     "pkv_decode_shared_plan": (_i64, [_p, _i64, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p, _p, _i64]),
     "pkv_decode_shared_rows": (_i32, [_i32, _i32, _i32, _i32, _i32]),
     "pkv_decode_first_split": (_i32, [_p, _p, _i32, _i32]),
+    "pkv_stream_read_words": (_i32, []),
+    "pkv_stream_read": (C.c_int, [_p, _i64, _p, _p]),
     "pkv_decode_plan_items_cap": (_i64, [_p, _i32, _i64, _i32, _i32]),
     "pkv_decode_plan": (_i64, [_p, _i64, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p, _p, _i64, _pi32]),
     "pkv_decode_attention_shared": (C.c_int, [_p, _p, _i32, _p, _p, _i32, _i64, _p, _p, _p, _i64, _p, _i32, _i32,

@@ -33,7 +33,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpkv.so")
 
 HOST_SOURCES = ["common.cpp", "radix_tree.cpp", "decode_plan.cpp"]
-HIP_SOURCES = ["kv_scatter.hip", "extend_attention.hip", "decode_attention.hip"]
+HIP_SOURCES = ["kv_scatter.hip", "extend_attention.hip", "decode_attention.hip", "hbm_probe.hip"]
 
 ARCH = "gfx950"
 # Packed-FP32 instructions are switched off for every HIP file.

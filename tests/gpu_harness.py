@@ -31,11 +31,11 @@ def src_tensor(torch, a: np.ndarray, shape, dev):
     return t.to(dev)
 
 
-def make_engine(wl, dev="cuda"):
+def make_engine(wl, dev="cuda", policy="lru"):
     from prefix_shared_kv_match_amd.runtime import Engine
     s = wl.shape
     return Engine(wl.pool_slots, s.hq, s.hkv, s.d, s.qo_dtype, s.pool_dtype, wl.free_order, dev,
-                  wl.k_scale, wl.v_scale, wl.k_inv_scale, wl.v_inv_scale, s.sm_scale)
+                  wl.k_scale, wl.v_scale, wl.k_inv_scale, wl.v_inv_scale, s.sm_scale, policy=policy)
 
 
 def check_tables(hb, num_slots):

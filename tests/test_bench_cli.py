@@ -35,3 +35,11 @@ def test_traffic_withheld_for_changed_sources(monkeypatch):
     monkeypatch.setitem(bench.TRAFFIC, "fewshot_bf16", entry)
     assert bench.traffic_bytes("fewshot_bf16", "extend_attention") is None
     assert bench.traffic_bytes("fewshot_bf16", "decode_attention") is None     # another kernel's figure
+
+
+def test_default_workload_is_the_long_context_case(monkeypatch):
+    """With no flags the bench runs the largest configuration that fits one GPU: the long-context
+    case (extend over a 32,768-token prefix, then 64 decode steps)."""
+    monkeypatch.setattr(sys, "argv", ["bench.py"])
+    a = bench.parse()
+    assert a.workload == "longctx_fp8" and a.gpus == 1

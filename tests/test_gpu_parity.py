@@ -301,14 +301,20 @@ def test_fewshot_full_sampled():
 
 
 def test_longctx_full_sampled():
+    """The long-context case at full size: extend, then all 64 decode steps (sampled sequences
+    compared at the first, middle and last step)."""
     log("longctx full")
-    stats = Run(workloads.longctx_fp8(steps=4), sample_rows=6).run(decode_sample=8)
+    stats = Run(workloads.longctx_fp8(), sample_rows=6).run(decode_sample=8)
+    assert sorted({s["step"] for s in stats if s["kind"] == "decode"}) == [0, 32, 63]
     report("longctx full", stats)
 
 
 def test_decode_full_sampled():
+    """The decode batch at full size: all 32 steps (sampled sequences compared at the first,
+    middle and last step)."""
     log("decode full")
-    stats = Run(workloads.decode_bf16(steps=3)).run(decode_sample=24)
+    stats = Run(workloads.decode_bf16()).run(decode_sample=24)
+    assert sorted({s["step"] for s in stats if s["kind"] == "decode"}) == [0, 16, 31]
     report("decode full", stats)
 
 
@@ -322,3 +328,147 @@ def test_tot_full_sampled():
     log("tot full")
     stats = Run(workloads.tot_bf16(decode_steps=4), sample_rows=4, req_stride=2).run(decode_sample=32)
     report("tot full", stats)
+
+
+# ---------------------------------------------------------------------------------------------
+# stress: sharp softmax and planted late keys (the running-maximum moves after the first tile)
+# ---------------------------------------------------------------------------------------------
+
+def _late_key_fraction(wl, plant_pos, first_tile=64):
+    """Host check that the case exercises what it is for: the fraction of (extend query row,
+    head) pairs that see a planted key whose logit exceeds the maximum over the first K/V tile
+    (positions 0..63) by more than 8 log2 units -- the lazy-rescale threshold of the MFMA
+    kernels, so each such row must move its reference maximum and rescale its accumulators."""
+    s = wl.shape
+    vt = wl.values
+    hits = tot = 0
+    for r in wl.batches[0]:
+        L = len(r.tokens)
+        p = L - len(r.rows[300:])
+        k = vt.k(r.rows[:L]).astype(np.float64)
+        q = vt.q(r.rows[p:L]).astype(np.float64)
+        qpos = np.arange(p, L)
+        for h in range(s.hq):
+            g = h // s.group
+            lg = s.sm_scale * (q[:, h] @ k[:, g].T) / math.log(2)      # log2 units
+            first = lg[:, :first_tile].max(axis=1)
+            fires = np.zeros(qpos.size, dtype=bool)
+            for pos in plant_pos(r):
+                if pos < L:
+                    fires |= (lg[:, pos] - first > 8) & (qpos >= pos)
+            hits += int(fires.sum())
+            tot += qpos.size
+    return hits / tot
+
+
+@pytest.mark.parametrize("hq,hkv,pool", [(8, 8, "bf16"), (32, 8, "bf16"), (64, 8, "bf16"),
+                                         (8, 8, "fp8_e4m3"), (32, 8, "fp8_e4m3"), (64, 8, "fp8_e4m3")])
+def test_sharp_softmax_planted_late_keys(hq, hkv, pool):
+    """Queries scaled by 4 (a sharp softmax) and two planted keys late in the contexts: one at
+    prefix position 200 (the fourth 64-token tile, seen by every extend and decode row, inside
+    the second tile of a 128-token shared-prefix decode chunk) and one 100 tokens into the
+    longest suffix (seen only by that request's later rows).  Their logits exceed the first
+    tile's maximum by more than 8 log2 units for most rows (checked on the host), so the
+    extend kernels (group sizes 1, 4, 8; bf16 and fp8 pools), the shared-prefix decode and the
+    split phase must all move their running maximum mid-stream.  Every row against the oracle."""
+    log(f"sharp softmax, planted keys {hq}/{hkv} {pool}")
+    wl = _shape_workload(hq, hkv, pool)
+    pre = wl.pre_insert[0].rows
+    longest = wl.batches[0][-1]
+    wl.values = workloads.StressValues(wl.values, q_mul=4.0, beta=8.0, gamma=60.0,
+                                       plant_rows=[int(pre[200]), int(longest.rows[400])])
+    if pool == "fp8_e4m3":
+        wl.k_scale, wl.v_scale = workloads.fp8_scales(wl.values)
+        wl.k_inv_scale = (np.float32(1.0) / wl.k_scale).astype(np.float32)
+        wl.v_inv_scale = (np.float32(1.0) / wl.v_scale).astype(np.float32)
+    frac = _late_key_fraction(wl, lambda r: [200] + ([400] if r is longest else []))
+    assert frac > 0.5, f"only {frac:.2f} of the rows meet a planted key beyond the rescale threshold"
+    r = Run(wl, check_pool=True)
+    r.eng.SHARED_MIN_WORKGROUPS = 1 << 20      # one item per chunk: position 200 sits in chunk 1's second tile
+    r.eng.PRIVATE_MAX_WORKGROUPS = 0
+    stats = r.run()
+    assert r.shared_items > 0
+    report(f"sharp/planted {hq}/{hkv} {pool} (late-key rows {frac:.2f})", stats)
+    assert {s["kind"] for s in stats} == {"extend", "decode"}
+
+
+# ---------------------------------------------------------------------------------------------
+# finished sequences whose decoded tokens another sequence already cached
+# ---------------------------------------------------------------------------------------------
+
+def test_finish_duplicates_then_reuse_decoded_tokens():
+    """Two sequences with the same prompt decode the same tokens (same K/V rows); a third decodes
+    others.  At finish the first one's decoded tokens are inserted with its slots and the second
+    one's slots for them are duplicates that go back to the free list (the radix-cache page: the
+    caller frees the indices insert reports as already cached).  Host state after finish equals
+    the oracle's; then a follow-up request extends the first sequence's full token list and must
+    reuse its decoded tokens' slots, whose K/V the decode steps wrote: its extend rows against
+    the oracle's attention over the whole context."""
+    import prefix_shared_kv_match_amd as pkv
+    log("finish duplicates, then reuse of decoded tokens")
+    shape = workloads.Shape(32, 8, 128, "bf16", "bf16", 1 / math.sqrt(128))
+    rng = np.random.default_rng(21)
+    b = workloads._Builder(rng, 5000)
+    pre = b.segment(0, 200)
+    s1 = b.segment(pre[0], 50)
+    s2 = b.segment(pre[0], 70)
+    reqs = [workloads._concat([pre, s1]), workloads._concat([pre, s1]), workloads._concat([pre, s2])]
+    steps = 3
+    dt, dr = workloads._decode(b, 3, steps)
+    dt[:, 1], dr[:, 1] = dt[:, 0], dr[:, 0]                     # sequence 1 decodes what sequence 0 decodes
+    follow = b.segment(int(dt[-1, 0]) + 1, 40)                  # rows of the follow-up's new tokens
+    vt = workloads.ValueTable(21, b.next_row, shape)
+    free = rng.permutation(8192).astype(np.int32)
+    wl = workloads.Workload("finish_dup", 21, shape, 8192, free,
+                            [workloads.Request(pre[1].copy(), pre[2].copy(), "prefix")], [reqs], True, dt, dr, vt)
+    r = Run(wl, check_pool=True)
+    stats = r.run()
+    assert {s["kind"] for s in stats} == {"extend", "decode"}
+    ol = r.oracle_log
+    eng = r.eng
+    assert pkv.rt_dump(eng.tree) == ol.dump
+    assert pkv.rt_copy_free_list(eng.tree).tolist() == ol.free
+    dup = [ol.decode_slots[s][1] for s in range(steps)]
+    assert ol.free[-steps:] == dup                              # sequence 1's decode slots went back
+    # follow-up: sequence 0's full token list plus 40 new tokens
+    full0 = np.concatenate([reqs[0].tokens, dt[:, 0]])
+    rows0 = np.concatenate([reqs[0].rows, dr[:, 0]])
+    fr = workloads.Request(np.concatenate([full0, follow[1]]).astype(np.int32),
+                           np.concatenate([rows0, follow[2]]).astype(np.int64), "follow-up")
+    hb = eng.prepare([fr.tokens], wl.max_len() + 64)
+    assert int(hb.prefix_lens[0]) == full0.size
+    row0 = ol.batches[0].rows[0] + [ol.decode_slots[s][0] for s in range(steps)]
+    assert hb.req_to_token[0, :full0.size].tolist() == row0
+    new_rows = fr.rows[full0.size:]
+    r.scatter(hb.new_slots, new_rows)
+    dtb = eng.device_tables(hb)
+    o = eng.extend(dtb, src_tensor(torch, wl.values.q(new_rows), shape, "cuda"))
+    torch.cuda.synchronize()
+    st = compare(o.float().cpu().numpy(), oa.extend_rows(wl, fr, full0.size), "bf16", "follow-up extend")
+    eng.release(hb)
+    log(f"finish duplicates: follow-up extend {st}")
+
+
+def test_kv_scatter_skips_slots_outside_the_pool():
+    """A slot list holding -1 and num_slots: those tokens are not written (no write leaves the
+    pools), every other token lands bit-exactly, and no other slot changes."""
+    import prefix_shared_kv_match_amd as pkv
+    log("kv_scatter with slots outside the pool")
+    rng = np.random.default_rng(5)
+    n, hkv, d, total = 64, 8, 128, 1024
+    src = workloads.round_to_bf16(rng.standard_normal((n, hkv, d)).astype(np.float32))
+    slots = rng.permutation(total)[:n].astype(np.int32)
+    slots[3], slots[40] = -1, total
+    kp = torch.zeros((total, hkv, d), dtype=torch.bfloat16, device="cuda")
+    vp = torch.zeros_like(kp)
+    x = torch.from_numpy(src).to(torch.bfloat16).cuda()
+    pkv.pkv_kv_scatter(x, x, torch.from_numpy(slots).cuda(), kp, vp)
+    torch.cuda.synchronize()
+    good = np.ones(n, dtype=bool)
+    good[[3, 40]] = False
+    got = kp.cpu()[torch.from_numpy(slots[good].astype(np.int64))].float().numpy()
+    np.testing.assert_array_equal(got, src[good])
+    mask = np.ones(total, dtype=bool)
+    mask[slots[good]] = False
+    assert torch.count_nonzero(kp.cpu()[torch.from_numpy(mask)]).item() == 0
+    assert torch.count_nonzero(vp.cpu()[torch.from_numpy(mask)]).item() == 0

@@ -47,17 +47,28 @@ def _extend_and_check(eng, wl, reqs, ends, hb, what):
     return compare(got, np.concatenate(ref), wl.shape.qo_dtype, what)
 
 
-@pytest.mark.parametrize("order", ["fcfs", "lpm"])
-def test_serve_multiturn_small(order):
+SERVE_CASES = [("fcfs", "lru"), ("lpm", "lru"), ("lpm", "lfu"), ("lpm", "slru"), ("lpm", "fifo"), ("lpm", "mru"),
+               ("lpm", "filo"), ("lpm", "priority")]
+
+
+@pytest.mark.parametrize("order,policy", SERVE_CASES)
+def test_serve_multiturn_small(order, policy):
+    """The serve loop over the multi-turn workload with eviction, under every eviction policy of
+    the radix-cache page's strategy list: the policy decides which rows are evicted and so which
+    slots later batches reuse and which they refill, i.e. the tables the kernels read.  Picks and
+    tables bit-exact against the oracle scheduler with the same policy; every extend row against
+    the oracle's attention."""
     from prefix_shared_kv_match_amd import runtime
-    log(f"serve multiturn small {order}")
+    log(f"serve multiturn small {order} {policy}")
     wl = workloads.multiturn_bf16(n_conv=24, turns=4, turn_range=(16, 96), batch=8, pool_slots=20000,
                                   capacity=8000)
     arr = [r for b in wl.batches for r in b]
     after = [r.after for r in arr]
-    olog = osch.serve(OracleTree(wl.pool_slots, wl.free_order), [r.tokens.tolist() for r in arr], after, order,
-                      batch=6, window=24)
-    eng = make_engine(wl)
+    prio = [r.priority for r in arr]
+    otree = OracleTree(wl.pool_slots, wl.free_order, policy)
+    olog = osch.serve(otree, [r.tokens.tolist() for r in arr], after, order, batch=6, window=24, priorities=prio)
+    assert otree.evlog, "eviction did not fire"
+    eng = make_engine(wl, policy=policy)
     stats = []
 
     def on_batch(pick, hb):
@@ -68,7 +79,8 @@ def test_serve_multiturn_small(order):
         reqs = [arr[i] for i in pick]
         stats.append(_extend_and_check(eng, wl, reqs, [len(r.tokens) for r in reqs], hb, f"round {k}"))
 
-    runtime.serve(eng.tree, [r.tokens for r in arr], after, order, 6, 24, wl.max_len(), on_batch=on_batch)
+    runtime.serve(eng.tree, [r.tokens for r in arr], after, order, 6, 24, wl.max_len(), priorities=prio,
+                  on_batch=on_batch)
     assert len(stats) == len(olog.picks)
     log(f"  {len(stats)} rounds, hit rate {olog.hit_rate:.3f}, worst {max(s['rel_rms'] for s in stats if s)}")
 

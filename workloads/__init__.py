@@ -155,6 +155,42 @@ class ValueTable:
         return out.reshape(self.n_rows, h, self.shape.d)
 
 
+class StressValues(ValueTable):
+    """A value table with a sharpened softmax and planted keys, for stress cases.
+
+    Every Q row is replaced by q_mul * q + beta * u_g (per query head, u_g a fixed unit vector of
+    its kv head drawn from the seed), and the K rows listed in ``plant_rows`` by gamma * u_g, all
+    rounded to the stored precision again.  A planted key then meets every query with a logit
+    of about gamma * (q_mul * <q, u> + beta) * scale, far above the others when gamma and beta are
+    large: a query that sees one after other keys must move its running maximum.  Input
+    construction only (scaling and replacing rows of the drawn tables)."""
+
+    def __init__(self, base: ValueTable, q_mul: float = 1.0, beta: float = 0.0, gamma: float = 0.0,
+                 plant_rows=()):
+        super().__init__(base.seed, base.n_rows, base.shape)
+        self.q_mul, self.beta, self.gamma = float(q_mul), float(beta), float(gamma)
+        self.plant = np.unique(np.asarray(plant_rows, dtype=np.int64))
+        rng = np.random.default_rng(np.random.SeedSequence([base.seed, 97]))
+        u = rng.standard_normal((base.shape.hkv, base.shape.d))
+        self.u = (u / np.linalg.norm(u, axis=1, keepdims=True)).astype(np.float32)
+
+    def _gen_block(self, tag: int, b: int) -> np.ndarray:
+        a = super()._gen_block(tag, b)
+        s = self.shape
+        if tag == TAG_Q and (self.q_mul != 1.0 or self.beta != 0.0):
+            g = np.arange(s.hq) // s.group
+            a = (a.reshape(BLOCK_ROWS, s.hq, s.d) * np.float32(self.q_mul)
+                 + np.float32(self.beta) * self.u[g][None]).reshape(BLOCK_ROWS, -1)
+            a = self._round(a.astype(np.float32))
+        elif tag == TAG_K and self.plant.size:
+            rows = b * BLOCK_ROWS + np.arange(BLOCK_ROWS)
+            hit = np.isin(rows, self.plant)
+            if hit.any():
+                a = a.copy()
+                a[hit] = self._round((np.float32(self.gamma) * self.u).reshape(1, -1))
+        return a
+
+
 @dataclasses.dataclass
 class Workload:
     name: str
