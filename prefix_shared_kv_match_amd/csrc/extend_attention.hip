@@ -36,6 +36,7 @@
 
 #include <algorithm>
 #include <new>
+#include <type_traits>
 
 #include "device.h"
 
@@ -172,6 +173,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t table_rsrc(const void* p, int 
 constexpr float kRescaleSlack = 8.f;
 
 // One wave's 32 query rows (two 16-row MFMA blocks nb) and their online-softmax state.
+//
+// S^T comes out of the products exactly (bf16 x bf16 products, float32 sums); the softmax
+// scale (log2 units, times the K scale for fp8 pools) and the reference max are applied in
+// float32 by one fused multiply-add per value before the exponential, so no logit carries a
+// rounding of a scaled operand.  Row sums come from one more MFMA per 32 tokens against a row
+// of ones (the same bf16 P values the PV product uses): the matrix cores have room where the
+// vector ALU has none.
+// A tile is processed in two halves that the tile loop places in different iterations:
+//   probs(S) -> P (exponentials, conversions, row sums), then qk(next tile) into the same S
+//   registers block by block (each block's products start once its exponentials are done),
+//   pv(P) (MFMA) beside later_max(next S) (vector max, rarely a rescale),
+// so each wave always has independent vector and matrix work to interleave.
 template <int G>
 struct WaveAttn {
   static constexpr int BT = kRows / G;   // query tokens per work item
@@ -183,8 +196,25 @@ struct WaveAttn {
   floatx4 lsum[2];       // (ones row) . P^T: element 0 of lanes 0..15 holds the row sum
   float m[2];            // reference max (log2 units)
   float sc;              // softmax scale in log2 units (times the K scale for fp8 pools)
-  int qpos0;             // position of the item's first query token
   bf16x8 ones_row;
+  int qpos0;             // earliest visible position of any row of the wave
+
+  __device__ __forceinline__ void load_q(const bf16* qp, bool ok, int nb) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const u32x4 v = ok ? *(const u32x4*)(qp + 32 * ks) : u32x4{0u, 0u, 0u, 0u};
+      qf[nb][ks] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+
+  __device__ __forceinline__ void reset(int nb) {
+    lsum[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int db = 0; db < 8; ++db) oacc[nb][db] = floatx4{0.f, 0.f, 0.f, 0.f};
+    m[nb] = 0.f;
+    const bf16 one = (bf16)(ln == 0 ? 1.f : 0.f);
+    ones_row = bf16x8{one, one, one, one, one, one, one, one};
+  }
 
   __device__ __forceinline__ void init(const bf16* q, int64_t qrow0, int hq, int g, int wave, int lane, int nq,
                                        int p, int j0, int ctx, float scale) {
@@ -199,28 +229,19 @@ struct WaveAttn {
       qt[nb] = r0 % BT + ln;
       vis[nb] = min(qpos0 + qt[nb], ctx - 1);   // padded rows see the whole context
       const bool ok = qt[nb] < nq;
-      const bf16* qp = q + ((qrow0 + (ok ? qt[nb] : 0)) * hq + qh[nb]) * kD + 8 * lg;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const u32x4 v = ok ? *(const u32x4*)(qp + 32 * ks) : u32x4{0u, 0u, 0u, 0u};
-        qf[nb][ks] = __builtin_bit_cast(bf16x8, v);
-      }
-      lsum[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int db = 0; db < 8; ++db) oacc[nb][db] = floatx4{0.f, 0.f, 0.f, 0.f};
-      m[nb] = -INFINITY;
+      load_q(q + ((qrow0 + (ok ? qt[nb] : 0)) * hq + qh[nb]) * kD + 8 * lg, ok, nb);
+      reset(nb);
     }
-    const bf16 one = (bf16)(ln == 0 ? 1.f : 0.f);
-    ones_row = bf16x8{one, one, one, one, one, one, one, one};
   }
 
   // Rows of a decode item instead of extend rows: row r of the workgroup is the newest token
   // of sequence members[m0 + r % BT] at head g * G + r / BT (nm real members), which sees
-  // positions 0 .. seq_lens[b] - 1.  A shared item's chunks lie inside every member's context,
-  // so its tiles never reach the mask; a one-member item over a sequence's own last chunk
-  // masks the positions past its newest token.
+  // positions 0 .. seq_lens[b] - 1 (and none at or past kv_end, the end of the item's chunks).
+  // A shared item's chunks lie inside every member's context, so its tiles never reach the mask;
+  // a one-member item over a sequence's own last chunk masks the positions past its newest token.
   __device__ __forceinline__ void init_shared(const bf16* q, const int32_t* members, const int32_t* seq_lens, int m0,
-                                              int nm, int batch, int hq, int g, int wave, int lane, float scale) {
+                                              int nm, int batch, int hq, int g, int wave, int lane, float scale,
+                                              int kv_end) {
     ln = lane & 15;
     lg = lane >> 4;
     sc = scale;
@@ -229,78 +250,63 @@ struct WaveAttn {
       const int r0 = 32 * wave + 16 * nb;
       qh[nb] = g * G + r0 / BT;
       qt[nb] = r0 % BT + ln;
-      vis[nb] = 0x3FFFFFFF;   // padding rows see everything
+      vis[nb] = kv_end - 1;   // padding rows see the whole item
       int b = qt[nb] < nm ? members[m0 + qt[nb]] : -1;
       const bool ok = b >= 0 && b < batch;   // a member index outside the batch is a padding row
       if (!ok) {
         b = 0;
         qt[nb] = BT;   // never stored
       } else {
-        vis[nb] = seq_lens[b] - 1;
+        vis[nb] = min(seq_lens[b], kv_end) - 1;
       }
-      const bf16* qp = q + ((int64_t)b * hq + qh[nb]) * kD + 8 * lg;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const u32x4 v = ok ? *(const u32x4*)(qp + 32 * ks) : u32x4{0u, 0u, 0u, 0u};
-        qf[nb][ks] = __builtin_bit_cast(bf16x8, v);
-      }
-      lsum[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int db = 0; db < 8; ++db) oacc[nb][db] = floatx4{0.f, 0.f, 0.f, 0.f};
-      m[nb] = -INFINITY;
+      load_q(q + ((int64_t)b * hq + qh[nb]) * kD + 8 * lg, ok, nb);
+      reset(nb);
     }
     // the wave's earliest newest-token position: tiles ending at or before it need no mask
     int v = min(vis[0], vis[1]);
 #pragma unroll
     for (int off = 32; off >= 1; off /= 2) v = min(v, __shfl_xor(v, off));
     qpos0 = v;
-    const bf16 one = (bf16)(ln == 0 ? 1.f : 0.f);
-    ones_row = bf16x8{one, one, one, one, one, one, one, one};
   }
 
-  // One 64-token tile at kv position kv0.  kop(mb, ks) returns the K operand (tokens of S^T
-  // block mb, d = 32 ks + 8 lg .. +7), vop(kk, db) the V^T operand (d = 16 db + ln, tokens
-  // 32 kk + 8 lg .. +7), both read from LDS.
-  template <class KOp, class VOp>
-  __device__ __forceinline__ void tile(int kv0, KOp kop, VOp vop) {
-    // S^T = K . Q^T
-    floatx4 s[4][2];
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) s[mb][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+  // S^T = K . Q^T for one 64-token tile; kop(mb, ks) returns the K operand (tokens of S^T
+  // block mb, d = 32 ks + 8 lg .. +7) read from LDS
+  template <class KOp>
+  __device__ __forceinline__ void qk(floatx4 (&s)[4][2], KOp kop) const {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
         const bf16x8 a = kop(mb, ks);
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) s[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[nb][ks], s[mb][nb], 0, 0, 0);
+        for (int nb = 0; nb < 2; ++nb)
+          s[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[nb][ks], ks == 0 ? floatx4{0.f, 0.f, 0.f, 0.f}
+                                                                                      : s[mb][nb], 0, 0, 0);
       }
     }
+  }
 
-    // causal / context mask, only on tiles reaching past the first query position
-    if (kv0 + kBN > qpos0 + 1) {
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const int lim = vis[nb] - kv0 - 8 * lg;   // visible iff token offset - 8 lg <= lim
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int off = 32 * (mb >> 1) + 4 * (mb & 1) + i;
-            s[mb][nb][i] = off <= lim ? s[mb][nb][i] : -INFINITY;
-          }
-      }
-    }
-
-    // online softmax (log2 domain) with lazy rescaling.  Each lane's max over its 16 logits
-    // of a row; the row max across the 4 lanes that share the query row is only formed when
-    // some lane may move the reference max (one wave-uniform test for both row blocks).
-    float mt[2];
+  // causal / context mask of the tile at kv0 (branch-free; callers use it on the tiles that
+  // reach past the earliest visible position)
+  __device__ __forceinline__ void mask(floatx4 (&s)[4][2], int kv0) const {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      // a linear chain, so each step is one three-input max
+      const int lim = vis[nb] - kv0 - 8 * lg;   // visible iff token offset - 8 lg <= lim
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int off = 32 * (mb >> 1) + 4 * (mb & 1) + i;
+          s[mb][nb][i] = off <= lim ? s[mb][nb][i] : -INFINITY;
+        }
+    }
+  }
+
+  // this lane's max over its 16 raw values of each row, in log2 units relative to the
+  // reference max (a linear chain of three-input maxes, then one fused multiply-add)
+  __device__ __forceinline__ void lane_max(const floatx4 (&s)[4][2], float (&mt)[2]) const {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
       float x = fmaxf(fmaxf(s[0][nb][0], s[0][nb][1]), s[0][nb][2]);
       x = fmaxf(fmaxf(x, s[0][nb][3]), s[1][nb][0]);
       x = fmaxf(fmaxf(x, s[1][nb][1]), s[1][nb][2]);
@@ -308,23 +314,51 @@ struct WaveAttn {
       x = fmaxf(fmaxf(x, s[2][nb][1]), s[2][nb][2]);
       x = fmaxf(fmaxf(x, s[2][nb][3]), s[3][nb][0]);
       x = fmaxf(fmaxf(x, s[3][nb][1]), s[3][nb][2]);
-      x = fmaxf(x, s[3][nb][3]);
-      mt[nb] = x * sc;
+      mt[nb] = fmaf(fmaxf(x, s[3][nb][3]), sc, -m[nb]);
     }
-    if (__any(mt[0] > m[0] + kRescaleSlack || mt[1] > m[1] + kRescaleSlack)) {   // rare after the first tile
+  }
+
+  // the row max across the four lanes that hold a query row (lanes ln, ln+16, ln+32, ln+48)
+  static __device__ __forceinline__ float row_max(float x) {
+    x = fmaxf(x, __shfl_xor(x, 16));
+    return fmaxf(x, __shfl_xor(x, 32));
+  }
+
+  // move the reference max of each row up by d (log2 units, >= 0): the output and the row
+  // sums follow
+  __device__ __forceinline__ void shift(int nb, float d) {
+    const float alpha = __builtin_amdgcn_exp2f(-d);   // 1 for rows that keep their max
+    lsum[nb] *= alpha;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) oacc[nb][db] *= alpha;
+    m[nb] += d;
+  }
+
+  // first tile (reference 0, nothing accumulated yet): the reference max becomes the row max
+  __device__ __forceinline__ void first_max(const floatx4 (&s)[4][2]) {
+    float mt[2];
+    lane_max(s, mt);
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) m[nb] = row_max(mt[nb]);
+  }
+
+  // later tiles: only where some lane's value exceeds the reference by more than the slack
+  // (one wave-uniform test, rare after the first tile) is the row max formed and the row moved
+  __device__ __forceinline__ void later_max(const floatx4 (&s)[4][2]) {
+    float mt[2];
+    lane_max(s, mt);
+    if (__any(mt[0] > kRescaleSlack || mt[1] > kRescaleSlack)) {
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
-        float x = fmaxf(mt[nb], __shfl_xor(mt[nb], 16));
-        x = fmaxf(x, __shfl_xor(x, 32));
-        const float mn = x > m[nb] + kRescaleSlack ? x : m[nb];
-        const float alpha = __builtin_amdgcn_exp2f(m[nb] - mn);   // 1 for rows that keep their max
-        lsum[nb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < 8; ++db) oacc[nb][db] *= alpha;
-        m[nb] = mn;
+        const float x = row_max(mt[nb]);
+        shift(nb, x > kRescaleSlack ? x : 0.f);
       }
     }
-    bf16x8 pf[2][2];
+  }
+
+  // P = 2^(sc S^T - m) as the bf16 B operand of the PV product (each lane's 8 values of a
+  // block pair are 8 consecutive kv tokens)
+  __device__ __forceinline__ void probs(const floatx4 (&s)[4][2], bf16x8 (&pf)[2][2]) const {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       const float nm = -m[nb];
@@ -339,10 +373,13 @@ struct WaveAttn {
         pf[nb][kk] = pv;
       }
     }
+  }
 
-    // O^T += V^T . P^T, and the row sums.  The wave issues them at raised priority: on a SIMD
-    // shared with a wave in its softmax, the products go first and the other wave's vector
-    // work fills the cycles between them.
+  // O^T += V^T . P^T, and the row sums; vop(kk, db) returns the V^T operand (d = 16 db + ln,
+  // tokens 32 kk + 8 lg .. +7) read from LDS.  Issued at raised wave priority: on a SIMD
+  // shared with a wave in its vector work, the products go first.
+  template <class VOp>
+  __device__ __forceinline__ void pv(const bf16x8 (&pf)[2][2], VOp vop) {
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
@@ -360,6 +397,9 @@ struct WaveAttn {
     __builtin_amdgcn_s_setprio(0);
   }
 
+  // the row sum sits in element 0 of lane ln (row 0 of the ones product)
+  __device__ __forceinline__ float row_sum(int nb) const { return __shfl(lsum[nb][0], ln); }
+
   // Split partials of a shared-prefix decode item, in the split phase's layout: for member b
   // and head h, partial p = (b * hq + h) * max_splits + s holds (reference max, row sum) at
   // ws_ml[2p], ws_ml[2p + 1] and the unnormalised output row (times omul) at ws_acc[p * d].
@@ -369,7 +409,7 @@ struct WaveAttn {
                                                 int hq, int max_splits, int s, int span, float omul) const {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      const float lt = __shfl(lsum[nb][0], ln);   // row sum sits in lane ln (row 0 of the block)
+      const float lt = row_sum(nb);
       if (qt[nb] >= nm) continue;
       const int64_t part = ((int64_t)members[m0 + qt[nb]] * hq + qh[nb]) * max_splits + s;
       float* ap = ws_acc + part * kD + 4 * lg;
@@ -384,7 +424,7 @@ struct WaveAttn {
   __device__ __forceinline__ void store(bf16* o, int64_t qrow0, int hq, int nq, float omul) const {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      const float lt = __shfl(lsum[nb][0], ln);   // row sum sits in lane ln (row 0 of the block)
+      const float lt = row_sum(nb);
       if (qt[nb] >= nq) continue;
       const float inv = omul / lt;
       bf16* op = o + ((qrow0 + qt[nb]) * hq + qh[nb]) * kD + 4 * lg;
@@ -397,6 +437,62 @@ struct WaveAttn {
     }
   }
 };
+
+// The tile loop shared by every MFMA kernel.  Tile t's K is consumed one iteration before its
+// V: iteration t runs the exponentials of tile t beside the S^T products of tile t + 1, then
+// tile t's PV products beside tile t + 1's max.  K and V tiles are double-buffered in LDS
+// (K(t) in kbuf[t & 1], V(t) in vbuf[t & 1]); iteration t stages K(t + 2) into kbuf[t & 1] and
+// V(t + 1) into vbuf[(t + 1) & 1], whose readers (tile t's products, tile t - 1's PV) all
+// passed the barrier that ends iteration t - 1, and ends with its own barrier.  The loop runs
+// the tiles that need no mask two per trip with the buffers and S^T arrays fixed by the
+// unrolling (so the compiler can tell the buffers apart), then the rest with the mask; the
+// step after the last tile multiplies a tile past the context that the mask hides entirely.
+// Stage must provide:
+//   prologue()         tiles K(0), V(0), K(1) staged and visible, then nothing in flight
+//   issue(t, kd, vd)   start staging K(t + 2) into kd and V(t + 1) into vd
+//   finish()           this thread's staging of iteration t complete (before the barrier)
+// kop(buf, mb, ks) / vop(buf, kk, db) read operands from a K / V buffer.
+template <int G, class Stage, class KOp, class VOp>
+__device__ __forceinline__ void tile_loop(WaveAttn<G>& wa, Stage& st, int kv_begin, int n_tiles, int n_plain,
+                                          bool active, char* k0, char* k1, char* v0, char* v1, KOp kop, VOp vop) {
+  floatx4 s[4][2];   // S^T of the tile being exponentiated, then of the next one
+  bf16x8 pf[2][2];
+  st.prologue();
+  __syncthreads();
+  if (active) {
+    wa.qk(s, [&](int mb, int ks) { return kop(k0, mb, ks); });
+    wa.mask(s, kv_begin);
+    wa.first_max(s);
+  }
+  __syncthreads();   // K(0)'s buffer takes K(2) next
+  auto step = [&](auto mask_next, int t, const char* kr, const char* vr, char* kd, char* vd) {
+    st.issue(t, kd, vd);
+    if (active) {   // wave-uniform; with one head per item a wave of only padding tokens just stages
+      wa.probs(s, pf);
+      wa.qk(s, [&](int mb, int ks) { return kop(kr, mb, ks); });
+      __builtin_amdgcn_sched_barrier(0);   // keep the PV operand reads out of the S^T half
+      wa.pv(pf, [&](int kk, int db) { return vop(vr, kk, db); });
+      if constexpr (decltype(mask_next)::value) wa.mask(s, kv_begin + (t + 1) * kBN);
+      wa.later_max(s);
+    }
+    st.finish();
+    __syncthreads();
+  };
+  using Plain = std::integral_constant<bool, false>;
+  using Masked = std::integral_constant<bool, true>;
+  int t = 0;
+  // iteration t needs no mask when tile t + 1 is an unmasked tile
+  for (; t + 2 < n_plain; t += 2) {
+    step(Plain{}, t, k1, v0, k0, v1);
+    step(Plain{}, t + 1, k0, v1, k1, v0);
+  }
+  // t is even here: the rest two per trip too, then possibly one more
+  for (; t + 1 < n_tiles; t += 2) {
+    step(Masked{}, t, k1, v0, k0, v1);
+    step(Masked{}, t + 1, k0, v1, k1, v0);
+  }
+  if (t < n_tiles) step(Masked{}, t, k1, v0, k0, v1);
+}
 
 // ------------------------------------------------------------------------------------------
 // bf16 pools: tiles staged by global-to-LDS loads
@@ -438,9 +534,9 @@ __device__ __forceinline__ bf16x8 lds_read_tr2(const char* p0, const char* p1) {
 }
 
 // Gathers of one tile's rows into LDS (16 bytes per lane, one 4-row block per load).  NARROW:
-// the pool is read as a structured buffer (record = slot, so a gathered row costs no address
-// arithmetic and a slot past the pool reads zero); its 32-bit offsets reach 2 GiB of pool.
-// Otherwise 64-bit addresses (slot * slot bytes), a slot past the pool clamped to the last.
+// the pool is read as a raw buffer whose range check covers it (offset slot * slot bytes +
+// column, one multiply-add per row; a slot past the pool reads zero); its 32-bit offsets
+// reach 2 GiB of pool.  Otherwise 64-bit addresses, a slot past the pool clamped to the last.
 template <bool NARROW>
 struct PoolGather {
   const uint8_t *kcol, *vcol;   // pool + this lane's byte column
@@ -451,23 +547,108 @@ struct PoolGather {
       : kcol(kpool + col_), vcol(vpool + col_), slot_bytes((uint32_t)(hkv * 2 * kD)),
         max_slot((uint32_t)(num_slots - 1)), col(col_) {
     if constexpr (NARROW) {
-      kp = __builtin_amdgcn_make_buffer_rsrc((void*)kpool, (short)(hkv * 2 * kD), num_slots, kBufWord3);
-      vp = __builtin_amdgcn_make_buffer_rsrc((void*)vpool, (short)(hkv * 2 * kD), num_slots, kBufWord3);
+      const int bytes = (int)((int64_t)num_slots * hkv * 2 * kD);
+      kp = __builtin_amdgcn_make_buffer_rsrc((void*)kpool, (short)0, bytes, kBufWord3);
+      vp = __builtin_amdgcn_make_buffer_rsrc((void*)vpool, (short)0, bytes, kBufWord3);
     }
   }
-  __device__ __forceinline__ void operator()(uint32_t slot, char* kd, char* vd) const {
-    if constexpr (NARROW) {
-      __builtin_amdgcn_struct_ptr_buffer_load_lds(kp, (lds_void*)kd, 16, (int)slot, col, 0, 0, 0);
-      __builtin_amdgcn_struct_ptr_buffer_load_lds(vp, (lds_void*)vd, 16, (int)slot, col, 0, 0, 0);
-    } else {
-      const uint64_t off = (uint64_t)min(slot, max_slot) * slot_bytes;
-      __builtin_amdgcn_global_load_lds((glob_void*)(kcol + off), (lds_void*)kd, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((glob_void*)(vcol + off), (lds_void*)vd, 16, 0, 0);
-    }
+  __device__ __forceinline__ void k(uint32_t slot, char* d) const {
+    if constexpr (NARROW)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kp, (lds_void*)d, 16, (int)(slot * slot_bytes + col), 0, 0, 0);
+    else
+      __builtin_amdgcn_global_load_lds((glob_void*)(kcol + (uint64_t)min(slot, max_slot) * slot_bytes), (lds_void*)d,
+                                       16, 0, 0);
+  }
+  __device__ __forceinline__ void v(uint32_t slot, char* d) const {
+    if constexpr (NARROW)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vp, (lds_void*)d, 16, (int)(slot * slot_bytes + col), 0, 0, 0);
+    else
+      __builtin_amdgcn_global_load_lds((glob_void*)(vcol + (uint64_t)min(slot, max_slot) * slot_bytes), (lds_void*)d,
+                                       16, 0, 0);
   }
 };
 // pools up to this size are gathered through buffer offsets
 constexpr int64_t kNarrowPoolBytes = (int64_t)1 << 31;
+
+// Staging of a bf16 pool's tiles by global-to-LDS loads.  Wave w fills blocks 4w + i
+// (i = 0..3) of a tile; lane l writes row l / 16 (token kv_tok(4w + i, l / 16)), byte column
+// 16 (l % 16) of kv head g.  Those tokens are t, t + 16, t + 1, t + 17 for i = 0..3: two
+// 8-byte slot-table reads per tile.  The slot table is read one tile ahead of the rows it
+// addresses (each tile's slots serve its K at one iteration and its V at the next).  Tiles at
+// or past the last one are staged as the last one (into buffers nobody reads after).
+template <bool NARROW>
+struct DmaStage {
+  const PoolGather<NARROW>& gather;
+  __amdgpu_buffer_rsrc_t tab;
+  int row_bytes, kv_begin, last, tok0, wave;
+  char *k0, *v0, *k1;
+  u32x2 s_k[2], s_v[2];   // slots of the next K tile to stage (t + 2) and of the next V tile (t + 1)
+  __device__ __forceinline__ void slots(int tile, u32x2* sl) const {
+    // the whole byte offset goes in the vector offset, which the buffer's range check covers
+    const int kv0 = kv_begin + min(tile, last) * kBN;
+    sl[0] = buf_load_raw_x2(tab, row_bytes + 4 * (kv0 + tok0), 0, 0);
+    sl[1] = buf_load_raw_x2(tab, row_bytes + 4 * (kv0 + tok0 + 16), 0, 0);
+  }
+  __device__ __forceinline__ void stage_k(char* d, const u32x2* sl) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) gather.k(sl[i & 1][i >> 1], d + kBlk * (4 * wave + i));
+  }
+  __device__ __forceinline__ void stage_v(char* d, const u32x2* sl) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) gather.v(sl[i & 1][i >> 1], d + kBlk * (4 * wave + i));
+  }
+  __device__ __forceinline__ void prologue() {
+    slots(0, s_v);
+    slots(1, s_k);
+    stage_k(k0, s_v);
+    stage_v(v0, s_v);
+    stage_k(k1, s_k);
+    s_v[0] = s_k[0];
+    s_v[1] = s_k[1];
+    slots(2, s_k);
+    // this wave's global-to-LDS loads are complete (vmcnt(0): the table loads issued after
+    // them are waited for too); then the caller's barrier publishes the tiles
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+  }
+  // iteration t: K(t + 2) with the slots read one iteration ago, V(t + 1) with those of K(t + 1);
+  // then the slots of K(t + 3), which finish() waits for
+  __device__ __forceinline__ void issue(int t, char* kd, char* vd) {
+    stage_k(kd, s_k);
+    stage_v(vd, s_v);
+    s_v[0] = s_k[0];
+    s_v[1] = s_k[1];
+    slots(t + 3, s_k);
+  }
+  __device__ __forceinline__ void finish() const { __builtin_amdgcn_s_waitcnt(0x0F70); }
+};
+
+// K operand of S^T block mb at chunk ks, and the V^T operand of (kk, db), from a DMA-staged
+// tile at per-lane bases: K row sigma(mb, ln) at chunk lg (+ 4 ks); V rows 32 kk + 8 lg + 4 h +
+// ln / 4 at d = 4 (ln % 4) (+ 16 db)
+struct DmaOperands {
+  int kb[4], vb[2][2];
+  __device__ __forceinline__ DmaOperands(int ln, int lg) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) kb[mb] = kv_off(sigma(mb, ln)) + 16 * lg;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) vb[kk][h] = kv_off(32 * kk + 8 * lg + 4 * h + (ln >> 2)) + 8 * (ln & 3);
+  }
+  __device__ __forceinline__ bf16x8 k(const char* K, int mb, int ks) const {
+    return *(const bf16x8*)(K + kb[mb] + 64 * ks);
+  }
+  __device__ __forceinline__ bf16x8 v(const char* V, int kk, int db) const {
+    return lds_read_tr2(V + vb[kk][0] + 32 * db, V + vb[kk][1] + 32 * db);
+  }
+};
+
+// tiles of an item before the first one that reaches past position `first_visible` (they
+// need no mask)
+__device__ __forceinline__ int plain_tiles(int kv_begin, int first_visible, int n_tiles) {
+  const int n = (first_visible + 1 - kv_begin) / kBN;   // tiles ending at or before first_visible + 1
+  return max(0, min(n, n_tiles));
+}
 
 template <int G, bool NARROW>
 __global__ __launch_bounds__(256, 2) void extend_dma(const bf16* __restrict__ q, bf16* __restrict__ o,
@@ -494,69 +675,21 @@ __global__ __launch_bounds__(256, 2) void extend_dma(const bf16* __restrict__ q,
   const int ctx = p + j0 + nq;
   const int hq = hkv * G;
   const int64_t qrow0 = (int64_t)qo_indptr[req] + j0;
-  const __amdgpu_buffer_rsrc_t tab = table_rsrc(r2t, table_bytes);
-  const int row_bytes = (int)((int64_t)req * stride * 4);
 
-  // staging: wave w fills blocks 4w + i (i = 0..3) of the K and V tiles; lane l writes row
-  // l / 16 (token kv_tok(4w + i, l / 16)), byte column 16 (l % 16) of kv head g.  Those tokens
-  // are t, t + 16, t + 1, t + 17 for i = 0..3: two 8-byte table reads.
-  const int tok0 = kv_tok(4 * wave, lg);
-  const int col = g * kD * 2 + 16 * ln;
-  auto slots = [&](int kv0, u32x2* sl) {
-    // the whole byte offset goes in the vector offset, which the buffer's range check covers
-    sl[0] = buf_load_raw_x2(tab, row_bytes + 4 * (kv0 + tok0), 0, 0);
-    sl[1] = buf_load_raw_x2(tab, row_bytes + 4 * (kv0 + tok0 + 16), 0, 0);
-  };
-  const PoolGather<NARROW> gather(kpool, vpool, hkv, num_slots, col);
-  auto stage = [&](char* kd, char* vd, const u32x2* sl) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) gather(sl[i & 1][i >> 1], kd + kBlk * (4 * wave + i), vd + kBlk * (4 * wave + i));
-  };
+  const PoolGather<NARROW> gather(kpool, vpool, hkv, num_slots, g * kD * 2 + 16 * ln);
+  const int n_tiles = (ctx + kBN - 1) / kBN;
+  DmaStage<NARROW> st{gather, table_rsrc(r2t, table_bytes), (int)((int64_t)req * stride * 4), 0, n_tiles - 1,
+                      kv_tok(4 * wave, lg), wave, k0s, v0s, k1s};
 
   WaveAttn<G> wa;
   wa.init(q, qrow0, hq, g, wave, lane, nq, p, j0, ctx, scale_log2);
   // only for G = 1 (a wave's rows are 32 consecutive tokens): is any of them a real query?
   const bool active = G != 1 || 32 * wave < nq;
-  // operand read bases (bytes within a tile): K row sigma(mb, ln) at chunk lg (+ 4 ks);
-  // V rows 32 kk + 8 lg + 4 h + ln / 4 at d = 4 (ln % 4) (+ 16 db)
-  int kb[4], vb[2][2];
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb) kb[mb] = kv_off(sigma(mb, ln)) + 16 * lg;
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-    for (int h = 0; h < 2; ++h) vb[kk][h] = kv_off(32 * kk + 8 * lg + 4 * h + (ln >> 2)) + 8 * (ln & 3);
-
-  const int n_tiles = (ctx + kBN - 1) / kBN;
-  const int last = n_tiles - 1;
-  u32x2 sl[2];
-  slots(0, sl);
-  stage(k0s, v0s, sl);
-  slots(min(1, last) * kBN, sl);
-  // this wave's global-to-LDS loads are complete (vmcnt(0): the table loads issued after them
-  // are waited for too); then the barrier publishes the tile to the other waves
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-  __syncthreads();
-  // iteration kt computes tile kt from (K, V) and loads tile kt + 1 into (Kn, Vn), whose
-  // readers (tile kt - 1) all passed the previous barrier
-  auto step = [&](int kt, const char* K, const char* V, char* Kn, char* Vn) {
-    // past the last tile the last one is loaded again into a buffer nobody reads
-    stage(Kn, Vn, sl);
-    slots(min(kt + 2, last) * kBN, sl);
-    if (active)   // wave-uniform; with one head per item a wave of only padding tokens just stages
-      wa.tile(
-          kt * kBN, [&](int mb, int ks) { return *(const bf16x8*)(K + kb[mb] + 64 * ks); },
-          [&](int kk, int db) { return lds_read_tr2(V + vb[kk][0] + 32 * db, V + vb[kk][1] + 32 * db); });
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // this wave's loads of tile kt + 1 are in LDS
-    __syncthreads();
-  };
-  int kt = 0;
-  for (; kt + 1 < n_tiles; kt += 2) {
-    step(kt, k0s, v0s, k1s, v1s);
-    step(kt + 1, k1s, v1s, k0s, v0s);
-  }
-  if (kt < n_tiles) step(kt, k0s, v0s, k1s, v1s);
-
+  const DmaOperands ops(ln, lg);
+  // the item's first query token is the earliest visible position of every wave
+  tile_loop<G>(wa, st, 0, n_tiles, plain_tiles(0, p + j0, n_tiles), active, k0s, k1s, v0s, v1s,
+               [&](const char* K, int mb, int ks) { return ops.k(K, mb, ks); },
+               [&](const char* V, int kk, int db) { return ops.v(V, kk, db); });
   wa.store(o, qrow0, hq, nq, 1.f);
 }
 
@@ -566,6 +699,8 @@ __global__ __launch_bounds__(256, 2) void extend_dma(const bf16* __restrict__ q,
 
 constexpr int kKStride = kD + 8;        // bf16 elements per K row in LDS (272 B)
 constexpr int kVStride = kBN + 8;       // bf16 elements per V^T row in LDS (144 B)
+constexpr int kFp8KBytes = kBN * kKStride * 2;
+constexpr int kFp8VBytes = kD * kVStride * 2;
 
 // LDS row of kv token t in the K tile.  With a 272 B row stride a row starts at bank 4*row
 // (mod 64), and one MFMA block reads tokens {0-3, 8-11, 16-19, 24-27} (+4, +32): flipping
@@ -573,71 +708,112 @@ constexpr int kVStride = kBN + 8;       // bf16 elements per V^T row in LDS (144
 // 16 different banks.
 __device__ __forceinline__ int krow(int t) { return t ^ (((t >> 4) & 1) << 2); }
 
-// two E4M3 codes (low 16 bits) -> two bf16 (exact: every E4M3 value is a bf16 value)
-__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t codes2) {
-  const float2 f = e4m3x2_to_f32<false>(codes2);
-  return __builtin_amdgcn_perm(__float_as_uint(f.y), __float_as_uint(f.x), 0x07060302u);
-}
-__device__ __forceinline__ u32x4 dec4(u32x2 c) {
-  return u32x4{e4m3x2_to_bf16x2(c[0]), e4m3x2_to_bf16x2(c[0] >> 16), e4m3x2_to_bf16x2(c[1]),
-               e4m3x2_to_bf16x2(c[1] >> 16)};
+// four E4M3 codes -> four bf16 (exact: every E4M3 value is a bf16 value), with gfx950's
+// packed conversion (scale 1)
+__device__ __forceinline__ u32x2 dec4(uint32_t c) {
+  return u32x2{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c, 1.f, false)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c, 1.f, true))};
 }
 
-// Staging of one 64-token tile of codes: global -> registers (prefetch) -> LDS.
+// Staging of an fp8 pool's tiles: global -> registers -> decoded -> LDS.
 //   K: 64 rows x 128 B = 512 chunks of 16 B, 2 per thread (rows 2*(tid/8), +1, chunk tid%8).
-//   V: thread -> 4 consecutive tokens (4*(tid%16) .. +3) x 8 d (8*(tid/16) .. +7).
-// The table entries of a thread's 2 K tokens and 4 V tokens are one 8- and one 16-byte read.
-// Tokens at or past the context read whatever slot the table holds there (or zero past the
-// table's end); they are masked later.
+//   V: thread -> 4 consecutive tokens (4*(tid%16) .. +3) x 8 d (8*(tid/16) .. +7), stored
+//      transposed (V^T [d][token]).
+// Iteration t stores K(t + 2) and V(t + 1) from the registers they were loaded into during
+// iteration t - 1, then loads K(t + 3) and V(t + 2).  The slot-table entries run one more
+// tile ahead.  Tokens at or past the context read whatever slot the table holds there (or
+// zero past the table's end), rows past the pool the last slot; they are masked later.
 struct Fp8Stage {
-  struct Slots {
-    u32x2 k;
-    u32x4 v;
-  };
-  u32x4 k0, k1;
-  u32x2 v0, v1, v2, v3;
-  static __device__ __forceinline__ Slots slots(__amdgpu_buffer_rsrc_t tab, int row_bytes, int kv0, int tid) {
-    const int tb = row_bytes + 4 * kv0;
-    return Slots{buf_load_raw_x2(tab, tb + 8 * (tid >> 3), 0, 0), buf_load_raw_x4(tab, tb + 16 * (tid & 15), 0, 0)};
+  __amdgpu_buffer_rsrc_t tab;
+  const uint8_t *kc, *vc;    // pool + this thread's byte column of kv head g
+  uint32_t slot_bytes, max_slot;
+  int row_bytes, kv_begin, last, tid;
+  char *k0, *v0, *k1;
+  u32x4 kr0, kr1;            // K codes of 2 tokens (16 B each), in flight
+  u32x2 vr[4];               // V codes of 4 tokens (8 B each), in flight
+  u32x2 sk;                  // slots of the next K tile to load
+  u32x4 sv;                  // slots of the next V tile to load
+  __device__ __forceinline__ u32x2 kslots(int tile) const {
+    return buf_load_raw_x2(tab, row_bytes + 4 * (kv_begin + min(tile, last) * kBN) + 8 * (tid >> 3), 0, 0);
   }
-  // K/V records by 64-bit address (a pool may exceed 4 GiB); a slot past the pool (an entry
-  // past the context) reads the last slot instead, masked later
-  __device__ __forceinline__ void load(const uint8_t* kpool, const uint8_t* vpool, uint32_t slot_bytes,
-                                       uint32_t max_slot, const Slots& sl, int g, int tid) {
-    const uint8_t* kc = kpool + g * kD + (tid & 7) * 16;
-    const uint8_t* vc = vpool + g * kD + (tid >> 4) * 8;
-    auto off = [&](uint32_t slot) { return (uint64_t)min(slot, max_slot) * slot_bytes; };
-    k0 = *(const u32x4*)(kc + off(sl.k[0]));
-    k1 = *(const u32x4*)(kc + off(sl.k[1]));
-    v0 = *(const u32x2*)(vc + off(sl.v[0]));
-    v1 = *(const u32x2*)(vc + off(sl.v[1]));
-    v2 = *(const u32x2*)(vc + off(sl.v[2]));
-    v3 = *(const u32x2*)(vc + off(sl.v[3]));
+  __device__ __forceinline__ u32x4 vslots(int tile) const {
+    return buf_load_raw_x4(tab, row_bytes + 4 * (kv_begin + min(tile, last) * kBN) + 16 * (tid & 15), 0, 0);
   }
-  static __device__ __forceinline__ void store_k(bf16* dst, u32x4 c) {
-    *(u32x4*)dst = dec4(u32x2{c[0], c[1]});
-    *(u32x4*)(dst + 8) = dec4(u32x2{c[2], c[3]});
+  __device__ __forceinline__ uint64_t off(uint32_t slot) const { return (uint64_t)min(slot, max_slot) * slot_bytes; }
+  __device__ __forceinline__ void load_k(u32x2 s) {
+    kr0 = *(const u32x4*)(kc + off(s[0]));
+    kr1 = *(const u32x4*)(kc + off(s[1]));
+  }
+  __device__ __forceinline__ void load_v(u32x4 s) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vr[i] = *(const u32x2*)(vc + off(s[i]));
+  }
+  static __device__ __forceinline__ void store_k16(bf16* dst, u32x4 c) {
+    const u32x2 a = dec4(c[0]), b = dec4(c[1]), d = dec4(c[2]), e = dec4(c[3]);
+    *(u32x4*)dst = u32x4{a[0], a[1], b[0], b[1]};
+    *(u32x4*)(dst + 8) = u32x4{d[0], d[1], e[0], e[1]};
+  }
+  __device__ __forceinline__ void store_k(char* Kd) const {
+    bf16* Ks = (bf16*)Kd;
+    const int r = 2 * (tid >> 3);   // tokens r, r+1
+    bf16* kd = Ks + (tid & 7) * 16;
+    store_k16(kd + krow(r) * kKStride, kr0);
+    store_k16(kd + krow(r + 1) * kKStride, kr1);
   }
   // 4 tokens x 8 d (token-major in registers) to V^T [d][token]; one byte permute builds each
   // pair of 16-bit values
-  static __device__ __forceinline__ void store_vt(bf16* Vt, int tid, u32x4 a, u32x4 b, u32x4 c, u32x4 d) {
+  __device__ __forceinline__ void store_v(char* Vd) const {
+    bf16* Vt = (bf16*)Vd;
+    u32x4 w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const u32x2 lo = dec4(vr[j][0]), hi = dec4(vr[j][1]);
+      w[j] = u32x4{lo[0], lo[1], hi[0], hi[1]};   // token j, d = d0 .. d0 + 7 as bf16 pairs
+    }
     const int d0 = 8 * (tid >> 4), t0 = 4 * (tid & 15);
     bf16* base = Vt + d0 * kVStride + t0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      // d = d0 + 2i (low halves) and d0 + 2i + 1 (high halves)
-      const u32x2 lo = {__builtin_amdgcn_perm(b[i], a[i], 0x05040100u), __builtin_amdgcn_perm(d[i], c[i], 0x05040100u)};
-      const u32x2 hi = {__builtin_amdgcn_perm(b[i], a[i], 0x07060302u), __builtin_amdgcn_perm(d[i], c[i], 0x07060302u)};
+      // d = d0 + 2i (low halves) and d0 + 2i + 1 (high halves) of tokens 0..3
+      const u32x2 lo = {__builtin_amdgcn_perm(w[1][i], w[0][i], 0x05040100u),
+                        __builtin_amdgcn_perm(w[3][i], w[2][i], 0x05040100u)};
+      const u32x2 hi = {__builtin_amdgcn_perm(w[1][i], w[0][i], 0x07060302u),
+                        __builtin_amdgcn_perm(w[3][i], w[2][i], 0x07060302u)};
       *(u32x2*)(base + (2 * i) * kVStride) = lo;
       *(u32x2*)(base + (2 * i + 1) * kVStride) = hi;
     }
   }
-  __device__ __forceinline__ void store(bf16* Ks, bf16* Vt, int tid) const {
-    const int r = 2 * (tid >> 3);   // tokens r, r+1
-    bf16* kd = Ks + (tid & 7) * 16;
-    store_k(kd + krow(r) * kKStride, k0);
-    store_k(kd + krow(r + 1) * kKStride, k1);
-    store_vt(Vt, tid, dec4(v0), dec4(v1), dec4(v2), dec4(v3));
+  __device__ __forceinline__ void prologue() {
+    // K(0), V(0), K(1) to LDS; K(2), V(1) into registers; slots of K(3), V(2) in flight
+    load_k(kslots(0));
+    load_v(vslots(0));
+    store_k(k0);
+    store_v(v0);
+    load_k(kslots(1));
+    store_k(k1);
+    load_k(kslots(2));
+    load_v(vslots(1));
+    sk = kslots(3);
+    sv = vslots(2);
+  }
+  __device__ __forceinline__ void issue(int t, char* kd, char* vd) {
+    store_k(kd);          // K(t + 2)
+    store_v(vd);          // V(t + 1)
+    load_k(sk);           // K(t + 3)
+    load_v(sv);           // V(t + 2)
+    sk = kslots(t + 4);
+    sv = vslots(t + 3);
+  }
+  __device__ __forceinline__ void finish() const {}
+};
+
+struct Fp8Operands {
+  int ln, lg;
+  __device__ __forceinline__ bf16x8 k(const char* K, int mb, int ks) const {
+    return *(const bf16x8*)((const bf16*)K + krow(sigma(mb, ln)) * kKStride + 32 * ks + 8 * lg);
+  }
+  __device__ __forceinline__ bf16x8 v(const char* V, int kk, int db) const {
+    return *(const bf16x8*)((const bf16*)V + (16 * db + ln) * kVStride + 32 * kk + 8 * lg);
   }
 };
 
@@ -653,10 +829,8 @@ __global__ __launch_bounds__(256, 2) void extend_mfma(const bf16* __restrict__ q
                                                       const int32_t* __restrict__ qo_indptr,
                                                       const int32_t* __restrict__ work, int hkv,
                                                       float scale_log2, int num_slots, int table_bytes) {
-  // two K (row-major) / V^T tile buffers: tile t is computed from buffer t & 1 while tile
-  // t + 1 is written to the other one, so one barrier per tile suffices
-  __shared__ __attribute__((aligned(16))) bf16 Ks[2][kBN * kKStride];
-  __shared__ __attribute__((aligned(16))) bf16 Vt[2][kD * kVStride];
+  // two K (row-major) / V^T tile buffers each
+  __shared__ __attribute__((aligned(16))) char k0s[kFp8KBytes], k1s[kFp8KBytes], v0s[kFp8VBytes], v1s[kFp8VBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -669,39 +843,29 @@ __global__ __launch_bounds__(256, 2) void extend_mfma(const bf16* __restrict__ q
   const int ctx = p + j0 + nq;
   const int hq = hkv * G;
   const int64_t qrow0 = (int64_t)qo_indptr[req] + j0;
-  const __amdgpu_buffer_rsrc_t tab = table_rsrc(r2t, table_bytes);
-  const uint32_t slot_bytes = (uint32_t)(hkv * kD), max_slot = (uint32_t)(num_slots - 1);
-  const int row_bytes = (int)((int64_t)req * stride * 4);
+  const int n_tiles = (ctx + kBN - 1) / kBN;
+
+  Fp8Stage st;
+  st.tab = table_rsrc(r2t, table_bytes);
+  st.kc = kpool + g * kD + (tid & 7) * 16;
+  st.vc = vpool + g * kD + (tid >> 4) * 8;
+  st.slot_bytes = (uint32_t)(hkv * kD);
+  st.max_slot = (uint32_t)(num_slots - 1);
+  st.row_bytes = (int)((int64_t)req * stride * 4);
+  st.kv_begin = 0;
+  st.last = n_tiles - 1;
+  st.tid = tid;
+  st.k0 = k0s;
+  st.v0 = v0s;
+  st.k1 = k1s;
 
   WaveAttn<G> wa;
   wa.init(q, qrow0, hq, g, wave, lane, nq, p, j0, ctx, scale_log2 * kscale[g]);
   const bool active = G != 1 || 32 * wave < nq;
-
-  Fp8Stage stage;
-  const int n_tiles = (ctx + kBN - 1) / kBN;
-  stage.load(kpool, vpool, slot_bytes, max_slot, Fp8Stage::slots(tab, row_bytes, 0, tid), g, tid);
-  stage.store(Ks[0], Vt[0], tid);
-  stage.load(kpool, vpool, slot_bytes, max_slot, Fp8Stage::slots(tab, row_bytes, min(1, n_tiles - 1) * kBN, tid), g, tid);
-  // slot-table entries run one tile ahead of the K/V records they address
-  auto nslots = Fp8Stage::slots(tab, row_bytes, min(2, n_tiles - 1) * kBN, tid);
-  __syncthreads();
-  for (int kt = 0; kt < n_tiles; ++kt) {
-    const bf16* K = Ks[kt & 1];
-    const bf16* V = Vt[kt & 1];
-    // tile kt + 1 (in registers since the last iteration) goes to the other buffer, whose
-    // readers (tile kt - 1) all passed the previous barrier; then prefetch tile kt + 2.
-    // Branch-free, so it interleaves with the S^T products: past the last tile the last tile
-    // is fetched again (from L2) and stored to a buffer nobody reads any more.
-    stage.store(Ks[(kt + 1) & 1], Vt[(kt + 1) & 1], tid);
-    stage.load(kpool, vpool, slot_bytes, max_slot, nslots, g, tid);
-    nslots = Fp8Stage::slots(tab, row_bytes, min(kt + 3, n_tiles - 1) * kBN, tid);
-    if (active)
-      wa.tile(
-          kt * kBN,
-          [&](int mb, int ks) { return *(const bf16x8*)(K + krow(sigma(mb, ln)) * kKStride + 32 * ks + 8 * lg); },
-          [&](int kk, int db) { return *(const bf16x8*)(V + (16 * db + ln) * kVStride + 32 * kk + 8 * lg); });
-    __syncthreads();
-  }
+  const Fp8Operands ops{ln, lg};
+  tile_loop<G>(wa, st, 0, n_tiles, plain_tiles(0, p + j0, n_tiles), active, k0s, k1s, v0s, v1s,
+               [&](const char* K, int mb, int ks) { return ops.k(K, mb, ks); },
+               [&](const char* V, int kk, int db) { return ops.v(V, kk, db); });
   wa.store(o, qrow0, hq, nq, vscale[g]);
 }
 
@@ -718,7 +882,26 @@ __global__ __launch_bounds__(256, 2) void extend_mfma(const bf16* __restrict__ q
 // per (item, kv head), blockIdx.x = item * hkv + g, reads chunks s .. s + span - 1 (their
 // slots from the first member's row).  The output is the split phase's partial at chunk s of
 // every member (chunks s + 1 .. marked empty), which the reduce then merges with the other
-// chunks.  Same tile pipeline as extend_dma / extend_mfma.
+// chunks.  Same tile loop as extend_dma / extend_mfma.
+
+// the item's earliest newest-token position over all its members (the same in every wave):
+// tiles ending before it need no mask
+__device__ __forceinline__ int item_first_visible(const int32_t* members, const int32_t* seq_lens, int m0, int nm,
+                                                  int batch, int kv_end, int lane) {
+  int v = kv_end - 1;
+  for (int i = lane; i < nm; i += 64) {
+    const int b = members[m0 + i];
+    if (b >= 0 && b < batch) v = min(v, seq_lens[b] - 1);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off /= 2) v = min(v, __shfl_xor(v, off));
+  return v;
+}
+
+// an item outside the batch or the workspace is ignored (the whole workgroup leaves)
+__device__ __forceinline__ bool bad_item(int m0, int nm, int rows, int batch, int s, int span, int max_splits) {
+  return m0 < 0 || nm <= 0 || nm > rows || m0 > batch - nm || s < 0 || span <= 0 || s > max_splits - span;
+}
 
 template <int G, bool NARROW>
 __global__ __launch_bounds__(256, 2) void decode_shared_dma(const bf16* __restrict__ q,
@@ -739,62 +922,23 @@ __global__ __launch_bounds__(256, 2) void decode_shared_dma(const bf16* __restri
   const int g = blockIdx.x % hkv;
   const int it = blockIdx.x / hkv;
   const int m0 = items[4 * it], nm = items[4 * it + 1], s = items[4 * it + 2], span = items[4 * it + 3];
-  // an item outside the batch or the workspace is ignored (the whole workgroup leaves)
-  if (m0 < 0 || nm <= 0 || nm > WaveAttn<G>::BT || m0 > batch - nm || s < 0 || span <= 0 || s > max_splits - span)
-    return;
+  if (bad_item(m0, nm, WaveAttn<G>::BT, batch, s, span, max_splits)) return;
   const int hq = hkv * G;
-  const __amdgpu_buffer_rsrc_t tab = table_rsrc(r2t, table_bytes);
-  const int row_bytes = (int)((int64_t)members[m0] * stride * 4);
   const int kv_begin = s * chunk;
+  const int n_tiles = span * chunk / kBN;
 
-  const int tok0 = kv_tok(4 * wave, lg);
-  const int col = g * kD * 2 + 16 * ln;
-  auto slots = [&](int kv0, u32x2* sl) {
-    sl[0] = buf_load_raw_x2(tab, row_bytes + 4 * (kv0 + tok0), 0, 0);
-    sl[1] = buf_load_raw_x2(tab, row_bytes + 4 * (kv0 + tok0 + 16), 0, 0);
-  };
-  const PoolGather<NARROW> gather(kpool, vpool, hkv, num_slots, col);
-  auto stage = [&](char* kd, char* vd, const u32x2* sl) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) gather(sl[i & 1][i >> 1], kd + kBlk * (4 * wave + i), vd + kBlk * (4 * wave + i));
-  };
+  const PoolGather<NARROW> gather(kpool, vpool, hkv, num_slots, g * kD * 2 + 16 * ln);
+  DmaStage<NARROW> st{gather, table_rsrc(r2t, table_bytes), (int)((int64_t)members[m0] * stride * 4), kv_begin,
+                      n_tiles - 1, kv_tok(4 * wave, lg), wave, k0s, v0s, k1s};
 
   WaveAttn<G> wa;
-  wa.init_shared(q, members, seq_lens, m0, nm, batch, hq, g, wave, lane, scale_log2);
+  wa.init_shared(q, members, seq_lens, m0, nm, batch, hq, g, wave, lane, scale_log2, kv_begin + n_tiles * kBN);
   const bool active = G != 1 || 32 * wave < nm;
-  int kb[4], vb[2][2];
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb) kb[mb] = kv_off(sigma(mb, ln)) + 16 * lg;
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-    for (int h = 0; h < 2; ++h) vb[kk][h] = kv_off(32 * kk + 8 * lg + 4 * h + (ln >> 2)) + 8 * (ln & 3);
-
-  const int n_tiles = span * chunk / kBN;
-  const int last = n_tiles - 1;
-  u32x2 sl[2];
-  slots(kv_begin, sl);
-  stage(k0s, v0s, sl);
-  slots(kv_begin + min(1, last) * kBN, sl);
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-  __syncthreads();
-  auto step = [&](int kt, const char* K, const char* V, char* Kn, char* Vn) {
-    stage(Kn, Vn, sl);
-    slots(kv_begin + min(kt + 2, last) * kBN, sl);
-    if (active)
-      wa.tile(
-          kv_begin + kt * kBN, [&](int mb, int ks) { return *(const bf16x8*)(K + kb[mb] + 64 * ks); },
-          [&](int kk, int db) { return lds_read_tr2(V + vb[kk][0] + 32 * db, V + vb[kk][1] + 32 * db); });
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
-  };
-  int kt = 0;
-  for (; kt + 1 < n_tiles; kt += 2) {
-    step(kt, k0s, v0s, k1s, v1s);
-    step(kt + 1, k1s, v1s, k0s, v0s);
-  }
-  if (kt < n_tiles) step(kt, k0s, v0s, k1s, v1s);
-
+  const DmaOperands ops(ln, lg);
+  const int first = item_first_visible(members, seq_lens, m0, nm, batch, kv_begin + n_tiles * kBN, lane);
+  tile_loop<G>(wa, st, kv_begin, n_tiles, plain_tiles(kv_begin, first, n_tiles), active, k0s, k1s, v0s, v1s,
+               [&](const char* K, int mb, int ks) { return ops.k(K, mb, ks); },
+               [&](const char* V, int kk, int db) { return ops.v(V, kk, db); });
   wa.store_partial(ws_ml, ws_acc, members, m0, nm, hq, max_splits, s, span, 1.f);
 }
 
@@ -811,8 +955,7 @@ __global__ __launch_bounds__(256, 2) void decode_shared_fp8(const bf16* __restri
                                                             int max_splits, int hkv, float scale_log2, int num_slots,
                                                             int table_bytes, int batch, float* __restrict__ ws_ml,
                                                             float* __restrict__ ws_acc) {
-  __shared__ __attribute__((aligned(16))) bf16 Ks[2][kBN * kKStride];
-  __shared__ __attribute__((aligned(16))) bf16 Vt[2][kD * kVStride];
+  __shared__ __attribute__((aligned(16))) char k0s[kFp8KBytes], k1s[kFp8KBytes], v0s[kFp8VBytes], v1s[kFp8VBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -820,39 +963,34 @@ __global__ __launch_bounds__(256, 2) void decode_shared_fp8(const bf16* __restri
   const int g = blockIdx.x % hkv;
   const int it = blockIdx.x / hkv;
   const int m0 = items[4 * it], nm = items[4 * it + 1], s = items[4 * it + 2], span = items[4 * it + 3];
-  // an item outside the batch or the workspace is ignored (the whole workgroup leaves)
-  if (m0 < 0 || nm <= 0 || nm > WaveAttn<G>::BT || m0 > batch - nm || s < 0 || span <= 0 || s > max_splits - span)
-    return;
+  if (bad_item(m0, nm, WaveAttn<G>::BT, batch, s, span, max_splits)) return;
   const int hq = hkv * G;
-  const __amdgpu_buffer_rsrc_t tab = table_rsrc(r2t, table_bytes);
-  const uint32_t slot_bytes = (uint32_t)(hkv * kD), max_slot = (uint32_t)(num_slots - 1);
-  const int row_bytes = (int)((int64_t)members[m0] * stride * 4);
   const int kv_begin = s * chunk;
+  const int n_tiles = span * chunk / kBN;
+
+  Fp8Stage st;
+  st.tab = table_rsrc(r2t, table_bytes);
+  st.kc = kpool + g * kD + (tid & 7) * 16;
+  st.vc = vpool + g * kD + (tid >> 4) * 8;
+  st.slot_bytes = (uint32_t)(hkv * kD);
+  st.max_slot = (uint32_t)(num_slots - 1);
+  st.row_bytes = (int)((int64_t)members[m0] * stride * 4);
+  st.kv_begin = kv_begin;
+  st.last = n_tiles - 1;
+  st.tid = tid;
+  st.k0 = k0s;
+  st.v0 = v0s;
+  st.k1 = k1s;
 
   WaveAttn<G> wa;
-  wa.init_shared(q, members, seq_lens, m0, nm, batch, hq, g, wave, lane, scale_log2 * kscale[g]);
+  wa.init_shared(q, members, seq_lens, m0, nm, batch, hq, g, wave, lane, scale_log2 * kscale[g],
+                 kv_begin + n_tiles * kBN);
   const bool active = G != 1 || 32 * wave < nm;
-
-  Fp8Stage stage;
-  const int n_tiles = span * chunk / kBN;
-  stage.load(kpool, vpool, slot_bytes, max_slot, Fp8Stage::slots(tab, row_bytes, kv_begin, tid), g, tid);
-  stage.store(Ks[0], Vt[0], tid);
-  stage.load(kpool, vpool, slot_bytes, max_slot, Fp8Stage::slots(tab, row_bytes, kv_begin + min(1, n_tiles - 1) * kBN, tid), g, tid);
-  auto nslots = Fp8Stage::slots(tab, row_bytes, kv_begin + min(2, n_tiles - 1) * kBN, tid);
-  __syncthreads();
-  for (int kt = 0; kt < n_tiles; ++kt) {
-    const bf16* K = Ks[kt & 1];
-    const bf16* V = Vt[kt & 1];
-    stage.store(Ks[(kt + 1) & 1], Vt[(kt + 1) & 1], tid);
-    stage.load(kpool, vpool, slot_bytes, max_slot, nslots, g, tid);
-    nslots = Fp8Stage::slots(tab, row_bytes, kv_begin + min(kt + 3, n_tiles - 1) * kBN, tid);
-    if (active)
-      wa.tile(
-          kv_begin + kt * kBN,
-          [&](int mb, int ks) { return *(const bf16x8*)(K + krow(sigma(mb, ln)) * kKStride + 32 * ks + 8 * lg); },
-          [&](int kk, int db) { return *(const bf16x8*)(V + (16 * db + ln) * kVStride + 32 * kk + 8 * lg); });
-    __syncthreads();
-  }
+  const Fp8Operands ops{ln, lg};
+  const int first = item_first_visible(members, seq_lens, m0, nm, batch, kv_begin + n_tiles * kBN, lane);
+  tile_loop<G>(wa, st, kv_begin, n_tiles, plain_tiles(kv_begin, first, n_tiles), active, k0s, k1s, v0s, v1s,
+               [&](const char* K, int mb, int ks) { return ops.k(K, mb, ks); },
+               [&](const char* V, int kk, int db) { return ops.v(V, kk, db); });
   wa.store_partial(ws_ml, ws_acc, members, m0, nm, hq, max_splits, s, span, vscale[g]);
 }
 
