@@ -401,6 +401,25 @@ int pkv_decode_attention_shared(const void* q, void* o, int32_t qo_dtype, const 
                                 const int32_t* members, const int32_t* skip, const int32_t* items, int64_t n_items,
                                 int32_t first_split, void* workspace, size_t ws_bytes, void* stream);
 
+/* Decode for callers that cannot allocate device memory (code under graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): pkv_decode_attention_shared (n_items = 0 is
+ * the plain decode) with the split partials in a file-scope device array of
+ * PKV_DECODE_STATIC_SCRATCH_BYTES instead of a caller workspace.  Each GPU the library runs on
+ * holds its own copy of the array until the process ends; its address is looked up once per
+ * device on the first call there.  Calls that overlap on one GPU share the array and race.
+ * chunk = 0 takes the automatic chunk, doubled while the partials do not fit when there is no
+ * plan (n_items = 0 and first_split = 0; a plan is tied to the chunk it was made for); a call whose
+ * partials still exceed the array (at the chunk given) fails with PKV_ERR_INVAL and a message
+ * giving the sizes.  Allocates nothing; other arguments and errors as for
+ * pkv_decode_attention_shared. */
+#define PKV_DECODE_STATIC_SCRATCH_BYTES (64LL << 20)
+int pkv_decode_attention_static(const void* q, void* o, int32_t qo_dtype, const void* k_pool, const void* v_pool,
+                                int32_t pool_dtype, int64_t num_slots, const float* k_scale, const float* v_scale,
+                                const int32_t* req_to_token, int64_t stride, const int32_t* seq_lens, int32_t batch,
+                                int32_t max_seq_len, int32_t hq, int32_t hkv, int32_t d, float sm_scale, int32_t chunk,
+                                const int32_t* members, const int32_t* skip, const int32_t* items, int64_t n_items,
+                                int32_t first_split, void* stream);
+
 /* first_split value meaning "no split phase at all". */
 #define PKV_NO_SPLIT_PHASE (1 << 30)
 /* The first chunk the split phase must launch for a plan's skip [batch] at the current

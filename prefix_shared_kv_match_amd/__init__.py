@@ -11,7 +11,8 @@ from typing import List, Optional, Sequence, Tuple
 
 import numpy as np
 
-from ._capi import PKV_BF16, PKV_F32, PKV_FP8_E4M3, PKV_NO_SPLIT_PHASE, PkvError, check, lib
+from ._capi import (PKV_BF16, PKV_DECODE_STATIC_SCRATCH_BYTES, PKV_F32, PKV_FP8_E4M3, PKV_NO_SPLIT_PHASE, PkvError,
+                    check, lib)
 
 __all__ = [
     "PKV_F32", "PKV_BF16", "PKV_FP8_E4M3", "PkvError", "lib",
@@ -24,6 +25,7 @@ __all__ = [
     "rt_decode_step", "rt_finish", "pkv_kv_scatter", "pkv_append_slots", "pkv_extend_tile", "pkv_extend_plan",
     "pkv_extend_attention", "pkv_decode_chunk", "pkv_decode_workspace_bytes", "pkv_decode_attention",
     "pkv_decode_shared_rows", "pkv_decode_shared_plan", "pkv_decode_attention_shared",
+    "pkv_decode_attention_static", "PKV_DECODE_STATIC_SCRATCH_BYTES",
 ]
 
 import ctypes as C
@@ -494,3 +496,32 @@ def pkv_decode_attention_shared(q, o, k_pool, v_pool, req_to_token, seq_lens, ma
             _dev(items, "items", torch.int32), items.shape[0], int(first_split), _dev(workspace, "workspace"),
             workspace.numel() * workspace.element_size(), _stream(stream))
     check(lib().pkv_decode_attention_shared(*args))
+
+
+def pkv_decode_attention_static(q, o, k_pool, v_pool, req_to_token, seq_lens, max_seq_len, sm_scale,
+                                chunk: int = 0, members=None, skip=None, items=None, first_split: int = 0,
+                                k_scale=None, v_scale=None, stream=None) -> None:
+    """pkv_decode_attention (or, with a plan, pkv_decode_attention_shared) with the partials in
+    the library's static device array instead of a workspace: allocates nothing."""
+    torch = _torch()
+    b, hq, d = q.shape
+    ns, hkv, d2 = k_pool.shape
+    if o.shape != q.shape or v_pool.shape != k_pool.shape or d2 != d or seq_lens.shape != (b,) \
+            or req_to_token.dim() != 2 or req_to_token.shape[0] < b:
+        raise ValueError("decode: shape mismatch")
+    if items is None:
+        if members is not None or skip is not None:
+            raise ValueError("decode: members and skip come with items")
+        n_items = 0
+    else:
+        if members is None or skip is None or members.shape != (b,) or skip.shape != (b,) or items.dim() != 2 \
+                or items.shape[1] != 4:
+            raise ValueError("decode: plan shape mismatch")
+        n_items = items.shape[0]
+    args = (_dev(q, "q"), _dev(o, "o", q.dtype), _dtype_code(q), _dev(k_pool, "k_pool"),
+            _dev(v_pool, "v_pool", k_pool.dtype), _dtype_code(k_pool), ns, _dev(k_scale, "k_scale", torch.float32),
+            _dev(v_scale, "v_scale", torch.float32), _dev(req_to_token, "req_to_token", torch.int32),
+            req_to_token.shape[1], _dev(seq_lens, "seq_lens", torch.int32), b, int(max_seq_len), hq, hkv, d,
+            float(sm_scale), int(chunk), _dev(members, "members", torch.int32), _dev(skip, "skip", torch.int32),
+            _dev(items, "items", torch.int32), n_items, int(first_split), _stream(stream))
+    check(lib().pkv_decode_attention_static(*args))

@@ -10,6 +10,7 @@ LIB_PATH = os.environ.get("PKV_LIBRARY") or os.path.join(_HERE, "libpkv.so")
 
 PKV_F32, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2
 PKV_NO_SPLIT_PHASE = 1 << 30
+PKV_DECODE_STATIC_SCRATCH_BYTES = 64 << 20
 ERRORS = {-1: "PKV_ERR_INVAL", -2: "PKV_ERR_OOM", -3: "PKV_ERR_LOCK", -4: "PKV_ERR_SLOT", -5: "PKV_ERR_NODE",
           -6: "PKV_ERR_HIP", -7: "PKV_ERR_UNSUPPORTED", -8: "PKV_ERR_INTERNAL"}
 
@@ -78,6 +79,8 @@ SIGNATURES = {
     "pkv_decode_plan": (_i64, [_p, _i64, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p, _p, _i64, _pi32]),
     "pkv_decode_attention_shared": (C.c_int, [_p, _p, _i32, _p, _p, _i32, _i64, _p, _p, _p, _i64, _p, _i32, _i32,
                                               _i32, _i32, _i32, _f32, _i32, _p, _p, _p, _i64, _i32, _p, _sz, _p]),
+    "pkv_decode_attention_static": (C.c_int, [_p, _p, _i32, _p, _p, _i32, _i64, _p, _p, _p, _i64, _p, _i32, _i32,
+                                              _i32, _i32, _i32, _f32, _i32, _p, _p, _p, _i64, _i32, _p]),
 }
 
 _lib = None

@@ -30,6 +30,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "device.h"
 
@@ -734,4 +735,78 @@ extern "C" int pkv_decode_attention_shared(const void* q, void* o, int32_t qo_dt
   return decode_impl(q, o, qo_dtype, k_pool, v_pool, pool_dtype, num_slots, k_scale, v_scale, req_to_token, stride,
                      seq_lens, batch, max_seq_len, hq, hkv, d, sm_scale, chunk, members, n_items > 0 ? skip : nullptr,
                      items, n_items, first_split, workspace, ws_bytes, stream);
+}
+
+// ------------------------------------------------------------------------------------------
+// Decode without a caller workspace: the split partials go to a file-scope device array.
+// ------------------------------------------------------------------------------------------
+//
+// For callers that cannot allocate (code under graph capture, tight serving loops): the
+// partials of pkv_decode_attention_shared live in `scratch`, one copy per GPU, held until the
+// process ends.  In host code the array's name is only a stand-in, so its device address is
+// taken once per device with hipGetSymbolAddress (with that device current) and that address
+// is what the kernels get.  Every call on a GPU shares its array: calls that overlap on one GPU
+// race.  Nothing needs clearing between calls: every partial the reduce reads is written by
+// the split phase or a plan item of the same call (the array keeps the last call's partials).
+
+static __device__ __align__(256) char scratch[PKV_DECODE_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+int g_scratch_rc[kMaxDevices];
+
+int scratch_for_current_device(void** out) {
+  int dev = 0;
+  if (int rc = hip_check(hipGetDevice(&dev), "decode (static): hipGetDevice")) return rc;
+  if (dev < 0 || dev >= kMaxDevices) return fail(PKV_ERR_UNSUPPORTED, "decode (static): device %d", dev);
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    g_scratch_rc[dev] = e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+    g_scratch_ptr[dev] = e == hipSuccess ? ptr : nullptr;
+  });
+  if (g_scratch_rc[dev] != PKV_OK || !g_scratch_ptr[dev])
+    return fail(PKV_ERR_HIP, "decode (static): hipGetSymbolAddress of the scratch array failed on device %d", dev);
+  *out = g_scratch_ptr[dev];
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" int pkv_decode_attention_static(const void* q, void* o, int32_t qo_dtype, const void* k_pool,
+                                           const void* v_pool, int32_t pool_dtype, int64_t num_slots,
+                                           const float* k_scale, const float* v_scale, const int32_t* req_to_token,
+                                           int64_t stride, const int32_t* seq_lens, int32_t batch,
+                                           int32_t max_seq_len, int32_t hq, int32_t hkv, int32_t d, float sm_scale,
+                                           int32_t chunk, const int32_t* members, const int32_t* skip,
+                                           const int32_t* items, int64_t n_items, int32_t first_split,
+                                           void* stream) {
+  if (batch < 0 || hq <= 0 || hkv <= 0 || max_seq_len <= 0)
+    return fail(PKV_ERR_INVAL, "decode (static): bad sizes (batch %d hq %d hkv %d max_seq_len %d)", batch, hq, hkv,
+                max_seq_len);
+  if (batch == 0) return PKV_OK;
+  if (chunk == 0) {
+    // the automatic chunk; for a plain decode (no plan, whose items and first split are tied to
+    // its chunk) doubled while the partials would not fit the array
+    chunk = pkv_decode_chunk(batch, hkv, max_seq_len);
+    while (n_items == 0 && first_split == 0 &&
+           pkv_decode_workspace_bytes(batch, hq, d, max_seq_len, chunk) > (size_t)PKV_DECODE_STATIC_SCRATCH_BYTES &&
+           chunk < max_seq_len)
+      chunk *= 2;
+  }
+  const size_t need = pkv_decode_workspace_bytes(batch, hq, d, max_seq_len, chunk);
+  if (need > (size_t)PKV_DECODE_STATIC_SCRATCH_BYTES)
+    return fail(PKV_ERR_INVAL,
+                "decode (static): %d sequences x %d q heads over %d tokens in chunks of %d need %zu bytes of partials, "
+                "more than the %lld-byte static scratch array",
+                batch, hq, max_seq_len, chunk, need, (long long)PKV_DECODE_STATIC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (int rc = scratch_for_current_device(&ws)) return rc;
+  return pkv_decode_attention_shared(q, o, qo_dtype, k_pool, v_pool, pool_dtype, num_slots, k_scale, v_scale,
+                                     req_to_token, stride, seq_lens, batch, max_seq_len, hq, hkv, d, sm_scale, chunk,
+                                     members, skip, items, n_items, first_split, ws,
+                                     (size_t)PKV_DECODE_STATIC_SCRATCH_BYTES, stream);
 }
