@@ -46,17 +46,20 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
 CSRC = os.path.join(ROOT, "prefix_shared_kv_match_amd", "csrc")
-# HBM bytes per launch of each workload's dominant kernel from two rocprofv3 --pmc passes
-# (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch; profiles/<workload>_kernels.md), scaled by
-# what the same counters read for a plain 1 GiB device copy (FETCH x2.0, WRITE x1.0).  Each
-# entry holds the hash of the kernel sources it was taken on; a changed kernel reports null.
+# HBM bytes per launch of the extend kernel and per decode step (split phase, shared-prefix pass
+# and reduce) of each workload, from two rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE, KiB
+# per dispatch; profiles/<workload>_kernels.md), scaled by what the same counters read for a
+# plain 1 GiB device copy (FETCH x2.0, WRITE x1.0).  Each entry holds the hash of the kernel
+# sources it was taken on; a changed kernel reports null.
 TRAFFIC = {
-    "fewshot_bf16": dict(kernel="extend_attention", src_hash="331a9425f55b6f4a",
-                         fetch_kib=204946.0, write_kib=102979.0),
-    "decode_bf16": dict(kernel="decode_attention", src_hash="d2553de404a13387",
-                        fetch_kib=4214637.0 + 35187.0 + 23302.0, write_kib=39256.0 + 8704.0 + 4096.0),
-    "longctx_fp8": dict(kernel="extend_attention", src_hash="331a9425f55b6f4a",
-                        fetch_kib=1704504.0, write_kib=262145.0),
+    ("fewshot_bf16", "extend_attention"): dict(src_hash="de802891b695bf13", fetch_kib=207276.0, write_kib=102968.3),
+    ("fewshot_bf16", "decode_attention"): dict(src_hash="c7fd2b86058ebf82", fetch_kib=30294.6 + 8390.0,
+                                               write_kib=8482.7 + 512.0),
+    ("decode_bf16", "decode_attention"): dict(src_hash="c7fd2b86058ebf82", fetch_kib=4214561.2 + 35237.7 + 23302.0,
+                                              write_kib=39187.4 + 8704.0 + 4096.0),
+    ("longctx_fp8", "extend_attention"): dict(src_hash="de802891b695bf13", fetch_kib=1474762.5, write_kib=319488.0),
+    ("longctx_fp8", "decode_attention"): dict(src_hash="c7fd2b86058ebf82", fetch_kib=56574.9 + 32326.9,
+                                              write_kib=35604.9 + 256.0),
 }
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 # (warmup, timed) steps when not given: a few hundred ms of warmup for sub-millisecond steps,
@@ -81,8 +84,8 @@ def kernel_src_hash(kernel: str) -> str:
 
 
 def traffic_bytes(workload: str, kernel: str):
-    t = TRAFFIC.get(workload)
-    if t is None or t["kernel"] != kernel or kernel_src_hash(kernel) != t["src_hash"]:
+    t = TRAFFIC.get((workload, kernel))
+    if t is None or kernel_src_hash(kernel) != t["src_hash"]:
         return None
     return (t["fetch_kib"] * FETCH_SCALE + t["write_kib"] * WRITE_SCALE) * 1024.0
 
@@ -118,7 +121,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=64, help="requests in the oracle's timed sample")
     ap.add_argument("--cpu-rows", type=int, default=-1,
-                    help="extend rows per request in the oracle's timed sample (0 = all; -1 = 48 for the "
+                    help="extend rows per request in the oracle's timed sample (0 = all; -1 = 16 for the "
                          "long-context case, whose rows each cost ~2 GFLOP in float64, else all)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (reference for HBM byte counters)")
@@ -797,7 +800,7 @@ def main():
         "library": os.path.relpath(pkv._capi.LIB_PATH, ROOT),
     }
     if not a.no_cpu_baseline:
-        rows = a.cpu_rows if a.cpu_rows >= 0 else (48 if wl.name == "longctx_fp8" else 0)
+        rows = a.cpu_rows if a.cpu_rows >= 0 else (16 if wl.name == "longctx_fp8" else 0)
         out["cpu_baseline"] = cpu_baseline(wl, hb, a.cpu_sample, b.decode_only, timed_step_i, rows_per_req=rows)
     print(json.dumps(out), flush=True)
     return 0

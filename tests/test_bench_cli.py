@@ -25,16 +25,16 @@ def test_default_steps_for_every_workload():
 
 
 def test_traffic_withheld_for_changed_sources(monkeypatch):
-    t = dict(bench.TRAFFIC)
-    entry = dict(t["fewshot_bf16"])
+    key = ("fewshot_bf16", "extend_attention")
+    entry = dict(bench.TRAFFIC[key])
     entry["src_hash"] = bench.kernel_src_hash("extend_attention")
-    monkeypatch.setitem(bench.TRAFFIC, "fewshot_bf16", entry)
-    got = bench.traffic_bytes("fewshot_bf16", "extend_attention")
+    monkeypatch.setitem(bench.TRAFFIC, key, entry)
+    got = bench.traffic_bytes(*key)
     assert got == (entry["fetch_kib"] * bench.FETCH_SCALE + entry["write_kib"] * bench.WRITE_SCALE) * 1024.0
-    entry = dict(entry, src_hash="0" * 16)
-    monkeypatch.setitem(bench.TRAFFIC, "fewshot_bf16", entry)
-    assert bench.traffic_bytes("fewshot_bf16", "extend_attention") is None
-    assert bench.traffic_bytes("fewshot_bf16", "decode_attention") is None     # another kernel's figure
+    monkeypatch.setitem(bench.TRAFFIC, key, dict(entry, src_hash="0" * 16))
+    assert bench.traffic_bytes(*key) is None
+    monkeypatch.delitem(bench.TRAFFIC, ("fewshot_bf16", "decode_attention"))
+    assert bench.traffic_bytes("fewshot_bf16", "decode_attention") is None     # no figure for that kernel
 
 
 def test_default_workload_is_the_long_context_case(monkeypatch):
