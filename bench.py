@@ -112,9 +112,9 @@ def parse():
                     help="decode without the shared-prefix plan (every sequence gathers its whole context)")
     ap.add_argument("--decode-chunk", type=int, default=0,
                     help="tokens per decode split (a multiple of 64; 0 = the library's automatic choice)")
-    ap.add_argument("--shared-min-workgroups", type=int, default=0,
-                    help="shared-prefix decode: merge chunks into longer items while this many workgroups remain "
-                         "(0 = the engine's default)")
+    ap.add_argument("--resident-workgroups", type=int, default=0,
+                    help="shared-prefix decode: workgroups resident at once, by which the plan costs its item "
+                         "span (0 = the engine's default)")
     ap.add_argument("--private-max-workgroups", type=int, default=-1,
                     help="shared-prefix decode: give the private tails to the shared-prefix kernel too when items "
                          "and tails need at most this many workgroups (-1 = the engine's default, 0 = never)")
@@ -350,8 +350,8 @@ class JobBench:
         s = wl.shape
         self.eng = eng = Engine(wl.pool_slots, s.hq, s.hkv, s.d, s.qo_dtype, s.pool_dtype, wl.free_order, "cuda",
                                 sm_scale=s.sm_scale, policy=a.policy)
-        if a.shared_min_workgroups:
-            eng.SHARED_MIN_WORKGROUPS = a.shared_min_workgroups
+        if a.resident_workgroups:
+            eng.RESIDENT_WORKGROUPS = a.resident_workgroups
         if a.private_max_workgroups >= 0:
             eng.PRIVATE_MAX_WORKGROUPS = a.private_max_workgroups
         self.stride = wl.max_len()
@@ -680,9 +680,9 @@ def main():
     extra = min(30, a.steps)      # untimed steps after the timed ones, for the other kernels' spans
     b = PathBench(torch, a.workload, a.warmup + a.steps + extra, shared_decode=not a.plain_decode,
                   decode_chunk=a.decode_chunk)
-    if a.shared_min_workgroups or a.private_max_workgroups >= 0:
-        if a.shared_min_workgroups:
-            b.eng.SHARED_MIN_WORKGROUPS = a.shared_min_workgroups
+    if a.resident_workgroups or a.private_max_workgroups >= 0:
+        if a.resident_workgroups:
+            b.eng.RESIDENT_WORKGROUPS = a.resident_workgroups
         if a.private_max_workgroups >= 0:
             b.eng.PRIVATE_MAX_WORKGROUPS = a.private_max_workgroups
         if b.plan is not None:      # a decode-only batch planned at construction: plan again

@@ -433,14 +433,17 @@ int32_t pkv_decode_first_split(const int32_t* skip, const int32_t* seq_lens, int
 int64_t pkv_decode_plan_items_cap(const int32_t* seq_lens, int32_t batch, int64_t stride, int32_t chunk, int32_t rows);
 /* The shared-prefix plan with its choices made [the radix tree gives sequences that share a
  * prefix the same slots: RC "프리픽스 매칭"; EX: matched KV is reused]: pkv_decode_shared_plan
- * over rows from one radix tree; when the shared items and the private tails together need
+ * over rows from one radix tree.  When the shared items and the private tails together need
  * at most private_max_workgroups workgroups (items x hkv), the tails become one-member items
- * too; when that many items x hkv reach 2 x shared_min_workgroups, items span several chunks
- * (as many as keep about shared_min_workgroups workgroups).  Outputs as for
- * pkv_decode_shared_plan, plus *first_split = pkv_decode_first_split at these lengths.
- * Returns the number of items (0: nothing is shared, decode without a plan; *first_split 0). */
+ * too.  Items then span the number of chunks `span` in 1 .. min(longest context in chunks,
+ * 64) that minimizes ceil(items(span) x hkv / resident_workgroups) x (4 + span x chunk / 64)
+ * (launch rounds of resident_workgroups, each as long as its longest item: 4 tiles of fixed
+ * cost plus its tiles), the longer span on a tie.  Outputs as for pkv_decode_shared_plan,
+ * plus *first_split = pkv_decode_first_split at these lengths.  Returns the number of items
+ * (0: nothing is shared, decode without a plan; *first_split 0); PKV_ERR_INVAL on bad
+ * arguments. */
 int64_t pkv_decode_plan(const int32_t* req_to_token, int64_t stride, const int32_t* seq_lens, int32_t batch,
-                        int32_t chunk, int32_t rows, int32_t hkv, int32_t shared_min_workgroups,
+                        int32_t chunk, int32_t rows, int32_t hkv, int32_t resident_workgroups,
                         int32_t private_max_workgroups, int32_t* members, int32_t* skip, int32_t* items,
                         int64_t items_cap, int32_t* first_split);
 

@@ -452,7 +452,7 @@ def pkv_decode_first_split(skip, seq_lens, chunk: int) -> int:
 
 
 def pkv_decode_plan(req_to_token: np.ndarray, seq_lens, chunk: int, rows: int, hkv: int,
-                    shared_min_workgroups: int, private_max_workgroups: int):
+                    resident_workgroups: int, private_max_workgroups: int):
     """The shared-prefix plan with the library's choices (spans, private items) over host slot
     rows from one radix tree: (members, skip, items [n, 4], first_split), or None when nothing
     is shared."""
@@ -467,7 +467,7 @@ def pkv_decode_plan(req_to_token: np.ndarray, seq_lens, chunk: int, rows: int, h
     items = np.empty((max(cap, 1), 4), dtype=np.int32)
     first = C.c_int32()
     n = int(check(lib().pkv_decode_plan(_ptr(r2t), r2t.shape[1], _ptr(sl), b, int(chunk), int(rows), int(hkv),
-                                        int(shared_min_workgroups), int(private_max_workgroups), _ptr(members),
+                                        int(resident_workgroups), int(private_max_workgroups), _ptr(members),
                                         _ptr(skip), _ptr(items), cap, C.byref(first))))
     if n == 0:
         return None

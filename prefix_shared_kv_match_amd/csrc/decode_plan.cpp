@@ -175,29 +175,52 @@ extern "C" int64_t pkv_decode_plan_items_cap(const int32_t* seq_lens, int32_t ba
 }
 
 extern "C" int64_t pkv_decode_plan(const int32_t* req_to_token, int64_t stride, const int32_t* seq_lens, int32_t batch,
-                                   int32_t chunk, int32_t rows, int32_t hkv, int32_t shared_min_workgroups,
+                                   int32_t chunk, int32_t rows, int32_t hkv, int32_t resident_workgroups,
                                    int32_t private_max_workgroups, int32_t* members, int32_t* skip, int32_t* items,
                                    int64_t items_cap, int32_t* first_split) {
-  if (hkv <= 0 || shared_min_workgroups <= 0 || !first_split)
-    return fail(PKV_ERR_INVAL, "decode plan: bad arguments (hkv %d, shared_min_workgroups %d)", hkv,
-                shared_min_workgroups);
+  if (hkv <= 0 || resident_workgroups <= 0 || chunk <= 0 || !first_split)
+    return fail(PKV_ERR_INVAL, "decode plan: bad arguments (hkv %d, resident_workgroups %d, chunk %d)", hkv,
+                resident_workgroups, chunk);
   *first_split = 0;
   // rows from one radix tree (the caller holds the batch's locks): each chunk's last slot decides
   int64_t n = pkv_decode_shared_plan(req_to_token, stride, seq_lens, batch, chunk, rows, 1, 1, 0, members, skip,
                                      items, items_cap);
   if (n <= 0) return n;
   int64_t tails = 0;   // private chunks left to the split phase
-  for (int32_t b = 0; b < batch; ++b) tails += ((int64_t)seq_lens[b] + chunk - 1) / chunk - skip[b];
+  int64_t longest = 1;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t c = ((int64_t)seq_lens[b] + chunk - 1) / chunk;
+    tails += c - skip[b];
+    longest = std::max(longest, c);
+  }
   // few, short private tails: one-member items take them too, and the split phase (whose
   // workgroups would be latency-bound) is not launched
   const bool priv = (n + tails) * hkv <= (int64_t)private_max_workgroups;
-  // a long shared prefix: items spanning several chunks while about shared_min_workgroups
-  // workgroups (items x kv heads) remain, so fewer partials are written
-  const int64_t span = (n + (priv ? tails : 0)) * hkv / shared_min_workgroups;
-  if (span >= 2 || priv) {
-    n = pkv_decode_shared_plan(req_to_token, stride, seq_lens, batch, chunk, rows,
-                               (int32_t)std::min<int64_t>(std::max<int64_t>(span, 1), 1 << 20), 1, priv ? 1 : 0,
-                               members, skip, items, items_cap);
+  // Span: workgroups start in rounds of about resident_workgroups (what the GPU holds at
+  // once) and a round lasts about as long as its longest item, so a plan costs about
+  //   ceil(items x hkv / resident_workgroups) x (kItemFixed + span x chunk / 64)  tile times,
+  // kItemFixed being a workgroup's fixed cost in tiles (its q rows, the pipeline fill, the
+  // partial store).  The cheapest span in 1 .. min(longest context in chunks, 64) is taken,
+  // the longer one on a tie (fewer partials to write and merge).
+  constexpr int64_t kItemFixed = 4;
+  const int64_t tiles_per_chunk = std::max<int64_t>(chunk / 64, 1);
+  const int32_t max_span = (int32_t)std::min<int64_t>(longest, 64);
+  int32_t best = 0;
+  int64_t best_cost = 0;
+  for (int32_t sp = 1; sp <= max_span; ++sp) {
+    n = pkv_decode_shared_plan(req_to_token, stride, seq_lens, batch, chunk, rows, sp, 1, priv ? 1 : 0, members,
+                               skip, items, items_cap);
+    if (n < 0) return n;
+    const int64_t rounds = (n * hkv + resident_workgroups - 1) / resident_workgroups;
+    const int64_t cost = rounds * (kItemFixed + (int64_t)sp * tiles_per_chunk);
+    if (best == 0 || cost <= best_cost) {
+      best = sp;
+      best_cost = cost;
+    }
+  }
+  if (best != max_span) {   // the outputs hold the last span's plan
+    n = pkv_decode_shared_plan(req_to_token, stride, seq_lens, batch, chunk, rows, best, 1, priv ? 1 : 0, members,
+                               skip, items, items_cap);
     if (n < 0) return n;
   }
   const int32_t fs = pkv_decode_first_split(skip, seq_lens, batch, chunk);

@@ -152,11 +152,12 @@ class StagedUpload:
 class Engine:
     """One radix tree plus its device KV pools."""
 
-    # the two knobs of the library's decode plan (pkv_decode_plan): items span several chunks
-    # while about SHARED_MIN_WORKGROUPS workgroups remain; plans whose items and private tails
-    # together need at most PRIVATE_MAX_WORKGROUPS workgroups give the tails to the
+    # the two knobs of the library's decode plan (pkv_decode_plan): RESIDENT_WORKGROUPS, the
+    # shared-prefix kernel's workgroups the GPU holds at once (two per CU), sets the item span
+    # (the launch is costed in rounds of that many workgroups); plans whose items and private
+    # tails together need at most PRIVATE_MAX_WORKGROUPS workgroups give the tails to the
     # shared-prefix kernel too
-    SHARED_MIN_WORKGROUPS = 512
+    RESIDENT_WORKGROUPS = 512
     PRIVATE_MAX_WORKGROUPS = 4096
     NO_SPLIT_PHASE = PKV_NO_SPLIT_PHASE
 
@@ -370,7 +371,7 @@ class Engine:
         if rows <= 0:
             return None
         # the rows come from this engine's tree (its locks keep them)
-        plan = pkv_decode_plan(req_to_token, seq_lens, chunk, rows, self.hkv, self.SHARED_MIN_WORKGROUPS,
+        plan = pkv_decode_plan(req_to_token, seq_lens, chunk, rows, self.hkv, self.RESIDENT_WORKGROUPS,
                                self.PRIVATE_MAX_WORKGROUPS)
         if plan is None:
             return None

@@ -188,33 +188,58 @@ def test_first_split_at_current_lengths():
 
 @settings(max_examples=80, deadline=None)
 @given(seed=st.integers(0, 10_000), n=st.integers(1, 40), hkv=st.sampled_from([1, 4, 8, 32]),
-       shared_min=st.sampled_from([1, 16, 512]), private_max=st.sampled_from([0, 64, 4096, 1 << 20]))
-def test_plan_choices_of_the_library(seed, n, hkv, shared_min, private_max):
+       resident=st.sampled_from([1, 16, 512]), private_max=st.sampled_from([0, 64, 4096, 1 << 20]))
+def test_plan_choices_of_the_library(seed, n, hkv, resident, private_max):
     """pkv_decode_plan (the library's choices) equals pkv_decode_shared_plan called the way its
     documentation states: private items when items plus private tails need at most
-    private_max_workgroups workgroups (times hkv), spans of (items [+ tails]) x hkv /
-    shared_min_workgroups chunks when that reaches 2, and first_split at these lengths."""
+    private_max_workgroups workgroups (times hkv); the span in 1 .. min(longest context in
+    chunks, 64) with the lowest ceil(items x hkv / resident) x (4 + span x chunk / 64), the
+    longer one on a tie; and first_split at these lengths."""
     rng = np.random.default_rng(seed)
     chunk, stride, rows = 64, 512, 8
     paths = [[int(x) for x in rng.integers(0, 3, size=4)] for _ in range(n)]
     lens = [int(x) for x in rng.integers(1, stride + 1, size=n)]
     r2t = rows_from_paths(rng, paths, lens, chunk, stride)
-    got = pkv.pkv_decode_plan(r2t, lens, chunk, rows, hkv, shared_min, private_max)
+    got = pkv.pkv_decode_plan(r2t, lens, chunk, rows, hkv, resident, private_max)
     m, skip, items = pkv.pkv_decode_shared_plan(r2t, lens, chunk, rows, rows_from_tree=True)
     if items.shape[0] == 0:
         assert got is None
         return
     tails = int(sum((L + chunk - 1) // chunk for L in lens) - skip.sum())
     priv = (items.shape[0] + tails) * hkv <= private_max
-    span = (items.shape[0] + (tails if priv else 0)) * hkv // shared_min
-    if span >= 2 or priv:
-        m, skip, items = pkv.pkv_decode_shared_plan(r2t, lens, chunk, rows, rows_from_tree=True,
-                                                    max_span=max(span, 1), private_items=priv)
+    longest = max((L + chunk - 1) // chunk for L in lens)
+    costs = {}
+    for span in range(1, min(longest, 64) + 1):
+        k = pkv.pkv_decode_shared_plan(r2t, lens, chunk, rows, rows_from_tree=True, max_span=span,
+                                       private_items=priv)[2].shape[0]
+        costs[span] = -(-k * hkv // resident) * (4 + span * chunk // 64)
+    best = max(s for s, c in costs.items() if c == min(costs.values()))
+    m, skip, items = pkv.pkv_decode_shared_plan(r2t, lens, chunk, rows, rows_from_tree=True, max_span=best,
+                                                private_items=priv)
     gm, gs, gi, first = got
     assert np.array_equal(gm, m) and np.array_equal(gs, skip) and np.array_equal(gi, items)
     assert first == pkv.pkv_decode_first_split(skip, lens, chunk)
     need = [s for s, L in zip(skip.tolist(), lens) if (L + chunk - 1) // chunk > s]
     assert first == (min(need) if need else pkv.PKV_NO_SPLIT_PHASE)
+
+
+def test_plan_span_fills_one_round_on_the_long_context_shape():
+    """The span choice on the long-context decode shape (16 sequences over one 32,768-token
+    prefix with 1,088-token private tails, chunk 256, 8 kv heads, private items): span 3 would
+    make 600 workgroups, two rounds of 512; span 4 makes exactly 512, one round, and is taken."""
+    rng = np.random.default_rng(5)
+    n, chunk, pre, tail = 16, 256, 32768, 1088
+    stride = pre + tail
+    shared = rng.permutation(1 << 20)[: pre + n * tail].astype(np.int32)
+    r2t = np.zeros((n, stride), dtype=np.int32)
+    for i in range(n):
+        r2t[i, :pre] = shared[:pre]
+        r2t[i, pre:] = shared[pre + i * tail: pre + (i + 1) * tail]
+    lens = [stride] * n
+    members, skip, items, first = pkv.pkv_decode_plan(r2t, lens, chunk, 16, 8, 512, 4096)
+    assert first == pkv.PKV_NO_SPLIT_PHASE
+    assert items.shape[0] * 8 == 512
+    assert int(items[:, 3].max()) == 4
 
 
 def test_first_split_and_plan_reject_bad_arguments():

@@ -245,7 +245,7 @@ def test_decode_shared_spans(case, private):
     else:
         wl = workloads.fewshot_bf16(n_req=6, prefix_len=900, suffix_range=(40, 120), decode_steps=2)
     r = Run(wl)
-    r.eng.SHARED_MIN_WORKGROUPS = 16
+    r.eng.RESIDENT_WORKGROUPS = 16
     r.eng.PRIVATE_MAX_WORKGROUPS = 1 << 20 if private else 0
     stats = r.run()
     assert r.plan is not None and int(r.plan["items"][:, 3].max()) >= 2, "no item spans two chunks"
@@ -384,7 +384,7 @@ def test_sharp_softmax_planted_late_keys(hq, hkv, pool):
     frac = _late_key_fraction(wl, lambda r: [200] + ([400] if r is longest else []))
     assert frac > 0.5, f"only {frac:.2f} of the rows meet a planted key beyond the rescale threshold"
     r = Run(wl, check_pool=True)
-    r.eng.SHARED_MIN_WORKGROUPS = 1 << 20      # one item per chunk: position 200 sits in chunk 1's second tile
+    r.eng.RESIDENT_WORKGROUPS = 1 << 20      # one item per chunk: position 200 sits in chunk 1's second tile
     r.eng.PRIVATE_MAX_WORKGROUPS = 0
     stats = r.run()
     assert r.shared_items > 0
