@@ -309,8 +309,10 @@ int32_t pkv_extend_tile(int32_t qo_dtype, int32_t pool_dtype, int32_t hq, int32_
  * device int32; work device int32 [n_work, 2] from pkv_extend_plan with the tile of
  * pkv_extend_tile.  fp8 pools: the dequantised value is code * k_scale[g] (v_scale[g]),
  * device float32 [hkv]; the scale is folded into the float32 logits / output.
- * Supported: (F32 q/o, F32 pool, d 64 or 128), (BF16 q/o, BF16 or FP8_E4M3 pool,
- * d 128), hq % hkv == 0.  Softmax and accumulation in float32. */
+ * Supported: (F32 q/o, F32 pool, d 64 or 128) and (BF16 q/o, BF16 or FP8_E4M3 pool, d 64)
+ * for any hq % hkv == 0 (VALU kernel); (BF16 q/o, BF16 or FP8_E4M3 pool, d 128) with hq / hkv
+ * in {1, 2, 4, 8} and a slot of at most 16,383 bytes (MFMA kernels).  Softmax and
+ * accumulation in float32. */
 int pkv_extend_attention(const void* q, void* o, int32_t qo_dtype, const void* k_pool, const void* v_pool,
                          int32_t pool_dtype, int64_t num_slots, const float* k_scale, const float* v_scale,
                          const int32_t* req_to_token, int64_t stride, const int32_t* prefix_lens,
@@ -329,7 +331,8 @@ int pkv_extend_attention(const void* q, void* o, int32_t qo_dtype, const void* k
  * seq_lens device int32 [batch], each in [1, max_seq_len].  chunk: tokens per split, a
  * multiple of 64, or 0 for automatic.  workspace: device memory of at least
  * pkv_decode_workspace_bytes(batch, hq, d, max_seq_len, chunk) bytes.
- * Supported shapes as for pkv_extend_attention.  Slots past the pool read the pool's last
+ * Supported: (F32 q/o, F32 pool) and (BF16 q/o, BF16 or FP8_E4M3 pool), d 64 or 128, with
+ * hq / hkv in {1, 2, 4, 8}.  Slots past the pool read the pool's last
  * slot (no access leaves the pools).  Errors: PKV_ERR_INVAL (sizes, null pointers, a
  * workspace too small), PKV_ERR_UNSUPPORTED (shape), PKV_ERR_HIP (launch).
  * pkv_decode_workspace_bytes: the caller-owned device workspace the split phase needs for

@@ -701,6 +701,12 @@ int decode_impl(const void* q, void* o, int32_t qo_dtype, const void* k_pool, co
   else if (qo_dtype == PKV_F32 && pool_dtype == PKV_F32 && d == 128)
     rc = launch_split<float, PKV_F32, 128>(G, batch, s0, ns, per_head, st, q, k_pool, v_pool, k_scale, v_scale, req_to_token, stride,
                                            seq_lens, hkv, chunk, max_splits, sc, ml, acc, skip, mslot);
+  else if (qo_dtype == PKV_BF16 && pool_dtype == PKV_BF16 && d == 64)
+    rc = launch_split<bf16, PKV_BF16, 64>(G, batch, s0, ns, per_head, st, q, k_pool, v_pool, k_scale, v_scale, req_to_token, stride,
+                                          seq_lens, hkv, chunk, max_splits, sc, ml, acc, skip, mslot);
+  else if (qo_dtype == PKV_BF16 && pool_dtype == PKV_FP8_E4M3 && d == 64)
+    rc = launch_split<bf16, PKV_FP8_E4M3, 64>(G, batch, s0, ns, per_head, st, q, k_pool, v_pool, k_scale, v_scale, req_to_token,
+                                              stride, seq_lens, hkv, chunk, max_splits, sc, ml, acc, skip, mslot);
   else if (qo_dtype == PKV_BF16 && pool_dtype == PKV_BF16 && d == 128)
     rc = launch_split<bf16, PKV_BF16, 128>(G, batch, s0, ns, per_head, st, q, k_pool, v_pool, k_scale, v_scale, req_to_token, stride,
                                            seq_lens, hkv, chunk, max_splits, sc, ml, acc, skip, mslot);
@@ -726,6 +732,9 @@ int decode_impl(const void* q, void* o, int32_t qo_dtype, const void* k_pool, co
   else if (qo_dtype == PKV_F32)
     hipLaunchKernelGGL((decode_reduce<float, 128>), rgrid, dim3(256), 0, st, ml, acc, seq_lens, batch, hq, chunk,
                        max_splits, (float*)o);
+  else if (d == 64)
+    hipLaunchKernelGGL((decode_reduce<bf16, 64>), rgrid, dim3(256), 0, st, ml, acc, seq_lens, batch, hq, chunk,
+                       max_splits, (bf16*)o);
   else
     hipLaunchKernelGGL((decode_reduce<bf16, 128>), rgrid, dim3(256), 0, st, ml, acc, seq_lens, batch, hq, chunk,
                        max_splits, (bf16*)o);

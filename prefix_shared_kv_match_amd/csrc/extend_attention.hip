@@ -29,8 +29,9 @@
 //    output.  The slot table is read with buffer loads one tile ahead of the K/V records it
 //    addresses, so a gathered row waits on no dependent load; rows are addressed in 64 bits
 //    (slot * slot bytes), so pools beyond 4 GiB work.
-//  - extend_f32 (f32 q/o, f32 pool, d 64 or 128): one wave per (tile, q head), VALU only;
-//    it serves the small fp32 case.
+//  - extend_vec (f32 q/o with an f32 pool at d 64 or 128, and bf16 q/o with a bf16 or fp8
+//    pool at d 64): one wave per (tile, q head), VALU only; it serves the small fp32 case and
+//    the head dim the MFMA kernels are not built for.
 
 #include <math.h>
 
@@ -44,7 +45,7 @@ namespace pkv {
 namespace {
 
 // ------------------------------------------------------------------------------------------
-// fp32 path
+// VALU path (fp32, and head dim 64 for bf16 q/o)
 // ------------------------------------------------------------------------------------------
 
 constexpr int kF32Tile = 16;   // query tokens per work item
@@ -61,9 +62,19 @@ __device__ __forceinline__ float wave_sum64(float x) {
   return x;
 }
 
-template <int D>
-__global__ __launch_bounds__(64) void extend_f32(const float* __restrict__ q, float* __restrict__ o,
-                                                 const float* __restrict__ kpool, const float* __restrict__ vpool,
+// one pool or q element as a float (fp8 codes decoded exactly; their scale is applied by the caller)
+__device__ __forceinline__ float elem_f(float x) { return x; }
+__device__ __forceinline__ float elem_f(bf16 x) { return (float)x; }
+__device__ __forceinline__ float elem_f(uint8_t x) { return e4m3x2_to_f32<false>((uint32_t)x).x; }
+__device__ __forceinline__ void put_f(float* p, float x) { *p = x; }
+__device__ __forceinline__ void put_f(bf16* p, float x) { *p = (bf16)x; }
+
+// QT: q/o element type; PT: pool element type (float, bf16, or uint8_t E4M3 codes with
+// per-kv-head scales kscale / vscale)
+template <typename QT, typename PT, int D>
+__global__ __launch_bounds__(64) void extend_vec(const QT* __restrict__ q, QT* __restrict__ o,
+                                                 const PT* __restrict__ kpool, const PT* __restrict__ vpool,
+                                                 const float* __restrict__ kscale, const float* __restrict__ vscale,
                                                  const int32_t* __restrict__ r2t, int64_t stride,
                                                  const int32_t* __restrict__ prefix_lens,
                                                  const int32_t* __restrict__ extend_lens,
@@ -71,6 +82,7 @@ __global__ __launch_bounds__(64) void extend_f32(const float* __restrict__ q, fl
                                                  const int32_t* __restrict__ work, int hq, int hkv,
                                                  float scale_log2, uint32_t max_slot) {
   constexpr int PER = D / 64;
+  constexpr bool kFp8 = std::is_same<PT, uint8_t>::value;
   __shared__ float qs[kF32Tile][D];
   __shared__ float ps[kF32Kv];
   __shared__ int32_t sl[kF32Kv];
@@ -81,10 +93,12 @@ __global__ __launch_bounds__(64) void extend_f32(const float* __restrict__ q, fl
   const int p = prefix_lens[req], e = extend_lens[req];
   const int nq = min(kF32Tile, e - j0);
   const int g = h / (hq / hkv);
+  const float kmul = kFp8 ? scale_log2 * kscale[g] : scale_log2;
+  const float vmul = kFp8 ? vscale[g] : 1.f;
   const int64_t qrow0 = (int64_t)qo_indptr[req] + j0;
   for (int x = lane; x < kF32Tile * D; x += 64) {
     const int t = x / D, dd = x - t * D;
-    qs[t][dd] = t < nq ? q[((qrow0 + t) * hq + h) * D + dd] : 0.f;
+    qs[t][dd] = t < nq ? elem_f(q[((qrow0 + t) * hq + h) * D + dd]) : 0.f;
   }
   float m[kF32Tile], l[kF32Tile], acc[kF32Tile][PER];
 #pragma unroll
@@ -102,15 +116,15 @@ __global__ __launch_bounds__(64) void extend_f32(const float* __restrict__ q, fl
     const bool kin = k < ctx;
     const int64_t slot = min((uint32_t)row[kin ? k : 0], max_slot);   // a slot past the pool reads the last one
     sl[lane] = (int32_t)slot;
-    const float* krow = kpool + (slot * hkv + g) * D;
+    const PT* krow = kpool + (slot * hkv + g) * D;
     __syncthreads();
 #pragma unroll
     for (int t = 0; t < kF32Tile; ++t) {
       if (t < nq) {  // uniform across the wave
         const int pos = p + j0 + t;
         float dot = 0.f;
-        for (int dd = 0; dd < D; ++dd) dot = fmaf(qs[t][dd], krow[dd], dot);
-        const float s = (kin && k <= pos) ? dot * scale_log2 : -INFINITY;
+        for (int dd = 0; dd < D; ++dd) dot = fmaf(qs[t][dd], elem_f(krow[dd]), dot);
+        const float s = (kin && k <= pos) ? dot * kmul : -INFINITY;
         const float mn = fmaxf(m[t], wave_max64(s));   // finite: kv 0 is visible to every row
         const float alpha = exp2f(m[t] - mn);
         const float pk = exp2f(s - mn);
@@ -122,7 +136,7 @@ __global__ __launch_bounds__(64) void extend_f32(const float* __restrict__ q, fl
         for (int i = 0; i < PER; ++i) {
           float a = acc[t][i] * alpha;
           for (int kk = 0; kk < nk; ++kk)
-            a = fmaf(ps[kk], vpool[((int64_t)sl[kk] * hkv + g) * D + lane + 64 * i], a);
+            a = fmaf(ps[kk], elem_f(vpool[((int64_t)sl[kk] * hkv + g) * D + lane + 64 * i]), a);
           acc[t][i] = a;
         }
         m[t] = mn;
@@ -133,9 +147,9 @@ __global__ __launch_bounds__(64) void extend_f32(const float* __restrict__ q, fl
 #pragma unroll
   for (int t = 0; t < kF32Tile; ++t) {
     if (t < nq) {
-      const float inv = 1.f / l[t];
+      const float inv = vmul / l[t];
 #pragma unroll
-      for (int i = 0; i < PER; ++i) o[((qrow0 + t) * hq + h) * D + lane + 64 * i] = acc[t][i] * inv;
+      for (int i = 0; i < PER; ++i) put_f(o + ((qrow0 + t) * hq + h) * D + lane + 64 * i, acc[t][i] * inv);
     }
   }
 }
@@ -1045,6 +1059,7 @@ extern "C" int32_t pkv_extend_tile(int32_t qo_dtype, int32_t pool_dtype, int32_t
   if (hq <= 0 || hkv <= 0 || hq % hkv) return PKV_ERR_INVAL;
   const int G = hq / hkv;
   if (qo_dtype == PKV_F32 && pool_dtype == PKV_F32 && (d == 64 || d == 128)) return kF32Tile;
+  if (qo_dtype == PKV_BF16 && (pool_dtype == PKV_BF16 || pool_dtype == PKV_FP8_E4M3) && d == 64) return kF32Tile;
   if (qo_dtype == PKV_BF16 && (pool_dtype == PKV_BF16 || pool_dtype == PKV_FP8_E4M3) && d == 128 &&
       (G == 1 || G == 2 || G == 4 || G == 8))
     return mfma_tile(G);
@@ -1107,23 +1122,32 @@ extern "C" int pkv_extend_attention(const void* q, void* o, int32_t qo_dtype, co
                 pool_dtype, hq, hkv, d);
   if (pool_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale)) return fail(PKV_ERR_INVAL, "extend: fp8 pool needs scales");
   if (!(sm_scale > 0.f)) return fail(PKV_ERR_INVAL, "extend: sm_scale must be positive");
-  if ((int64_t)n_work * (qo_dtype == PKV_F32 ? hq : hkv) > 0x7FFFFFFFLL) return fail(PKV_ERR_INVAL, "extend: grid too large");
+  if ((int64_t)n_work * (qo_dtype == PKV_F32 || d == 64 ? hq : hkv) > 0x7FFFFFFFLL)
+    return fail(PKV_ERR_INVAL, "extend: grid too large");
   hipStream_t st = (hipStream_t)stream;
   const float sc = sm_scale * kLog2e;
   const int G = hq / hkv;
-  if (qo_dtype == PKV_F32) {
+  if (qo_dtype == PKV_F32 || d == 64) {
     if (num_slots > 0x7FFFFFFFLL) return fail(PKV_ERR_UNSUPPORTED, "extend: pool beyond int32 slots");
     const uint32_t mslot = (uint32_t)(num_slots - 1);
     const dim3 grid((unsigned)(n_work * hq));
-    if (d == 64)
-      hipLaunchKernelGGL((extend_f32<64>), grid, dim3(64), 0, st, (const float*)q, (float*)o, (const float*)k_pool,
-                         (const float*)v_pool, req_to_token, stride, prefix_lens, extend_lens, qo_indptr, work, hq,
-                         hkv, sc, mslot);
+    if (qo_dtype == PKV_F32 && d == 64)
+      hipLaunchKernelGGL((extend_vec<float, float, 64>), grid, dim3(64), 0, st, (const float*)q, (float*)o,
+                         (const float*)k_pool, (const float*)v_pool, k_scale, v_scale, req_to_token, stride,
+                         prefix_lens, extend_lens, qo_indptr, work, hq, hkv, sc, mslot);
+    else if (qo_dtype == PKV_F32)
+      hipLaunchKernelGGL((extend_vec<float, float, 128>), grid, dim3(64), 0, st, (const float*)q, (float*)o,
+                         (const float*)k_pool, (const float*)v_pool, k_scale, v_scale, req_to_token, stride,
+                         prefix_lens, extend_lens, qo_indptr, work, hq, hkv, sc, mslot);
+    else if (pool_dtype == PKV_BF16)
+      hipLaunchKernelGGL((extend_vec<bf16, bf16, 64>), grid, dim3(64), 0, st, (const bf16*)q, (bf16*)o,
+                         (const bf16*)k_pool, (const bf16*)v_pool, k_scale, v_scale, req_to_token, stride,
+                         prefix_lens, extend_lens, qo_indptr, work, hq, hkv, sc, mslot);
     else
-      hipLaunchKernelGGL((extend_f32<128>), grid, dim3(64), 0, st, (const float*)q, (float*)o, (const float*)k_pool,
-                         (const float*)v_pool, req_to_token, stride, prefix_lens, extend_lens, qo_indptr, work, hq,
-                         hkv, sc, mslot);
-    return hip_check(hipGetLastError(), "extend_f32 launch");
+      hipLaunchKernelGGL((extend_vec<bf16, uint8_t, 64>), grid, dim3(64), 0, st, (const bf16*)q, (bf16*)o,
+                         (const uint8_t*)k_pool, (const uint8_t*)v_pool, k_scale, v_scale, req_to_token, stride,
+                         prefix_lens, extend_lens, qo_indptr, work, hq, hkv, sc, mslot);
+    return hip_check(hipGetLastError(), "extend_vec launch");
   }
   const int64_t slot_bytes = (int64_t)hkv * (pool_dtype == PKV_FP8_E4M3 ? 128 : 256);
   const int64_t table_bytes = (int64_t)num_reqs * stride * 4;

@@ -170,10 +170,10 @@ def _edge_workload(qo):
                               np.zeros((0, 5), np.int32), np.zeros((0, 5), np.int64), vt)
 
 
-def _shape_workload(hq, hkv, pool):
+def _shape_workload(hq, hkv, pool, d=128):
     """A shared 300-token prefix, five suffixes of 1-200 tokens and 3 decode steps for one head
     layout: every group size and kv-head count the kernels dispatch on."""
-    shape = workloads.Shape(hq, hkv, 128, "bf16", pool, 1 / math.sqrt(128))
+    shape = workloads.Shape(hq, hkv, d, "bf16", pool, 1 / math.sqrt(d))
     rng = np.random.default_rng(hq * 100 + hkv)
     b = workloads._Builder(rng, 5000)
     pre = b.segment(0, 300)
@@ -198,6 +198,21 @@ def test_head_layouts_every_row(hq, hkv, pool):
     stats = Run(_shape_workload(hq, hkv, pool), check_pool=True).run()
     report(f"head layout {hq}/{hkv} {pool}", stats)
     assert {s["kind"] for s in stats} == {"extend", "decode"}
+
+
+@pytest.mark.parametrize("hq,hkv,pool", [(32, 8, "bf16"), (16, 16, "fp8_e4m3"), (24, 8, "bf16")])
+def test_head_dim_64_every_row(hq, hkv, pool):
+    """Head dim 64 with bf16 q/o (the VALU extend kernel, the d = 64 split kernels; no
+    shared-prefix pass at this head dim), including a group size of 3 for extend."""
+    log(f"head dim 64 {hq}/{hkv} {pool}")
+    wl = _shape_workload(hq, hkv, pool, d=64)
+    if hq // hkv == 3:   # decode takes group sizes 1, 2, 4 and 8 only
+        wl.decode_tokens = wl.decode_tokens[:0]
+        wl.decode_rows = wl.decode_rows[:0]
+    stats = Run(wl, check_pool=True).run()
+    report(f"head dim 64 {hq}/{hkv} {pool}", stats)
+    kinds = {s["kind"] for s in stats}
+    assert "extend" in kinds and (hq // hkv == 3 or "decode" in kinds)
 
 
 @pytest.mark.parametrize("qo", ["bf16", "f32"])

@@ -57,7 +57,7 @@ def scatter(**kw):
     (dict(num_reqs=-1), INVAL),
     (dict(stride=0), INVAL),
     (dict(q=None), INVAL),
-    (dict(d=64), UNSUP),                        # bf16 path is d = 128 only
+    (dict(d=96), UNSUP),                        # head dims 64 and 128 only
     (dict(hq=24, hkv=8), UNSUP),                # group size 3
     (dict(pool=PKV_FP8_E4M3), INVAL),           # fp8 pool without scales
     (dict(sm=0.0), INVAL),
@@ -81,7 +81,7 @@ def test_extend_empty_is_a_no_op():
     (dict(ws_bytes=16), INVAL),                 # workspace too small
     (dict(pool=PKV_FP8_E4M3), INVAL),           # fp8 pool without scales
     (dict(ws=None), INVAL),
-    (dict(d=64), UNSUP),
+    (dict(d=96), UNSUP),
 ])
 def test_decode_rejects(kw, code):
     assert decode(**kw) == code
@@ -158,3 +158,7 @@ def test_workspace_and_chunk_helpers():
     assert lib.pkv_extend_tile(PKV_BF16, PKV_BF16, 32, 32, 128) == 128
     assert lib.pkv_extend_tile(PKV_F32, PKV_F32, 8, 8, 64) > 0
     assert lib.pkv_extend_tile(PKV_BF16, PKV_BF16, 24, 8, 128) == UNSUP
+    # head dim 64 with bf16 q/o: the VALU kernel, 16 query tokens per work item, any group size
+    assert lib.pkv_extend_tile(PKV_BF16, PKV_BF16, 32, 8, 64) == 16
+    assert lib.pkv_extend_tile(PKV_BF16, PKV_FP8_E4M3, 24, 8, 64) == 16
+    assert lib.pkv_extend_tile(PKV_BF16, PKV_BF16, 32, 8, 96) == UNSUP
