@@ -209,6 +209,7 @@ class PathBench:
         self.torch = torch
         kw = {"steps": max(32, total_steps)} if wl_name == "decode_bf16" else {}
         self.wl = wl = workloads.make(wl_name, **kw)
+        self.wl_kw = kw
         self.name = wl_name
         self.decode_only = not wl.extend_attention
         s = wl.shape
@@ -551,17 +552,6 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def blas_threads() -> int:
-    try:
-        import threadpoolctl
-        info = [x for x in threadpoolctl.threadpool_info() if x.get("user_api") == "blas"]
-        if info:
-            return int(info[0]["num_threads"])
-    except Exception:
-        pass
-    return 1
-
-
 def main_job(a, torch):
     import prefix_shared_kv_match_amd as pkv
     b = JobBench(torch, a)
@@ -620,44 +610,79 @@ def main_job(a, torch):
     return 0
 
 
-def cpu_baseline(wl, hb, n_req, decode_only=False, steps_done=0, min_seconds=10.0, rows_per_req=0):
-    """The float64 oracle on a bounded sample, repeated until at least min_seconds of CPU work:
-    the extend rows of the first n_req requests (with rows_per_req > 0, that many rows of each,
-    a seeded sample that holds the first and last), or (decode workload) the newest decode row
-    of the first n_req sequences over their whole current context."""
+def _cpu_worker(job):
+    """One process of the CPU baseline: the oracle over its share of the sample (one BLAS
+    thread), repeated until at least min_seconds of work; returns (query tokens, seconds)."""
+    name, kw, decode_only, items, min_seconds = job
+    import workloads
     from oracle import attention as oa
-    threads = blas_threads()
+    wl = workloads.make(name, **kw)
+    reqs = wl.batches[-1]
+    n, t0 = 0, time.perf_counter()
+    while True:
+        for it in items:
+            if decode_only:
+                i, steps = it
+                oa.decode_row(wl, np.concatenate([reqs[i].rows, wl.decode_rows[:steps, i]]))
+                n += 1
+            else:
+                i, p, pos = it
+                oa.extend_rows(wl, reqs[i], p, sample=pos)
+                n += len(pos)
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            return n, dt
+
+
+def cpu_baseline(wl, wl_kw, hb, n_req, decode_only=False, steps_done=0, min_seconds=10.0, rows_per_req=0,
+                 max_workers=16):
+    """The float64 oracle on a bounded sample in a pool of processes with one BLAS thread each
+    (at most max_workers, the host cores a one-GPU job gets): the extend rows of the first n_req
+    requests (with rows_per_req > 0, that many rows of each, a seeded sample that holds the
+    first and last), or (decode workload) the newest decode row of the first n_req sequences
+    over their whole current context.  Work is cut into (request, rows) units dealt round-robin
+    to the processes; each repeats its share until min_seconds have passed, and the rate is the
+    tokens done over the longest process's time."""
+    import multiprocessing
+    from concurrent.futures import ProcessPoolExecutor
     reqs = wl.batches[-1][:n_req]
+    workers = max(1, min(max_workers, os.cpu_count() or 1))
     rng = np.random.default_rng(0)
-    picks = []
+    units = []
     for i, r in enumerate(reqs):
+        if decode_only:
+            units.append((i, int(steps_done)))
+            continue
         p = int(hb.prefix_lens[i])
         pos = np.arange(p, len(r.tokens))
         if rows_per_req and pos.size > rows_per_req:
             mid = rng.choice(pos[1:-1], size=rows_per_req - 2, replace=False)
             pos = np.sort(np.concatenate([[pos[0], pos[-1]], mid]))
-        picks.append(pos)
-    t0 = time.perf_counter()
-    rows, passes = 0, 0
-    while True:
-        for i, r in enumerate(reqs):
-            if decode_only:
-                oa.decode_row(wl, np.concatenate([r.rows, wl.decode_rows[:steps_done, i]]))
-                rows += 1
+        parts = max(1, min(pos.size, -(-workers // max(len(reqs), 1))))
+        units += [(i, p, c) for c in np.array_split(pos, parts) if c.size]
+    workers = min(workers, len(units))
+    shares = [units[w::workers] for w in range(workers)]
+    saved = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
+    os.environ.update({k: "1" for k in saved})
+    try:
+        with ProcessPoolExecutor(workers, mp_context=multiprocessing.get_context("spawn")) as ex:
+            res = list(ex.map(_cpu_worker, [(wl.name, wl_kw, decode_only, sh, min_seconds) for sh in shares]))
+    finally:
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
             else:
-                oa.extend_rows(wl, r, int(hb.prefix_lens[i]), sample=picks[i])
-                rows += picks[i].size
-        passes += 1
-        dt = time.perf_counter() - t0
-        if dt >= min_seconds:
-            break
+                os.environ[k] = v
+    rows = sum(n for n, _ in res)
+    dt = max(t for _, t in res)
     what = "newest decode row" if decode_only else (
         f"{rows_per_req} sampled extend rows" if rows_per_req else "extend rows")
-    return {"value": rows / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "cpu_model": cpu_model(),
-            "sample": f"float64 numpy oracle (BLAS threads = {threads}, {cpu_model()}): {what} of the first "
-                      f"{len(reqs)} of {len(wl.batches[-1])} {'sequences' if decode_only else 'requests'} over "
-                      f"their full contexts, {passes} pass(es), {rows} query tokens in {dt:.1f} s"}
+    return {"value": rows / dt, "unit": "tokens/s", "cores": workers, "kind": "oracle", "cpu_model": cpu_model(),
+            "sample": f"float64 numpy oracle in {workers} processes of one BLAS thread each ({cpu_model()}): {what} "
+                      f"of the first {len(reqs)} of {len(wl.batches[-1])} "
+                      f"{'sequences' if decode_only else 'requests'} over their full contexts, cut into "
+                      f"{len(units)} (request, rows) units; {rows} query tokens, the longest process "
+                      f"{dt:.1f} s"}
 
 
 def main():
@@ -801,7 +826,8 @@ def main():
     }
     if not a.no_cpu_baseline:
         rows = a.cpu_rows if a.cpu_rows >= 0 else (16 if wl.name == "longctx_fp8" else 0)
-        out["cpu_baseline"] = cpu_baseline(wl, hb, a.cpu_sample, b.decode_only, timed_step_i, rows_per_req=rows)
+        out["cpu_baseline"] = cpu_baseline(wl, b.wl_kw, hb, a.cpu_sample, b.decode_only, timed_step_i,
+                                           rows_per_req=rows)
     print(json.dumps(out), flush=True)
     return 0
 

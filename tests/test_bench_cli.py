@@ -5,6 +5,8 @@ import os
 import subprocess
 import sys
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
 
@@ -43,3 +45,18 @@ def test_default_workload_is_the_long_context_case(monkeypatch):
     monkeypatch.setattr(sys, "argv", ["bench.py"])
     a = bench.parse()
     assert a.workload == "longctx_fp8" and a.gpus == 1
+
+
+def test_cpu_baseline_process_pool():
+    """The CPU baseline runs the oracle in a pool of one-thread processes over (request, rows)
+    units and reports the tokens done over the longest process's time."""
+    import types
+    import workloads
+    wl = workloads.make("fewshot_bf16")
+    hb = types.SimpleNamespace(prefix_lens=np.zeros(len(wl.batches[-1]), dtype=np.int32))
+    out = bench.cpu_baseline(wl, {}, hb, 2, min_seconds=0.2, rows_per_req=6, max_workers=3)
+    assert out["kind"] == "oracle" and out["unit"] == "tokens/s" and out["cores"] == 3
+    assert out["value"] > 0 and "3 processes" in out["sample"] and "6 sampled extend rows" in out["sample"]
+    dec = bench.cpu_baseline(workloads.make("decode_bf16", steps=2), {"steps": 2}, None, 2, decode_only=True,
+                             steps_done=1, min_seconds=0.1, max_workers=2)
+    assert dec["cores"] == 2 and dec["value"] > 0 and "newest decode row" in dec["sample"]
