@@ -31,6 +31,7 @@
 
 #include <algorithm>
 #include <mutex>
+#include <type_traits>
 
 #include "device.h"
 
@@ -501,16 +502,18 @@ __device__ __forceinline__ float wave_sum(float x) {
 
 // One wave per (sequence, q head): merge that head's chunk partials.  A partial with running
 // max -inf is empty (a later chunk of a shared-prefix span): it has no weight and its row,
-// never written, is not read.  The (m, l) pairs of 64 chunks come in with one load per lane;
-// the rows of the partials that carry weight (found with a ballot) are then gathered U at a
-// time with all U loads in flight, so a sequence with many chunks, most of them empty, costs
-// a few round trips rather than one per group of chunks.
+// never written, is not read.  The (m, l) pairs of the first 64 R chunks come in with R loads
+// per lane, all in flight together, and stay in registers; the rows of the partials that
+// carry weight (found with a ballot per 64 chunks) are then gathered U at a time with all U
+// loads in flight, so a sequence with many chunks, most of them empty, costs a few round
+// trips rather than one per group of chunks.
 template <typename OT, int D>
 __global__ __launch_bounds__(256) void decode_reduce(const float* __restrict__ ws_ml, const float* __restrict__ ws_acc,
                                                      const int32_t* __restrict__ seq_lens, int batch, int hq,
                                                      int chunk, int max_splits, OT* __restrict__ o) {
   constexpr int PER = D / 64;
-  constexpr int U = 16;
+  constexpr int U = 32;
+  constexpr int R = 4;
   const int lane = threadIdx.x & 63;
   const int idx = blockIdx.x * kWaves + (threadIdx.x >> 6);
   if (idx >= batch * hq) return;
@@ -518,42 +521,69 @@ __global__ __launch_bounds__(256) void decode_reduce(const float* __restrict__ w
   const int ns = min((seq_lens[b] + chunk - 1) / chunk, max_splits);
   const float* ml = ws_ml + (int64_t)idx * max_splits * 2;
   const float* acc = ws_acc + (int64_t)idx * max_splits * D + lane * PER;
-  float M = -INFINITY;
-  for (int s = lane; s < ns; s += 64) M = fmaxf(M, ml[2 * s]);
+  float mr[R], lr[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int s = lane + 64 * r;
+    const float2 v = s < ns ? *(const float2*)(ml + 2 * s) : float2{-INFINITY, 0.f};
+    mr[r] = v.x;
+    lr[r] = v.y;
+  }
+  float M = mr[0];
+#pragma unroll
+  for (int r = 1; r < R; ++r) M = fmaxf(M, mr[r]);
+  for (int s = lane + 64 * R; s < ns; s += 64) M = fmaxf(M, ml[2 * s]);
   M = wave_max(M);
   float lsum = 0.f;
   float out[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) out[i] = 0.f;
-  for (int s0 = 0; s0 < ns; s0 += 64) {
+  for (int s0 = 0, r = 0; s0 < ns; s0 += 64, ++r) {
     const int s = s0 + lane;
-    const float m = s < ns ? ml[2 * s] : -INFINITY;
+    float m, l;
+    if (r < R) {   // the same in every lane
+      m = mr[0];
+      l = lr[0];
+#pragma unroll
+      for (int k = 1; k < R; ++k)
+        if (r == k) {
+          m = mr[k];
+          l = lr[k];
+        }
+    } else {
+      m = s < ns ? ml[2 * s] : -INFINITY;
+      l = s < ns ? ml[2 * s + 1] : 0.f;
+    }
     const bool used = m != -INFINITY;
     const float w = used ? exp2f(m - M) : 0.f;
-    if (used) lsum = fmaf(w, ml[2 * s + 1], lsum);
+    if (used) lsum = fmaf(w, l, lsum);
     uint64_t mask = __ballot(used);   // the same in every lane
-    while (mask) {
+    // U rows at a time: many partials in 32s, the last few in 8s
+    auto gather = [&](auto uu) {
+      constexpr int UU = decltype(uu)::value;
       const int j0 = __builtin_ctzll(mask);
-      int js[U];
+      int js[UU];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
+      for (int u = 0; u < UU; ++u) {
         js[u] = mask ? __builtin_ctzll(mask) : -1;   // -1: padding, weight 0, re-reads chunk j0
         mask &= mask - 1;
       }
-      float av[U][PER];
+      float av[UU][PER];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
+      for (int u = 0; u < UU; ++u) {
         const int j = js[u] < 0 ? j0 : js[u];
 #pragma unroll
         for (int i = 0; i < PER; ++i) av[u][i] = acc[(int64_t)(s0 + j) * D + i];
       }
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
+      for (int u = 0; u < UU; ++u) {
         const float wu = js[u] < 0 ? 0.f : __shfl(w, js[u]);
 #pragma unroll
         for (int i = 0; i < PER; ++i) out[i] = fmaf(wu, av[u][i], out[i]);
       }
-    }
+    };
+    while (__builtin_popcountll(mask) > 8) gather(std::integral_constant<int, U>{});
+    while (mask) gather(std::integral_constant<int, 8>{});
   }
   lsum = wave_sum(lsum);
   const float inv = 1.f / lsum;
