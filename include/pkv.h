@@ -244,6 +244,24 @@ int rt_finish(rt_tree* t, int32_t n, const int32_t* tokens, const int64_t* tok_i
               const int32_t* req_to_token, int64_t stride, const int32_t* prompt_lens,
               const rt_node* prompt_last, rt_node* out_end);
 
+/* One round of the serve loop [OV and EX: cache-aware scheduling, waiting requests served
+ * longest cached prefix first rather than first come first served].  Requests
+ * tokens[tok_indptr[r] .. tok_indptr[r+1]), r < num_reqs, arrive in index order; after[r] is
+ * a request that must be scheduled in an earlier round (a conversation's previous turn), or
+ * -1; scheduled[r] (0/1, host) marks those served in earlier rounds.  The waiting queue is
+ * the `window` lowest-indexed requests not yet scheduled; the ready ones (after[r] < 0 or
+ * scheduled[after[r]]) are taken in index order (order RT_ORDER_FCFS) or by descending
+ * rt_peek_prefix length, ties in index order (RT_ORDER_LPM), and the first `batch` of them
+ * are written to out_pick (caller-owned, capacity batch).  The tree is not changed (the
+ * caller prepares, runs and releases the round, then marks its picks scheduled).  Returns
+ * the number picked (0 once every request is scheduled); PKV_ERR_INVAL on bad arguments, an
+ * after[r] not below r, or a queue with no ready request. */
+#define RT_ORDER_FCFS 0
+#define RT_ORDER_LPM 1
+int32_t rt_serve_round(const rt_tree* t, int32_t num_reqs, const int32_t* tokens, const int64_t* tok_indptr,
+                       const int32_t* after, const uint8_t* scheduled, int32_t window, int32_t order, int32_t batch,
+                       int32_t* out_pick);
+
 /* One launch of chunked prefill (a cap of `budget` new tokens per extend launch) [the
  * deployment-tuning page's chunked-prefill option; requests keep their order]: from request
  * `head` on, each request contributes min(its tokens not yet prefilled, budget left) and the

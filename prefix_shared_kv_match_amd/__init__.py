@@ -22,7 +22,7 @@ __all__ = [
     "rt_evict", "rt_alloc", "rt_free", "rt_take_eviction_log", "rt_set_eviction_log", "rt_evictable_size",
     "rt_protected_size",
     "rt_free_size", "rt_clock", "rt_copy_free_list", "rt_dump", "rt_prepare_extend", "rt_release",
-    "rt_decode_step", "rt_finish", "pkv_kv_scatter", "pkv_append_slots", "pkv_extend_tile", "pkv_extend_plan",
+    "rt_decode_step", "rt_finish", "rt_serve_round", "rt_chunk_launch", "pkv_kv_scatter", "pkv_append_slots", "pkv_extend_tile", "pkv_extend_plan",
     "pkv_extend_attention", "pkv_decode_chunk", "pkv_decode_workspace_bytes", "pkv_decode_attention",
     "pkv_decode_shared_rows", "pkv_decode_shared_plan", "pkv_decode_attention_shared",
     "pkv_decode_attention_static", "PKV_DECODE_STATIC_SCRATCH_BYTES",
@@ -283,6 +283,28 @@ def rt_chunk_launch(t, tokens: np.ndarray, tok_indptr: np.ndarray, done, head: i
     k = int(check(lib().rt_chunk_launch(t, n, _ptr(toks), _ptr(ip), _ptr(dn), int(head), int(budget), _ptr(reqs),
                                         _ptr(ends))))
     return reqs[:k], ends[:k]
+
+
+RT_ORDERS = {"fcfs": 0, "lpm": 1}
+
+
+def rt_serve_round(t, tokens: np.ndarray, tok_indptr: np.ndarray, after, scheduled, window: int, order: str,
+                   batch: int) -> np.ndarray:
+    """One serve round: the requests picked from the `window` oldest unscheduled ones (ready
+    ones only), in arrival order ("fcfs") or longest cached prefix first ("lpm")."""
+    if order not in RT_ORDERS:
+        raise ValueError(f"unknown scheduling order {order!r}")
+    ip = np.ascontiguousarray(tok_indptr, dtype=np.int64)
+    n = int(ip.size - 1)
+    af = _i32(after)
+    sc = np.ascontiguousarray(scheduled, dtype=np.uint8)
+    if af.size != n or sc.size != n:
+        raise ValueError("rt_serve_round: after and scheduled must hold one entry per request")
+    toks = _i32(tokens)
+    pick = np.empty(max(int(batch), 1), dtype=np.int32)
+    k = int(check(lib().rt_serve_round(t, n, _ptr(toks), _ptr(ip), _ptr(af), _ptr(sc), int(window),
+                                       RT_ORDERS[order], int(batch), _ptr(pick))))
+    return pick[:k]
 
 
 # ------------------------------------------------------------------------------------------

@@ -511,6 +511,47 @@ int rt_schedule_longest_prefix(const rt_tree* t, int32_t num_reqs, const int32_t
   });
 }
 
+int32_t rt_serve_round(const rt_tree* t, int32_t num_reqs, const int32_t* tokens, const int64_t* tok_indptr,
+                       const int32_t* after, const uint8_t* scheduled, int32_t window, int32_t order, int32_t batch,
+                       int32_t* out_pick) {
+  return guard([&]() -> int32_t {
+    if (!t || num_reqs < 0 || window < 1 || batch < 1 || (order != RT_ORDER_FCFS && order != RT_ORDER_LPM) ||
+        (num_reqs > 0 && (!tokens || !tok_indptr || !after || !scheduled || !out_pick)))
+      return pkv::fail(PKV_ERR_INVAL, "bad arguments to rt_serve_round");
+    // the waiting queue: the `window` oldest requests not yet scheduled; of those, the ones
+    // whose predecessor was scheduled in an earlier round (or that have none)
+    std::vector<int32_t> ready;
+    int32_t waiting = 0;
+    for (int32_t r = 0; r < num_reqs && waiting < window; ++r) {
+      if (scheduled[r]) continue;
+      ++waiting;
+      const int32_t a = after[r];
+      if (a >= r) return pkv::fail(PKV_ERR_INVAL, "request %d waits for request %d, which is not earlier", r, a);
+      if (a < 0 || scheduled[a]) ready.push_back(r);
+    }
+    if (waiting == 0) return 0;
+    if (ready.empty()) return pkv::fail(PKV_ERR_INVAL, "no waiting request is ready");
+    if (order == RT_ORDER_LPM) {
+      std::vector<int64_t> m(ready.size());
+      for (size_t i = 0; i < ready.size(); ++i) {
+        const int32_t r = ready[i];
+        const int64_t L = tok_indptr[r + 1] - tok_indptr[r];
+        if (L < 0) return pkv::fail(PKV_ERR_INVAL, "request %d has a negative length", r);
+        m[i] = t->peek(tokens + tok_indptr[r], L);
+      }
+      std::vector<size_t> idx(ready.size());
+      for (size_t i = 0; i < idx.size(); ++i) idx[i] = i;
+      std::stable_sort(idx.begin(), idx.end(), [&](size_t a, size_t b) { return m[a] > m[b]; });
+      std::vector<int32_t> sorted(ready.size());
+      for (size_t i = 0; i < idx.size(); ++i) sorted[i] = ready[idx[i]];
+      ready.swap(sorted);
+    }
+    const int32_t k = std::min<int32_t>(batch, (int32_t)ready.size());
+    std::copy(ready.begin(), ready.begin() + k, out_pick);
+    return k;
+  });
+}
+
 int32_t rt_chunk_launch(const rt_tree* t, int32_t num_reqs, const int32_t* tokens, const int64_t* tok_indptr,
                         const int64_t* done, int32_t head, int64_t budget, int32_t* out_reqs, int64_t* out_ends) {
   return guard([&]() -> int32_t {

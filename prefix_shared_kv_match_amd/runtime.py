@@ -22,8 +22,8 @@ import numpy as np
 from . import (PKV_BF16, PKV_F32, PKV_FP8_E4M3, PKV_NO_SPLIT_PHASE, check, lib, pkv_decode_chunk,
                pkv_decode_first_split, pkv_decode_plan, pkv_decode_shared_rows, pkv_decode_workspace_bytes,
                pkv_extend_plan, pkv_extend_tile, rt_chunk_launch, rt_create_policy, rt_dec_lock_ref, rt_decode_step,
-               rt_destroy, rt_finish, rt_prepare_extend, rt_prepare_extend_prio, rt_release,
-               rt_schedule_longest_prefix, rt_set_eviction_log)
+               rt_destroy, rt_finish, rt_prepare_extend, rt_prepare_extend_prio, rt_release, rt_serve_round,
+               rt_set_eviction_log)
 
 _DT = {"f32": PKV_F32, "bf16": PKV_BF16, "fp8_e4m3": PKV_FP8_E4M3}
 
@@ -478,43 +478,25 @@ def prepare_prio(tree, token_lists: Sequence[np.ndarray], stride: int, prioritie
 
 def serve(tree, token_lists: Sequence[np.ndarray], after: Sequence[int], order: str, batch: int, window: int,
           stride: int, priorities=None, on_batch=None):
-    """Cache-aware serve loop over a fixed arrival order (one batch per round).
-
-    The scheduler sees the `window` oldest requests not yet scheduled; a request whose
-    `after` request has not been scheduled in an earlier round waits.  `order` "fcfs" takes
-    the eligible requests in arrival order, "lpm" by descending cached prefix
-    (rt_schedule_longest_prefix, ties in arrival order).  Each round's batch is prepared,
-    handed to on_batch(pick, host_batch) for its device work, and released.
-    Returns [(pick, host_batch)] in round order."""
-    if order not in ("fcfs", "lpm"):
-        raise ValueError(f"unknown scheduling order {order!r}")
-    if batch < 1 or window < 1:
-        raise ValueError("batch and window must be positive")
-    n = len(token_lists)
-    scheduled = np.zeros(n, dtype=bool)
-    nxt, queue, out = 0, [], []
-    while nxt < n or queue:
-        while nxt < n and len(queue) < window:
-            queue.append(nxt)
-            nxt += 1
-        elig = [i for i in queue if after[i] < 0 or scheduled[after[i]]]
-        if not elig:
-            raise RuntimeError("no eligible request (a dependency points forward)")
-        if order == "lpm":
-            toks, indptr = flatten([token_lists[i] for i in elig])
-            ordr, _ = rt_schedule_longest_prefix(tree, toks, indptr)
-            pick = [elig[j] for j in ordr[:batch]]
-        else:
-            pick = elig[:batch]
+    """Cache-aware serve loop over a fixed arrival order, one batch per round: the library
+    picks each round (rt_serve_round: the `window` oldest unscheduled requests, those whose
+    `after` request ran in an earlier round, in arrival order for "fcfs" or longest cached
+    prefix first for "lpm"); the batch is prepared, handed to on_batch(pick, host_batch) for
+    its device work, and released.  Returns [(pick, host_batch)] in round order."""
+    toks, indptr = flatten(token_lists)
+    scheduled = np.zeros(len(token_lists), dtype=np.uint8)
+    out = []
+    while True:
+        pick = rt_serve_round(tree, toks, indptr, after, scheduled, window, order, batch).tolist()
+        if not pick:
+            return out
         hb = prepare_prio(tree, [token_lists[i] for i in pick], stride,
                           None if priorities is None else [priorities[i] for i in pick])
         if on_batch is not None:
             on_batch(pick, hb)
         rt_release(tree, hb.last_nodes)
-        scheduled[pick] = True
-        queue = [i for i in queue if not scheduled[i]]
+        scheduled[pick] = 1
         out.append((pick, hb))
-    return out
 
 
 def chunked_prefill(tree, token_lists: Sequence[np.ndarray], budget: int, stride: int, on_launch=None):

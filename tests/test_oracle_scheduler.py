@@ -4,6 +4,8 @@
   batch driver over consecutive arrivals (itself pinned by the worked examples).
 - Two hand-derived traces on a 12-slot pool (derivations in the test bodies) fix the
   longest-prefix-first order, its eviction interplay and the chunk cut points.
+- A hand-derived serve trace (tests/golden/serve_window_dependency.json) fixes the waiting
+  window, a dependency and the tie rule in both orders.
 - Invariants on the multi-turn workload: every request is served once, never before the
   request it depends on, batches stay within size, and LPM's order is a valid sort.
 """
@@ -68,6 +70,31 @@ def test_lpm_order_and_ties():
     assert t.clock == clock                      # ordering reads the tree only
     with pytest.raises(OracleError):
         scheduler.schedule_order(t, reqs, "random")
+
+
+def _serve_hand():
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "serve_window_dependency.json")) as f:
+        return json.load(f)
+
+
+@pytest.mark.parametrize("case", _serve_hand()["cases"], ids=lambda c: f"w{c['window']}-{c['order']}-n{c['n']}")
+def test_serve_window_and_dependency_hand_trace(case):
+    """Serve rounds under a waiting window, a dependency (r2 waits for r0) and a tie of cached
+    prefix lengths, in both orders, against the hand derivation in the fixture."""
+    g = _serve_hand()
+    n = case["n"]
+    t = OracleTree(64)
+    bt = driver.prepare_batch(t, [g["cached"]])
+    driver.release(t, bt.last_nodes)
+    log = scheduler.serve(t, g["requests"][:n], g["after"][:n], case["order"], g["batch"], case["window"])
+    assert log.picks == case["picks"]
+    by_req = {}
+    for pick, tab in zip(log.picks, log.tables):
+        for r, pl in zip(pick, tab.prefix_lens):
+            by_req[r] = pl
+    assert [by_req[r] for r in range(n)] == case["prefix_by_request"]
 
 
 @pytest.mark.parametrize("order", scheduler.ORDERS)

@@ -1,6 +1,6 @@
-"""The library-side serve loop (rt_schedule_longest_prefix + rt_prepare_extend_prio) and
-chunked prefill (rt_peek_prefix + rt_prepare_extend) on the CPU: bit-exact with the oracle's
-scheduler (batch picks, slot tables, final tree, free list)."""
+"""The library-side serve loop (rt_serve_round + rt_prepare_extend_prio) and chunked prefill
+(rt_chunk_launch + rt_prepare_extend) on the CPU: bit-exact with the oracle's scheduler (batch
+picks, slot tables, final tree, free list), and on the hand-derived serve trace."""
 import numpy as np
 import pytest
 
@@ -49,9 +49,9 @@ def test_serve_rejects_bad_arguments():
     try:
         with pytest.raises(ValueError):
             runtime.serve(t, [np.array([1])], [-1], "random", 1, 1, 4)
-        with pytest.raises(ValueError):
+        with pytest.raises(pkv.PkvError, match="bad arguments"):
             runtime.serve(t, [np.array([1])], [-1], "fcfs", 0, 1, 4)
-        with pytest.raises(RuntimeError):
+        with pytest.raises(pkv.PkvError, match="not earlier"):      # a dependency that points forward
             runtime.serve(t, [np.array([1]), np.array([2])], [1, -1], "fcfs", 1, 1, 4)
     finally:
         pkv.rt_destroy(t)
@@ -101,5 +101,34 @@ def test_chunk_launch_hand_example():
             pkv.rt_chunk_launch(t, toks, indptr, [-1, -1], 0, 0)       # no budget
         with pytest.raises(pkv.PkvError):
             pkv.rt_chunk_launch(t, toks, indptr, [9, -1], 0, 4)       # more done than the request holds
+    finally:
+        pkv.rt_destroy(t)
+
+
+def _hand():
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "serve_window_dependency.json")) as f:
+        return json.load(f)
+
+
+@pytest.mark.parametrize("case", _hand()["cases"], ids=lambda c: f"w{c['window']}-{c['order']}-n{c['n']}")
+def test_serve_rounds_hand_example(case):
+    """The library's rounds (rt_serve_round) on the hand-derived serve trace
+    (tests/golden/serve_window_dependency.json) the oracle's serve loop is pinned to."""
+    g = _hand()
+    n = case["n"]
+    t = pkv.rt_create(64)
+    try:
+        hb = runtime.prepare_prio(t, [np.array(g["cached"])], 16, None)
+        pkv.rt_release(t, hb.last_nodes)
+        got = runtime.serve(t, [np.array(r) for r in g["requests"][:n]], g["after"][:n], case["order"], g["batch"],
+                            case["window"], 16)
+        assert [p for p, _ in got] == case["picks"]
+        by_req = {}
+        for p, hb in got:
+            for i, r in enumerate(p):
+                by_req[r] = int(hb.prefix_lens[i])
+        assert [by_req[r] for r in range(n)] == case["prefix_by_request"]
     finally:
         pkv.rt_destroy(t)
