@@ -507,13 +507,13 @@ __device__ __forceinline__ float wave_sum(float x) {
 // carry weight (found with a ballot per 64 chunks) are then gathered U at a time with all U
 // loads in flight, so a sequence with many chunks, most of them empty, costs a few round
 // trips rather than one per group of chunks.
-template <typename OT, int D>
+// U and R are template parameters: a launch whose sequences have at most 64 chunks takes
+// (U, R) = (8, 1), so the registers of the long-context gathers do not cost it occupancy.
+template <typename OT, int D, int U, int R>
 __global__ __launch_bounds__(256) void decode_reduce(const float* __restrict__ ws_ml, const float* __restrict__ ws_acc,
                                                      const int32_t* __restrict__ seq_lens, int batch, int hq,
                                                      int chunk, int max_splits, OT* __restrict__ o) {
   constexpr int PER = D / 64;
-  constexpr int U = 32;
-  constexpr int R = 4;
   const int lane = threadIdx.x & 63;
   const int idx = blockIdx.x * kWaves + (threadIdx.x >> 6);
   if (idx >= batch * hq) return;
@@ -582,7 +582,8 @@ __global__ __launch_bounds__(256) void decode_reduce(const float* __restrict__ w
         for (int i = 0; i < PER; ++i) out[i] = fmaf(wu, av[u][i], out[i]);
       }
     };
-    while (__builtin_popcountll(mask) > 8) gather(std::integral_constant<int, U>{});
+    if constexpr (U > 8)
+      while (__builtin_popcountll(mask) > 8) gather(std::integral_constant<int, U>{});
     while (mask) gather(std::integral_constant<int, 8>{});
   }
   lsum = wave_sum(lsum);
@@ -756,18 +757,24 @@ int decode_impl(const void* q, void* o, int32_t qo_dtype, const void* k_pool, co
     if (rc < 0) return rc;
   }
   const dim3 rgrid((unsigned)(((int64_t)batch * hq + kWaves - 1) / kWaves));
-  if (qo_dtype == PKV_F32 && d == 64)
-    hipLaunchKernelGGL((decode_reduce<float, 64>), rgrid, dim3(256), 0, st, ml, acc, seq_lens, batch, hq, chunk,
-                       max_splits, (float*)o);
-  else if (qo_dtype == PKV_F32)
-    hipLaunchKernelGGL((decode_reduce<float, 128>), rgrid, dim3(256), 0, st, ml, acc, seq_lens, batch, hq, chunk,
-                       max_splits, (float*)o);
-  else if (d == 64)
-    hipLaunchKernelGGL((decode_reduce<bf16, 64>), rgrid, dim3(256), 0, st, ml, acc, seq_lens, batch, hq, chunk,
-                       max_splits, (bf16*)o);
-  else
-    hipLaunchKernelGGL((decode_reduce<bf16, 128>), rgrid, dim3(256), 0, st, ml, acc, seq_lens, batch, hq, chunk,
-                       max_splits, (bf16*)o);
+  const bool few = max_splits <= 64;
+#define PKV_REDUCE(OT, DD)                                                                                     \
+  if (few)                                                                                                   \
+    hipLaunchKernelGGL((decode_reduce<OT, DD, 8, 1>), rgrid, dim3(256), 0, st, ml, acc, seq_lens, batch, hq, chunk, \
+                       max_splits, (OT*)o);                                                                  \
+  else                                                                                                       \
+    hipLaunchKernelGGL((decode_reduce<OT, DD, 32, 4>), rgrid, dim3(256), 0, st, ml, acc, seq_lens, batch, hq,     \
+                       chunk, max_splits, (OT*)o);
+  if (qo_dtype == PKV_F32 && d == 64) {
+    PKV_REDUCE(float, 64)
+  } else if (qo_dtype == PKV_F32) {
+    PKV_REDUCE(float, 128)
+  } else if (d == 64) {
+    PKV_REDUCE(bf16, 64)
+  } else {
+    PKV_REDUCE(bf16, 128)
+  }
+#undef PKV_REDUCE
   return hip_check(hipGetLastError(), "decode reduce launch");
 }
 
