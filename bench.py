@@ -119,6 +119,8 @@ def parse():
                     help="shared-prefix decode: give the private tails to the shared-prefix kernel too when items "
                          "and tails need at most this many workgroups (-1 = the engine's default, 0 = never)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode-batch", action="store_true",
+                    help="long-context line: skip the extra key timing one step of the 512-sequence decode batch")
     ap.add_argument("--cpu-sample", type=int, default=64, help="requests in the oracle's timed sample")
     ap.add_argument("--cpu-rows", type=int, default=-1,
                     help="extend rows per request in the oracle's timed sample (0 = all; -1 = 16 for the "
@@ -610,6 +612,32 @@ def main_job(a, torch):
     return 0
 
 
+def decode_batch_key(torch, warmup=20, steps=40):
+    """One decode step of the 512-sequence decode batch (contexts U[2048, 8192], 16 shared
+    1,024-token prefixes, bf16): the HBM-bound decode case, timed like the decode workload's
+    own line (HIP events around the decode span on the launch stream, after warmup steps).
+    Bytes are those of the last timed step's contexts."""
+    b = PathBench(torch, "decode_bf16", warmup + steps)
+    b.timer.live = {"decode_attention"}
+    for _ in range(warmup):
+        b.step()
+    b.timer.reset()
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        b.step()
+    torch.cuda.synchronize()
+    b.timer.collect()
+    hb, s = b.last_tables, b.wl.shape
+    ms = b.timer.avg_ms("decode_attention")
+    kv_tok = kv_row_bytes(s)
+    uniq = float(np.unique(np.concatenate([hb.req_to_token[i, :hb.seq_lens[i]] for i in range(hb.n)])).size) * kv_tok
+    hbm = traffic_bytes("decode_bf16", "decode_attention")
+    return {"workload": "decode_bf16", "sequences": int(hb.n), "steps": steps, "ms": ms,
+            "unique_kv_bytes": uniq, "unique_gbps": uniq / ms / 1e6, "frac_hbm_unique": uniq / ms / 1e6 / PEAK_HBM_GBPS,
+            "hbm_bytes": hbm, "hbm_gbps": None if hbm is None else hbm / ms / 1e6,
+            "frac_hbm": None if hbm is None else hbm / ms / 1e6 / PEAK_HBM_GBPS}
+
+
 def _cpu_worker(job):
     """One process of the CPU baseline: the oracle over its share of the sample (one BLAS
     thread), repeated until at least min_seconds of work; returns (query tokens, seconds)."""
@@ -824,9 +852,14 @@ def main():
         "hbm_practical_read_gbps": hbm_practical,
         "library": os.path.relpath(pkv._capi.LIB_PATH, ROOT),
     }
+    wl_kw, decode_only = b.wl_kw, b.decode_only
+    if wl.name == "longctx_fp8" and not a.no_decode_batch:
+        del b
+        torch.cuda.empty_cache()
+        out["decode_batch"] = decode_batch_key(torch)
     if not a.no_cpu_baseline:
         rows = a.cpu_rows if a.cpu_rows >= 0 else (16 if wl.name == "longctx_fp8" else 0)
-        out["cpu_baseline"] = cpu_baseline(wl, b.wl_kw, hb, a.cpu_sample, b.decode_only, timed_step_i,
+        out["cpu_baseline"] = cpu_baseline(wl, wl_kw, hb, a.cpu_sample, decode_only, timed_step_i,
                                            rows_per_req=rows)
     print(json.dumps(out), flush=True)
     return 0
