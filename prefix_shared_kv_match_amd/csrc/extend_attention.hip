@@ -249,7 +249,8 @@ struct WaveAttn {
   }
 
   // Rows of a decode item instead of extend rows: row r of the workgroup is the newest token
-  // of sequence members[m0 + r % BT] at head g * G + r / BT (nm real members), which sees
+  // of sequence members[m0 + r / G] at head g * G + r % G (nm real members, so rows 0 ..
+  // nm G - 1 are real and a wave whose 32 rows start at or past nm G has none), which sees
   // positions 0 .. seq_lens[b] - 1 (and none at or past kv_end, the end of the item's chunks).
   // A shared item's chunks lie inside every member's context, so its tiles never reach the mask;
   // a one-member item over a sequence's own last chunk masks the positions past its newest token.
@@ -261,9 +262,9 @@ struct WaveAttn {
     sc = scale;
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      const int r0 = 32 * wave + 16 * nb;
-      qh[nb] = g * G + r0 / BT;
-      qt[nb] = r0 % BT + ln;
+      const int r = 32 * wave + 16 * nb + ln;
+      qh[nb] = g * G + r % G;
+      qt[nb] = r / G;
       vis[nb] = kv_end - 1;   // padding rows see the whole item
       int b = qt[nb] < nm ? members[m0 + qt[nb]] : -1;
       const bool ok = b >= 0 && b < batch;   // a member index outside the batch is a padding row
@@ -947,7 +948,7 @@ __global__ __launch_bounds__(256, 2) void decode_shared_dma(const bf16* __restri
 
   WaveAttn<G> wa;
   wa.init_shared(q, members, seq_lens, m0, nm, batch, hq, g, wave, lane, scale_log2, kv_begin + n_tiles * kBN);
-  const bool active = G != 1 || 32 * wave < nm;
+  const bool active = 32 * wave < nm * G;   // a wave of only padding rows just stages
   const DmaOperands ops(ln, lg);
   const int first = item_first_visible(members, seq_lens, m0, nm, batch, kv_begin + n_tiles * kBN, lane);
   tile_loop<G>(wa, st, kv_begin, n_tiles, plain_tiles(kv_begin, first, n_tiles), active, k0s, k1s, v0s, v1s,
@@ -999,7 +1000,7 @@ __global__ __launch_bounds__(256, 2) void decode_shared_fp8(const bf16* __restri
   WaveAttn<G> wa;
   wa.init_shared(q, members, seq_lens, m0, nm, batch, hq, g, wave, lane, scale_log2 * kscale[g],
                  kv_begin + n_tiles * kBN);
-  const bool active = G != 1 || 32 * wave < nm;
+  const bool active = 32 * wave < nm * G;   // a wave of only padding rows just stages
   const Fp8Operands ops{ln, lg};
   const int first = item_first_visible(members, seq_lens, m0, nm, batch, kv_begin + n_tiles * kBN, lane);
   tile_loop<G>(wa, st, kv_begin, n_tiles, plain_tiles(kv_begin, first, n_tiles), active, k0s, k1s, v0s, v1s,
