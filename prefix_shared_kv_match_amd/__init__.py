@@ -22,7 +22,8 @@ __all__ = [
     "rt_evict", "rt_alloc", "rt_free", "rt_take_eviction_log", "rt_set_eviction_log", "rt_evictable_size",
     "rt_protected_size",
     "rt_free_size", "rt_clock", "rt_copy_free_list", "rt_dump", "rt_prepare_extend", "rt_release",
-    "rt_decode_step", "rt_finish", "rt_serve_round", "rt_chunk_launch", "pkv_kv_scatter", "pkv_append_slots", "pkv_extend_tile", "pkv_extend_plan",
+    "rt_decode_step", "rt_finish", "rt_serve_round", "rt_chunk_launch", "rt_chunk_prepare", "rt_chunk_finish",
+    "pkv_kv_scatter", "pkv_append_slots", "pkv_extend_tile", "pkv_extend_plan",
     "pkv_extend_attention", "pkv_decode_chunk", "pkv_decode_workspace_bytes", "pkv_decode_attention",
     "pkv_decode_shared_rows", "pkv_decode_shared_plan", "pkv_decode_attention_shared",
     "pkv_decode_attention_static", "PKV_DECODE_STATIC_SCRATCH_BYTES",
@@ -283,6 +284,44 @@ def rt_chunk_launch(t, tokens: np.ndarray, tok_indptr: np.ndarray, done, head: i
     k = int(check(lib().rt_chunk_launch(t, n, _ptr(toks), _ptr(ip), _ptr(dn), int(head), int(budget), _ptr(reqs),
                                         _ptr(ends))))
     return reqs[:k], ends[:k]
+
+
+def rt_chunk_prepare(t, tokens: np.ndarray, tok_indptr: np.ndarray, done: np.ndarray, held: np.ndarray, head: int,
+                     budget: int, req_to_token: np.ndarray):
+    """One chunked-prefill launch: (requests taken, chunk ends, prefix_lens, extend_lens,
+    qo_indptr, new_slots) for the taken requests, their rows written into req_to_token
+    [>= taken, stride]; done / held (int64 [num_reqs], -1 before the first launch) are
+    updated in place."""
+    ip = np.ascontiguousarray(tok_indptr, dtype=np.int64)
+    n = int(ip.size - 1)
+    if done.dtype != np.int64 or held.dtype != np.int64 or done.size != n or held.size != n \
+            or not done.flags.c_contiguous or not held.flags.c_contiguous:
+        raise ValueError("rt_chunk_prepare: done and held must be contiguous int64 [num_reqs]")
+    if req_to_token.dtype != np.int32 or req_to_token.ndim != 2 or not req_to_token.flags.c_contiguous:
+        raise ValueError("rt_chunk_prepare: req_to_token must be a contiguous int32 [rows, stride] array")
+    toks = _i32(tokens)
+    cap = max(n - int(head), 1)
+    if req_to_token.shape[0] < cap:
+        raise ValueError("rt_chunk_prepare: req_to_token needs a row per request that may be taken")
+    reqs = np.empty(cap, dtype=np.int32)
+    ends = np.empty(cap, dtype=np.int64)
+    pl = np.zeros(cap, dtype=np.int32)
+    el = np.zeros(cap, dtype=np.int32)
+    qo = np.zeros(cap + 1, dtype=np.int32)
+    new = np.empty(max(int(ip[-1]), 1), dtype=np.int32)
+    n_new = C.c_int64()
+    k = int(check(lib().rt_chunk_prepare(t, n, _ptr(toks), _ptr(ip), _ptr(done), _ptr(held), int(head), int(budget),
+                                         _ptr(req_to_token), req_to_token.shape[1], _ptr(pl), _ptr(el), _ptr(qo),
+                                         _ptr(new), new.size, _ptr(reqs), _ptr(ends), C.byref(n_new))))
+    return reqs[:k], ends[:k], pl[:k], el[:k], qo[:k + 1], new[:n_new.value]
+
+
+def rt_chunk_finish(t, tok_indptr: np.ndarray, reqs, done: np.ndarray, held: np.ndarray, head: int) -> int:
+    """After a launch's kernels: unlock the finished requests' end nodes; the new head."""
+    ip = np.ascontiguousarray(tok_indptr, dtype=np.int64)
+    rq = _i32(reqs)
+    return int(check(lib().rt_chunk_finish(t, int(ip.size - 1), _ptr(ip), _ptr(rq), rq.size, _ptr(done), _ptr(held),
+                                           int(head))))
 
 
 RT_ORDERS = {"fcfs": 0, "lpm": 1}

@@ -60,6 +60,8 @@ SIGNATURES = {
     "rt_finish": (C.c_int, [_p, _i32, _p, _p, _p, _i64, _p, _p, _p]),
     "rt_chunk_launch": (_i32, [_p, _i32, _p, _p, _p, _i32, _i64, _p, _p]),
     "rt_serve_round": (_i32, [_p, _i32, _p, _p, _p, _p, _i32, _i32, _i32, _p]),
+    "rt_chunk_prepare": (_i32, [_p, _i32, _p, _p, _p, _p, _i32, _i64, _p, _i64, _p, _p, _p, _p, _i64, _p, _p, _p]),
+    "rt_chunk_finish": (_i32, [_p, _i32, _p, _p, _i32, _p, _p, _i32]),
     "pkv_kv_scatter": (C.c_int, [_p, _p, _i32, _p, _i64, _p, _p, _i32, _i64, _i32, _i32, _p, _p, _p]),
     "pkv_append_slots": (C.c_int, [_p, _i64, _p, _p, _i32, _p]),
     "pkv_extend_plan_size": (_i64, [_p, _i32, _i32]),

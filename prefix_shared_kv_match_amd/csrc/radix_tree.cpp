@@ -768,6 +768,69 @@ int rt_release(rt_tree* t, const rt_node* nodes, int32_t n) {
   return PKV_OK;
 }
 
+int32_t rt_chunk_prepare(rt_tree* t, int32_t num_reqs, const int32_t* tokens, const int64_t* tok_indptr,
+                         int64_t* done, rt_node* held, int32_t head, int64_t budget, int32_t* req_to_token,
+                         int64_t stride, int32_t* prefix_lens, int32_t* extend_lens, int32_t* qo_indptr,
+                         int32_t* new_slots, int64_t new_cap, int32_t* out_reqs, int64_t* out_ends,
+                         int64_t* out_new) {
+  return guard([&]() -> int32_t {
+    if (!t || num_reqs < 0 || (num_reqs > 0 && (!done || !held || !out_new)))
+      return pkv::fail(PKV_ERR_INVAL, "bad arguments to rt_chunk_prepare");
+    const int32_t k = rt_chunk_launch(t, num_reqs, tokens, tok_indptr, done, head, budget, out_reqs, out_ends);
+    if (k <= 0) {
+      if (k == 0 && out_new) *out_new = 0;
+      return k;
+    }
+    // the taken requests' truncated token lists, contiguous
+    std::vector<int64_t> ip((size_t)k + 1, 0);
+    for (int32_t i = 0; i < k; ++i) ip[(size_t)i + 1] = ip[(size_t)i] + out_ends[i];
+    std::vector<int32_t> toks((size_t)ip[(size_t)k]);
+    for (int32_t i = 0; i < k; ++i)
+      std::copy(tokens + tok_indptr[out_reqs[i]], tokens + tok_indptr[out_reqs[i]] + out_ends[i],
+                toks.begin() + ip[(size_t)i]);
+    std::vector<rt_node> last((size_t)k, -1);
+    const int64_t n_new = rt_prepare_extend(t, k, toks.data(), ip.data(), req_to_token, stride, prefix_lens,
+                                            extend_lens, qo_indptr, new_slots, new_cap, last.data());
+    if (n_new < 0) {
+      rt_release(t, last.data(), k);   // the requests prepared before the failure
+      return (int32_t)n_new;
+    }
+    // the previous chunk's lock is held until its continuation is prepared
+    for (int32_t i = 0; i < k; ++i) {
+      const int32_t r = out_reqs[i];
+      if (held[r] >= 0) {
+        const int rc = t->dec_lock(held[r]);
+        if (rc < 0) return rc;
+      }
+      held[r] = last[(size_t)i];
+      done[r] = out_ends[i];
+    }
+    *out_new = n_new;
+    return k;
+  });
+}
+
+int32_t rt_chunk_finish(rt_tree* t, int32_t num_reqs, const int64_t* tok_indptr, const int32_t* reqs, int32_t n,
+                        const int64_t* done, rt_node* held, int32_t head) {
+  return guard([&]() -> int32_t {
+    if (!t || num_reqs < 0 || n < 0 || head < 0 || head > num_reqs ||
+        (num_reqs > 0 && (!tok_indptr || !done || !held)) || (n > 0 && !reqs))
+      return pkv::fail(PKV_ERR_INVAL, "bad arguments to rt_chunk_finish");
+    auto len = [&](int32_t r) { return tok_indptr[r + 1] - tok_indptr[r]; };
+    for (int32_t i = 0; i < n; ++i) {
+      const int32_t r = reqs[i];
+      if (r < 0 || r >= num_reqs) return pkv::fail(PKV_ERR_INVAL, "request %d out of range", r);
+      if (done[r] >= len(r) && held[r] >= 0) {
+        const int rc = t->dec_lock(held[r]);
+        if (rc < 0) return rc;
+        held[r] = -1;
+      }
+    }
+    while (head < num_reqs && done[head] >= len(head) && held[head] < 0) ++head;
+    return head;
+  });
+}
+
 int64_t rt_decode_step(rt_tree* t, int32_t batch, int32_t* req_to_token, int64_t stride, int32_t* seq_lens,
                        int32_t* out_slots) {
   return guard([&]() -> int64_t {

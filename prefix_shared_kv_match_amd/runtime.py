@@ -21,7 +21,7 @@ import numpy as np
 
 from . import (PKV_BF16, PKV_F32, PKV_FP8_E4M3, PKV_NO_SPLIT_PHASE, check, lib, pkv_decode_chunk,
                pkv_decode_first_split, pkv_decode_plan, pkv_decode_shared_rows, pkv_decode_workspace_bytes,
-               pkv_extend_plan, pkv_extend_tile, rt_chunk_launch, rt_create_policy, rt_dec_lock_ref, rt_decode_step,
+               pkv_extend_plan, pkv_extend_tile, rt_chunk_finish, rt_chunk_prepare, rt_create_policy, rt_decode_step,
                rt_destroy, rt_finish, rt_prepare_extend, rt_prepare_extend_prio, rt_release, rt_serve_round,
                rt_set_eviction_log)
 
@@ -500,38 +500,27 @@ def serve(tree, token_lists: Sequence[np.ndarray], after: Sequence[int], order: 
 
 
 def chunked_prefill(tree, token_lists: Sequence[np.ndarray], budget: int, stride: int, on_launch=None):
-    """Prefill one batch in launches of at most `budget` new tokens.
-
-    Requests are taken in order; the head request contributes min(remaining uncached
-    tokens, budget left), and a request cut by the budget continues in the next launch.  A
-    chunk ending at position e is prepared as the truncated token list [:e] so its match
-    reuses the earlier chunks; the end node of a request's previous chunk stays locked until
-    its next chunk is prepared.  on_launch(reqs, ends, host_batch) runs each launch's device
-    work before the finished requests are released.  Returns [(reqs, ends, host_batch)]."""
+    """Prefill one batch in launches of at most `budget` new tokens: the library cuts and
+    prepares each launch (rt_chunk_prepare: requests in order, a request cut by the budget
+    continues in the next launch, its earlier chunks reused through the tree and kept locked
+    until the continuation is prepared); on_launch(reqs, ends, host_batch) runs the launch's
+    device work; rt_chunk_finish then unlocks the requests that reached their end.
+    Returns [(reqs, ends, host_batch)]."""
     if budget < 1:
         raise ValueError("chunk budget must be positive")
     n = len(token_lists)
     toks, indptr = flatten(token_lists)
-    done = np.full(n, -1, dtype=np.int64)   # tokens prefilled of a request under way, -1 before it starts
-    held = [-1] * n
+    done = np.full(n, -1, dtype=np.int64)
+    held = np.full(n, -1, dtype=np.int64)
     out = []
     head = 0
     while head < n:
-        reqs, ends = rt_chunk_launch(tree, toks, indptr, done, head, budget)
-        reqs, ends = reqs.tolist(), ends.tolist()
-        hb = prepare(tree, [np.asarray(token_lists[i])[:e] for i, e in zip(reqs, ends)], stride)
-        for i, e, last in zip(reqs, ends, hb.last_nodes.tolist()):
-            if held[i] >= 0:
-                rt_dec_lock_ref(tree, held[i])
-            held[i] = last
-            done[i] = e
+        r2t = np.full((n - head, stride), -1, dtype=np.int32)
+        reqs, ends, pl, el, qo, new = rt_chunk_prepare(tree, toks, indptr, done, held, head, budget, r2t)
+        k = int(reqs.size)
+        hb = HostBatch(k, r2t[:k], pl, el, qo, new, held[reqs].copy(), ends.astype(np.int32))
         if on_launch is not None:
-            on_launch(reqs, ends, hb)
-        finished = [i for i in reqs if done[i] >= len(token_lists[i])]
-        rt_release(tree, [held[i] for i in finished])
-        for i in finished:
-            held[i] = -1
-        out.append((reqs, ends, hb))
-        while head < n and done[head] >= len(token_lists[head]) and held[head] < 0:
-            head += 1
+            on_launch(reqs.tolist(), ends.tolist(), hb)
+        head = rt_chunk_finish(tree, indptr, reqs, done, held, head)
+        out.append((reqs.tolist(), ends.tolist(), hb))
     return out

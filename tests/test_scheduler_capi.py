@@ -1,5 +1,5 @@
 """The library-side serve loop (rt_serve_round + rt_prepare_extend_prio) and chunked prefill
-(rt_chunk_launch + rt_prepare_extend) on the CPU: bit-exact with the oracle's scheduler (batch
+(rt_chunk_prepare + rt_chunk_finish) on the CPU: bit-exact with the oracle's scheduler (batch
 picks, slot tables, final tree, free list), and on the hand-derived serve trace."""
 import numpy as np
 import pytest
@@ -77,6 +77,66 @@ def test_chunked_prefill_matches_oracle(budget):
             assert hb.new_slots.tolist() == l.tables.new_slots
         same_tree(t, o)
         assert pkv.rt_protected_size(t) == 0
+    finally:
+        pkv.rt_destroy(t)
+
+
+def test_chunk_prepare_and_finish_hand_example():
+    """rt_chunk_prepare / rt_chunk_finish on the two-launch example: budget 4, r0 = [1..6],
+    r1 = [1, 2, 3, 9], nothing cached.  Launch 1 takes r0 to 4 and leaves r0's end node
+    locked (4 protected tokens); launch 2 continues r0 to 6 and takes r1's 1 new token after
+    its 3 cached ones, moving r0's lock to its new end node before the old one is dropped;
+    the finish unlocks both finished requests and the head passes them."""
+    t = pkv.rt_create(32)
+    try:
+        toks, indptr = runtime.flatten([np.arange(1, 7), np.array([1, 2, 3, 9])])
+        done = np.full(2, -1, dtype=np.int64)
+        held = np.full(2, -1, dtype=np.int64)
+        r2t = np.full((2, 8), -1, dtype=np.int32)
+        reqs, ends, pl, el, qo, new = pkv.rt_chunk_prepare(t, toks, indptr, done, held, 0, 4, r2t)
+        assert reqs.tolist() == [0] and ends.tolist() == [4]
+        assert pl.tolist() == [0] and el.tolist() == [4] and qo.tolist() == [0, 4] and new.size == 4
+        assert done.tolist() == [4, -1] and held[0] >= 0 and held[1] == -1
+        first_rows = r2t[0, :4].copy()
+        assert pkv.rt_protected_size(t) == 4
+        assert pkv.rt_chunk_finish(t, indptr, reqs, done, held, 0) == 0      # r0 not finished: still held
+        assert pkv.rt_protected_size(t) == 4
+        old = int(held[0])
+        r2t[:] = -1
+        reqs, ends, pl, el, qo, new = pkv.rt_chunk_prepare(t, toks, indptr, done, held, 0, 4, r2t)
+        assert reqs.tolist() == [0, 1] and ends.tolist() == [6, 4]
+        assert pl.tolist() == [4, 3] and el.tolist() == [2, 1] and qo.tolist() == [0, 2, 3]
+        assert r2t[0, :4].tolist() == first_rows.tolist() and r2t[1, :3].tolist() == first_rows[:3].tolist()
+        assert held[0] != old and done.tolist() == [6, 4]
+        # lock_ref per node key: r0's path [1,2,3]-[4]-[5,6] and r1's [1,2,3]-[9] hold one
+        # lock each; a first-chunk lock left behind would put 3 on [1,2,3] and 2 on [4]
+        locks = {key: lock for _, _, lock, _, key, _ in pkv.rt_dump(t)}
+        assert locks == {(1, 2, 3): 2, (4,): 1, (5, 6): 1, (9,): 1}
+        assert pkv.rt_chunk_finish(t, indptr, reqs, done, held, 0) == 2
+        assert held.tolist() == [-1, -1] and pkv.rt_protected_size(t) == 0
+        assert pkv.rt_evictable_size(t) == 7
+        with pytest.raises(pkv.PkvError):
+            pkv.rt_chunk_finish(t, indptr, np.array([2], dtype=np.int32), done, held, 0)   # no request 2
+    finally:
+        pkv.rt_destroy(t)
+
+
+def test_chunk_prepare_failure_leaves_state():
+    """A launch whose prepare runs out of slots fails, leaves done / held as they were and
+    leaves no lock behind: a 6-slot pool, r0 = 4 tokens held from a first launch, then a
+    launch needing 4 more tokens (2 for r0, 2 for a new r1) while only 2 slots are free."""
+    t = pkv.rt_create(6)
+    try:
+        toks, indptr = runtime.flatten([np.arange(1, 7), np.array([7, 8])])
+        done = np.full(2, -1, dtype=np.int64)
+        held = np.full(2, -1, dtype=np.int64)
+        r2t = np.full((2, 8), -1, dtype=np.int32)
+        pkv.rt_chunk_prepare(t, toks, indptr, done, held, 0, 4, r2t)
+        state = (done.copy(), held.copy())
+        with pytest.raises(pkv.PkvError):
+            pkv.rt_chunk_prepare(t, toks, indptr, done, held, 0, 8, r2t)
+        assert done.tolist() == state[0].tolist() and held.tolist() == state[1].tolist()
+        assert pkv.rt_protected_size(t) == 4        # only r0's first chunk, as before the call
     finally:
         pkv.rt_destroy(t)
 
