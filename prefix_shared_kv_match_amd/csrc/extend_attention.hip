@@ -197,7 +197,8 @@ constexpr float kRescaleSlack = 8.f;
 // A tile is processed in two halves that the tile loop places in different iterations:
 //   probs(S) -> P (exponentials, conversions, row sums), then qk(next tile) into the same S
 //   registers block by block (each block's products start once its exponentials are done),
-//   pv(P) (MFMA) beside later_max(next S) (vector max, rarely a rescale),
+//   pv(P) (MFMA) beside the lane maxima of the next S (vector max; the rare rescale, which
+//   must follow the products, comes after them),
 // so each wave always has independent vector and matrix work to interleave.
 template <int G>
 struct WaveAttn {
@@ -318,18 +319,17 @@ struct WaveAttn {
   }
 
   // this lane's max over its 16 raw values of each row, in log2 units relative to the
-  // reference max (a linear chain of three-input maxes, then one fused multiply-add)
+  // reference max (three-input maxes in a shallow tree, then one fused multiply-add)
   __device__ __forceinline__ void lane_max(const floatx4 (&s)[4][2], float (&mt)[2]) const {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      float x = fmaxf(fmaxf(s[0][nb][0], s[0][nb][1]), s[0][nb][2]);
-      x = fmaxf(fmaxf(x, s[0][nb][3]), s[1][nb][0]);
-      x = fmaxf(fmaxf(x, s[1][nb][1]), s[1][nb][2]);
-      x = fmaxf(fmaxf(x, s[1][nb][3]), s[2][nb][0]);
-      x = fmaxf(fmaxf(x, s[2][nb][1]), s[2][nb][2]);
-      x = fmaxf(fmaxf(x, s[2][nb][3]), s[3][nb][0]);
-      x = fmaxf(fmaxf(x, s[3][nb][1]), s[3][nb][2]);
-      mt[nb] = fmaf(fmaxf(x, s[3][nb][3]), sc, -m[nb]);
+      const float a = fmaxf(fmaxf(s[0][nb][0], s[0][nb][1]), s[0][nb][2]);
+      const float b = fmaxf(fmaxf(s[0][nb][3], s[1][nb][0]), s[1][nb][1]);
+      const float c = fmaxf(fmaxf(s[1][nb][2], s[1][nb][3]), s[2][nb][0]);
+      const float d = fmaxf(fmaxf(s[2][nb][1], s[2][nb][2]), s[2][nb][3]);
+      const float e = fmaxf(fmaxf(s[3][nb][0], s[3][nb][1]), s[3][nb][2]);
+      const float x = fmaxf(fmaxf(fmaxf(a, b), c), fmaxf(fmaxf(d, e), s[3][nb][3]));
+      mt[nb] = fmaf(x, sc, -m[nb]);
     }
   }
 
@@ -357,11 +357,10 @@ struct WaveAttn {
     for (int nb = 0; nb < 2; ++nb) m[nb] = row_max(mt[nb]);
   }
 
-  // later tiles: only where some lane's value exceeds the reference by more than the slack
-  // (one wave-uniform test, rare after the first tile) is the row max formed and the row moved
-  __device__ __forceinline__ void later_max(const floatx4 (&s)[4][2]) {
-    float mt[2];
-    lane_max(s, mt);
+  // later tiles, from the lane maxima: only where some lane's value exceeds the reference by
+  // more than the slack (one wave-uniform test, rare after the first tile) is the row max
+  // formed and the row moved
+  __device__ __forceinline__ void later_shift(const float (&mt)[2]) {
     if (__any(mt[0] > kRescaleSlack || mt[1] > kRescaleSlack)) {
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
@@ -392,10 +391,12 @@ struct WaveAttn {
 
   // O^T += V^T . P^T, and the row sums; vop(kk, db) returns the V^T operand (d = 16 db + ln,
   // tokens 32 kk + 8 lg .. +7) read from LDS.  Issued at raised wave priority: on a SIMD
-  // shared with a wave in its vector work, the products go first.
-  template <class VOp>
-  __device__ __forceinline__ void pv(const bf16x8 (&pf)[2][2], VOp vop) {
+  // shared with a wave in its vector work, the products go first.  pre() runs in the same
+  // region, so its vector work (independent of the products) can fill their gaps.
+  template <class VOp, class Pre>
+  __device__ __forceinline__ void pv(const bf16x8 (&pf)[2][2], VOp vop, Pre pre) {
     __builtin_amdgcn_s_setprio(1);
+    pre();
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
@@ -486,9 +487,12 @@ __device__ __forceinline__ void tile_loop(WaveAttn<G>& wa, Stage& st, int kv_beg
       wa.probs(s, pf);
       wa.qk(s, [&](int mb, int ks) { return kop(kr, mb, ks); });
       __builtin_amdgcn_sched_barrier(0);   // keep the PV operand reads out of the S^T half
-      wa.pv(pf, [&](int kk, int db) { return vop(vr, kk, db); });
-      if constexpr (decltype(mask_next)::value) wa.mask(s, kv_begin + (t + 1) * kBN);
-      wa.later_max(s);
+      float mt[2];
+      wa.pv(pf, [&](int kk, int db) { return vop(vr, kk, db); }, [&]() {
+        if constexpr (decltype(mask_next)::value) wa.mask(s, kv_begin + (t + 1) * kBN);
+        wa.lane_max(s, mt);
+      });
+      wa.later_shift(mt);
     }
     st.finish();
     __syncthreads();
