@@ -806,7 +806,7 @@ def main():
         uniq = float(np.unique(np.concatenate([hb.req_to_token[i, :hb.seq_lens[i]] for i in range(hb.n)])).size)
         hbm = traffic_bytes(wl.name, "decode_attention")
         kernels["decode_attention"] = {
-            "ms": dec_ms,
+            "ms": dec_ms, "chunk": int(getattr(b, "chunk", 0)),
             "gathered_bytes": dec_bytes, "effective_gbps": dec_bytes / dec_ms / 1e6,
             "unique_kv_bytes": uniq * kv_tok, "unique_gbps": uniq * kv_tok / dec_ms / 1e6,
             "frac_hbm_unique": uniq * kv_tok / dec_ms / 1e6 / PEAK_HBM_GBPS,
