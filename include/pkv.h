@@ -244,29 +244,6 @@ int rt_finish(rt_tree* t, int32_t n, const int32_t* tokens, const int64_t* tok_i
               const int32_t* req_to_token, int64_t stride, const int32_t* prompt_lens,
               const rt_node* prompt_last, rt_node* out_end);
 
-/* One launch of chunked prefill from cut to host tables [the deployment-tuning page's
- * chunked-prefill option; the radix tree's prefix match lets a request's next chunk reuse its
- * earlier ones: RC "프리픽스 매칭"]: the requests rt_chunk_launch takes from `head` (at most
- * `budget` new tokens), prepared with rt_prepare_extend as their truncated token lists
- * [0, end_r), in order; then for each taken request r the end node of its previous chunk
- * (held[r] >= 0) is unlocked and held[r] = the new chunk's end node, done[r] = end_r.
- * done and held [num_reqs] are caller-owned state carried across launches, both -1 before
- * the first.  Outputs: out_reqs / out_ends (capacity num_reqs - head), the extend tables as
- * rt_prepare_extend writes them for the taken requests in order (new_cap >= the sum of their
- * ends), *out_new = the new tokens.  Returns the number of requests taken (0 when none is
- * left); a negative error (a failed prepare leaves done / held unchanged and unlocks what it
- * prepared). */
-int32_t rt_chunk_prepare(rt_tree* t, int32_t num_reqs, const int32_t* tokens, const int64_t* tok_indptr,
-                         int64_t* done, rt_node* held, int32_t head, int64_t budget, int32_t* req_to_token,
-                         int64_t stride, int32_t* prefix_lens, int32_t* extend_lens, int32_t* qo_indptr,
-                         int32_t* new_slots, int64_t new_cap, int32_t* out_reqs, int64_t* out_ends,
-                         int64_t* out_new);
-/* After a chunked-prefill launch's kernels: the taken requests reqs[0..n) that reached their
- * end (done[r] >= their length) have their end node unlocked and held[r] = -1.  Returns the
- * new head: the first request from `head` on that is not finished (num_reqs when all are). */
-int32_t rt_chunk_finish(rt_tree* t, int32_t num_reqs, const int64_t* tok_indptr, const int32_t* reqs, int32_t n,
-                        const int64_t* done, rt_node* held, int32_t head);
-
 /* One round of the serve loop [OV and EX: cache-aware scheduling, waiting requests served
  * longest cached prefix first rather than first come first served].  Requests
  * tokens[tok_indptr[r] .. tok_indptr[r+1]), r < num_reqs, arrive in index order; after[r] is
@@ -297,6 +274,29 @@ int32_t rt_serve_round(const rt_tree* t, int32_t num_reqs, const int32_t* tokens
  * PKV_ERR_INVAL on bad arguments. */
 int32_t rt_chunk_launch(const rt_tree* t, int32_t num_reqs, const int32_t* tokens, const int64_t* tok_indptr,
                         const int64_t* done, int32_t head, int64_t budget, int32_t* out_reqs, int64_t* out_ends);
+
+/* One launch of chunked prefill from cut to host tables [the deployment-tuning page's
+ * chunked-prefill option; the radix tree's prefix match lets a request's next chunk reuse its
+ * earlier ones: RC "프리픽스 매칭"]: the requests rt_chunk_launch takes from `head` (at most
+ * `budget` new tokens), prepared with rt_prepare_extend as their truncated token lists
+ * [0, end_r), in order; then for each taken request r the end node of its previous chunk
+ * (held[r] >= 0) is unlocked and held[r] = the new chunk's end node, done[r] = end_r.
+ * done and held [num_reqs] are caller-owned state carried across launches, both -1 before
+ * the first.  Outputs: out_reqs / out_ends (capacity num_reqs - head), the extend tables as
+ * rt_prepare_extend writes them for the taken requests in order (new_cap >= the sum of their
+ * ends), *out_new = the new tokens.  Returns the number of requests taken (0 when none is
+ * left); a negative error (a failed prepare leaves done / held unchanged and unlocks what it
+ * prepared). */
+int32_t rt_chunk_prepare(rt_tree* t, int32_t num_reqs, const int32_t* tokens, const int64_t* tok_indptr,
+                         int64_t* done, rt_node* held, int32_t head, int64_t budget, int32_t* req_to_token,
+                         int64_t stride, int32_t* prefix_lens, int32_t* extend_lens, int32_t* qo_indptr,
+                         int32_t* new_slots, int64_t new_cap, int32_t* out_reqs, int64_t* out_ends,
+                         int64_t* out_new);
+/* After a chunked-prefill launch's kernels: the taken requests reqs[0..n) that reached their
+ * end (done[r] >= their length) have their end node unlocked and held[r] = -1.  Returns the
+ * new head: the first request from `head` on that is not finished (num_reqs when all are). */
+int32_t rt_chunk_finish(rt_tree* t, int32_t num_reqs, const int64_t* tok_indptr, const int32_t* reqs, int32_t n,
+                        const int64_t* done, rt_node* held, int32_t head);
 
 /* ----------------------------------------------------------------------------------
  * Kernels (device)
