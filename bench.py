@@ -52,14 +52,14 @@ CSRC = os.path.join(ROOT, "prefix_shared_kv_match_amd", "csrc")
 # plain 1 GiB device copy (FETCH x2.0, WRITE x1.0).  Each entry holds the hash of the kernel
 # sources it was taken on; a changed kernel reports null.
 TRAFFIC = {
-    ("fewshot_bf16", "extend_attention"): dict(src_hash="683ee100878f8c0c", fetch_kib=208313.1, write_kib=102968.2),
-    ("fewshot_bf16", "decode_attention"): dict(src_hash="66fa8ae53f04b6c2", fetch_kib=30303.1 + 4291.0,
-                                               write_kib=8495.1 + 512.0),
-    ("decode_bf16", "decode_attention"): dict(src_hash="66fa8ae53f04b6c2", fetch_kib=4215473.3 + 35235.7 + 23299.0,
-                                              write_kib=39169.5 + 8704.0 + 4096.0),
-    ("longctx_fp8", "extend_attention"): dict(src_hash="683ee100878f8c0c", fetch_kib=1471211.1, write_kib=319488.0),
-    ("longctx_fp8", "decode_attention"): dict(src_hash="66fa8ae53f04b6c2", fetch_kib=50975.9 + 9307.0,
-                                              write_kib=18548.4 + 256.0),
+    ("fewshot_bf16", "extend_attention"): dict(src_hash="fdaee6d5e67079b5", fetch_kib=205002.8, write_kib=102975.3),
+    ("fewshot_bf16", "decode_attention"): dict(src_hash="78117e06109569ec", fetch_kib=30293.5 + 4291.0,
+                                               write_kib=8494.2 + 512.0),
+    ("decode_bf16", "decode_attention"): dict(src_hash="78117e06109569ec", fetch_kib=4215458.8 + 35224.7 + 23298.8,
+                                              write_kib=39169.9 + 8704.0 + 4096.0),
+    ("longctx_fp8", "extend_attention"): dict(src_hash="fdaee6d5e67079b5", fetch_kib=1471781.2, write_kib=319488.0),
+    ("longctx_fp8", "decode_attention"): dict(src_hash="78117e06109569ec", fetch_kib=50994.1 + 9307.0,
+                                              write_kib=18551.6 + 256.0),
 }
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 # (warmup, timed) steps when not given: a few hundred ms of warmup for sub-millisecond steps,

@@ -464,6 +464,9 @@ struct WaveAttn {
 // unrolling (so the compiler can tell the buffers apart), then the rest with the mask; the
 // step after the last tile multiplies a tile past the context that the mask hides entirely.
 // Stage must provide:
+//   kMaxBesidePV       whether the next tile's lane maxima are formed beside the PV products
+//                      (the register-staged fp8 path keeps them after: beside the products they
+//                      push its register count past the limit)
 //   prologue()         tiles K(0), V(0), K(1) staged and visible, then nothing in flight
 //   issue(t, kd, vd)   start staging K(t + 2) into kd and V(t + 1) into vd
 //   finish()           this thread's staging of iteration t complete (before the barrier)
@@ -488,10 +491,16 @@ __device__ __forceinline__ void tile_loop(WaveAttn<G>& wa, Stage& st, int kv_beg
       wa.qk(s, [&](int mb, int ks) { return kop(kr, mb, ks); });
       __builtin_amdgcn_sched_barrier(0);   // keep the PV operand reads out of the S^T half
       float mt[2];
-      wa.pv(pf, [&](int kk, int db) { return vop(vr, kk, db); }, [&]() {
+      if constexpr (Stage::kMaxBesidePV) {
+        wa.pv(pf, [&](int kk, int db) { return vop(vr, kk, db); }, [&]() {
+          if constexpr (decltype(mask_next)::value) wa.mask(s, kv_begin + (t + 1) * kBN);
+          wa.lane_max(s, mt);
+        });
+      } else {
+        wa.pv(pf, [&](int kk, int db) { return vop(vr, kk, db); }, [] {});
         if constexpr (decltype(mask_next)::value) wa.mask(s, kv_begin + (t + 1) * kBN);
         wa.lane_max(s, mt);
-      });
+      }
       wa.later_shift(mt);
     }
     st.finish();
@@ -597,6 +606,7 @@ constexpr int64_t kNarrowPoolBytes = (int64_t)1 << 31;
 // or past the last one are staged as the last one (into buffers nobody reads after).
 template <bool NARROW>
 struct DmaStage {
+  static constexpr bool kMaxBesidePV = true;
   const PoolGather<NARROW>& gather;
   __amdgpu_buffer_rsrc_t tab;
   int row_bytes, kv_begin, last, tok0, wave;
@@ -743,6 +753,7 @@ __device__ __forceinline__ u32x2 dec4(uint32_t c) {
 // tile ahead.  Tokens at or past the context read whatever slot the table holds there (or
 // zero past the table's end), rows past the pool the last slot; they are masked later.
 struct Fp8Stage {
+  static constexpr bool kMaxBesidePV = false;
   __amdgpu_buffer_rsrc_t tab;
   const uint8_t *kc, *vc;    // pool + this thread's byte column of kv head g
   uint32_t slot_bytes, max_slot;
