@@ -3,11 +3,12 @@
 picks, slot tables, final tree, free list), and on the hand-derived serve trace."""
 import numpy as np
 import pytest
+from hypothesis import given, settings, strategies as st
 
 import prefix_shared_kv_match_amd as pkv
 from prefix_shared_kv_match_amd import runtime
 from oracle import driver, scheduler
-from oracle.radix_tree import OracleTree
+from oracle.radix_tree import OOMError, OracleTree
 
 
 def same_tree(t, o):
@@ -70,6 +71,38 @@ def test_chunked_prefill_matches_oracle(budget):
             pkv.rt_release(t, runtime.prepare(t, [r.tokens], 256).last_nodes)
         ls = scheduler.chunked_prefill(o, [x.tolist() for x in reqs], budget)
         got = runtime.chunked_prefill(t, reqs, budget, 256)
+        assert [(r_, e_) for r_, e_, _ in got] == [(l.reqs, l.ends) for l in ls]
+        for (_, _, hb), l in zip(got, ls):
+            assert hb.prefix_lens.tolist() == l.tables.prefix_lens
+            assert hb.extend_lens.tolist() == l.tables.extend_lens
+            assert hb.new_slots.tolist() == l.tables.new_slots
+        same_tree(t, o)
+        assert pkv.rt_protected_size(t) == 0
+    finally:
+        pkv.rt_destroy(t)
+
+
+@settings(max_examples=120, deadline=None)
+@given(st.lists(st.lists(st.integers(0, 2), min_size=1, max_size=12), min_size=1, max_size=6),
+       st.integers(1, 20), st.lists(st.integers(0, 2), max_size=8), st.integers(12, 60))
+def test_chunked_prefill_random_matches_oracle(reqs, budget, cached, slots):
+    """Random small batches (vocab 3, so requests share and split nodes), a random cached
+    prefix, budgets from one token up and pools small enough that launches evict: the
+    library's launches (rt_chunk_prepare / rt_chunk_finish) equal the oracle's, launch for
+    launch (cut, prefix and extend lengths, new slots), and the final trees match."""
+    o = OracleTree(slots)
+    t = pkv.rt_create(slots)
+    try:
+        if cached:
+            driver.release(o, driver.prepare_batch(o, [cached]).last_nodes)
+            pkv.rt_release(t, runtime.prepare(t, [np.array(cached)], 16).last_nodes)
+        try:
+            ls = scheduler.chunked_prefill(o, reqs, budget)
+        except OOMError:   # both sides run out of slots (in the same launch)
+            with pytest.raises(pkv.PkvError):
+                runtime.chunked_prefill(t, [np.array(r) for r in reqs], budget, 16)
+            return
+        got = runtime.chunked_prefill(t, [np.array(r) for r in reqs], budget, 16)
         assert [(r_, e_) for r_, e_, _ in got] == [(l.reqs, l.ends) for l in ls]
         for (_, _, hb), l in zip(got, ls):
             assert hb.prefix_lens.tolist() == l.tables.prefix_lens
